@@ -1,0 +1,340 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: the pages'
+worked examples (tests/golden, each file cites its page and section),
+textbook values, closed forms, finite differences and brute-force loops.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Worked examples printed on the pages (exact).
+# ---------------------------------------------------------------------------
+
+def test_v1_column_and_row_split_of_2x2():
+    g = _golden("v1_block_2x2.json")
+    X, A = np.array(g["X"], float), np.array(g["A"], float)
+    t = 2
+    for i in range(t):
+        cs = oracle.column_slice(2, t, i)
+        Y, pre = oracle.column_fwd(X, A[:, cs])
+        assert pre is None
+        assert np.array_equal(Y, np.array(g["column_t2"]["shard_outputs"][i], float))
+    parts = []
+    for i in range(t):
+        rs = oracle.row_slice(2, t, i)
+        Z = oracle.row_fwd(X[:, rs], A[rs, :])
+        assert np.array_equal(Z, np.array(g["row_t2"]["shard_partials"][i], float))
+        parts.append(Z)
+    assert np.array_equal(oracle.sum_partials(parts), np.array(g["row_t2"]["sum"], float))
+    assert np.array_equal(oracle.sum_partials(parts), np.array(g["XA"], float))
+
+
+def test_v2_column_t3_forward_backward():
+    g = _golden("v2_column_t3.json")
+    X, W, dY = (np.array(g[k], float) for k in ("X", "W", "dY"))
+    t = g["t"]
+    dx_parts = []
+    for i in range(t):
+        cs = oracle.column_slice(3, t, i)
+        Y, _ = oracle.column_fwd(X, W[:, cs])
+        assert np.array_equal(Y, np.array(g["Y_shards"][i], float))
+        dXp, dA, dA2, db, db2 = oracle.column_bwd(dY[:, cs], X, W[:, cs])
+        assert dA2 is None and db2 is None
+        assert np.array_equal(dA, np.array(g["dW_shards"][i], float))
+        assert np.array_equal(dXp, np.array(g["dX_parts"][i], float))
+        assert np.array_equal(db, dY[0, cs])
+        dx_parts.append(dXp)
+    assert np.array_equal(oracle.sum_partials(dx_parts), np.array(g["dX"], float))
+
+
+def test_v3_activation_never_acts_on_partials():
+    g = _golden("v3_relu_partials.json")
+    p = [np.array([[v]], float) for v in g["partials"]]
+    relu = lambda x: np.maximum(x, 0.0)  # the page's own example activation
+    assert oracle.sum_partials(p)[0, 0] == 1.0
+    assert relu(oracle.sum_partials(p))[0, 0] == g["relu_of_sum"]
+    assert oracle.sum_partials([relu(q) for q in p])[0, 0] == g["sum_of_relu"]
+    # The same failure with the activations this library fuses.
+    assert oracle.gelu(oracle.sum_partials(p))[0, 0] != pytest.approx(
+        oracle.sum_partials([oracle.gelu(q) for q in p])[0, 0], rel=1e-3)
+    # And the right order (column -> act -> row -> sum) equals the unsharded MLP.
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((5, 6))
+    A = rng.standard_normal((6, 8))
+    B = rng.standard_normal((8, 6))
+    full = oracle.gelu(X @ A) @ B
+    parts = []
+    for i in range(2):
+        cs = oracle.column_slice(8, 2, i)
+        Y, _ = oracle.column_fwd(X, A[:, cs], act="gelu")
+        parts.append(oracle.row_fwd(Y, B[cs, :]))
+    np.testing.assert_allclose(oracle.sum_partials(parts), full, rtol=1e-12, atol=1e-12)
+
+
+def test_v4_fig2_two_gpu_allreduce_result():
+    g = _golden("v4_fig2_allreduce.json")
+    parts = [np.array([v], float) for v in g["gpu_inputs"]]
+    Z = oracle.sum_partials(parts)
+    assert np.array_equal(Z, np.array([g["all_gather"][0]], float))
+    assert Z[0, 0] == g["reduce_scatter"]["gpu0_first_half"]
+    assert Z[0, 1] == g["reduce_scatter"]["gpu1_second_half"]
+
+
+def test_v5_row_bias_added_once():
+    # Page 'v4: Tensor Parallel and Sequence Parallel', section 'Self-test':
+    # the row bias is not split; adding it on every card adds it t times.
+    g = _golden("v1_block_2x2.json")
+    parts = [np.array(p, float) for p in g["row_t2"]["shard_partials"]]
+    b = np.array([10.0, 20.0])
+    assert np.array_equal(oracle.sum_partials(parts, bias=b), np.array([[17.0, 30.0]]))
+    wrong = oracle.sum_partials([p + b for p in parts])
+    assert np.array_equal(wrong, oracle.sum_partials(parts, bias=b) + (len(parts) - 1) * b)
+
+
+# ---------------------------------------------------------------------------
+# Activations: textbook values, closed forms, finite differences.
+# ---------------------------------------------------------------------------
+
+# Standard normal CDF from tables: Phi(1), Phi(2), Phi(-1); logistic(1) = e/(1+e).
+PHI1 = 0.8413447460685429
+PHI2 = 0.9772498680518208
+PHIM1 = 0.15865525393145707
+SIG1 = 0.7310585786300049
+
+
+def test_gelu_textbook_values():
+    x = np.array([0.0, 1.0, -1.0, 2.0])
+    np.testing.assert_allclose(oracle.gelu(x), [0.0, PHI1, -PHIM1, 2 * PHI2], rtol=1e-15, atol=0)
+    # GeLU'(0) = Phi(0) = 1/2 ; GeLU'(1) = Phi(1) + phi(1)
+    phi1 = math.exp(-0.5) / math.sqrt(2 * math.pi)
+    np.testing.assert_allclose(oracle.gelu_grad(np.array([0.0, 1.0])), [0.5, PHI1 + phi1], rtol=1e-15)
+
+
+def test_silu_textbook_values():
+    x = np.array([0.0, 1.0, -1.0, 40.0, -40.0])
+    np.testing.assert_allclose(oracle.sigmoid(x[:3]), [0.5, SIG1, 1 - SIG1], rtol=1e-15)
+    np.testing.assert_allclose(oracle.silu(x[:3]), [0.0, SIG1, -(1 - SIG1)], rtol=1e-15, atol=0)
+    # silu'(0) = 1/2; large |x| limits without overflow
+    assert oracle.silu_grad(np.array([0.0]))[0] == 0.5
+    np.testing.assert_allclose(oracle.silu(x[3:]), [40.0, -40.0 * math.exp(-40.0) / (1 + math.exp(-40.0))],
+                               rtol=1e-13)
+
+
+def test_activation_odd_part_identities():
+    x = np.linspace(-6, 6, 121)
+    np.testing.assert_allclose(oracle.gelu(x) - oracle.gelu(-x), x, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(oracle.silu(x) - oracle.silu(-x), x, rtol=0, atol=1e-14)
+
+
+def test_activation_grads_by_central_differences():
+    x = np.linspace(-5, 5, 101) + 0.0137
+    h = 1e-5
+    for f, df in ((oracle.gelu, oracle.gelu_grad), (oracle.silu, oracle.silu_grad)):
+        fd = (f(x + h) - f(x - h)) / (2 * h)
+        np.testing.assert_allclose(df(x), fd, rtol=0, atol=1e-9)
+
+
+def test_activations_match_torch_cpu_fp64():
+    torch = pytest.importorskip("torch")
+    x = np.linspace(-8, 8, 1001)
+    tx = torch.from_numpy(x)
+    np.testing.assert_allclose(oracle.gelu(x), torch.nn.functional.gelu(tx, approximate="none").numpy(),
+                               rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(oracle.silu(x), torch.nn.functional.silu(tx).numpy(), rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# GEMM building blocks against pure-Python loops (tiny shapes).
+# ---------------------------------------------------------------------------
+
+def _loop_mm(a, b):
+    m, k = len(a), len(a[0])
+    n = len(b[0])
+    return [[sum(a[i][p] * b[p][j] for p in range(k)) for j in range(n)] for i in range(m)]
+
+
+def _T(a):
+    return [list(r) for r in zip(*a)]
+
+
+def test_gemms_against_python_loops():
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((3, 5))
+    A = rng.standard_normal((5, 4))
+    dY = rng.standard_normal((3, 4))
+    Xl, Al, dYl = X.tolist(), A.tolist(), dY.tolist()
+    np.testing.assert_allclose(oracle.row_fwd(X, A), _loop_mm(Xl, Al), rtol=1e-13)
+    Y, _ = oracle.column_fwd(X, A)
+    np.testing.assert_allclose(Y, _loop_mm(Xl, Al), rtol=1e-13)
+    np.testing.assert_allclose(oracle.dgrad(dY, A), _loop_mm(dYl, _T(Al)), rtol=1e-13)
+    np.testing.assert_allclose(oracle.wgrad(X, dY), _loop_mm(_T(Xl), dYl), rtol=1e-13)
+    # bias goes inside the linear, before the activation
+    b = rng.standard_normal(4)
+    Yg, P = oracle.column_fwd(X, A, act="gelu", bias=b)
+    loop = _loop_mm(Xl, Al)
+    for i in range(3):
+        for j in range(4):
+            p = loop[i][j] + b[j]
+            assert P[i, j] == pytest.approx(p, rel=1e-13)
+            assert Yg[i, j] == pytest.approx(0.5 * p * (1 + math.erf(p / math.sqrt(2))), rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Block-matrix invariants over shard counts, activations and bias.
+# ---------------------------------------------------------------------------
+
+def _mlp_full(X, A, A2, ba, ba2, B, bB, act):
+    Y, _ = oracle.column_fwd(X, A, act=act, bias=ba, A2=A2, bias2=ba2)
+    Z = Y @ B
+    return Z + bB[None, :] if bB is not None else Z
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("act", ["none", "gelu", "swiglu"])
+@pytest.mark.parametrize("bias", [False, True])
+def test_sharded_mlp_equals_unsharded(t, act, bias):
+    rng = np.random.default_rng(100 * t + len(act) + bias)
+    M, H, F = 7, 6, 24
+    X = rng.standard_normal((M, H))
+    A = rng.standard_normal((H, F)) * 0.5
+    A2 = rng.standard_normal((H, F)) * 0.5 if act == "swiglu" else None
+    B = rng.standard_normal((F, H)) * 0.5
+    ba = rng.standard_normal(F) if bias else None
+    ba2 = rng.standard_normal(F) if (bias and act == "swiglu") else None
+    bB = rng.standard_normal(H) if bias else None
+    dZ = rng.standard_normal((M, H))
+
+    Yfull, _ = oracle.column_fwd(X, A, act=act, bias=ba, A2=A2, bias2=ba2)
+    zparts, dxparts, dAs, dA2s, dbs, dBs = [], [], [], [], [], []
+    for i in range(t):
+        cs = oracle.column_slice(F, t, i)
+        Y, Pre = oracle.column_fwd(X, A[:, cs], act=act, bias=None if ba is None else ba[cs],
+                                   A2=None if A2 is None else A2[:, cs],
+                                   bias2=None if ba2 is None else ba2[cs])
+        np.testing.assert_allclose(Y, Yfull[:, cs], rtol=1e-12, atol=1e-12)
+        zparts.append(oracle.row_fwd(Y, B[cs, :]))
+        dY, dBi, dbrow = oracle.row_bwd(dZ, Y, B[cs, :])
+        dBs.append(dBi)
+        np.testing.assert_allclose(dbrow, dZ.sum(axis=0), rtol=1e-12)
+        dXp, dA, dA2, db, db2 = oracle.column_bwd(dY, X, A[:, cs], Pre, act, None if A2 is None else A2[:, cs])
+        dxparts.append(dXp)
+        dAs.append(dA)
+        dA2s.append(dA2)
+        dbs.append(db)
+    Z = oracle.sum_partials(zparts, bias=bB)
+    np.testing.assert_allclose(Z, _mlp_full(X, A, A2, ba, ba2, B, bB, act), rtol=1e-11, atol=1e-11)
+
+    # Unsharded backward via finite differences of L = <dZ, Z>.
+    def loss(Xv=X, Av=A, A2v=A2, Bv=B):
+        return float((dZ * _mlp_full(Xv, Av, A2v, ba, ba2, Bv, bB, act)).sum())
+
+    dX = oracle.sum_partials(dxparts)
+    h = 1e-6
+    for (idx, arr, grad, key) in [((2, 3), X, dX, "Xv"),
+                                  ((1, 5), A, np.concatenate(dAs, axis=1), "Av"),
+                                  ((4, 2), B, np.concatenate(dBs, axis=0), "Bv")]:
+        ap, am = arr.copy(), arr.copy()
+        ap[idx] += h
+        am[idx] -= h
+        fd = (loss(**{key: ap}) - loss(**{key: am})) / (2 * h)
+        assert grad[idx] == pytest.approx(fd, rel=1e-6, abs=1e-7)
+    if act == "swiglu":
+        ap, am = A2.copy(), A2.copy()
+        ap[3, 7] += h
+        am[3, 7] -= h
+        fd = (loss(A2v=ap) - loss(A2v=am)) / (2 * h)
+        assert np.concatenate(dA2s, axis=1)[3, 7] == pytest.approx(fd, rel=1e-6, abs=1e-7)
+    if bias:
+        # column bias gradient: d/db_a of L = sum over tokens of dP
+        db = np.concatenate(dbs)
+        bp, bm = ba.copy(), ba.copy()
+        bp[5] += h
+        bm[5] -= h
+        fd = (float((dZ * _mlp_full(X, A, A2, bp, ba2, B, bB, act)).sum())
+              - float((dZ * _mlp_full(X, A, A2, bm, ba2, B, bB, act)).sum())) / (2 * h)
+        assert db[5] == pytest.approx(fd, rel=1e-6, abs=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# Vocab-parallel cross-entropy partials.
+# ---------------------------------------------------------------------------
+
+def test_ce_hand_example_ln6():
+    # logits [0, ln 2, ln 3]: lse = ln 6; shard 0 owns id 0, shard 1 owns ids 1-2.
+    H = np.array([[1.0]])
+    W = np.array([[0.0], [math.log(2)], [math.log(3)]])
+    p0 = oracle.vocab_ce_partials(H, W[0:1], np.array([1]), 0)
+    p1 = oracle.vocab_ce_partials(H, W[1:3], np.array([1]), 1)
+    assert (p0[0][0], p0[1][0], p0[2][0]) == (0.0, 1.0, 0.0)
+    assert p1[0][0] == pytest.approx(math.log(3), rel=1e-15)
+    assert p1[1][0] == pytest.approx(5.0 / 3.0, rel=1e-15)
+    assert p1[2][0] == pytest.approx(math.log(2), rel=1e-15)
+    lse, tgt, loss = oracle.lse_recombine([p0, p1])
+    assert lse[0] == pytest.approx(math.log(6), rel=1e-15)
+    assert tgt[0] == pytest.approx(math.log(2), rel=1e-15)
+    assert loss[0] == pytest.approx(math.log(3), rel=1e-14)
+
+
+def test_ce_partials_against_python_loops_and_full_vocab():
+    rng = np.random.default_rng(5)
+    M, K, V, R = 6, 5, 24, 4
+    Hm = rng.standard_normal((M, K))
+    W = rng.standard_normal((V, K))
+    target = np.array([0, 5, 6, 23, 17, 11])
+    vr = V // R
+    parts = []
+    for r in range(R):
+        m, s, tg = oracle.vocab_ce_partials(Hm, W[r * vr:(r + 1) * vr], target, r * vr)
+        for i in range(M):
+            z = [sum(Hm[i, k] * W[r * vr + j, k] for k in range(K)) for j in range(vr)]
+            mx = max(z)
+            assert m[i] == pytest.approx(mx, rel=1e-13)
+            assert s[i] == pytest.approx(sum(math.exp(v - mx) for v in z), rel=1e-13)
+            own = r * vr <= target[i] < (r + 1) * vr
+            assert tg[i] == (pytest.approx(z[target[i] - r * vr], rel=1e-13) if own else 0.0)
+        parts.append((m, s, tg))
+    lse, tgt, loss = oracle.lse_recombine(parts)
+    for i in range(M):
+        z = [sum(Hm[i, k] * W[j, k] for k in range(K)) for j in range(V)]
+        mx = max(z)
+        ref = mx + math.log(sum(math.exp(v - mx) for v in z))
+        assert lse[i] == pytest.approx(ref, rel=1e-13)
+        assert tgt[i] == pytest.approx(z[target[i]], rel=1e-13)
+        assert loss[i] == pytest.approx(ref - z[target[i]], rel=1e-12, abs=1e-13)
+    # single shard: lse = m + ln s
+    lse1, _, _ = oracle.lse_recombine([parts[2]])
+    np.testing.assert_allclose(lse1, parts[2][0] + np.log(parts[2][1]), rtol=1e-15)
+
+
+def test_ce_target_out_of_range_contributes_zero():
+    rng = np.random.default_rng(6)
+    Hm = rng.standard_normal((4, 3))
+    W = rng.standard_normal((5, 3))
+    _, _, tg = oracle.vocab_ce_partials(Hm, W, np.array([-1, 4, 9, 10]), 5)
+    z = Hm @ W.T
+    assert tg[0] == 0.0 and tg[1] == 0.0 and tg[3] == 0.0
+    assert tg[2] == pytest.approx(z[2, 4], rel=1e-14)
+
+
+def test_ce_large_logits_do_not_overflow():
+    Hm = np.array([[30.0], [-30.0]])
+    W = np.array([[30.0], [29.0], [-5.0]])
+    m, s, _ = oracle.vocab_ce_partials(Hm, W, np.array([0, 2]), 0)
+    assert m[0] == 900.0 and np.isfinite(s).all()
+    lse, _, _ = oracle.lse_recombine([(m, s, np.zeros(2))])
+    assert lse[0] == pytest.approx(900.0 + math.log(1 + math.exp(-30.0) + math.exp(-1050.0)), rel=1e-15)
