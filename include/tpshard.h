@@ -1,0 +1,200 @@
+/*
+ * tpshard.h -- C ABI of libtpshard: one tensor-parallel rank's share of a
+ * transformer block on one MI355X (gfx950) GPU.
+ *
+ * Sources of the operations (page titles and sections):
+ *   [TP/SP]  "v4: Tensor Parallel and Sequence Parallel"
+ *   [TPcomm] "TP communication: how many all-reduces per layer, how much data"
+ *
+ * Common conventions
+ * ------------------
+ * Layout.    Every matrix is row-major with a leading dimension `ld` counted
+ *            in elements (ld >= row width).  Weights use the math layout of
+ *            Y = X W: a column shard A_i is [K, N_i], a row shard B_i is
+ *            [K_i, N]; the LM-head shard W_r is [V_r, K] (vocab rows).
+ * Pointers.  All tensor pointers are DEVICE pointers owned by the caller.
+ *            The library never allocates, frees or keeps device memory and
+ *            has no global mutable state; calls are reentrant.
+ * Streams.   `stream` is a hipStream_t (NULL = the null stream).  Every call
+ *            validates its arguments synchronously, then only enqueues work
+ *            on `stream` and returns; the caller synchronizes.
+ * Errors.    Validation runs fully before anything is enqueued: on any error
+ *            code except TP_E_HIP nothing is launched and no output byte is
+ *            written.  A failed launch returns TP_E_HIP (outputs undefined).
+ *            A device fault surfaces at the caller's next synchronization.
+ * Shapes.    M, N, K >= 1 (int64, each < 2^31); tails of any size are masked
+ *            inside the kernels.
+ * Alignment. Every base pointer must be 16-byte aligned and every `ld` a
+ *            multiple of 8 elements for bf16 (4 for fp32), so 16-byte vector
+ *            accesses are legal.  The kernels may READ each input row up to
+ *            its width rounded up to that multiple (never past ld); values
+ *            there are ignored.  Outputs are written only inside their width.
+ * Dtypes.    TP_BF16: bf16 storage, fp32 accumulation, fp32 epilogue math,
+ *            outputs rounded to bf16 (round to nearest even).
+ *            TP_FP32: fp32 storage and accumulation.
+ *            Outputs take the input dtype except the CE outputs (fp32).
+ * Aliasing.  Outputs must not overlap inputs or each other, except where a
+ *            call states otherwise.
+ * Determinism. No atomics take part in any result: two identical calls give
+ *            bitwise identical outputs.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TP_ABI_VERSION 1
+
+#ifndef TP_API
+#define TP_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_E_NULL = 1,      /* a required pointer is NULL */
+  TP_E_SHAPE = 2,     /* a size < 1 or >= 2^31, ld < width, t < 1 */
+  TP_E_ALIGN = 3,     /* base pointer not 16-byte aligned or ld not a multiple of 8 (bf16) / 4 (fp32) */
+  TP_E_DTYPE = 4,     /* unknown dtype, or dtype not supported by this call */
+  TP_E_ACT = 5,       /* unknown activation, or activation arguments inconsistent */
+  TP_E_WORKSPACE = 6, /* workspace NULL or smaller than the matching *_workspace_bytes() */
+  TP_E_HIP = 7        /* a HIP launch failed */
+} tp_status;
+
+typedef enum { TP_FP32 = 0, TP_BF16 = 1 } tp_dtype;
+
+typedef enum {
+  TP_ACT_NONE = 0,
+  TP_ACT_GELU = 1,   /* exact GeLU: x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)) */
+  TP_ACT_SWIGLU = 2  /* silu(gate) * up, silu(x) = x * sigmoid(x) */
+} tp_act;
+
+/* Returns TP_ABI_VERSION. */
+TP_API int tp_abi_version(void);
+
+/* Static, never-NULL description of a status code (unknown codes included). */
+TP_API const char* tp_status_str(int status);
+
+/*
+ * Column-parallel shard forward.  [TP/SP] "TP math: block matrix
+ * multiplication" (X[A_1, A_2] = [X A_1, X A_2]), "Full flow: column
+ * parallel, t = 3" (f is the identity forward: the full X goes in; the column
+ * bias is split with the columns) and "MLP: column first, then row" (GeLU or
+ * SwiGLU gate x up applied locally on the shard).
+ *
+ *   P  = X A + bias                      X [M,K], A [K,N], bias [N] (nullable)
+ *   NONE   : Y = P                        (Pre unused, may be NULL)
+ *   GELU   : Y = GeLU(P),  Pre = P        Pre [M,N]
+ *   SWIGLU : U = X A2 + bias2,  Y = silu(P) * U,
+ *            Pre = [P | U]                Pre [M,2N]: P in columns [0,N), U in [N,2N)
+ * Y is [M,N].  A2 is required for SWIGLU (else ignored); bias2 is nullable.
+ * Pre holds the pre-activation (bias included) rounded to the dtype; the
+ * column backward consumes it.
+ */
+TP_API tp_status tp_column_fwd(int dtype, int act, int64_t M, int64_t N, int64_t K,
+                        const void* X, int64_t ldx, const void* A, int64_t lda,
+                        const void* A2, int64_t lda2, const void* bias, const void* bias2,
+                        void* Y, int64_t ldy, void* Pre, int64_t ldpre, void* stream);
+
+/*
+ * Row-parallel shard forward.  [TP/SP] "TP math": [X_1, X_2][A_1; A_2] =
+ * X_1 A_1 + X_2 A_2.  The shard emits the full-shape partial Zp = X_i B_i,
+ * X_i [M,K], B_i [K,N], Zp [M,N], in the input dtype.  No bias and no
+ * activation: the bias is added once after the sum (tp_sum_partials) and an
+ * activation cannot act on a partial ("MLP: column first, then row").
+ */
+TP_API tp_status tp_row_fwd(int dtype, int64_t M, int64_t N, int64_t K,
+                     const void* Xi, int64_t ldx, const void* Bi, int64_t ldb,
+                     void* Zp, int64_t ldz, void* stream);
+
+/*
+ * Sum of t shard partials held on ONE device -- the value that g's forward
+ * all-reduce (or f's backward all-reduce) leaves on every rank; this is not a
+ * collective.  [TP/SP] "Full flow" (f and g), "Self-test" (the row bias is
+ * added once, after the sum); [TPcomm] Fig. 2.
+ *
+ *   out = sum_{i<t} parts_i (+ bias once)     parts_i = parts + i*part_stride (elements)
+ * Each parts_i is [M,N] with leading dimension ld; out is [M,N] with ldo;
+ * bias [N] nullable.  Accumulation is fp32 in ascending i with one final
+ * rounding.  `out` may be exactly parts_0 (same pointer, ldo == ld); no other
+ * overlap is allowed.  part_stride must be a multiple of 8 (bf16) / 4 (fp32).
+ */
+TP_API tp_status tp_sum_partials(int dtype, int t, int64_t M, int64_t N,
+                          const void* parts, int64_t ld, int64_t part_stride,
+                          const void* bias, void* out, int64_t ldo, void* stream);
+
+/*
+ * Row-parallel shard backward.  [TP/SP] "Where column and row communicate":
+ * g's backward is the identity, so the shard holds the full dZ and its input
+ * gradient dX_i = dZ B_i^T is local; the weight gradient is dB_i = X_i^T dZ.
+ *
+ *   dXi   = dZ  B_i^T     dZ [M,N], B_i [K,N] -> dXi [M,K]     (nullable: skipped)
+ *   dBi   = X_i^T dZ      X_i [M,K]           -> dBi [K,N]     (nullable: skipped)
+ *   dbias = sum_m dZ      fp32-accumulated, dtype out, [N]     (nullable: skipped)
+ * dbias is the gradient of the replicated row bias; it needs a workspace of
+ * tp_row_bwd_workspace_bytes() bytes (workspace may be NULL when dbias is NULL).
+ */
+TP_API tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K,
+                     const void* dZ, int64_t lddz, const void* Xi, int64_t ldx,
+                     const void* Bi, int64_t ldb,
+                     void* dXi, int64_t lddx, void* dBi, int64_t lddb, void* dbias,
+                     void* workspace, size_t ws_bytes, void* stream);
+TP_API size_t tp_row_bwd_workspace_bytes(int dtype, int64_t M, int64_t N);
+
+/*
+ * Column-parallel shard backward.  [TP/SP] "Where column and row
+ * communicate" and "Full flow: column parallel, t = 3": the input gradient is
+ * a partial (dX = sum_i dY_i A_i^T, summed by f's backward -- use
+ * tp_sum_partials), the weight gradient dA_i = X^T dY_i is complete locally.
+ *
+ *   dP      = dY                               (NONE)
+ *           = dY * GeLU'(Pre)                  (GELU, Pre [M,N])
+ *           = [dY*U*silu'(G) | dY*silu(G)]     (SWIGLU, Pre = [G|U] [M,2N])
+ *   dXpart  = dP_g A^T (+ dP_u A2^T)           [M,K]  (nullable: skipped)
+ *   dA      = X^T dP_g,  dA2 = X^T dP_u        [K,N]  (nullable: skipped; SWIGLU: both or neither)
+ *   dbias   = sum_m dP_g, dbias2 = sum_m dP_u  [N]    (nullable)
+ * dY [M,N], X [M,K], A/A2 [K,N].  dP is materialized in the workspace, in the
+ * dtype, for GELU/SWIGLU; bias gradients use fp32 partial sums there too.
+ * ws_bytes must be >= tp_column_bwd_workspace_bytes(dtype, act, M, N, bias
+ * gradients requested).
+ */
+TP_API tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t K,
+                        const void* dY, int64_t lddy, const void* X, int64_t ldx,
+                        const void* A, int64_t lda, const void* A2, int64_t lda2,
+                        const void* Pre, int64_t ldpre,
+                        void* dXpart, int64_t lddx, void* dA, int64_t ldda,
+                        void* dA2, int64_t ldda2, void* dbias, void* dbias2,
+                        void* workspace, size_t ws_bytes, void* stream);
+TP_API size_t tp_column_bwd_workspace_bytes(int dtype, int act, int64_t M, int64_t N, int with_bias_grad);
+
+/*
+ * Vocab-parallel LM-head shard with cross-entropy partials.  [TP/SP]
+ * "Embedding and LM head: split by vocab": the LM head is column parallel
+ * over the vocabulary and the loss never gathers the logits -- each token
+ * all-reduces only the max, the sum of e^z and the target logit.
+ *
+ * Shard [v0, v0+Vr):  z = H W^T (H [M,K], W [Vr,K]); z is never written.
+ *   out_max[m]    = max_j z[m,j]
+ *   out_sumexp[m] = sum_j exp(z[m,j] - out_max[m])
+ *   out_tgt[m]    = z[m, target[m]-v0] if v0 <= target[m] < v0+Vr, else 0
+ * target: int32 [M] (device).  Outputs fp32 [M] (device).  Logits, exp and
+ * sums are fp32.  workspace >= tp_vocab_ce_workspace_bytes(M, Vr).
+ * Only TP_BF16 is supported (TP_FP32 returns TP_E_DTYPE).
+ * Combining shards: M* = max_r m_r, S* = sum_r s_r e^(m_r-M*),
+ * lse = M* + ln S*, loss = lse - sum_r tgt_r.
+ */
+TP_API tp_status tp_vocab_ce_partials(int dtype, int64_t M, int64_t Vr, int64_t K,
+                               const void* H, int64_t ldh, const void* W, int64_t ldw,
+                               const int32_t* target, int64_t v0,
+                               float* out_max, float* out_sumexp, float* out_tgt,
+                               void* workspace, size_t ws_bytes, void* stream);
+TP_API size_t tp_vocab_ce_workspace_bytes(int64_t M, int64_t Vr);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPSHARD_H */

@@ -1,0 +1,368 @@
+// C ABI of libtpshard (declared in include/tpshard.h): argument validation,
+// workspace carving and kernel dispatch.  Every entry point validates all of
+// its arguments before it enqueues anything.
+#include "tpshard.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kernels.hpp"
+
+namespace {
+
+using tps::GemmLaunch;
+using tps::Problem;
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr size_t kWsAlign = 256;
+
+bool valid_dtype(int d) { return d == TP_FP32 || d == TP_BF16; }
+bool valid_act(int a) { return a == TP_ACT_NONE || a == TP_ACT_GELU || a == TP_ACT_SWIGLU; }
+int64_t vec_elems(int dtype) { return dtype == TP_BF16 ? 8 : 4; }
+size_t esize(int dtype) { return dtype == TP_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool bad_dim(int64_t v) { return v < 1 || v > kMaxDim; }
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+size_t align_ws(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Matrix operand: [rows][ld] with `width` used columns.  Rows are validated
+// separately (bad_dim); here: ld range, ld multiple, base alignment.
+tp_status check_mat(const void* p, int64_t ld, int64_t width, int dtype) {
+  if (ld < width || ld > (int64_t(1) << 40)) return TP_E_SHAPE;
+  if (ld % vec_elems(dtype) != 0 || !aligned16(p)) return TP_E_ALIGN;
+  return TP_OK;
+}
+
+tp_status check_vec(const void* p) { return (p && !aligned16(p)) ? TP_E_ALIGN : TP_OK; }
+
+#define TPS_TRY(expr)                  \
+  do {                                 \
+    const tp_status st_ = (expr);      \
+    if (st_ != TP_OK) return st_;      \
+  } while (0)
+
+// Tile-count limits of the launch grids (bf16: 256 x 128 smallest tile; fp32:
+// 64 x 32 tiles with the row tiles on grid.y).
+tp_status check_grid(int dtype, int64_t M, int64_t N) {
+  if (dtype == TP_BF16) {
+    if (((M + 255) / 256) * ((N + 127) / 128) > kMaxDim) return TP_E_SHAPE;
+  } else {
+    if ((M + 63) / 64 > 65535 || (N + 31) / 32 > kMaxDim) return TP_E_SHAPE;
+  }
+  return TP_OK;
+}
+
+hipError_t run_gemm(int dtype, GemmLaunch& L, hipStream_t s) {
+  return dtype == TP_BF16 ? tps::launch_gemm_bf16(L, s) : tps::launch_gemm_f32(L, s);
+}
+
+Problem make_problem(int64_t M, int64_t N, int layout, int epi) {
+  Problem P = {};
+  P.M = M;
+  P.N = N;
+  P.layout = layout;
+  P.epi = epi;
+  P.nseg = 1;
+  return P;
+}
+
+int64_t colpart_rows(int64_t M) { return (M + tps::kColpartRows - 1) / tps::kColpartRows; }
+
+size_t colpart_bytes(int64_t M, int64_t N) {
+  return align_ws((size_t)colpart_rows(M) * 2 * (size_t)round_up(N, 4) * sizeof(float));
+}
+
+size_t dp_bytes(int dtype, int64_t M, int64_t N) {
+  return align_ws((size_t)M * (size_t)round_up(N, 8) * esize(dtype));
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_abi_version(void) { return TP_ABI_VERSION; }
+
+const char* tp_status_str(int status) {
+  switch (status) {
+    case TP_OK: return "TP_OK: success";
+    case TP_E_NULL: return "TP_E_NULL: a required pointer is NULL";
+    case TP_E_SHAPE: return "TP_E_SHAPE: a size is out of range or a leading dimension is smaller than the row width";
+    case TP_E_ALIGN: return "TP_E_ALIGN: a pointer is not 16-byte aligned or a leading dimension is not a multiple of 8 (bf16) / 4 (fp32) elements";
+    case TP_E_DTYPE: return "TP_E_DTYPE: unknown dtype or dtype not supported by this call";
+    case TP_E_ACT: return "TP_E_ACT: unknown activation or inconsistent activation arguments";
+    case TP_E_WORKSPACE: return "TP_E_WORKSPACE: workspace missing or too small";
+    case TP_E_HIP: return "TP_E_HIP: a HIP kernel launch failed";
+    default: return "unknown tp_status code";
+  }
+}
+
+tp_status tp_column_fwd(int dtype, int act, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx,
+                        const void* A, int64_t lda, const void* A2, int64_t lda2, const void* bias,
+                        const void* bias2, void* Y, int64_t ldy, void* Pre, int64_t ldpre, void* stream) {
+  if (!valid_dtype(dtype)) return TP_E_DTYPE;
+  if (!valid_act(act)) return TP_E_ACT;
+  if (!X || !A || !Y) return TP_E_NULL;
+  if (act != TP_ACT_NONE && !Pre) return TP_E_NULL;
+  if (act == TP_ACT_SWIGLU && !A2) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_grid(dtype, M, N));
+  TPS_TRY(check_mat(X, ldx, K, dtype));
+  TPS_TRY(check_mat(A, lda, N, dtype));
+  if (act == TP_ACT_SWIGLU) TPS_TRY(check_mat(A2, lda2, N, dtype));
+  TPS_TRY(check_mat(Y, ldy, N, dtype));
+  if (act != TP_ACT_NONE) TPS_TRY(check_mat(Pre, ldpre, act == TP_ACT_SWIGLU ? 2 * N : N, dtype));
+  TPS_TRY(check_vec(bias));
+  if (act == TP_ACT_SWIGLU) TPS_TRY(check_vec(bias2));
+
+  GemmLaunch L = {};
+  L.nprob = 1;
+  Problem& P = L.p[0];
+  P = make_problem(M, N, tps::L_NN, act == TP_ACT_NONE ? tps::E_STORE : act == TP_ACT_GELU ? tps::E_GELU : tps::E_SWIGLU);
+  P.seg[0] = tps::Seg{X, A, ldx, lda, K};
+  if (act == TP_ACT_SWIGLU) {
+    P.b_up = A2;
+    P.ldb_up = lda2;
+    P.bias2 = bias2;
+  }
+  P.bias = bias;
+  P.c = Y;
+  P.ldc = ldy;
+  P.pre = Pre;
+  P.ldpre = ldpre;
+  return run_gemm(dtype, L, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
+}
+
+tp_status tp_row_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* Xi, int64_t ldx, const void* Bi,
+                     int64_t ldb, void* Zp, int64_t ldz, void* stream) {
+  if (!valid_dtype(dtype)) return TP_E_DTYPE;
+  if (!Xi || !Bi || !Zp) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_grid(dtype, M, N));
+  TPS_TRY(check_mat(Xi, ldx, K, dtype));
+  TPS_TRY(check_mat(Bi, ldb, N, dtype));
+  TPS_TRY(check_mat(Zp, ldz, N, dtype));
+  GemmLaunch L = {};
+  L.nprob = 1;
+  L.p[0] = make_problem(M, N, tps::L_NN, tps::E_STORE);
+  L.p[0].seg[0] = tps::Seg{Xi, Bi, ldx, ldb, K};
+  L.p[0].c = Zp;
+  L.p[0].ldc = ldz;
+  return run_gemm(dtype, L, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
+}
+
+tp_status tp_sum_partials(int dtype, int t, int64_t M, int64_t N, const void* parts, int64_t ld,
+                          int64_t part_stride, const void* bias, void* out, int64_t ldo, void* stream) {
+  if (!valid_dtype(dtype)) return TP_E_DTYPE;
+  if (!parts || !out) return TP_E_NULL;
+  if (t < 1 || bad_dim(M) || bad_dim(N) || part_stride < 0) return TP_E_SHAPE;
+  TPS_TRY(check_mat(parts, ld, N, dtype));
+  TPS_TRY(check_mat(out, ldo, N, dtype));
+  if (part_stride % vec_elems(dtype) != 0) return TP_E_ALIGN;
+  TPS_TRY(check_vec(bias));
+  tps::SumArgs a = {t, M, N, parts, ld, part_stride, bias, out, ldo};
+  return tps::launch_sum_partials(dtype == TP_BF16, a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK
+                                                                                                       : TP_E_HIP;
+}
+
+size_t tp_row_bwd_workspace_bytes(int dtype, int64_t M, int64_t N) {
+  (void)dtype;
+  if (bad_dim(M) || bad_dim(N)) return 0;
+  return colpart_bytes(M, N);
+}
+
+tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* dZ, int64_t lddz, const void* Xi,
+                     int64_t ldx, const void* Bi, int64_t ldb, void* dXi, int64_t lddx, void* dBi, int64_t lddb,
+                     void* dbias, void* workspace, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return TP_E_DTYPE;
+  if (!dZ || !Xi || !Bi) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_grid(dtype, M, K));
+  TPS_TRY(check_grid(dtype, K, N));
+  TPS_TRY(check_mat(dZ, lddz, N, dtype));
+  TPS_TRY(check_mat(Xi, ldx, K, dtype));
+  TPS_TRY(check_mat(Bi, ldb, N, dtype));
+  if (dXi) TPS_TRY(check_mat(dXi, lddx, K, dtype));
+  if (dBi) TPS_TRY(check_mat(dBi, lddb, N, dtype));
+  TPS_TRY(check_vec(dbias));
+  if (dbias) {
+    if (!workspace || ws_bytes < tp_row_bwd_workspace_bytes(dtype, M, N)) return TP_E_WORKSPACE;
+    if (!aligned16(workspace)) return TP_E_ALIGN;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dXi) {   // dX_i = dZ B_i^T: NT over K' = N
+    GemmLaunch L = {};
+    L.nprob = 1;
+    L.p[0] = make_problem(M, K, tps::L_NT, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{dZ, Bi, lddz, ldb, N};
+    L.p[0].c = dXi;
+    L.p[0].ldc = lddx;
+    if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
+  }
+  if (dBi) {   // dB_i = X_i^T dZ: TN over K' = M
+    GemmLaunch L = {};
+    L.nprob = 1;
+    L.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{Xi, dZ, ldx, lddz, M};
+    L.p[0].c = dBi;
+    L.p[0].ldc = lddb;
+    if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
+  }
+  if (dbias) {
+    float* colpart = static_cast<float*>(workspace);
+    const int64_t ldcp = round_up(N, 4);
+    tps::ActBwdArgs a = {};
+    a.M = M;
+    a.N = N;
+    a.act = tps::E_STORE;
+    a.dY = dZ;
+    a.lddy = lddz;
+    a.colpart = colpart;
+    a.ldcp = ldcp;
+    if (tps::launch_act_bwd(dtype == TP_BF16, a, s) != hipSuccess) return TP_E_HIP;
+    if (tps::launch_colsum_finalize(dtype == TP_BF16, colpart, colpart_rows(M), ldcp, N, 0, dbias, s) != hipSuccess)
+      return TP_E_HIP;
+  }
+  return TP_OK;
+}
+
+size_t tp_column_bwd_workspace_bytes(int dtype, int act, int64_t M, int64_t N, int with_bias_grad) {
+  if (!valid_dtype(dtype) || !valid_act(act) || bad_dim(M) || bad_dim(N)) return 0;
+  size_t bytes = 0;
+  if (act != TP_ACT_NONE) bytes += dp_bytes(dtype, M, N) * (act == TP_ACT_SWIGLU ? 2 : 1);
+  if (with_bias_grad) bytes += colpart_bytes(M, N);
+  return bytes;
+}
+
+tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t K, const void* dY, int64_t lddy,
+                        const void* X, int64_t ldx, const void* A, int64_t lda, const void* A2, int64_t lda2,
+                        const void* Pre, int64_t ldpre, void* dXpart, int64_t lddx, void* dA, int64_t ldda,
+                        void* dA2, int64_t ldda2, void* dbias, void* dbias2, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  if (!valid_dtype(dtype)) return TP_E_DTYPE;
+  if (!valid_act(act)) return TP_E_ACT;
+  const bool swiglu = act == TP_ACT_SWIGLU;
+  if (!dY || !X || !A) return TP_E_NULL;
+  if (act != TP_ACT_NONE && !Pre) return TP_E_NULL;
+  if (swiglu && !A2) return TP_E_NULL;
+  if (swiglu && ((dA == nullptr) != (dA2 == nullptr))) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_grid(dtype, M, K));
+  TPS_TRY(check_grid(dtype, K, N));
+  TPS_TRY(check_mat(dY, lddy, N, dtype));
+  TPS_TRY(check_mat(X, ldx, K, dtype));
+  TPS_TRY(check_mat(A, lda, N, dtype));
+  if (swiglu) TPS_TRY(check_mat(A2, lda2, N, dtype));
+  if (act != TP_ACT_NONE) TPS_TRY(check_mat(Pre, ldpre, swiglu ? 2 * N : N, dtype));
+  if (dXpart) TPS_TRY(check_mat(dXpart, lddx, K, dtype));
+  if (dA) TPS_TRY(check_mat(dA, ldda, N, dtype));
+  if (swiglu && dA2) TPS_TRY(check_mat(dA2, ldda2, N, dtype));
+  TPS_TRY(check_vec(dbias));
+  if (swiglu) TPS_TRY(check_vec(dbias2));
+  const bool want_bias = dbias || (swiglu && dbias2);
+  const size_t need = tp_column_bwd_workspace_bytes(dtype, act, M, N, want_bias);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need) return TP_E_WORKSPACE;
+    if (!aligned16(workspace)) return TP_E_ALIGN;
+  }
+  if (!dXpart && !dA && !want_bias) return TP_OK;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t lddp = round_up(N, 8);
+  const void* dPg = dY;     // act NONE: dP = dY
+  const void* dPu = nullptr;
+  int64_t ldp = lddy;
+  size_t off = 0;
+  tps::ActBwdArgs a = {};
+  a.M = M;
+  a.N = N;
+  a.act = act == TP_ACT_NONE ? tps::E_STORE : act == TP_ACT_GELU ? tps::E_GELU : tps::E_SWIGLU;
+  a.dY = dY;
+  a.lddy = lddy;
+  a.pre = Pre;
+  a.ldpre = ldpre;
+  if (act != TP_ACT_NONE) {
+    a.dp = ws + off;
+    off += dp_bytes(dtype, M, N);
+    if (swiglu) {
+      a.dp_up = ws + off;
+      off += dp_bytes(dtype, M, N);
+    }
+    a.lddp = lddp;
+    dPg = a.dp;
+    dPu = a.dp_up;
+    ldp = lddp;
+  }
+  float* colpart = nullptr;
+  const int64_t ldcp = round_up(N, 4);
+  if (want_bias) {
+    colpart = reinterpret_cast<float*>(ws + off);
+    a.colpart = colpart;
+    a.ldcp = ldcp;
+  }
+  if (act != TP_ACT_NONE || want_bias) {
+    if (tps::launch_act_bwd(dtype == TP_BF16, a, s) != hipSuccess) return TP_E_HIP;
+  }
+  if (want_bias) {
+    if (dbias && tps::launch_colsum_finalize(dtype == TP_BF16, colpart, colpart_rows(M), ldcp, N, 0, dbias, s) !=
+                     hipSuccess)
+      return TP_E_HIP;
+    if (swiglu && dbias2 &&
+        tps::launch_colsum_finalize(dtype == TP_BF16, colpart, colpart_rows(M), ldcp, N, 1, dbias2, s) != hipSuccess)
+      return TP_E_HIP;
+  }
+  if (dXpart) {   // dX_part = dP_g A^T (+ dP_u A2^T): NT over K' = N per segment
+    GemmLaunch L = {};
+    L.nprob = 1;
+    L.p[0] = make_problem(M, K, tps::L_NT, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{dPg, A, ldp, lda, N};
+    if (swiglu) {
+      L.p[0].seg[1] = tps::Seg{dPu, A2, ldp, lda2, N};
+      L.p[0].nseg = 2;
+    }
+    L.p[0].c = dXpart;
+    L.p[0].ldc = lddx;
+    if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
+  }
+  if (dA) {   // dA = X^T dP_g, dA2 = X^T dP_u: TN over K' = M, one launch
+    GemmLaunch L = {};
+    L.nprob = swiglu ? 2 : 1;
+    L.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{X, dPg, ldx, ldp, M};
+    L.p[0].c = dA;
+    L.p[0].ldc = ldda;
+    if (swiglu) {
+      L.p[1] = make_problem(K, N, tps::L_TN, tps::E_STORE);
+      L.p[1].seg[0] = tps::Seg{X, dPu, ldx, ldp, M};
+      L.p[1].c = dA2;
+      L.p[1].ldc = ldda2;
+    }
+    if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
+  }
+  return TP_OK;
+}
+
+size_t tp_vocab_ce_workspace_bytes(int64_t M, int64_t Vr) {
+  if (bad_dim(M) || bad_dim(Vr)) return 0;
+  return tps::ce_workspace_bytes(M, Vr);
+}
+
+tp_status tp_vocab_ce_partials(int dtype, int64_t M, int64_t Vr, int64_t K, const void* H, int64_t ldh,
+                               const void* W, int64_t ldw, const int32_t* target, int64_t v0, float* out_max,
+                               float* out_sumexp, float* out_tgt, void* workspace, size_t ws_bytes, void* stream) {
+  if (dtype != TP_BF16) return TP_E_DTYPE;
+  if (!H || !W || !target || !out_max || !out_sumexp || !out_tgt) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(Vr) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_grid(dtype, M, Vr));
+  TPS_TRY(check_mat(H, ldh, K, dtype));
+  TPS_TRY(check_mat(W, ldw, K, dtype));
+  if (!aligned16(target) || !aligned16(out_max) || !aligned16(out_sumexp) || !aligned16(out_tgt)) return TP_E_ALIGN;
+  if (!workspace || ws_bytes < tp_vocab_ce_workspace_bytes(M, Vr)) return TP_E_WORKSPACE;
+  if (!aligned16(workspace)) return TP_E_ALIGN;
+  tps::CEArgs a = {M, Vr, K, H, ldh, W, ldw, target, v0, out_max, out_sumexp, out_tgt, static_cast<float*>(workspace)};
+  return tps::launch_ce_partials(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal launch descriptors shared by the HIP kernels and the C-ABI layer.
+// Not part of the public ABI (include/tpshard.h is).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tps {
+
+// Operand layouts of C[M,N] = sum_k A(m,k) B(k,n), both stored row-major:
+//   L_NN: A [M][K] (K contiguous), B [K][N] (N contiguous)   -- forward Y = X W
+//   L_NT: A [M][K],                B [N][K] (K contiguous)   -- dgrad dX = dY W^T, LM head
+//   L_TN: A [K][M] (M contiguous), B [K][N]                  -- wgrad dW = X^T dY
+enum Layout : int { L_NN = 0, L_NT = 1, L_TN = 2 };
+
+// Epilogues applied to the fp32 accumulator tile.
+//   E_STORE : C = acc (+ bias)
+//   E_GELU  : P = acc + bias; Pre = P; C = GeLU(P)
+//   E_SWIGLU: G = acc_gate + bias, U = acc_up + bias2; Pre = [G | U]; C = silu(G) * U
+enum EpiMode : int { E_STORE = 0, E_GELU = 1, E_SWIGLU = 2 };
+
+// One K-segment: C += A_seg * B_seg over K elements.  A problem may chain
+// two segments that accumulate into the same tile (the SwiGLU dgrad sums the
+// gate and up contributions).
+struct Seg {
+  const void* a;
+  const void* b;
+  int64_t lda, ldb, K;
+};
+
+struct Problem {
+  int64_t M, N;          // output rows / columns (SwiGLU: columns of Y = gate width)
+  Seg seg[2];
+  int nseg;
+  int layout;            // Layout (shared by both segments)
+  int epi;               // EpiMode
+  const void* b_up;      // E_SWIGLU: up-projection weight [K][N] (layout L_NN, one segment)
+  int64_t ldb_up;
+  const void* bias;      // [N] or nullptr
+  const void* bias2;     // [N] or nullptr (SwiGLU up bias)
+  void* c;               // output [M][ldc]
+  int64_t ldc;
+  void* pre;             // E_GELU / E_SWIGLU pre-activation output
+  int64_t ldpre;
+  // filled by the launcher
+  int tiles_m, tiles_n, tile_begin;
+};
+
+// Up to two independent GEMM problems share one launch (their tiles are
+// concatenated), so a short GEMM can fill the CUs another one leaves idle.
+struct GemmLaunch {
+  Problem p[2];
+  int nprob;
+};
+
+struct CEArgs {
+  int64_t M, Vr, K;
+  const void* H;
+  int64_t ldh;
+  const void* W;
+  int64_t ldw;
+  const int32_t* target;
+  int64_t v0;
+  float* out_max;
+  float* out_sumexp;
+  float* out_tgt;
+  float* ws;             // [ceil(Vr/256)][M] (max,sum) pairs, then [M] target logits
+};
+
+// Elementwise backward of the column epilogue, fused with fp32 column
+// partial sums for the bias gradients.
+struct ActBwdArgs {
+  int64_t M, N;
+  int act;               // E_STORE (= no activation), E_GELU, E_SWIGLU
+  const void* dY;
+  int64_t lddy;
+  const void* pre;
+  int64_t ldpre;
+  void* dp;              // gate part (or the only part) [M][lddp]; nullptr: not written
+  void* dp_up;           // SwiGLU up part [M][lddp]
+  int64_t lddp;
+  float* colpart;        // [ceil(M/64)][2][ldcp] fp32 or nullptr
+  int64_t ldcp;
+};
+
+struct SumArgs {
+  int t;
+  int64_t M, N;
+  const void* parts;
+  int64_t ld, part_stride;
+  const void* bias;
+  void* out;
+  int64_t ldo;
+};
+
+constexpr int kColpartRows = 64;   // rows per column-partial block
+
+hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s);
+hipError_t launch_gemm_f32(GemmLaunch& L, hipStream_t s);
+hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s);
+size_t ce_workspace_bytes(int64_t M, int64_t Vr);
+hipError_t launch_act_bwd(int is_bf16, const ActBwdArgs& a, hipStream_t s);
+hipError_t launch_colsum_finalize(int is_bf16, const float* colpart, int64_t nrb, int64_t ldcp,
+                                  int64_t N, int part, void* out, hipStream_t s);
+hipError_t launch_sum_partials(int is_bf16, const SumArgs& a, hipStream_t s);
+
+}  // namespace tps

@@ -1,0 +1,158 @@
+"""torch-tensor front end of the libtpshard binding.
+
+Argument marshalling only: shapes and leading dimensions are read from the
+tensors, outputs and workspaces are allocated with ``torch.empty`` on the
+inputs' device (padded so every leading dimension meets the library's
+alignment rule), and the call goes to the C ABI on torch's current stream.
+No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_column_bwd,
+               tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
+               tp_sum_partials, tp_vocab_ce_partials, tp_vocab_ce_workspace_bytes)
+
+ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _vec(dtype: torch.dtype) -> int:
+    return 8 if dtype == torch.bfloat16 else 4
+
+
+def empty_padded(rows: int, cols: int, dtype, device) -> torch.Tensor:
+    """[rows, cols] view of a buffer whose row stride is a multiple of the vector width."""
+    v = _vec(dtype)
+    ld = (cols + v - 1) // v * v
+    return torch.empty(rows, ld, dtype=dtype, device=device)[:, :cols]
+
+
+def aligned(t: torch.Tensor) -> torch.Tensor:
+    """Return ``t`` if it already satisfies the ABI layout rule, else a padded copy."""
+    if t is None:
+        return None
+    if t.dim() == 1:
+        return t if (t.is_contiguous() and t.data_ptr() % 16 == 0) else t.clone()
+    v = _vec(t.dtype)
+    if t.stride(1) == 1 and t.stride(0) % v == 0 and t.data_ptr() % 16 == 0 and t.stride(0) >= t.shape[1]:
+        return t
+    out = empty_padded(t.shape[0], t.shape[1], t.dtype, t.device)
+    out.copy_(t)
+    return out
+
+
+def ld(t: torch.Tensor) -> int:
+    return t.stride(0)
+
+
+def column_fwd(X, A, act="none", A2=None, bias=None, bias2=None):
+    """Y = act(X A + b) (SwiGLU: silu(X A + b) * (X A2 + b2)); returns (Y, Pre)."""
+    X, A, A2, bias, bias2 = (aligned(t) for t in (X, A, A2, bias, bias2))
+    M, K = X.shape
+    N = A.shape[1]
+    Y = empty_padded(M, N, X.dtype, X.device)
+    Pre = None
+    if act == "gelu":
+        Pre = empty_padded(M, N, X.dtype, X.device)
+    elif act == "swiglu":
+        Pre = empty_padded(M, 2 * N, X.dtype, X.device)
+    tp_column_fwd(dtype_code(X), ACTS[act], M, N, K, X, ld(X), A, ld(A), A2, ld(A2) if A2 is not None else 0,
+                  bias, bias2, Y, ld(Y), Pre, ld(Pre) if Pre is not None else 0)
+    return Y, Pre
+
+
+def row_fwd(Xi, Bi):
+    """Full-shape partial Z_i = X_i B_i."""
+    Xi, Bi = aligned(Xi), aligned(Bi)
+    M, K = Xi.shape
+    N = Bi.shape[1]
+    Z = empty_padded(M, N, Xi.dtype, Xi.device)
+    tp_row_fwd(dtype_code(Xi), M, N, K, Xi, ld(Xi), Bi, ld(Bi), Z, ld(Z))
+    return Z
+
+
+def stack_partials(parts):
+    """Copy a list of [M, N] partials into one padded [t, M, ld] buffer."""
+    t = len(parts)
+    M, N = parts[0].shape
+    v = _vec(parts[0].dtype)
+    ldp = (N + v - 1) // v * v
+    buf = torch.empty(t, M, ldp, dtype=parts[0].dtype, device=parts[0].device)
+    for i, p in enumerate(parts):
+        buf[i, :, :N].copy_(p)
+    return buf, N
+
+
+def sum_partials(buf, N, bias=None, out=None):
+    """out = sum_i buf[i, :, :N] (+ bias once); ``buf`` is a [t, M, ld] tensor."""
+    t, M, ldp = buf.shape
+    bias = aligned(bias)
+    if out is None:
+        out = empty_padded(M, N, buf.dtype, buf.device)
+    tp_sum_partials(dtype_code(buf), t, M, N, buf, ldp, M * ldp, bias, out, ld(out))
+    return out
+
+
+def row_bwd(dZ, Xi, Bi, want_dx=True, want_dw=True, want_db=False):
+    """(dX_i, dB_i, dbias) of the row shard; unrequested outputs are None."""
+    dZ, Xi, Bi = aligned(dZ), aligned(Xi), aligned(Bi)
+    M, N = dZ.shape
+    K = Xi.shape[1]
+    dt = dtype_code(dZ)
+    dX = empty_padded(M, K, dZ.dtype, dZ.device) if want_dx else None
+    dB = empty_padded(K, N, dZ.dtype, dZ.device) if want_dw else None
+    db = torch.empty(N, dtype=dZ.dtype, device=dZ.device) if want_db else None
+    ws_n = tp_row_bwd_workspace_bytes(dt, M, N) if want_db else 0
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dZ.device) if want_db else None
+    tp_row_bwd(dt, M, N, K, dZ, ld(dZ), Xi, ld(Xi), Bi, ld(Bi), dX, ld(dX) if dX is not None else 0,
+               dB, ld(dB) if dB is not None else 0, db, ws, ws_n)
+    return dX, dB, db
+
+
+def column_bwd(dY, X, A, Pre=None, act="none", A2=None, want_dx=True, want_dw=True, want_db=False):
+    """(dX_part, dA, dA2, dbias, dbias2) of the column shard; unrequested outputs are None."""
+    dY, X, A, A2, Pre = (aligned(t) for t in (dY, X, A, A2, Pre))
+    M, N = dY.shape
+    K = X.shape[1]
+    dt = dtype_code(dY)
+    sw = act == "swiglu"
+    dX = empty_padded(M, K, dY.dtype, dY.device) if want_dx else None
+    dA = empty_padded(K, N, dY.dtype, dY.device) if want_dw else None
+    dA2 = empty_padded(K, N, dY.dtype, dY.device) if (want_dw and sw) else None
+    db = torch.empty(N, dtype=dY.dtype, device=dY.device) if want_db else None
+    db2 = torch.empty(N, dtype=dY.dtype, device=dY.device) if (want_db and sw) else None
+    ws_n = tp_column_bwd_workspace_bytes(dt, ACTS[act], M, N, want_db)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dY.device)
+    tp_column_bwd(dt, ACTS[act], M, N, K, dY, ld(dY), X, ld(X), A, ld(A), A2, ld(A2) if A2 is not None else 0,
+                  Pre, ld(Pre) if Pre is not None else 0, dX, ld(dX) if dX is not None else 0,
+                  dA, ld(dA) if dA is not None else 0, dA2, ld(dA2) if dA2 is not None else 0,
+                  db, db2, ws, ws_n)
+    return dX, dA, dA2, db, db2
+
+
+def vocab_ce_partials(H, W, target, v0):
+    """Per-token (max, sum exp(z - max), target logit) over the vocab shard starting at v0."""
+    H, W = aligned(H), aligned(W)
+    M, K = H.shape
+    Vr = W.shape[0]
+    target = target.to(torch.int32).contiguous()
+    m = torch.empty(M, dtype=torch.float32, device=H.device)
+    s = torch.empty(M, dtype=torch.float32, device=H.device)
+    tg = torch.empty(M, dtype=torch.float32, device=H.device)
+    ws_n = tp_vocab_ce_workspace_bytes(M, Vr)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=H.device)
+    tp_vocab_ce_partials(TP_BF16, M, Vr, K, H, ld(H), W, ld(W), target, v0, m, s, tg, ws, ws_n)
+    return m, s, tg
+
+
+__all__ = ["column_fwd", "row_fwd", "stack_partials", "sum_partials", "row_bwd", "column_bwd",
+           "vocab_ce_partials", "empty_padded", "aligned", "dtype_code", "TP_FP32", "TP_BF16"]

@@ -1,0 +1,125 @@
+"""The C ABI on the CPU: the library loads, exports exactly what the header
+declares, and rejects every invalid argument with its status code before any
+HIP call (no compute call is made here)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import tensor_transformer_linear_tp_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tp.LIB_PATH):
+        from tensor_transformer_linear_tp_amd import build
+        build.build()
+    return tp._load()
+
+
+def _header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^TP_API\s+[\w\s\*]+?\b(tp_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_match_header(lib):
+    declared = _header_functions()
+    assert declared == sorted(tp.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", tp.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = sorted(l.split()[-1] for l in out.stdout.splitlines() if " T tp_" in l)
+    assert exported == declared
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert tp.tp_abi_version() == 1
+    seen = set()
+    for code in range(8):
+        s = tp.tp_status_str(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert "unknown" in tp.tp_status_str(99)
+
+
+P = 0x100000  # a 16-byte aligned stand-in address; validation fails before it is ever used
+
+
+def _rc(fn, *args):
+    return getattr(tp._load(), fn)(*args)
+
+
+def test_column_fwd_validation(lib):
+    ok = dict(dtype=tp.TP_BF16, act=tp.TP_ACT_GELU, M=64, N=64, K=64, X=P, ldx=64, A=P, lda=64, A2=None, lda2=0,
+              bias=None, bias2=None, Y=P, ldy=64, Pre=P, ldpre=64, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return _rc("tp_column_fwd", *a.values())
+
+    assert call(dtype=7) == 4
+    assert call(act=9) == 5
+    assert call(X=None) == 1
+    assert call(Pre=None) == 1                              # GeLU needs Pre
+    assert call(act=tp.TP_ACT_SWIGLU, ldpre=128) == 1       # SwiGLU needs A2
+    assert call(M=0) == 2 and call(N=-1) == 2 and call(K=1 << 31) == 2
+    assert call(ldx=32) == 2                                # ld < width
+    assert call(ldx=68) == 3                                # ld not a multiple of 8 (bf16)
+    assert call(X=P + 8) == 3                               # misaligned base
+    assert call(bias=P + 2) == 3
+    assert call(act=tp.TP_ACT_SWIGLU, A2=P, lda2=64, ldpre=64) == 2   # SwiGLU Pre needs 2N columns
+    assert call(dtype=tp.TP_FP32, ldx=66) == 3              # fp32: multiple of 4
+
+
+def test_row_and_sum_validation(lib):
+    assert _rc("tp_row_fwd", 5, 8, 8, 8, P, 8, P, 8, P, 8, None) == 4
+    assert _rc("tp_row_fwd", tp.TP_BF16, 8, 8, 8, None, 8, P, 8, P, 8, None) == 1
+    assert _rc("tp_row_fwd", tp.TP_BF16, 8, 8, 8, P, 8, P, 8, P, 4, None) == 2
+    assert _rc("tp_sum_partials", tp.TP_BF16, 0, 8, 8, P, 8, 64, None, P, 8, None) == 2
+    assert _rc("tp_sum_partials", tp.TP_BF16, 2, 8, 8, P, 8, -64, None, P, 8, None) == 2
+    assert _rc("tp_sum_partials", tp.TP_BF16, 2, 8, 8, P, 8, 60, None, P, 8, None) == 3
+    assert _rc("tp_sum_partials", tp.TP_BF16, 2, 8, 8, None, 8, 64, None, P, 8, None) == 1
+
+
+def test_backward_validation_and_workspace(lib):
+    need = tp.tp_row_bwd_workspace_bytes(tp.TP_BF16, 100, 300)
+    assert need >= 2 * 4 * 300 * 2  # two 64-row partial blocks of fp32 column sums
+    # dbias without workspace
+    assert _rc("tp_row_bwd", tp.TP_BF16, 100, 300, 64, P, 304, P, 64, P, 304, P, 64, None, 0, P, None, 0, None) == 6
+    assert _rc("tp_row_bwd", tp.TP_BF16, 100, 300, 64, P, 304, P, 64, P, 304, P, 64, None, 0, P, P, need - 1,
+               None) == 6
+    # column bwd: SwiGLU needs both or neither weight gradients
+    args = [tp.TP_BF16, tp.TP_ACT_SWIGLU, 64, 64, 64, P, 64, P, 64, P, 64, P, 64, P, 128, P, 64, P, 64, None, 0,
+            None, None, P, 1 << 30, None]
+    assert _rc("tp_column_bwd", *args) == 1
+    args[19], args[20] = P, 64
+    ws = tp.tp_column_bwd_workspace_bytes(tp.TP_BF16, tp.TP_ACT_SWIGLU, 64, 64, 0)
+    assert ws == 2 * 64 * 64 * 2
+    args[23], args[24] = P, ws - 1
+    assert _rc("tp_column_bwd", *args) == 6
+    assert tp.tp_column_bwd_workspace_bytes(tp.TP_BF16, tp.TP_ACT_NONE, 64, 64, 0) == 0
+
+
+def test_ce_validation(lib):
+    ws = tp.tp_vocab_ce_workspace_bytes(8192, 18992)
+    assert ws == (2 * 75 * 8192 + 8192) * 4
+    base = [tp.TP_BF16, 8192, 18992, 4096, P, 4096, P, 4096, P, 0, P, P, P, P, ws, None]
+    a = list(base); a[0] = tp.TP_FP32
+    assert _rc("tp_vocab_ce_partials", *a) == 4
+    a = list(base); a[8] = None
+    assert _rc("tp_vocab_ce_partials", *a) == 1
+    a = list(base); a[14] = ws - 4
+    assert _rc("tp_vocab_ce_partials", *a) == 6
+    a = list(base); a[10] = P + 4
+    assert _rc("tp_vocab_ce_partials", *a) == 3
+
+
+def test_binding_raises_typed_errors(lib):
+    with pytest.raises(tp.TPError) as ei:
+        tp.tp_row_fwd(tp.TP_BF16, 0, 8, 8, P, 8, P, 8, P, 8, stream=0)
+    assert ei.value.status == 2 and ei.value.name == "TP_E_SHAPE"

@@ -1,0 +1,257 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times.  Outputs too large for the float64 oracle are checked on
+sampled rows / columns that the oracle computes one by one (the sample always
+includes the first and last index and tile edges)."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+
+from .gpu_util import TOL, TOL_CE, assert_close, cols, dev, host64, rows, sample_idx
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ops = pytest.importorskip("tensor_transformer_linear_tp_amd.torch_ops")
+
+BF = TOL[syn.BF16]
+
+
+# ---------------------------------------------------------------------------
+# c1: fp32 GeLU MLP, t shards of one full weight, with and without bias,
+# against the unsharded layer (the pages' self-test recipe).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("dtype", [syn.FP32, syn.BF16])
+def test_c1_sharded_mlp_matches_unsharded(t, bias, dtype):
+    cfg = syn.C1
+    M, H, F = cfg.M, cfg.H, cfg.F
+    s = cfg.seed + 100
+    X = syn.normal(s + 1, (M, H), 1.0, dtype)
+    A = syn.normal(s + 2, (H, F), cfg.std_w, dtype)
+    B = syn.normal(s + 3, (F, H), cfg.std_w, dtype)
+    dZ = syn.normal(s + 4, (M, H), 1.0, dtype)
+    bA = syn.normal(s + 5, (F,), 0.5, dtype) if bias else None
+    bB = syn.normal(s + 6, (H,), 0.5, dtype) if bias else None
+
+    Xd, dZd = dev(X), dev(dZ)
+    Ad, Bd = dev(A), dev(B)
+    zparts, dxparts, dAs, dBs, dbs = [], [], [], [], []
+    dbrow = None
+    for i in range(t):
+        cs = oracle.column_slice(F, t, i)
+        Y, Pre = ops.column_fwd(Xd, Ad[:, cs], "gelu", bias=dev(bA)[cs] if bias else None)
+        zparts.append(ops.row_fwd(Y, Bd[cs, :]))
+        dY, dB, db_row = ops.row_bwd(dZd, Y, Bd[cs, :], want_db=bias)
+        dX, dA, _, db, _ = ops.column_bwd(dY, Xd, Ad[:, cs], Pre=Pre, act="gelu", want_db=bias)
+        dxparts.append(dX)
+        dAs.append(dA)
+        dBs.append(dB)
+        dbs.append(db)
+        dbrow = db_row
+    buf, N = ops.stack_partials(zparts)
+    Z = ops.sum_partials(buf, N, bias=dev(bB) if bias else None)
+    buf2, N2 = ops.stack_partials(dxparts)
+    dXs = ops.sum_partials(buf2, N2)
+    torch.cuda.synchronize()
+
+    # Unsharded reference (t = 1 of the oracle).
+    Yr, Pr = oracle.column_fwd(X.f64, A.f64, "gelu", bias=bA.f64 if bias else None)
+    Zr = oracle.sum_partials([oracle.row_fwd(Yr, B.f64)], bias=bB.f64 if bias else None)
+    dYr, dBr, dbrow_r = oracle.row_bwd(dZ.f64, Yr, B.f64)
+    dXr, dAr, _, dbr, _ = oracle.column_bwd(dYr, X.f64, A.f64, Pr, "gelu")
+    tol = TOL[dtype]
+    assert_close("Z", host64(Z), Zr, tol)
+    assert_close("dX", host64(dXs), dXr, tol)
+    assert_close("dA", np.concatenate([host64(a) for a in dAs], axis=1), dAr, tol)
+    assert_close("dB", np.concatenate([host64(b) for b in dBs], axis=0), dBr, tol)
+    if bias:
+        assert_close("db_col", np.concatenate([host64(b) for b in dbs]), dbr, tol)
+        assert_close("db_row", host64(dbrow), dbrow_r, tol)
+
+
+# ---------------------------------------------------------------------------
+# c2: Qwen3-8B-shaped SwiGLU shard, t = 8.
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def c2():
+    return syn.mlp_shard_inputs(syn.C2, shard=0)
+
+
+def test_c2_shard_chain_sampled(c2):
+    cfg = syn.C2
+    X, A, A2, B, dZ = (c2[k] for k in ("X", "A", "A2", "B", "dZ"))
+    Xd, Ad, A2d, Bd, dZd = (dev(c2[k]) for k in ("X", "A", "A2", "B", "dZ"))
+    Y, Pre = ops.column_fwd(Xd, Ad, "swiglu", A2=A2d)
+    Z = ops.row_fwd(Y, Bd)
+    dY, dB, _ = ops.row_bwd(dZd, Y, Bd)
+    dX, dA, dA2, _, _ = ops.column_bwd(dY, Xd, Ad, Pre=Pre, act="swiglu", A2=A2d)
+    torch.cuda.synchronize()
+
+    ms = sample_idx(cfg.M, 48, 1)            # token rows
+    ks = sample_idx(cfg.Fi, 40, 2)           # intermediate columns of this shard
+    Xf, Af, A2f, Bf, dZf = X.f64, A.f64, A2.f64, B.f64, dZ.f64
+    # forward rows
+    Yr, Prer = oracle.column_fwd(Xf[ms], Af, "swiglu", A2=A2f)
+    assert_close("Y rows", rows(Y, ms), Yr, BF)
+    assert_close("Pre rows", rows(Pre, ms), Prer, BF)
+    assert_close("Z rows", rows(Z, ms), oracle.row_fwd(Yr, Bf), BF)
+    # backward rows: dY, dX_part
+    dYr = oracle.dgrad(dZf[ms], Bf)
+    assert_close("dY rows", rows(dY, ms), dYr, BF)
+    dXr = oracle.column_bwd(dYr, Xf[ms], Af, Prer, "swiglu", A2f)[0]
+    assert_close("dXpart rows", rows(dX, ms), dXr, BF)
+    # weight gradients on sampled intermediate columns (reductions over all tokens)
+    Yk, Prek = oracle.column_fwd(Xf, Af[:, ks], "swiglu", A2=A2f[:, ks])
+    assert_close("dB rows", rows(dB, ks), oracle.wgrad(Yk, dZf), BF)
+    dYk = oracle.dgrad(dZf, Bf[ks, :])
+    _, dAk, dA2k, _, _ = oracle.column_bwd(dYk, Xf, Af[:, ks], Prek, "swiglu", A2f[:, ks])
+    assert_close("dA cols", cols(dA, ks), dAk, BF)
+    assert_close("dA2 cols", cols(dA2, ks), dA2k, BF)
+
+
+def test_c2_per_call_sampled(c2):
+    """Each call on its own seeded inputs (none taken from another GPU call)."""
+    cfg = syn.C2
+    M, H, Fi = cfg.M, cfg.H, cfg.Fi
+    Yin = syn.normal(2900, (M, Fi), 1.0, syn.BF16)
+    dYin = syn.normal(2901, (M, Fi), 1.0, syn.BF16)
+    Pin = syn.normal(2902, (M, 2 * Fi), 1.0, syn.BF16)
+    X, A, A2, B, dZ = (c2[k] for k in ("X", "A", "A2", "B", "dZ"))
+    Z = ops.row_fwd(dev(Yin), dev(B))
+    dYo, dB, db = ops.row_bwd(dev(dZ), dev(Yin), dev(B), want_db=True)
+    dX, dA, dA2, dbg, dbu = ops.column_bwd(dev(dYin), dev(X), dev(A), Pre=dev(Pin), act="swiglu", A2=dev(A2),
+                                           want_db=True)
+    torch.cuda.synchronize()
+    ms = sample_idx(M, 48, 3)
+    ks = sample_idx(Fi, 40, 4)
+    ns = sample_idx(H, 40, 5)
+    assert_close("Z", rows(Z, ms), oracle.row_fwd(Yin.f64[ms], B.f64), BF)
+    assert_close("dY", rows(dYo, ms), oracle.dgrad(dZ.f64[ms], B.f64), BF)
+    assert_close("dB", cols(dB, ns), oracle.wgrad(Yin.f64, dZ.f64[:, ns]), BF)
+    assert_close("db_row", host64(db), dZ.f64.sum(axis=0), BF)
+    P = Pin.f64
+    r = oracle.column_bwd(dYin.f64[ms], X.f64[ms], A.f64, P[ms], "swiglu", A2.f64)
+    assert_close("dXpart", rows(dX, ms), r[0], BF)
+    Pk = np.concatenate([P[:, ks], P[:, Fi + ks]], axis=1)
+    r = oracle.column_bwd(dYin.f64[:, ks], X.f64, A.f64[:, ks], Pk, "swiglu", A2.f64[:, ks])
+    assert_close("dA", cols(dA, ks), r[1], BF)
+    assert_close("dA2", cols(dA2, ks), r[2], BF)
+    assert_close("db_gate", rows(dbg, ks), r[3], BF)
+    assert_close("db_up", rows(dbu, ks), r[4], BF)
+
+
+# ---------------------------------------------------------------------------
+# c3: attention projection shard (QKV column, W_O row), t = 8.
+# ---------------------------------------------------------------------------
+
+def test_c3_attention_projections_sampled():
+    cfg = syn.C3
+    d = syn.attn_proj_inputs(cfg)
+    QKV, _ = ops.column_fwd(dev(d["X"]), dev(d["Wqkv"]), "none")
+    Z = ops.row_fwd(dev(d["attn"]), dev(d["Wo"]))
+    dAttn, dWo, _ = ops.row_bwd(dev(d["dZ"]), dev(d["attn"]), dev(d["Wo"]))
+    dX, dWqkv, _, _, _ = ops.column_bwd(dev(d["dQKV"]), dev(d["X"]), dev(d["Wqkv"]), act="none")
+    torch.cuda.synchronize()
+    ms = sample_idx(cfg.M, 48, 6)
+    X, Wqkv, attn, Wo, dZ, dQKV = (d[k].f64 for k in ("X", "Wqkv", "attn", "Wo", "dZ", "dQKV"))
+    assert_close("QKV", rows(QKV, ms), oracle.column_fwd(X[ms], Wqkv)[0], BF)
+    assert_close("Z", rows(Z, ms), oracle.row_fwd(attn[ms], Wo), BF)
+    assert_close("dAttn", rows(dAttn, ms), oracle.dgrad(dZ[ms], Wo), BF)
+    ns = sample_idx(cfg.H, 40, 7)
+    assert_close("dWo", cols(dWo, ns), oracle.wgrad(attn, dZ[:, ns]), BF)
+    assert_close("dX", rows(dX, ms), oracle.dgrad(dQKV[ms], Wqkv), BF)
+    assert_close("dWqkv", host64(dWqkv), oracle.wgrad(X, dQKV), BF)
+
+
+# ---------------------------------------------------------------------------
+# c4: GeLU shard at h = 8192, t = 4, and the 4-way partial sum.
+# ---------------------------------------------------------------------------
+
+def test_c4_gelu_shard_sampled():
+    cfg = syn.C4
+    d = syn.mlp_shard_inputs(cfg, shard=0)
+    M, H, Fi = cfg.M, cfg.H, cfg.Fi
+    Yin = syn.normal(4900, (M, Fi), 1.0, syn.BF16)
+    Pin = syn.normal(4901, (M, Fi), 1.0, syn.BF16)
+    dYin = syn.normal(4902, (M, Fi), 1.0, syn.BF16)
+    X, A, B, dZ = (d[k] for k in ("X", "A", "B", "dZ"))
+    Y, Pre = ops.column_fwd(dev(X), dev(A), "gelu")
+    Z = ops.row_fwd(dev(Yin), dev(B))
+    dYo, dB, _ = ops.row_bwd(dev(dZ), dev(Yin), dev(B))
+    dX, dA, _, _, _ = ops.column_bwd(dev(dYin), dev(X), dev(A), Pre=dev(Pin), act="gelu")
+    torch.cuda.synchronize()
+    ms = sample_idx(M, 32, 8)
+    ks = sample_idx(Fi, 32, 9)
+    ns = sample_idx(H, 32, 10)
+    Yr, Pr = oracle.column_fwd(X.f64[ms], A.f64, "gelu")
+    assert_close("Y", rows(Y, ms), Yr, BF)
+    assert_close("Pre", rows(Pre, ms), Pr, BF)
+    assert_close("Z", rows(Z, ms), oracle.row_fwd(Yin.f64[ms], B.f64), BF)
+    assert_close("dY", rows(dYo, ms), oracle.dgrad(dZ.f64[ms], B.f64), BF)
+    assert_close("dB", cols(dB, ns), oracle.wgrad(Yin.f64, dZ.f64[:, ns]), BF)
+    r = oracle.column_bwd(dYin.f64[ms], X.f64[ms], A.f64, Pin.f64[ms], "gelu")
+    assert_close("dXpart", rows(dX, ms), r[0], BF)
+    r = oracle.column_bwd(dYin.f64[:, ks], X.f64, A.f64[:, ks], Pin.f64[:, ks], "gelu")
+    assert_close("dA", cols(dA, ks), r[1], BF)
+
+
+def test_c4_four_way_partial_sum_sampled():
+    cfg = syn.C4
+    seeded = [syn.normal(4950 + i, (cfg.M, cfg.H), 1.0, syn.BF16) for i in range(cfg.t)]
+    buf, N = ops.stack_partials([dev(p) for p in seeded])
+    Z = ops.sum_partials(buf, N)
+    torch.cuda.synchronize()
+    ms = sample_idx(cfg.M, 64, 11)
+    ref = oracle.sum_partials([p.f64[ms] for p in seeded])
+    assert_close("Z", rows(Z, ms), ref, BF)
+
+
+# ---------------------------------------------------------------------------
+# c5: vocab-parallel LM head + CE partials.
+# ---------------------------------------------------------------------------
+
+def test_c5_shard0_full_size_sampled():
+    cfg = syn.C5
+    d = syn.vocab_inputs(cfg, shard=0)
+    target = d["target"].copy()
+    # make sure a good number of sampled tokens have their target in shard 0
+    ms = sample_idx(cfg.M, 64, 12)
+    target[ms[::2]] = (ms[::2] * 7919) % cfg.Vr
+    m, s, tg = ops.vocab_ce_partials(dev(d["H"]), dev(d["W"]), torch.from_numpy(target).cuda(), d["v0"])
+    torch.cuda.synchronize()
+    rm, rs, rt = oracle.vocab_ce_partials(d["H"].f64[ms], d["W"].f64, target[ms], d["v0"])
+    gl, gt, gloss = oracle.lse_recombine([(host64(m)[ms], host64(s)[ms], host64(tg)[ms])])
+    rl, rt2, rloss = oracle.lse_recombine([(rm, rs, rt)])
+    assert_close("lse", gl, rl, TOL_CE)
+    assert_close("tgt", gt, rt2, TOL_CE)
+    assert_close("loss", gloss, rloss, TOL_CE)
+
+
+def test_c5_eight_shards_recombined():
+    cfg = syn.C5
+    Mt = 64
+    base = syn.vocab_inputs(cfg, shard=0, M=cfg.M)
+    H = base["H"]
+    Hs = syn.Tensor(syn.BF16, np.ascontiguousarray(H.raw[:Mt]), (Mt, cfg.H))
+    target = base["target"][:Mt].copy()
+    Hd = dev(Hs)
+    tgt_d = torch.from_numpy(target).cuda()
+    gparts, rparts = [], []
+    for r in range(cfg.shards):
+        W = syn.vocab_inputs(cfg, shard=r, M=1)["W"]
+        v0 = r * cfg.Vr
+        m, s, tg = ops.vocab_ce_partials(Hd, dev(W), tgt_d, v0)
+        torch.cuda.synchronize()
+        gparts.append((host64(m), host64(s), host64(tg)))
+        rparts.append(oracle.vocab_ce_partials(Hs.f64, W.f64, target, v0))
+        del W
+    gl, gt, gloss = oracle.lse_recombine(gparts)
+    rl, rt, rloss = oracle.lse_recombine(rparts)
+    assert_close("lse", gl, rl, TOL_CE)
+    assert_close("tgt", gt, rt, TOL_CE)
+    assert_close("loss", gloss, rloss, TOL_CE)

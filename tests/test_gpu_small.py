@@ -1,0 +1,214 @@
+"""GPU parity on the pages' worked examples and on small ragged shapes.
+
+Every call goes through the C ABI (via the torch front end of the binding)
+and is compared element by element with the float64 oracle on the same
+seeded inputs."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+
+from .gpu_util import TOL, assert_close, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ops = pytest.importorskip("tensor_transformer_linear_tp_amd.torch_ops")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DTYPES = [syn.FP32, syn.BF16]
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _t(values, dtype):
+    return dev(syn.from_values(values, dtype))
+
+
+def _exact(gpu, ref):
+    assert np.array_equal(host64(gpu), np.asarray(ref, dtype=np.float64)), (host64(gpu), ref)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_v1_block_2x2_on_gpu(dtype):
+    g = _golden("v1_block_2x2.json")
+    X = np.array(g["X"], np.float32)
+    A = np.array(g["A"], np.float32)
+    for i in range(2):
+        Y, _ = ops.column_fwd(_t(X, dtype), _t(A[:, i:i + 1], dtype))
+        torch.cuda.synchronize()
+        _exact(Y, g["column_t2"]["shard_outputs"][i])
+    parts = [ops.row_fwd(_t(X[:, i:i + 1], dtype), _t(A[i:i + 1, :], dtype)) for i in range(2)]
+    torch.cuda.synchronize()
+    for i in range(2):
+        _exact(parts[i], g["row_t2"]["shard_partials"][i])
+    buf, N = ops.stack_partials(parts)
+    Z = ops.sum_partials(buf, N)
+    torch.cuda.synchronize()
+    _exact(Z, g["row_t2"]["sum"])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_v2_column_t3_on_gpu(dtype):
+    g = _golden("v2_column_t3.json")
+    X = np.array(g["X"], np.float32)
+    W = np.array(g["W"], np.float32)
+    dY = np.array(g["dY"], np.float32)
+    parts = []
+    for i in range(3):
+        Xd = _t(X, dtype)
+        Y, _ = ops.column_fwd(Xd, _t(W[:, i:i + 1], dtype))
+        dXp, dA, dA2, db, db2 = ops.column_bwd(_t(dY[:, i:i + 1], dtype), Xd, _t(W[:, i:i + 1], dtype),
+                                                want_db=True)
+        torch.cuda.synchronize()
+        _exact(Y, g["Y_shards"][i])
+        _exact(dA, g["dW_shards"][i])
+        _exact(dXp, g["dX_parts"][i])
+        _exact(db, dY[0, i:i + 1])
+        assert dA2 is None and db2 is None
+        parts.append(dXp)
+    buf, N = ops.stack_partials(parts)
+    dX = ops.sum_partials(buf, N)
+    torch.cuda.synchronize()
+    _exact(dX, g["dX"])
+
+
+def test_bf16_output_rounding_is_nearest_even():
+    # Products exact in fp32; ties must go to the even bf16 neighbour.
+    h = 2.0 ** -9
+    X = np.array([[1.0, h]], np.float32)
+    A = np.array([[1, 1, 1, 1, 1], [2, 6, -1, 3, -3]], np.float32)
+    Y, _ = ops.column_fwd(_t(X, syn.BF16), _t(A, syn.BF16))
+    torch.cuda.synchronize()
+    _exact(Y, [[1.0, 1.015625, 1.0, 1.0078125, 0.9921875]])
+
+
+SHAPES = [(1, 1, 1), (5, 3, 17), (129, 200, 72), (300, 520, 136), (520, 300, 1030)]
+
+
+def _inputs(dtype, M, N, K, seed, act):
+    s = 1_000_000 + seed
+    d = {
+        "X": syn.normal(s + 1, (M, K), 1.0, dtype),
+        "A": syn.normal(s + 2, (K, N), 0.1, dtype),
+        "A2": syn.normal(s + 3, (K, N), 0.1, dtype),
+        "b": syn.normal(s + 4, (N,), 0.5, dtype),
+        "b2": syn.normal(s + 5, (N,), 0.5, dtype),
+        "dY": syn.normal(s + 6, (M, N), 1.0, dtype),
+        "Pre": syn.normal(s + 7, (M, 2 * N if act == "swiglu" else N), 1.0, dtype),
+        "B": syn.normal(s + 8, (N, K), 0.1, dtype),      # row weight [K_i = N, N_out = K]
+        "dZ": syn.normal(s + 9, (M, K), 1.0, dtype),
+    }
+    return d
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("act", ["none", "gelu", "swiglu"])
+@pytest.mark.parametrize("bias", [False, True])
+def test_column_fwd_ragged(dtype, shape, act, bias):
+    M, N, K = shape
+    d = _inputs(dtype, M, N, K, 7 * M + 13 * N + 17 * K + 3 * ["none", "gelu", "swiglu"].index(act) + int(bias), act)
+    Y, Pre = ops.column_fwd(dev(d["X"]), dev(d["A"]), act, A2=dev(d["A2"]) if act == "swiglu" else None,
+                            bias=dev(d["b"]) if bias else None,
+                            bias2=dev(d["b2"]) if (bias and act == "swiglu") else None)
+    torch.cuda.synchronize()
+    Yr, Prer = oracle.column_fwd(d["X"].f64, d["A"].f64, act, bias=d["b"].f64 if bias else None,
+                                 A2=d["A2"].f64 if act == "swiglu" else None,
+                                 bias2=d["b2"].f64 if (bias and act == "swiglu") else None)
+    assert_close("Y", host64(Y), Yr, TOL[dtype])
+    if act != "none":
+        assert_close("Pre", host64(Pre), Prer, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_row_fwd_and_bwd_ragged(dtype, shape):
+    M, N, K = shape   # row shard: X_i [M, N], B_i [N, K], Z [M, K]
+    d = _inputs(dtype, M, N, K, 7 + M, "none")
+    Xi, Bi = dev(d["dY"]), dev(d["B"])
+    Z = ops.row_fwd(Xi, Bi)
+    dX, dB, db = ops.row_bwd(dev(d["dZ"]), Xi, Bi, want_db=True)
+    torch.cuda.synchronize()
+    assert_close("Z", host64(Z), oracle.row_fwd(d["dY"].f64, d["B"].f64), TOL[dtype])
+    rdX, rdB, rdb = oracle.row_bwd(d["dZ"].f64, d["dY"].f64, d["B"].f64)
+    assert_close("dX", host64(dX), rdX, TOL[dtype])
+    assert_close("dB", host64(dB), rdB, TOL[dtype])
+    assert_close("db", host64(db), rdb, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("act", ["none", "gelu", "swiglu"])
+def test_column_bwd_ragged(dtype, shape, act):
+    M, N, K = shape
+    d = _inputs(dtype, M, N, K, 11 + N, act)
+    sw = act == "swiglu"
+    dX, dA, dA2, db, db2 = ops.column_bwd(dev(d["dY"]), dev(d["X"]), dev(d["A"]),
+                                          Pre=dev(d["Pre"]) if act != "none" else None, act=act,
+                                          A2=dev(d["A2"]) if sw else None, want_db=True)
+    torch.cuda.synchronize()
+    r = oracle.column_bwd(d["dY"].f64, d["X"].f64, d["A"].f64, d["Pre"].f64 if act != "none" else None, act,
+                          d["A2"].f64 if sw else None)
+    assert_close("dXpart", host64(dX), r[0], TOL[dtype])
+    assert_close("dA", host64(dA), r[1], TOL[dtype])
+    assert_close("db", host64(db), r[3], TOL[dtype])
+    if sw:
+        assert_close("dA2", host64(dA2), r[2], TOL[dtype])
+        assert_close("db2", host64(db2), r[4], TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("t", [1, 2, 3, 8])
+def test_sum_partials_with_bias_once(dtype, t):
+    M, N = 37, 70
+    seeded = [syn.normal(50 + i, (M, N), 1.0, dtype) for i in range(t)]
+    parts = [dev(p) for p in seeded]
+    bias = syn.normal(49, (N,), 1.0, dtype)
+    buf, n = ops.stack_partials(parts)
+    Z = ops.sum_partials(buf, n, bias=dev(bias))
+    Zin = ops.sum_partials(buf, n, out=buf[0, :, :n])      # exact aliasing of part 0 is allowed
+    torch.cuda.synchronize()
+    ref = oracle.sum_partials([p.f64 for p in seeded], bias=bias.f64)
+    assert_close("Z", host64(Z), ref, TOL[dtype])
+    assert_close("Z in place", host64(Zin), oracle.sum_partials([p.f64 for p in seeded]), TOL[dtype])
+
+
+@pytest.mark.parametrize("M,Vr,K", [(1, 1, 8), (37, 300, 72), (300, 600, 136), (260, 18992, 64)])
+def test_vocab_ce_small(M, Vr, K):
+    rng = np.random.default_rng(M + Vr)
+    H = syn.normal(70 + M, (M, K), 1.0, syn.BF16)
+    W = syn.normal(71 + Vr, (Vr, K), 0.3, syn.BF16)
+    v0 = 1000
+    target = rng.integers(v0 - 50, v0 + Vr + 50, size=M).astype(np.int32)
+    target[: min(M, 3)] = [v0, v0 + Vr - 1, -5][: min(M, 3)]
+    m, s, tg = ops.vocab_ce_partials(dev(H), dev(W), torch.from_numpy(target).cuda(), v0)
+    torch.cuda.synchronize()
+    rm, rs, rt = oracle.vocab_ce_partials(H.f64, W.f64, target, v0)
+    gl, gt, gloss = oracle.lse_recombine([(host64(m), host64(s), host64(tg))])
+    rl, rt2, rloss = oracle.lse_recombine([(rm, rs, rt)])
+    assert_close("lse", gl, rl, 1e-3)
+    assert_close("tgt", gt, rt2, 1e-3)
+    assert_close("loss", gloss, rloss, 1e-3)
+    owned = (target >= v0) & (target < v0 + Vr)
+    assert np.all(host64(tg)[~owned] == 0.0)
+
+
+def test_deterministic_bitwise():
+    d = _inputs(syn.BF16, 520, 300, 1030, 3, "swiglu")
+    outs = []
+    for _ in range(2):
+        Y, Pre = ops.column_fwd(dev(d["X"]), dev(d["A"]), "swiglu", A2=dev(d["A2"]))
+        dX, dA, dA2, _, _ = ops.column_bwd(dev(d["dY"]), dev(d["X"]), dev(d["A"]), Pre=dev(d["Pre"]),
+                                           act="swiglu", A2=dev(d["A2"]))
+        torch.cuda.synchronize()
+        outs.append([x.cpu() for x in (Y, Pre, dX, dA, dA2)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
