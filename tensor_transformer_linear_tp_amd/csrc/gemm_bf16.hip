@@ -28,37 +28,45 @@
 namespace tps {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int NTHREADS = 256;
-constexpr int TILE_BYTES = 256 * BK * 2;      // 32 KiB per operand tile
-constexpr int BUF_BYTES = 2 * TILE_BYTES;     // A + B
+constexpr int TILE_BYTES = 256 * BK * 2;      // 16 KiB per operand and stage
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // A + B
+constexpr int NSTAGE = 4;                     // LDS ring depth; copies run NSTAGE-1 stages ahead
 constexpr int GROUP_M = 8;                    // tile rows per L2 group
 
 // ---- LDS address maps ------------------------------------------------------
-// K-contiguous [256][64]: 128-byte rows, 8 chunks of 16 bytes each.
-__device__ __forceinline__ int kc_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int kc_off(int r, int c) { return r * 128 + ((c ^ kc_swz(r)) << 4); }
-// MN-contiguous [64][W]: rows of W bf16 (512 or 256 bytes); rows k%4 = 0,1,2,3
+// K-contiguous [256][32]: 64-byte rows of 4 chunks of 16 bytes; chunk c of row
+// r sits at c ^ kc_swz(r), which spreads any 16 consecutive rows reading the
+// same logical chunk over all 16 chunk slots of a 256-byte bank cycle.
+__device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ kc_swz(r)) << 4); }
+// MN-contiguous [32][W]: rows of W bf16 (512 or 256 bytes); rows k%4 = 0,1,2,3
 // XOR the chunk index with 0, 6, 10, 12.
 __device__ __forceinline__ int mn_swz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }
 template <int ROWB>
 __device__ __forceinline__ int mn_off(int k, int c) { return k * ROWB + ((c ^ mn_swz(k)) << 4); }
 
 // ---- global -> LDS streaming ---------------------------------------------------
-// Each operand stage (32 KiB) is copied by 32 wave-level buffer_load_dwordx4
-// ... lds instructions, 8 per wave; each writes 1 KiB of LDS contiguously in
+// Each operand stage (16 KiB) is copied by 16 wave-level buffer_load_dwordx4
+// ... lds instructions, 4 per wave; each writes 1 KiB of LDS contiguously in
 // lane order, so a lane's global address is chosen to land its 16 bytes at
 // the swizzled position.  Reads past the operand's extent return zero (the
 // buffer descriptor's range), which zero-fills rows beyond M/N and, for
 // MN-contiguous operands, rows beyond K.  The K tail of K-contiguous operands
 // lies inside the extent and is zeroed in LDS afterwards (kc_zero_tail).
+constexpr int DMA_PER_OPERAND = 4;            // copy instructions per wave per operand stage
+
+// Copy stream of one operand of one K segment of one tile.  Wave-uniform
+// scalars plus one or two per-lane byte offsets; block j of this wave adds a
+// uniform row offset at issue time.
+enum StreamKind : int { S_KC = 0, S_MN256 = 1, S_MN128 = 2 };
+
 struct OpStream {
-  const char* base;   // stage-0 origin of this wave's operand (bytes), wave-uniform
+  const char* base;   // stage-0 origin (bytes)
   int64_t remain;     // bytes from base to the end of the operand's extent
-  int64_t step;       // bytes between K stages
-  uint32_t voff[8];   // per-lane byte offsets of this wave's 8 blocks
-  int lds_off;        // byte offset of this wave's first block inside the tile
-  int lds_stride;     // bytes between this wave's blocks
+  int64_t ld;         // leading dimension (elements)
+  uint32_t lo0, lo1;  // per-lane byte offsets (lo1: odd blocks of S_MN256)
 };
 
 __device__ __forceinline__ int64_t extent_bytes(int64_t rows, int64_t ld, int64_t width) {
@@ -66,59 +74,69 @@ __device__ __forceinline__ int64_t extent_bytes(int64_t rows, int64_t ld, int64_
 }
 
 // K-contiguous operand: tile rows [row0, row0+256) of a [rows][K] matrix.
-__device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t rows, int64_t K, int64_t row0,
-                                              int wave) {
+// Block b (16 rows) of the stage: lane L copies row 16b + L/4, logical chunk
+// (L%4) ^ kc_swz(row) -- the swizzle only depends on the row's low 4 bits.
+__device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t rows, int64_t K, int64_t row0) {
   const int lane = threadIdx.x & 63;
   OpStream s;
   s.base = static_cast<const char*>(p) + row0 * ld * 2;
   s.remain = extent_bytes(rows, ld, K) - row0 * ld * 2;
-  s.step = BK * 2;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int b = 8 * wave + j;                      // block: rows 8b .. 8b+7
-    const int r = 8 * b + (lane >> 3);
-    const int c = (lane & 7) ^ kc_swz(r);            // logical chunk stored at physical slot lane&7
-    s.voff[j] = (uint32_t)((r * ld + 8 * c) * 2);
-  }
-  s.lds_off = 8 * wave * 1024;
-  s.lds_stride = 1024;
+  s.ld = ld;
+  const int r = lane >> 2;
+  const int c = (lane & 3) ^ kc_swz(r);
+  s.lo0 = s.lo1 = (uint32_t)((r * ld + 8 * c) * 2);
   return s;
 }
 
-// MN-contiguous operand: columns [col0, col0 + W) of a [K][cols] matrix,
-// W = 256 (512-byte rows, 2 rows per block) or 128 (256-byte rows, 4 rows
-// per block; `sub` selects which 16 KiB half of the tile this wave fills).
+// MN-contiguous operand: columns [col0, col0 + W) of a [K][cols] matrix.
+// W = 256: block b holds rows 2b, 2b+1 (lane L: row 2b + L/32, chunk L%32);
+// W = 128: block b holds rows 4b..4b+3 (lane L: row 4b + L/16, chunk L%16).
 template <int W>
-__device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t cols, int64_t K, int64_t col0,
-                                              int wave) {
+__device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t cols, int64_t K, int64_t col0) {
   const int lane = threadIdx.x & 63;
-  constexpr int ROWS_PER_BLOCK = 1024 / (W * 2);
   constexpr int CHUNKS = W / 8;
   OpStream s;
   s.base = static_cast<const char*>(p) + col0 * 2;
   s.remain = extent_bytes(K, ld, cols) - col0 * 2;
-  s.step = (int64_t)BK * ld * 2;
-  const int wb = (W == 256) ? wave : (wave & 1);     // W = 128: waves {0,1} and {2,3} fill the two halves
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int b = 8 * wb + j;
-    const int k = ROWS_PER_BLOCK * b + lane / CHUNKS;
-    const int c = (lane % CHUNKS) ^ mn_swz(k);
-    s.voff[j] = (uint32_t)((k * ld + 8 * c) * 2);
-  }
-  s.lds_off = (W == 256) ? 8 * wave * 1024 : (wave >> 1) * 16384 + 8 * wb * 1024;
-  s.lds_stride = 1024;
+  s.ld = ld;
+  const int k = lane / CHUNKS;   // row within the block
+  const int c0 = (lane % CHUNKS) ^ mn_swz(k);
+  const int c1 = (lane % CHUNKS) ^ mn_swz(k + 2);   // W = 256, odd blocks start at row 2 (mod 4)
+  s.lo0 = (uint32_t)((k * ld + 8 * c0) * 2);
+  s.lo1 = (uint32_t)((k * ld + 8 * c1) * 2);
   return s;
 }
 
-// Zero k >= kvalid (0 < kvalid < 64) of a K-contiguous [256][64] LDS tile.
+// Issue the copies of K stage `stage` of one operand into `tile` (this
+// wave's DMA_PER_OPERAND blocks).  live == false: empty range, zeros written.
+template <int KIND>
+__device__ __forceinline__ void stream_issue(const OpStream& st, int wave, int stage, bool live, TPS_LDS char* tile) {
+  const int64_t step = (KIND == S_KC) ? BK * 2 : (int64_t)BK * st.ld * 2;
+  const int64_t off = (int64_t)stage * step;
+  const int64_t rem = live ? st.remain - off : 0;
+  const uint32_t nrec = rem <= 0 ? 0u : (rem >= 0xffffffffll ? 0xffffffffu : (uint32_t)rem);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(live ? st.base + off : st.base), (short)0, (int)nrec, 0x00020000);
+  const int wb = (KIND == S_MN128) ? (wave & 1) : wave;
+  const int lds0 = (KIND == S_MN128) ? (wave >> 1) * (TILE_BYTES / 2) : 0;
+#pragma unroll
+  for (int j = 0; j < DMA_PER_OPERAND; ++j) {
+    const int b = DMA_PER_OPERAND * wb + j;
+    const int rows_before = (KIND == S_KC) ? 16 * b : (KIND == S_MN256 ? 2 * b : 4 * b);
+    const uint32_t lo = (KIND == S_MN256 && (j & 1)) ? st.lo1 : st.lo0;
+    const uint32_t v = lo + (uint32_t)(rows_before * st.ld * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(tile + lds0 + b * 1024), 16, v, 0, 0, 0);
+  }
+}
+
+// Zero k >= kvalid (0 < kvalid < 32) of a K-contiguous [256][32] LDS tile.
 __device__ __forceinline__ void kc_zero_tail(TPS_LDS char* tile, int kvalid) {
   const int t = threadIdx.x;
-  const int c = t & 7;
+  const int c = t & 3;
   if (8 * c + 8 <= kvalid) return;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (t >> 3) + 32 * i;
+  for (int i = 0; i < 4; ++i) {
+    const int r = (t >> 2) + 64 * i;
     TPS_LDS u32x4* q = reinterpret_cast<TPS_LDS u32x4*>(tile + kc_off(r, c));
     u32x4 v = *q;
 #pragma unroll
@@ -129,6 +147,13 @@ __device__ __forceinline__ void kc_zero_tail(TPS_LDS char* tile, int kvalid) {
     }
     *q = v;
   }
+}
+
+// s_waitcnt with the given vector-memory and LDS counts (expcnt left free).
+template <int VM, int LGKM>
+__device__ __forceinline__ void waitcnt() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
 }
 
 // ---- LDS -> MFMA fragments ---------------------------------------------------
@@ -182,77 +207,138 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
   tn = r / gm;
 }
 
+// The LDS ring: NSTAGE distinct arrays (distinct objects, so the compiler
+// tracks the copies into each separately).
+__shared__ __attribute__((aligned(16))) char lds_ring0[STAGE_BYTES];
+__shared__ __attribute__((aligned(16))) char lds_ring1[STAGE_BYTES];
+__shared__ __attribute__((aligned(16))) char lds_ring2[STAGE_BYTES];
+__shared__ __attribute__((aligned(16))) char lds_ring3[STAGE_BYTES];
+static_assert(NSTAGE == 4, "ring_slot enumerates four arrays");
+
+template <int S>
+__device__ __forceinline__ TPS_LDS char* ring_slot() {
+  if constexpr (S == 0) return (TPS_LDS char*)lds_ring0;
+  else if constexpr (S == 1) return (TPS_LDS char*)lds_ring1;
+  else if constexpr (S == 2) return (TPS_LDS char*)lds_ring2;
+  else return (TPS_LDS char*)lds_ring3;
+}
+
 // ---- main loop -------------------------------------------------------------------
-// Two LDS stages held in two distinct __shared__ arrays: while the MFMAs
-// consume one stage, the copy engine fills the other.  Because the arrays
-// are distinct objects, the compiler can see that reads of one stage do not
-// depend on copies into the other and adds no wait for them; the barrier at
-// the top of each step (with its vmcnt(0)) makes the step's stage complete
-// and visible.  The loop is unrolled by two so each step's stage is static.
-template <int LAYOUT, bool DUAL>
-struct MainLoop {
+// NSTAGE LDS stages held in NSTAGE distinct __shared__ arrays form a ring: the
+// copies of stage kt+NSTAGE-1 are issued while the MFMAs consume stage kt.
+// Because the arrays are distinct objects, the compiler's own waits on the
+// copies are per stage.  Each step waits until only the copies of the later
+// in-flight stages are outstanding (vmcnt), drains its LDS reads (so the ring
+// slot about to be refilled is no longer being read), and meets the other
+// waves at a barrier.  The loop is unrolled NSTAGE times so every step's
+// stage is static; a tile's stage count is padded to a multiple of NSTAGE
+// with empty (all-zero) stages.
+//
+// The stage stream continues across the tiles a workgroup processes: the
+// last NSTAGE-1 steps of a tile already issue the copies of the next tile's
+// first stages, so the next tile starts with a full ring and the current
+// tile's epilogue (which does not touch LDS) overlaps those copies.
+
+// Copy streams of one tile: per K segment (0, 1), one stream per operand.
+// Plain named members (no arrays of structs) keep all of it in registers.
+struct TileStreams {
+  OpStream a0, a1, b0, b1;
+  int64_t kseg0, kseg1;    // K of each segment
+  int nk0, nk, nk_pad;     // stages of segment 0, of the tile, and padded to NSTAGE
+};
+
+template <int LAYOUT, bool DUAL, bool SEG2>
+struct Pipe {
   static constexpr bool A_KC = LAYOUT != L_TN;
   static constexpr bool B_KC = LAYOUT == L_NT;
+  static constexpr int KA = A_KC ? S_KC : S_MN256;
+  static constexpr int KB = B_KC ? S_KC : (DUAL ? S_MN128 : S_MN256);
 
-  const Problem& P;
-  int64_t m0, n0;
-  TPS_LDS char* lds0;
-  TPS_LDS char* lds1;
   int wave, wm, wn;
-  OpStream sa[2], sb[2];   // per K segment
-  int nk0, nk;
+  TileStreams cur, nxt;   // nxt.nk == 0: no next tile (its copies are empty)
 
-  __device__ __forceinline__ void open_segment(int s) {
+  __device__ __forceinline__ void init_wave() {
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wm = wave >> 1;
+    wn = wave & 1;
+    init_frag_addr();
+  }
+
+  __device__ __forceinline__ void seg_streams(const Problem& P, int64_t m0, int64_t n0, bool use1, OpStream& sa,
+                                              OpStream& sb, int64_t& K) const {
     // Field-wise selection keeps the problem description in registers.
-    const void* pa = s ? P.seg[1].a : P.seg[0].a;
-    const void* pb = s ? P.seg[1].b : P.seg[0].b;
-    const int64_t lda = s ? P.seg[1].lda : P.seg[0].lda;
-    const int64_t ldb = s ? P.seg[1].ldb : P.seg[0].ldb;
-    const int64_t K = s ? P.seg[1].K : P.seg[0].K;
-    sa[s] = A_KC ? stream_kc(pa, lda, P.M, K, m0, wave) : stream_mn<256>(pa, lda, P.M, K, m0, wave);
+    const void* pa = use1 ? P.seg[1].a : P.seg[0].a;
+    const void* pb = use1 ? P.seg[1].b : P.seg[0].b;
+    const int64_t lda = use1 ? P.seg[1].lda : P.seg[0].lda;
+    const int64_t ldb = use1 ? P.seg[1].ldb : P.seg[0].ldb;
+    K = use1 ? P.seg[1].K : P.seg[0].K;
+    sa = A_KC ? stream_kc(pa, lda, P.M, K, m0) : stream_mn<256>(pa, lda, P.M, K, m0);
     if (B_KC) {
-      sb[s] = stream_kc(pb, ldb, P.N, K, n0, wave);
+      sb = stream_kc(pb, ldb, P.N, K, n0);
     } else if (DUAL) {   // waves 0,1 stream the gate weight, waves 2,3 the up weight
       const bool up = (wave >> 1) != 0;
-      sb[s] = stream_mn<128>(up ? P.b_up : pb, up ? P.ldb_up : ldb, P.N, K, n0, wave);
+      sb = stream_mn<128>(up ? P.b_up : pb, up ? P.ldb_up : ldb, P.N, K, n0);
     } else {
-      sb[s] = stream_mn<256>(pb, ldb, P.N, K, n0, wave);
+      sb = stream_mn<256>(pb, ldb, P.N, K, n0);
     }
   }
 
-  // Issue the copies of global K stage kt into `dst`; a stage past the end
-  // is issued with an empty range (no memory is read, zeros are written).
-  __device__ __forceinline__ void issue(int kt, TPS_LDS char* dst) {
-    const bool s1 = kt >= nk0;
-    const int stage = s1 ? kt - nk0 : kt;
-    const bool live = kt < nk;
-    issue_one(s1, sa, stage, live, dst);
-    issue_one(s1, sb, stage, live, dst + TILE_BYTES);
+  __device__ __forceinline__ TileStreams make_streams(const Problem& P, int64_t m0, int64_t n0) const {
+    TileStreams T;
+    seg_streams(P, m0, n0, false, T.a0, T.b0, T.kseg0);
+    if (SEG2) {
+      seg_streams(P, m0, n0, true, T.a1, T.b1, T.kseg1);
+    } else {
+      T.a1 = T.a0;
+      T.b1 = T.b0;
+      T.kseg1 = T.kseg0;
+    }
+    T.nk0 = (int)((T.kseg0 + BK - 1) / BK);
+    T.nk = T.nk0 + (SEG2 ? (int)((T.kseg1 + BK - 1) / BK) : 0);
+    T.nk_pad = (T.nk + NSTAGE - 1) / NSTAGE * NSTAGE;
+    return T;
   }
 
-  static __device__ __forceinline__ void issue_one(bool s1, const OpStream (&st)[2], int stage, bool live,
-                                                   TPS_LDS char* tile) {
-    const char* base = s1 ? st[1].base : st[0].base;
-    const int64_t step = s1 ? st[1].step : st[0].step;
-    const int64_t remain = s1 ? st[1].remain : st[0].remain;
-    const int64_t off = (int64_t)stage * step;
-    const int64_t rem = live ? remain - off : 0;
-    const uint32_t nrec = rem <= 0 ? 0u : (rem >= 0xffffffffll ? 0xffffffffu : (uint32_t)rem);
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), (short)0, (int)nrec, 0x00020000);
-    const int lds_off = st[0].lds_off;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t v = s1 ? st[1].voff[j] : st[0].voff[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(tile + lds_off + j * 1024), 16, v, 0, 0, 0);
-    }
+  __device__ __forceinline__ void no_next() {
+    nxt = cur;
+    nxt.nk = 0;
+    nxt.nk0 = 0;
+    nxt.nk_pad = 0;
+  }
+
+  // Issue the copies of stage ks into `dst`.  ks counts from the current
+  // tile's first stage; with MAYBE_NEXT, stages past its padded end belong to
+  // the next tile.  A stage that does not exist is issued with an empty range.
+  template <bool MAYBE_NEXT>
+  __device__ __forceinline__ void issue(int ks, TPS_LDS char* dst) {
+    const bool in_next = MAYBE_NEXT && ks >= cur.nk_pad;
+    const TileStreams& T = cur;
+    const int s = in_next ? ks - cur.nk_pad : ks;
+    const int nk0 = in_next ? nxt.nk0 : T.nk0;
+    const int nk = in_next ? nxt.nk : T.nk;
+    const bool s1 = SEG2 && s >= nk0;
+    const int stage = s1 ? s - nk0 : s;
+    const bool live = s < nk;
+    stream_issue<KA>(sel(in_next, s1, cur.a0, cur.a1, nxt.a0, nxt.a1), wave, stage, live, dst);
+    stream_issue<KB>(sel(in_next, s1, cur.b0, cur.b1, nxt.b0, nxt.b1), wave, stage, live, dst + TILE_BYTES);
+  }
+
+  static __device__ __forceinline__ OpStream sel(bool in_next, bool s1, const OpStream& c0, const OpStream& c1,
+                                                 const OpStream& n0, const OpStream& n1) {
+    OpStream r;
+    r.base = in_next ? (s1 ? n1.base : n0.base) : (s1 ? c1.base : c0.base);
+    r.remain = in_next ? (s1 ? n1.remain : n0.remain) : (s1 ? c1.remain : c0.remain);
+    r.ld = in_next ? (s1 ? n1.ld : n0.ld) : (s1 ? c1.ld : c0.ld);
+    r.lo0 = in_next ? (s1 ? n1.lo0 : n0.lo0) : (s1 ? c1.lo0 : c0.lo0);
+    r.lo1 = in_next ? (s1 ? n1.lo1 : n0.lo1) : (s1 ? c1.lo1 : c0.lo1);
+    return r;
   }
 
   // Per-lane LDS byte addresses of the fragments, computed once.  A fragment
   // read is then addr + a compile-time offset (K sub-step, block), which the
   // ds_read instruction's offset field absorbs.
   //   K-contiguous operand: one base per 16-deep K sub-step (the swizzle
-  //   mixes k into the chunk index); blocks are +32 rows = +4096 bytes.
+  //   mixes k into the chunk index); blocks are +32 rows = +2048 bytes.
   //   MN-contiguous operand: one base per 32-wide block (the swizzle mixes
   //   the column into the chunk index); K sub-steps are +16 rows.
   int adA[4], adB[4];
@@ -264,7 +350,7 @@ struct MainLoop {
     for (int x = 0; x < 4; ++x) {
       if (A_KC) {
         const int r = 128 * wm + (lane & 31);
-        adA[x] = kc_off(r, 2 * x + hi32);
+        adA[x] = kc_off(r, 2 * (x & 1) + hi32);
       } else {
         const int col = 128 * wm + 32 * x + 16 * (h & 1) + 4 * (q & 3);
         const int k = 8 * (h >> 1) + (q >> 2);
@@ -272,11 +358,11 @@ struct MainLoop {
       }
       if (B_KC) {
         const int r = 128 * wn + (lane & 31);
-        adB[x] = TILE_BYTES + kc_off(r, 2 * x + hi32);
+        adB[x] = TILE_BYTES + kc_off(r, 2 * (x & 1) + hi32);
       } else if (DUAL) {
         const int col = 64 * wn + 32 * (x & 1) + 16 * (h & 1) + 4 * (q & 3);
         const int k = 8 * (h >> 1) + (q >> 2);
-        adB[x] = TILE_BYTES + (x >> 1) * 16384 + mn_off<256>(k, col >> 3) + (col & 7) * 2;
+        adB[x] = TILE_BYTES + (x >> 1) * (TILE_BYTES / 2) + mn_off<256>(k, col >> 3) + (col & 7) * 2;
       } else {
         const int col = 128 * wn + 32 * x + 16 * (h & 1) + 4 * (q & 3);
         const int k = 8 * (h >> 1) + (q >> 2);
@@ -295,18 +381,18 @@ struct MainLoop {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  // Fragment register sets: sub-step kk of a stage lives in set kk & 1.
+  // Fragment register sets: sub-step kk of a stage lives in set kk.
   bf16x8 af[2][4], bfr[2][4];
 
-  __device__ __forceinline__ void load(const TPS_LDS char* base, int kk, int r) {
+  __device__ __forceinline__ void load(const TPS_LDS char* base, int kk) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      af[r][i] = A_KC ? rd_kc(base + adA[kk] + 4096 * i) : rd_mn(base + adA[i] + 16 * kk * 512, 512);
+      af[kk][i] = A_KC ? rd_kc(base + adA[kk] + 2048 * i) : rd_mn(base + adA[i] + 16 * kk * 512, 512);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (B_KC) bfr[r][j] = rd_kc(base + adB[kk] + 4096 * j);
-      else if (DUAL) bfr[r][j] = rd_mn(base + adB[j] + 16 * kk * 256, 256);
-      else bfr[r][j] = rd_mn(base + adB[j] + 16 * kk * 512, 512);
+      if (B_KC) bfr[kk][j] = rd_kc(base + adB[kk] + 2048 * j);
+      else if (DUAL) bfr[kk][j] = rd_mn(base + adB[j] + 16 * kk * 256, 256);
+      else bfr[kk][j] = rd_mn(base + adB[j] + 16 * kk * 512, 512);
     }
   }
 
@@ -318,6 +404,14 @@ struct MainLoop {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[r][j], af[r][i], acc[i][j], 0, 0, 0);
   }
 
+  __device__ __forceinline__ void zero_set1() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[1][i] = bf16x8{};
+      bfr[1][i] = bf16x8{};
+    }
+  }
+
   // Ask the scheduler to alternate one MFMA with one LDS read (and, in the
   // first phase of a step, one global->LDS copy), instead of loading each
   // fragment just before its first use.
@@ -325,92 +419,158 @@ struct MainLoop {
   static __device__ __forceinline__ void interleave(bool with_copies) {
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-      if (g < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      if (with_copies) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+      if (g < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // DS read
+      if (with_copies && g < 2 * DMA_PER_OPERAND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // One 64-deep K step on the stage in `cur`, prefetching stage kt+1 into
-  // `nxt`.  Software pipeline: the MFMAs of the previous stage's last
-  // sub-step (operands already in registers, set 1) run after the barrier,
-  // covering the latency of this stage's first fragment reads.
-  __device__ __forceinline__ void step(int kt, TPS_LDS char* cur, TPS_LDS char* nxt, f32x16 (&acc)[4][4]) {
-    __syncthreads();                                   // stage kt landed everywhere; stage kt-1 fully read
-    const bool s1 = kt >= nk0;
-    const int64_t kseg = s1 ? P.seg[1].K : P.seg[0].K;
-    const int64_t k0 = (int64_t)(s1 ? kt - nk0 : kt) * BK;
-    if ((A_KC || B_KC) && k0 + BK > kseg) {            // K tail of K-contiguous operands
-      if (A_KC) kc_zero_tail(cur, (int)(kseg - k0));
-      if (B_KC) kc_zero_tail(cur + TILE_BYTES, (int)(kseg - k0));
-      __syncthreads();
+  // One 32-deep K step on ring slot S (stage kt of the current tile).
+  // Software pipeline: the MFMAs of the previous stage's second sub-step
+  // (operands already in register set 1) run after the barrier, covering
+  // the latency of this stage's first fragment reads.
+  template <int S, bool MAYBE_NEXT>
+  __device__ __forceinline__ void step(int kt, f32x16 (&acc)[4][4]) {
+    TPS_LDS char* cur_slot = ring_slot<S>();
+    // Stage kt's copies are complete once only the later NSTAGE-2 stages'
+    // copies (2 * DMA_PER_OPERAND each) remain outstanding; lgkmcnt(0)
+    // retires this wave's reads of the slot that is refilled below.
+    waitcnt<(NSTAGE - 2) * 2 * DMA_PER_OPERAND, 0>();
+    __builtin_amdgcn_s_barrier();
+    const bool s1 = SEG2 && kt >= cur.nk0;
+    const int64_t kseg = s1 ? cur.kseg1 : cur.kseg0;
+    const int64_t k0 = (int64_t)(s1 ? kt - cur.nk0 : kt) * BK;
+    if ((A_KC || B_KC) && kt < cur.nk && k0 + BK > kseg) {   // K tail of K-contiguous operands
+      if (A_KC) kc_zero_tail(cur_slot, (int)(kseg - k0));
+      if (B_KC) kc_zero_tail(cur_slot + TILE_BYTES, (int)(kseg - k0));
+      waitcnt<63, 0>();
+      __builtin_amdgcn_s_barrier();
     }
     __builtin_amdgcn_sched_barrier(0);
-    issue(kt + 1, nxt);
-    load(cur, 0, 0);
-    mma(1, acc);              // previous stage, sub-step 3
+    issue<MAYBE_NEXT>(kt + NSTAGE - 1, ring_slot<(S + NSTAGE - 1) % NSTAGE>());
+    load(cur_slot, 0);
+    mma(1, acc);              // previous stage, sub-step 1
     interleave(true);
-    load(cur, 1, 1);
-    mma(0, acc);
-    interleave(false);
-    load(cur, 2, 0);
-    mma(1, acc);
-    interleave(false);
-    load(cur, 3, 1);
+    load(cur_slot, 1);
     mma(0, acc);
     interleave(false);
   }
 
-  __device__ __forceinline__ void run(f32x16 (&acc)[4][4]) {
+  // Run the current tile.  The copies of its first NSTAGE-1 stages must
+  // already be issued.  `next` is called before the last NSTAGE steps and
+  // must set nxt (or call no_next()); those steps issue the next tile's first
+  // stages.
+  template <class NextFn>
+  __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], NextFn&& next) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0.f};
-      af[1][i] = bf16x8{};      // the first step's deferred sub-step multiplies zeros
-      bfr[1][i] = bf16x8{};
-    }
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    wm = wave >> 1;
-    wn = wave & 1;
-    nk0 = (int)((P.seg[0].K + BK - 1) / BK);
-    nk = nk0 + (P.nseg > 1 ? (int)((P.seg[1].K + BK - 1) / BK) : 0);
-    init_frag_addr();
-    open_segment(0);
-    if (P.nseg > 1) open_segment(1);
-    else sa[1] = sa[0], sb[1] = sb[0];
-    issue(0, lds0);
+    zero_set1();              // the first step's deferred sub-step multiplies zeros
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, lds0, lds1, acc);
-      step(kt + 1, lds1, lds0, acc);
+    for (; kt + NSTAGE < cur.nk_pad; kt += NSTAGE) {
+      step<0, false>(kt, acc);
+      step<1, false>(kt + 1, acc);
+      step<2, false>(kt + 2, acc);
+      step<3, false>(kt + 3, acc);
     }
-    if (kt < nk) step(kt, lds0, lds1, acc);
-    mma(1, acc);              // last stage, sub-step 3
-    __syncthreads();          // LDS is reused by the epilogue
+    next();
+    step<0, true>(kt, acc);
+    step<1, true>(kt + 1, acc);
+    step<2, true>(kt + 2, acc);
+    step<3, true>(kt + 3, acc);
+    mma(1, acc);              // last stage, sub-step 1
+  }
+
+  __device__ __forceinline__ void prologue() {
+    issue<false>(0, ring_slot<0>());
+    issue<false>(1, ring_slot<1>());
+    issue<false>(2, ring_slot<2>());
   }
 };
 
-template <int LAYOUT>
-__device__ __forceinline__ void mainloop(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[4][4],
-                                         TPS_LDS char* lds0, TPS_LDS char* lds1) {
-  if (LAYOUT == L_NN && P.epi == E_SWIGLU) {
-    MainLoop<L_NN, true> ml{P, m0, n0, lds0, lds1};
-    ml.run(acc);
-  } else {
-    MainLoop<LAYOUT, false> ml{P, m0, n0, lds0, lds1};
-    ml.run(acc);
+// ---- GEMM epilogue -------------------------------------------------------------------
+// In a 32 x 32 accumulator block a lane holds row (lane % 32) and, for each
+// register quad r4, the four consecutive columns 8*r4 + 4*(lane / 32) .. +3.
+// SwiGLU waves hold gate blocks J = 0,1 and the matching up blocks J + 2.
+//
+// Fast path (whole tile inside the output, 16-byte aligned rows, no bias;
+// the persistent kernel):
+// values are finished in fp32, packed to bf16 pairs, and one
+// v_permlane32_swap per pair of quads hands each lane eight consecutive
+// columns (lanes < 32 keep quads 0/2, lanes >= 32 take quads 1/3), written
+// with one 16-byte store.  No LDS: the ring is already filling with the next
+// tile's stages.
+//
+// Generic path (edge tiles, bias, unaligned outputs; one tile per
+// workgroup): see generic_epilogue.
+
+__device__ __forceinline__ void swap_halves(uint32_t (&pk)[8]) {
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto r = __builtin_amdgcn_permlane32_swap(pk[4 * pr + w], pk[4 * pr + 2 + w], false, false);
+      pk[4 * pr + w] = r[0];
+      pk[4 * pr + 2 + w] = r[1];
+    }
+}
+
+__device__ __forceinline__ void store_pk(uint16_t* p, const uint32_t (&pk)[8]) {
+  *reinterpret_cast<u32x4*>(p) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  *reinterpret_cast<u32x4*>(p + 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+}
+
+template <int EPI, int I, int J>
+__device__ __forceinline__ void fast_block(const Problem& P, int64_t m0, int64_t n0, const f32x16& a,
+                                           const f32x16& b) {
+  constexpr bool dual = EPI == E_SWIGLU;
+  if (dual && J >= 2) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int64_t m = m0 + 128 * wm + 32 * I + (lane & 31);
+  const int64_t n = n0 + (dual ? 64 * wn + 32 * (J & 1) : 128 * wn + 32 * J) + 8 * (lane >> 5);
+  uint32_t py[8], pg[8], pu[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float v0 = a[2 * q], v1 = a[2 * q + 1];
+    if (EPI == E_STORE) {
+      py[q] = pack_bf2(v0, v1);
+    } else if (EPI == E_GELU) {
+      pg[q] = pack_bf2(v0, v1);
+      py[q] = pack_bf2(gelu_f(v0), gelu_f(v1));
+    } else {
+      const float u0 = b[2 * q], u1 = b[2 * q + 1];
+      pg[q] = pack_bf2(v0, v1);
+      pu[q] = pack_bf2(u0, u1);
+      py[q] = pack_bf2(silu_f(v0) * u0, silu_f(v1) * u1);
+    }
+  }
+  swap_halves(py);
+  store_pk(static_cast<uint16_t*>(P.c) + m * P.ldc + n, py);
+  if (EPI != E_STORE) {
+    swap_halves(pg);
+    uint16_t* pre = static_cast<uint16_t*>(P.pre) + m * P.ldpre;
+    store_pk(pre + n, pg);
+    if (dual) {
+      swap_halves(pu);
+      store_pk(pre + P.N + n, pu);
+    }
   }
 }
 
-// ---- GEMM epilogue -------------------------------------------------------------------
-// The accumulators leave through LDS one 32-row slice at a time: each wave
-// parks its 32 x 128 fp32 slice in a private LDS region, then each lane
-// finishes 8 consecutive output columns per step (bias, activation, bf16
-// rounding) and writes them with 16-byte stores.  SwiGLU waves hold
-// [64 gate | 64 up] columns, so a lane pairs staged columns c and 64 + c.
-constexpr int EPI_LD = 132;                      // floats per staged row (128 + 4 padding)
-constexpr int EPI_WAVE_FLOATS = 32 * EPI_LD;     // 16.5 KiB per wave
+template <int EPI, int... Is>
+__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[4][4],
+                                              std::integer_sequence<int, Is...>) {
+  ((fast_block<EPI, Is / 4, Is % 4>(P, m0, n0, acc[Is / 4][Is % 4], acc[Is / 4][(Is % 4) ^ 2]),
+    __builtin_amdgcn_sched_barrier(0)),
+   ...);
+}
+
+// Generic path: the ring is drained, and each wave stages 32-row slices of
+// its 32 x 128 accumulator rows in its own ring slot, then finishes eight
+// columns at a time with every bound checked.
+constexpr int EPI_LD = 132;                       // floats per staged row (128 + 4 padding)
 
 __device__ __forceinline__ void stage_block(TPS_LDS float* w, const f32x16& a, int j) {
   const int lane = threadIdx.x & 63;
@@ -497,10 +657,12 @@ __device__ __forceinline__ void store_slice(const Problem& P, const TPS_LDS floa
   }
 }
 
-__device__ __forceinline__ void epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[4][4],
-                                         TPS_LDS char* lds0, TPS_LDS char* lds1) {
-  const int wave = threadIdx.x >> 6;   // waves 0,1 stage in the first array, 2,3 in the second
-  TPS_LDS float* w = reinterpret_cast<TPS_LDS float*>(wave < 2 ? lds0 : lds1) + (wave & 1) * EPI_WAVE_FLOATS;
+// The ring must be drained (no copies in flight) and every wave past its
+// last fragment read.
+__device__ __forceinline__ void generic_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[4][4]) {
+  const int wave = threadIdx.x >> 6;   // wave w stages in ring slot w (16.5 KiB of 32 KiB)
+  TPS_LDS float* w = reinterpret_cast<TPS_LDS float*>(
+      wave < 2 ? (wave == 0 ? ring_slot<0>() : ring_slot<1>()) : (wave == 2 ? ring_slot<2>() : ring_slot<3>()));
 #pragma unroll 1
   for (int i = 0; i < 4; ++i) {
     switch (i) {   // constant indices into acc keep it in registers
@@ -509,9 +671,9 @@ __device__ __forceinline__ void epilogue(const Problem& P, int64_t m0, int64_t n
       case 2: for (int j = 0; j < 4; ++j) stage_block(w, acc[2][j], j); break;
       default: for (int j = 0; j < 4; ++j) stage_block(w, acc[3][j], j); break;
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
     store_slice(P, w, m0, n0, i);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next slice overwrites
   }
 }
 
@@ -527,28 +689,100 @@ __device__ __forceinline__ Problem pick_problem(const GemmLaunch& L, bool s) {
   TPS_PICK(nseg); TPS_PICK(layout); TPS_PICK(epi); TPS_PICK(b_up); TPS_PICK(ldb_up);
   TPS_PICK(bias); TPS_PICK(bias2); TPS_PICK(c); TPS_PICK(ldc); TPS_PICK(pre); TPS_PICK(ldpre);
   TPS_PICK(tiles_m); TPS_PICK(tiles_n); TPS_PICK(tile_begin);
+  TPS_PICK(edge_only); TPS_PICK(full_m); TPS_PICK(full_n);
 #undef TPS_PICK
   return P;
 }
 
-// One kernel per (operand layout, epilogue) pair, so each role of the shard
-// path is a distinct kernel in traces and gets its own specialised epilogue.
-template <int LAYOUT, int EPI>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch L, int total_tiles) {
-  __shared__ __attribute__((aligned(16))) char lds_a[BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_b[BUF_BYTES];
-  TPS_LDS char* lds0 = (TPS_LDS char*)lds_a;
-  TPS_LDS char* lds1 = (TPS_LDS char*)lds_b;
-  const int id = xcd_remap(blockIdx.x, total_tiles);
-  Problem P = pick_problem(L, L.nprob > 1 && id >= L.p[1].tile_begin);
-  P.epi = EPI;
+// Tile of a launch: its problem (selected field-wise) and its origin.
+template <bool EDGE>
+__device__ __forceinline__ void locate(const GemmLaunch& L, int id, int epi, Problem& P, int64_t& m0, int64_t& n0) {
+  P = pick_problem(L, L.nprob > 1 && id >= L.p[1].tile_begin);
+  P.epi = epi;
+  const int local = id - P.tile_begin;
   int tm, tn;
-  tile_coords(id - P.tile_begin, P.tiles_m, P.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int64_t n0 = (int64_t)tn * (EPI == E_SWIGLU ? BN / 2 : BN);
+  if (EDGE && P.edge_only) {   // right strip (whole-tile rows, ragged columns), then the bottom strip
+    const int rn = P.tiles_n - P.full_n;
+    const int right = P.full_m * rn;
+    if (local < right) {
+      tm = local / rn;
+      tn = P.full_n + local % rn;
+    } else {
+      tm = P.full_m + (local - right) / P.tiles_n;
+      tn = (local - right) % P.tiles_n;
+    }
+  } else {
+    tile_coords(local, P.tiles_m, P.tiles_n, tm, tn);
+  }
+  m0 = (int64_t)tm * BM;
+  n0 = (int64_t)tn * (epi == E_SWIGLU ? BN / 2 : BN);
+}
+
+// Fast kernels: one per (operand layout, epilogue, K segments), so each role
+// of the shard path is a distinct kernel in traces.  Whole tiles only, no
+// bias, aligned outputs.  Persistent: workgroup w processes tiles w',
+// w' + G, w' + 2G, ... (G = grid size; w' puts the tiles that run at the
+// same time on one XCD next to each other), with the K-stage stream running
+// on from tile to tile.
+template <int LAYOUT, int EPI, bool SEG2>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch L, int total_tiles) {
+  const int G = gridDim.x;
+  int id = (G % 8 == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  if (id >= total_tiles) return;
+  constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
+  Pipe<LAYOUT, DUAL, SEG2> pipe;
+  pipe.init_wave();
+  {
+    Problem P;
+    int64_t m0, n0;
+    locate<false>(L, id, EPI, P, m0, n0);
+    pipe.cur = pipe.make_streams(P, m0, n0);
+  }
+  pipe.prologue();
+  for (;;) {
+    const int nid = id + G;
+    const bool more = nid < total_tiles;
+    f32x16 acc[4][4];
+    pipe.run_tile(acc, [&]() {
+      if (more) {
+        Problem Pn;
+        int64_t m0n, n0n;
+        locate<false>(L, nid, EPI, Pn, m0n, n0n);
+        pipe.nxt = pipe.make_streams(Pn, m0n, n0n);
+      } else {
+        pipe.no_next();
+      }
+    });
+    {
+      Problem P;
+      int64_t m0, n0;
+      locate<false>(L, id, EPI, P, m0, n0);
+      fast_epilogue<EPI>(P, m0, n0, acc, std::make_integer_sequence<int, 16>{});
+    }
+    if (!more) break;
+    id = nid;
+    pipe.cur = pipe.nxt;
+  }
+  waitcnt<0, 0>();   // trailing (empty) copies retire before the workgroup ends
+}
+
+// Generic kernels: one tile per workgroup, any shape, bias, alignment.
+template <int LAYOUT, int EPI, bool SEG2>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmLaunch L, int total_tiles) {
+  const int id = xcd_remap(blockIdx.x, total_tiles);
+  constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
+  Problem P;
+  int64_t m0, n0;
+  locate<true>(L, id, EPI, P, m0, n0);
   f32x16 acc[4][4];
-  mainloop<LAYOUT>(P, m0, n0, acc, lds0, lds1);
-  epilogue(P, m0, n0, acc, lds0, lds1);
+  Pipe<LAYOUT, DUAL, SEG2> pipe;
+  pipe.init_wave();
+  pipe.cur = pipe.make_streams(P, m0, n0);
+  pipe.prologue();
+  pipe.run_tile(acc, [&]() { pipe.no_next(); });
+  waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
+  __syncthreads();
+  generic_epilogue(P, m0, n0, acc);
 }
 
 // Row statistics of one 32-row slice (I) of a wave's 128 x 128 logit block:
@@ -629,10 +863,6 @@ __device__ __forceinline__ void ce_rows_seq(const CEArgs& a, f32x16 (&acc)[4][4]
 // [n0, n0+256).  Writes ws_ms[tn][m] = (tile max, sum exp(z - tile max)) and,
 // for the tile holding a token's target, ws_tgt[m] = z[m, target - v0].
 __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const CEArgs a, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char lds_a[BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_b[BUF_BYTES];
-  TPS_LDS char* lds0 = (TPS_LDS char*)lds_a;
-  TPS_LDS char* lds1 = (TPS_LDS char*)lds_b;
   const int id = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   int tm, tn;
   tile_coords(id, tiles_m, tiles_n, tm, tn);
@@ -645,7 +875,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const CEArgs a, in
   P.layout = L_NT;
   P.epi = E_STORE;
   f32x16 acc[4][4];
-  mainloop<L_NT>(P, m0, n0, acc, lds0, lds1);
+  {
+    Pipe<L_NT, false, false> pipe;
+    pipe.init_wave();
+    pipe.cur = pipe.make_streams(P, m0, n0);
+    pipe.prologue();
+    pipe.run_tile(acc, [&]() { pipe.no_next(); });
+    waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
+    __syncthreads();
+  }
 
   const int wn = (threadIdx.x >> 6) & 1;
   const int64_t wcol = n0 + 128 * wn;                 // first column of this wave
@@ -653,7 +891,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const CEArgs a, in
   const int nvalid = (int)max<int64_t>(0, min<int64_t>(128, a.Vr - wcol));
   float* ws_ms = a.ws;
   float* ws_tgt = a.ws + 2 * (int64_t)tiles_n * a.M;
-  TPS_LDS float* red = (TPS_LDS float*)lds0;          // [2][256][2]; the main loop ended on a barrier
+  TPS_LDS float* red = (TPS_LDS float*)ring_slot<0>();          // [2][256][2]; the main loop ended on a barrier
   ce_rows_seq(a, acc, m0, wcol, nvalid, ws_tgt, red, std::make_integer_sequence<int, 4>{});
   __syncthreads();
   const int rl = threadIdx.x;
@@ -689,6 +927,39 @@ __global__ __launch_bounds__(256) void ce_merge_kernel(const CEArgs a, int tiles
 
 }  // namespace
 
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Whole tiles of this problem may take the fast kernel.
+bool fast_ok(const Problem& P) {
+  if (P.bias || P.bias2) return false;
+  if (!aligned16(P.c) || (P.ldc & 7)) return false;
+  if (P.epi != E_STORE && (!aligned16(P.pre) || (P.ldpre & 7))) return false;
+  if (P.epi == E_SWIGLU && (P.N & 7)) return false;
+  return true;
+}
+
+template <bool FAST>
+hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
+  const dim3 g(grid), block(NTHREADS);
+  const int layout = L.p[0].layout, epi = L.p[0].epi;
+  const bool seg2 = L.p[0].nseg > 1 || (L.nprob > 1 && L.p[1].nseg > 1);
+#define TPS_LAUNCH(LY, EP, S2)                                                                       \
+  hipLaunchKernelGGL((FAST ? gemm_bf16_kernel<LY, EP, S2> : gemm_bf16_edge_kernel<LY, EP, S2>), g, block, 0, \
+                     s, L, total)
+  if (layout == L_NN && epi == E_SWIGLU) TPS_LAUNCH(L_NN, E_SWIGLU, false);
+  else if (layout == L_NN && epi == E_GELU) TPS_LAUNCH(L_NN, E_GELU, false);
+  else if (layout == L_NN) TPS_LAUNCH(L_NN, E_STORE, false);
+  else if (layout == L_NT && seg2) TPS_LAUNCH(L_NT, E_STORE, true);
+  else if (layout == L_NT) TPS_LAUNCH(L_NT, E_STORE, false);
+  else TPS_LAUNCH(L_TN, E_STORE, false);
+#undef TPS_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   // Problems of one launch must share the operand layout and the epilogue;
   // otherwise split.  Only L_NN carries activation epilogues.
@@ -700,24 +971,36 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     hipError_t e = launch_gemm_bf16(a, s);
     return e != hipSuccess ? e : launch_gemm_bf16(b, s);
   }
-  int total = 0;
+  bool fast = true;
+  for (int i = 0; i < L.nprob; ++i) fast = fast && fast_ok(L.p[i]);
+  GemmLaunch F = L, E = L;   // whole tiles (fast kernel), remaining tiles (generic kernel)
+  int nf = 0, ne = 0;
   for (int i = 0; i < L.nprob; ++i) {
-    Problem& P = L.p[i];
+    const Problem& P = L.p[i];
     const int64_t bn = (P.epi == E_SWIGLU) ? BN / 2 : BN;
-    P.tiles_m = (int)((P.M + BM - 1) / BM);
-    P.tiles_n = (int)((P.N + bn - 1) / bn);
-    P.tile_begin = total;
-    total += P.tiles_m * P.tiles_n;
+    const int tm = (int)((P.M + BM - 1) / BM), tn = (int)((P.N + bn - 1) / bn);
+    const int fm = fast ? (int)(P.M / BM) : 0, fn = fast ? (int)(P.N / bn) : 0;
+    F.p[i].tiles_m = fm;
+    F.p[i].tiles_n = fn;
+    F.p[i].tile_begin = nf;
+    F.p[i].edge_only = 0;
+    nf += fm * fn;
+    E.p[i].tiles_m = tm;
+    E.p[i].tiles_n = tn;
+    E.p[i].full_m = fm;
+    E.p[i].full_n = fn;
+    E.p[i].edge_only = fast ? 1 : 0;
+    E.p[i].tile_begin = ne;
+    ne += tm * tn - fm * fn;
   }
-  if (total == 0) return hipSuccess;
-  const dim3 grid(total), block(NTHREADS);
-  const int layout = L.p[0].layout, epi = L.p[0].epi;
-  if (layout == L_NN && epi == E_SWIGLU) hipLaunchKernelGGL((gemm_bf16_kernel<L_NN, E_SWIGLU>), grid, block, 0, s, L, total);
-  else if (layout == L_NN && epi == E_GELU) hipLaunchKernelGGL((gemm_bf16_kernel<L_NN, E_GELU>), grid, block, 0, s, L, total);
-  else if (layout == L_NN) hipLaunchKernelGGL((gemm_bf16_kernel<L_NN, E_STORE>), grid, block, 0, s, L, total);
-  else if (layout == L_NT) hipLaunchKernelGGL((gemm_bf16_kernel<L_NT, E_STORE>), grid, block, 0, s, L, total);
-  else hipLaunchKernelGGL((gemm_bf16_kernel<L_TN, E_STORE>), grid, block, 0, s, L, total);
-  return hipGetLastError();
+  if (nf > 0) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    hipError_t e = dispatch<true>(F, nf, nf < cus ? nf : cus, s);
+    if (e != hipSuccess) return e;
+  }
+  if (ne > 0) return dispatch<false>(E, ne, ne, s);
+  return hipSuccess;
 }
 
 size_t ce_workspace_bytes(int64_t M, int64_t Vr) {

@@ -44,6 +44,8 @@ struct Problem {
   int64_t ldpre;
   // filled by the launcher
   int tiles_m, tiles_n, tile_begin;
+  int edge_only;         // tiles enumerate only the ragged edge (right strip, then bottom strip)
+  int full_m, full_n;    // whole tiles along M and N (edge_only)
 };
 
 // Up to two independent GEMM problems share one launch (their tiles are
