@@ -20,6 +20,9 @@
 // Accumulator orientation.  The MFMA is issued as (B fragment, A fragment),
 // so each lane holds four consecutive output columns of one row per
 // register quad; epilogue stores are 8-byte (bf16) vectors.
+#include <climits>
+#include <map>
+#include <mutex>
 #include <utility>
 
 #include "device_common.hpp"
@@ -239,12 +242,15 @@ __device__ __forceinline__ TPS_LDS char* ring_slot() {
 // first stages, so the next tile starts with a full ring and the current
 // tile's epilogue (which does not touch LDS) overlaps those copies.
 
-// Copy streams of one tile: per K segment (0, 1), one stream per operand.
-// Plain named members (no arrays of structs) keep all of it in registers.
+// Copy streams of one piece of a tile (a range of its K stages): per K
+// segment (0, 1), one stream per operand.  Plain named members (no arrays of
+// structs) keep all of it in registers.
 struct TileStreams {
   OpStream a0, a1, b0, b1;
   int64_t kseg0, kseg1;    // K of each segment
-  int nk0, nk, nk_pad;     // stages of segment 0, of the tile, and padded to NSTAGE
+  int nk0;                 // stages of segment 0
+  int s0, send;            // the piece: stages [s0, send) of the tile
+  int npad;                // send - s0 rounded up to NSTAGE
 };
 
 template <int LAYOUT, bool DUAL, bool SEG2>
@@ -255,7 +261,7 @@ struct Pipe {
   static constexpr int KB = B_KC ? S_KC : (DUAL ? S_MN128 : S_MN256);
 
   int wave, wm, wn;
-  TileStreams cur, nxt;   // nxt.nk == 0: no next tile (its copies are empty)
+  TileStreams cur, nxt;   // nxt.send == 0: no next piece (its copies are empty)
 
   __device__ __forceinline__ void init_wave() {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -283,7 +289,9 @@ struct Pipe {
     }
   }
 
-  __device__ __forceinline__ TileStreams make_streams(const Problem& P, int64_t m0, int64_t n0) const {
+  // Streams of stages [s0, min(s1, stages of the tile)) of the tile at (m0, n0).
+  __device__ __forceinline__ TileStreams make_streams(const Problem& P, int64_t m0, int64_t n0, int s0,
+                                                      int s1) const {
     TileStreams T;
     seg_streams(P, m0, n0, false, T.a0, T.b0, T.kseg0);
     if (SEG2) {
@@ -294,44 +302,33 @@ struct Pipe {
       T.kseg1 = T.kseg0;
     }
     T.nk0 = (int)((T.kseg0 + BK - 1) / BK);
-    T.nk = T.nk0 + (SEG2 ? (int)((T.kseg1 + BK - 1) / BK) : 0);
-    T.nk_pad = (T.nk + NSTAGE - 1) / NSTAGE * NSTAGE;
+    const int nk = T.nk0 + (SEG2 ? (int)((T.kseg1 + BK - 1) / BK) : 0);
+    T.s0 = s0;
+    T.send = min(s1, nk);
+    T.npad = (T.send - s0 + NSTAGE - 1) / NSTAGE * NSTAGE;
     return T;
   }
 
   __device__ __forceinline__ void no_next() {
     nxt = cur;
-    nxt.nk = 0;
-    nxt.nk0 = 0;
-    nxt.nk_pad = 0;
+    nxt.s0 = 0;
+    nxt.send = 0;
+    nxt.npad = 0;
   }
 
-  // Issue the copies of stage ks into `dst`.  ks counts from the current
-  // tile's first stage; with MAYBE_NEXT, stages past its padded end belong to
-  // the next tile.  A stage that does not exist is issued with an empty range.
-  template <bool MAYBE_NEXT>
-  __device__ __forceinline__ void issue(int ks, TPS_LDS char* dst) {
-    const bool in_next = MAYBE_NEXT && ks >= cur.nk_pad;
-    const TileStreams& T = cur;
-    const int s = in_next ? ks - cur.nk_pad : ks;
-    const int nk0 = in_next ? nxt.nk0 : T.nk0;
-    const int nk = in_next ? nxt.nk : T.nk;
-    const bool s1 = SEG2 && s >= nk0;
-    const int stage = s1 ? s - nk0 : s;
-    const bool live = s < nk;
-    stream_issue<KA>(sel(in_next, s1, cur.a0, cur.a1, nxt.a0, nxt.a1), wave, stage, live, dst);
-    stream_issue<KB>(sel(in_next, s1, cur.b0, cur.b1, nxt.b0, nxt.b1), wave, stage, live, dst + TILE_BYTES);
-  }
-
-  static __device__ __forceinline__ OpStream sel(bool in_next, bool s1, const OpStream& c0, const OpStream& c1,
-                                                 const OpStream& n0, const OpStream& n1) {
-    OpStream r;
-    r.base = in_next ? (s1 ? n1.base : n0.base) : (s1 ? c1.base : c0.base);
-    r.remain = in_next ? (s1 ? n1.remain : n0.remain) : (s1 ? c1.remain : c0.remain);
-    r.ld = in_next ? (s1 ? n1.ld : n0.ld) : (s1 ? c1.ld : c0.ld);
-    r.lo0 = in_next ? (s1 ? n1.lo0 : n0.lo0) : (s1 ? c1.lo0 : c0.lo0);
-    r.lo1 = in_next ? (s1 ? n1.lo1 : n0.lo1) : (s1 ? c1.lo1 : c0.lo1);
-    return r;
+  // Issue the copies of step r of the current piece (NEXT: of the next
+  // piece) into `dst`.  A stage past the piece's end is issued with an empty
+  // range (zeros).  Which piece is a compile-time choice: selecting between
+  // the two at run time would put the stream records in scratch memory.
+  template <bool NEXT>
+  __device__ __forceinline__ void issue(int r, TPS_LDS char* dst) {
+    const TileStreams& T = NEXT ? nxt : cur;
+    const int s = T.s0 + r;   // stage within the tile
+    const bool s1 = SEG2 && s >= T.nk0;
+    const int stage = s1 ? s - T.nk0 : s;
+    const bool live = s < T.send;
+    stream_issue<KA>(s1 ? T.a1 : T.a0, wave, stage, live, dst);
+    stream_issue<KB>(s1 ? T.b1 : T.b0, wave, stage, live, dst + TILE_BYTES);
   }
 
   // Per-lane LDS byte addresses of the fragments, computed once.  A fragment
@@ -426,11 +423,13 @@ struct Pipe {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // One 32-deep K step on ring slot S (stage kt of the current tile).
+  // One 32-deep K step on ring slot S (step kt of the current piece).
   // Software pipeline: the MFMAs of the previous stage's second sub-step
   // (operands already in register set 1) run after the barrier, covering
   // the latency of this stage's first fragment reads.
-  template <int S, bool MAYBE_NEXT>
+  // LAST: one of the piece's last NSTAGE steps, which issue the next piece's
+  // first stages (all but the first of them).
+  template <int S, bool LAST>
   __device__ __forceinline__ void step(int kt, f32x16 (&acc)[4][4]) {
     TPS_LDS char* cur_slot = ring_slot<S>();
     // Stage kt's copies are complete once only the later NSTAGE-2 stages'
@@ -438,17 +437,19 @@ struct Pipe {
     // retires this wave's reads of the slot that is refilled below.
     waitcnt<(NSTAGE - 2) * 2 * DMA_PER_OPERAND, 0>();
     __builtin_amdgcn_s_barrier();
-    const bool s1 = SEG2 && kt >= cur.nk0;
+    const int ka = cur.s0 + kt;   // stage within the tile
+    const bool s1 = SEG2 && ka >= cur.nk0;
     const int64_t kseg = s1 ? cur.kseg1 : cur.kseg0;
-    const int64_t k0 = (int64_t)(s1 ? kt - cur.nk0 : kt) * BK;
-    if ((A_KC || B_KC) && kt < cur.nk && k0 + BK > kseg) {   // K tail of K-contiguous operands
+    const int64_t k0 = (int64_t)(s1 ? ka - cur.nk0 : ka) * BK;
+    if ((A_KC || B_KC) && ka < cur.send && k0 + BK > kseg) {   // K tail of K-contiguous operands
       if (A_KC) kc_zero_tail(cur_slot, (int)(kseg - k0));
       if (B_KC) kc_zero_tail(cur_slot + TILE_BYTES, (int)(kseg - k0));
       waitcnt<63, 0>();
       __builtin_amdgcn_s_barrier();
     }
     __builtin_amdgcn_sched_barrier(0);
-    issue<MAYBE_NEXT>(kt + NSTAGE - 1, ring_slot<(S + NSTAGE - 1) % NSTAGE>());
+    if (LAST && S > 0) issue<true>(S - 1, ring_slot<(S + NSTAGE - 1) % NSTAGE>());
+    else issue<false>(kt + NSTAGE - 1, ring_slot<(S + NSTAGE - 1) % NSTAGE>());
     load(cur_slot, 0);
     mma(1, acc);              // previous stage, sub-step 1
     interleave(true);
@@ -457,19 +458,16 @@ struct Pipe {
     interleave(false);
   }
 
-  // Run the current tile.  The copies of its first NSTAGE-1 stages must
-  // already be issued.  `next` is called before the last NSTAGE steps and
-  // must set nxt (or call no_next()); those steps issue the next tile's first
-  // stages.
-  template <class NextFn>
-  __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], NextFn&& next) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0.f};
+  // Run the current piece.  The copies of its first NSTAGE-1 stages must
+  // already be issued.  `init` sets the accumulators' starting values.
+  // `next` is called before the last NSTAGE steps and must set nxt (or call
+  // no_next()); those steps issue the next piece's first stages.
+  template <class InitFn, class NextFn>
+  __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], InitFn&& init, NextFn&& next) {
+    init(acc);
     zero_set1();              // the first step's deferred sub-step multiplies zeros
     int kt = 0;
-    for (; kt + NSTAGE < cur.nk_pad; kt += NSTAGE) {
+    for (; kt + NSTAGE < cur.npad; kt += NSTAGE) {
       step<0, false>(kt, acc);
       step<1, false>(kt + 1, acc);
       step<2, false>(kt + 2, acc);
@@ -489,6 +487,13 @@ struct Pipe {
     issue<false>(2, ring_slot<2>());
   }
 };
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0.f};
+}
 
 // ---- GEMM epilogue -------------------------------------------------------------------
 // In a 32 x 32 accumulator block a lane holds row (lane % 32) and, for each
@@ -689,7 +694,7 @@ __device__ __forceinline__ Problem pick_problem(const GemmLaunch& L, bool s) {
   TPS_PICK(nseg); TPS_PICK(layout); TPS_PICK(epi); TPS_PICK(b_up); TPS_PICK(ldb_up);
   TPS_PICK(bias); TPS_PICK(bias2); TPS_PICK(c); TPS_PICK(ldc); TPS_PICK(pre); TPS_PICK(ldpre);
   TPS_PICK(tiles_m); TPS_PICK(tiles_n); TPS_PICK(tile_begin);
-  TPS_PICK(edge_only); TPS_PICK(full_m); TPS_PICK(full_n);
+  TPS_PICK(edge_only); TPS_PICK(full_m); TPS_PICK(full_n); TPS_PICK(ustages);
 #undef TPS_PICK
   return P;
 }
@@ -718,49 +723,183 @@ __device__ __forceinline__ void locate(const GemmLaunch& L, int id, int epi, Pro
   n0 = (int64_t)tn * (epi == E_SWIGLU ? BN / 2 : BN);
 }
 
+// ---- schedule of the fast kernels -------------------------------------------------------
+// The whole tiles of a launch are laid end to end as one sequence of K work
+// units (a unit is `ustages` K stages; a tile's last unit may be short), and
+// workgroup g of G takes the units [g W / G, (g+1) W / G).  The launcher
+// picks the unit: a whole tile when there are at least half as many tiles
+// as CUs (each workgroup then runs whole tiles), else 1/s of a tile's K with
+// s = CUs / tiles and G = s * tiles (split-K: each workgroup runs one K
+// slice, and workgroups at the same K offset of neighbouring tiles share
+// operand panels in L2).
+//
+// A tile split over several workgroups is finished by the last of them to
+// arrive: each stores its fp32 part in a slot of the partial buffer and
+// counts itself in at the tile's arrival counter; the one that completes
+// the count sums the parts (in workgroup order, so the result does not
+// depend on arrival order), runs the epilogue and clears the counter.
+// Nobody waits for anybody.  Slots: workgroup g uses slot 2g for the piece
+// at the end of its range and 2g + 1 for the one at its start (a range splits
+// at most those two).  Counters: indexed by the workgroup holding the
+// tile's first unit, which no other split tile shares.
+
+// Tile holding global unit q: its launch-wide index, first unit and units.
+__device__ __forceinline__ void unit_tile(const GemmLaunch& L, int q, int& tile, int& tq0, int& nq) {
+  const bool p1 = L.nprob > 1 && q >= L.p[1].q_begin;
+  const int qb = p1 ? L.p[1].q_begin : L.p[0].q_begin;
+  nq = p1 ? L.p[1].nq : L.p[0].nq;
+  const int local = (q - qb) / nq;
+  tile = (p1 ? L.p[1].tile_begin : L.p[0].tile_begin) + local;
+  tq0 = qb + local * nq;
+}
+
+// First unit of workgroup g's range, and the workgroup whose range holds unit q
+// (the largest g with floor(g W / G) <= q).
+__device__ __forceinline__ int range_begin(int g, int W, int G) { return (int)((int64_t)g * W / G); }
+__device__ __forceinline__ int unit_wg(int q, int W, int G) { return (int)(((int64_t)(q + 1) * G - 1) / W); }
+
+constexpr int SK_SLOT_FLOATS = BM * BN;   // one fp32 partial tile
+
+// Slot layout: chunk c (4 floats) of thread t at float 4 (256 c + t), so each
+// store/load instruction of the workgroup covers 4 KiB contiguously.  Chunk
+// c = 4 (4 i + j) + r holds registers 4r..4r+3 of accumulator block (i, j).
+//
+// Coherence across XCDs (each has its own L2): the parts are written and
+// read with device-scope cache policy (sc1), so stores reach the coherent
+// level and loads do not hit stale L2 lines; a wave's stores are complete
+// once vmcnt reaches zero.  No whole-cache write-back or invalidate is
+// needed, which would cost the other CUs of the XCD their cached operands.
+constexpr int CPOL_DEVICE = 16;   // sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float* slot) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(slot), (short)0, SK_SLOT_FLOATS * 4, 0x00020000);
+}
+
+template <int I, int J>
+__device__ __forceinline__ void sk_store_block(__amdgpu_buffer_rsrc_t slot, const f32x16& a) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int c = (4 * I + J) * 4 + r;
+    const u32x4 v = {__float_as_uint(a[4 * r]), __float_as_uint(a[4 * r + 1]), __float_as_uint(a[4 * r + 2]),
+                     __float_as_uint(a[4 * r + 3])};
+    __builtin_amdgcn_raw_buffer_store_b128(v, slot, 16 * (256 * c + t), 0, CPOL_DEVICE);
+  }
+}
+
+// Each block either goes through the epilogue (whole tile) or into the slot.
+template <int EPI, int... Is>
+__device__ __forceinline__ void piece_blocks(bool whole, const Problem& P, int64_t m0, int64_t n0,
+                                             __amdgpu_buffer_rsrc_t slot,
+                                             f32x16 (&acc)[4][4], std::integer_sequence<int, Is...>) {
+  ((whole ? fast_block<EPI, Is / 4, Is % 4>(P, m0, n0, acc[Is / 4][Is % 4], acc[Is / 4][(Is % 4) ^ 2])
+          : sk_store_block<Is / 4, Is % 4>(slot, acc[Is / 4][Is % 4]),
+    __builtin_amdgcn_sched_barrier(0)),
+   ...);
+}
+
+__device__ __forceinline__ f32x16 join4(const f32x4& a, const f32x4& b, const f32x4& c, const f32x4& d) {
+  return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
+}
+
+// Sum of the parts of a split tile, block row I, then its epilogue.
+template <int EPI, int I>
+__device__ __forceinline__ void sk_reduce_row(const GemmLaunch& L, const Problem& P, int64_t m0, int64_t n0,
+                                              int gfirst, int glast, int last_slot) {
+  const int t = threadIdx.x;
+  f32x4 v[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) v[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int gp = gfirst; gp <= glast; ++gp) {
+    const __amdgpu_buffer_rsrc_t slot =
+        slot_rsrc(L.sk_part + (int64_t)(gp == glast ? last_slot : 2 * gp) * SK_SLOT_FLOATS);
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      v[c] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(slot, 16 * (256 * (16 * I + c) + t), 0,
+                                                                               CPOL_DEVICE));
+  }
+  fast_block<EPI, I, 0>(P, m0, n0, join4(v[0], v[1], v[2], v[3]), join4(v[8], v[9], v[10], v[11]));
+  fast_block<EPI, I, 1>(P, m0, n0, join4(v[4], v[5], v[6], v[7]), join4(v[12], v[13], v[14], v[15]));
+  fast_block<EPI, I, 2>(P, m0, n0, join4(v[8], v[9], v[10], v[11]), join4(v[0], v[1], v[2], v[3]));
+  fast_block<EPI, I, 3>(P, m0, n0, join4(v[12], v[13], v[14], v[15]), join4(v[4], v[5], v[6], v[7]));
+}
+
+// Finish one piece (units [q0, q1) of the tile starting at unit tq0, nq units).
+template <int EPI>
+__device__ __forceinline__ void finish_piece(const GemmLaunch& L, int g, int qb, int tile, int tq0, int q0, int q1,
+                                             int nq, f32x16 (&acc)[4][4]) {
+  const bool whole = q0 == 0 && q1 == nq;
+  Problem P;
+  int64_t m0, n0;
+  locate<false>(L, tile, EPI, P, m0, n0);
+  const int my_slot = 2 * g + (tq0 + q1 == qb ? 0 : 1);
+  piece_blocks<EPI>(whole, P, m0, n0, slot_rsrc(L.sk_part + (int64_t)my_slot * SK_SLOT_FLOATS), acc,
+                    std::make_integer_sequence<int, 16>{});
+  if (whole) return;
+  const int G = gridDim.x, W = L.sk_W;
+  const int gfirst = unit_wg(tq0, W, G), glast = unit_wg(tq0 + nq - 1, W, G);
+  waitcnt<0, 15>();   // this wave's part is stored at device scope
+  __syncthreads();    // ... and so are the other three waves' parts
+  uint32_t old = 0;
+  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(L.sk_count + gfirst, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool last = __syncthreads_or(threadIdx.x == 0 && old == (uint32_t)(glast - gfirst));
+  if (!last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(L.sk_count + gfirst, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int last_slot = 2 * glast + (range_begin(glast + 1, W, G) > tq0 + nq ? 1 : 0);
+  sk_reduce_row<EPI, 0>(L, P, m0, n0, gfirst, glast, last_slot);
+  sk_reduce_row<EPI, 1>(L, P, m0, n0, gfirst, glast, last_slot);
+  sk_reduce_row<EPI, 2>(L, P, m0, n0, gfirst, glast, last_slot);
+  sk_reduce_row<EPI, 3>(L, P, m0, n0, gfirst, glast, last_slot);
+}
+
 // Fast kernels: one per (operand layout, epilogue, K segments), so each role
 // of the shard path is a distinct kernel in traces.  Whole tiles only, no
-// bias, aligned outputs.  Persistent: workgroup w processes tiles w',
-// w' + G, w' + 2G, ... (G = grid size; w' puts the tiles that run at the
-// same time on one XCD next to each other), with the K-stage stream running
-// on from tile to tile.
+// bias, aligned outputs; stream-K schedule (above), one workgroup per CU,
+// with the K-stage stream running on from piece to piece.  Workgroup g sits
+// on XCD g / (G / 8), so neighbouring ranges share an L2.
 template <int LAYOUT, int EPI, bool SEG2>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch L, int total_tiles) {
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch L) {
   const int G = gridDim.x;
-  int id = (G % 8 == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  if (id >= total_tiles) return;
+  const int g = (G % 8 == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int W = L.sk_W;
+  const int qa = range_begin(g, W, G), qb = range_begin(g + 1, W, G);
+  if (qa >= qb) return;
   constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
   Pipe<LAYOUT, DUAL, SEG2> pipe;
   pipe.init_wave();
+  int tile, tq0, nq;
+  unit_tile(L, qb - 1, tile, tq0, nq);
+  int q0 = max(qa, tq0) - tq0, q1 = qb - tq0;   // this piece: units [q0, q1) of the tile
   {
     Problem P;
     int64_t m0, n0;
-    locate<false>(L, id, EPI, P, m0, n0);
-    pipe.cur = pipe.make_streams(P, m0, n0);
+    locate<false>(L, tile, EPI, P, m0, n0);
+    pipe.cur = pipe.make_streams(P, m0, n0, P.ustages * q0, P.ustages * q1);
   }
   pipe.prologue();
   for (;;) {
-    const int nid = id + G;
-    const bool more = nid < total_tiles;
+    const int cursor = tq0 + q0;   // first unit of this piece; the next piece ends there
+    const bool more = cursor > qa;
+    int ntile = 0, ntq0 = 0, nnq = 1;
     f32x16 acc[4][4];
-    pipe.run_tile(acc, [&]() {
+    pipe.run_tile(acc, zero_acc, [&]() {
       if (more) {
+        unit_tile(L, cursor - 1, ntile, ntq0, nnq);
         Problem Pn;
         int64_t m0n, n0n;
-        locate<false>(L, nid, EPI, Pn, m0n, n0n);
-        pipe.nxt = pipe.make_streams(Pn, m0n, n0n);
+        locate<false>(L, ntile, EPI, Pn, m0n, n0n);
+        pipe.nxt = pipe.make_streams(Pn, m0n, n0n, Pn.ustages * (max(qa, ntq0) - ntq0), Pn.ustages * (cursor - ntq0));
       } else {
         pipe.no_next();
       }
     });
-    {
-      Problem P;
-      int64_t m0, n0;
-      locate<false>(L, id, EPI, P, m0, n0);
-      fast_epilogue<EPI>(P, m0, n0, acc, std::make_integer_sequence<int, 16>{});
-    }
+    finish_piece<EPI>(L, g, qb, tile, tq0, q0, q1, nq, acc);
     if (!more) break;
-    id = nid;
+    q0 = max(qa, ntq0) - ntq0;
+    q1 = cursor - ntq0;
+    tile = ntile;
+    tq0 = ntq0;
+    nq = nnq;
     pipe.cur = pipe.nxt;
   }
   waitcnt<0, 0>();   // trailing (empty) copies retire before the workgroup ends
@@ -777,9 +916,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmL
   f32x16 acc[4][4];
   Pipe<LAYOUT, DUAL, SEG2> pipe;
   pipe.init_wave();
-  pipe.cur = pipe.make_streams(P, m0, n0);
+  pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
   pipe.prologue();
-  pipe.run_tile(acc, [&]() { pipe.no_next(); });
+  pipe.run_tile(acc, zero_acc, [&]() { pipe.no_next(); });
   waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
   __syncthreads();
   generic_epilogue(P, m0, n0, acc);
@@ -878,9 +1017,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const CEArgs a, in
   {
     Pipe<L_NT, false, false> pipe;
     pipe.init_wave();
-    pipe.cur = pipe.make_streams(P, m0, n0);
+    pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
     pipe.prologue();
-    pipe.run_tile(acc, [&]() { pipe.no_next(); });
+    pipe.run_tile(acc, zero_acc, [&]() { pipe.no_next(); });
     waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
     __syncthreads();
   }
@@ -945,9 +1084,11 @@ hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
   const dim3 g(grid), block(NTHREADS);
   const int layout = L.p[0].layout, epi = L.p[0].epi;
   const bool seg2 = L.p[0].nseg > 1 || (L.nprob > 1 && L.p[1].nseg > 1);
-#define TPS_LAUNCH(LY, EP, S2)                                                                       \
-  hipLaunchKernelGGL((FAST ? gemm_bf16_kernel<LY, EP, S2> : gemm_bf16_edge_kernel<LY, EP, S2>), g, block, 0, \
-                     s, L, total)
+#define TPS_LAUNCH(LY, EP, S2)                                                           \
+  do {                                                                                   \
+    if (FAST) hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2>), g, block, 0, s, L);     \
+    else hipLaunchKernelGGL((gemm_bf16_edge_kernel<LY, EP, S2>), g, block, 0, s, L, total); \
+  } while (0)
   if (layout == L_NN && epi == E_SWIGLU) TPS_LAUNCH(L_NN, E_SWIGLU, false);
   else if (layout == L_NN && epi == E_GELU) TPS_LAUNCH(L_NN, E_GELU, false);
   else if (layout == L_NN) TPS_LAUNCH(L_NN, E_STORE, false);
@@ -956,6 +1097,55 @@ hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
   else TPS_LAUNCH(L_TN, E_STORE, false);
 #undef TPS_LAUNCH
   return hipGetLastError();
+}
+
+// Stream-K partial buffers, one per (device, stream): calls on one stream are
+// ordered, so they can share one; calls on different streams must not.
+// Allocated on first use (two fp32 tile slots per CU plus one arrival
+// counter per CU, the counters zeroed once; every launch leaves them zero)
+// and kept until the process ends.
+struct SkBuffer {
+  float* part = nullptr;
+  uint32_t* count = nullptr;
+  int wgs = 0;
+};
+
+std::mutex g_sk_mu;
+std::map<std::pair<int, hipStream_t>, SkBuffer> g_sk;
+
+hipError_t sk_buffer(int dev, int wgs, hipStream_t s, float*& part, uint32_t*& count) {
+  std::lock_guard<std::mutex> lk(g_sk_mu);
+  SkBuffer& b = g_sk[{dev, s}];
+  if (b.wgs < wgs) {
+    if (b.part) {   // a larger grid than before on this stream: retire the old buffer first
+      hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return e;
+      hipFree(b.part);
+      b = SkBuffer{};
+    }
+    const size_t part_bytes = (size_t)2 * wgs * SK_SLOT_FLOATS * sizeof(float);
+    const size_t bytes = part_bytes + (size_t)wgs * sizeof(uint32_t);
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return e;
+    e = hipMemset(static_cast<char*>(p) + part_bytes, 0, bytes - part_bytes);
+    if (e != hipSuccess) {
+      hipFree(p);
+      return e;
+    }
+    b.part = static_cast<float*>(p);
+    b.count = reinterpret_cast<uint32_t*>(static_cast<char*>(p) + part_bytes);
+    b.wgs = wgs;
+  }
+  part = b.part;
+  count = b.count;
+  return hipSuccess;
+}
+
+int stages_of(const Problem& P) {
+  int nk = (int)((P.seg[0].K + BK - 1) / BK);
+  if (P.nseg > 1) nk += (int)((P.seg[1].K + BK - 1) / BK);
+  return nk;
 }
 
 }  // namespace
@@ -975,15 +1165,39 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   for (int i = 0; i < L.nprob; ++i) fast = fast && fast_ok(L.p[i]);
   GemmLaunch F = L, E = L;   // whole tiles (fast kernel), remaining tiles (generic kernel)
   int nf = 0, ne = 0;
+  int64_t W = 0;
+  int cus = 256, dev = 0;
+  {
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  int whole_tiles = 0;
+  for (int i = 0; i < L.nprob; ++i) {
+    const Problem& P = L.p[i];
+    const int64_t bn = (P.epi == E_SWIGLU) ? BN / 2 : BN;
+    if (fast) whole_tiles += (int)(P.M / BM) * (int)(P.N / bn);
+  }
+  // split factor: K slices per tile (1: whole tiles)
+  const int split = (whole_tiles > 0 && 2 * whole_tiles <= cus) ? cus / whole_tiles : 1;
   for (int i = 0; i < L.nprob; ++i) {
     const Problem& P = L.p[i];
     const int64_t bn = (P.epi == E_SWIGLU) ? BN / 2 : BN;
     const int tm = (int)((P.M + BM - 1) / BM), tn = (int)((P.N + bn - 1) / bn);
     const int fm = fast ? (int)(P.M / BM) : 0, fn = fast ? (int)(P.N / bn) : 0;
+    const int nk = std::max(1, stages_of(P));
+    const int quads = (nk + NSTAGE - 1) / NSTAGE;
+    const int s_i = std::min(split, quads);                      // at least one ring of stages per slice
+    const int uq = (quads + s_i - 1) / s_i;                      // quads per unit
     F.p[i].tiles_m = fm;
     F.p[i].tiles_n = fn;
     F.p[i].tile_begin = nf;
     F.p[i].edge_only = 0;
+    F.p[i].ustages = uq * NSTAGE;
+    F.p[i].nq = (quads + uq - 1) / uq;
+    F.p[i].q_begin = (int)W;
+    W += (int64_t)fm * fn * F.p[i].nq;
     nf += fm * fn;
     E.p[i].tiles_m = tm;
     E.p[i].tiles_n = tn;
@@ -993,10 +1207,13 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     E.p[i].tile_begin = ne;
     ne += tm * tn - fm * fn;
   }
+  if (W >= INT_MAX) return hipErrorInvalidValue;
   if (nf > 0) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    hipError_t e = dispatch<true>(F, nf, nf < cus ? nf : cus, s);
+    const int grid = (int)std::min<int64_t>(cus, W);
+    F.sk_W = (int)W;
+    hipError_t e = sk_buffer(dev, cus, s, F.sk_part, F.sk_count);
+    if (e != hipSuccess) return e;
+    e = dispatch<true>(F, nf, grid, s);
     if (e != hipSuccess) return e;
   }
   if (ne > 0) return dispatch<false>(E, ne, ne, s);
