@@ -27,10 +27,20 @@ bool bad_dim(int64_t v) { return v < 1 || v > kMaxDim; }
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 size_t align_ws(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// bf16 matrices are addressed through buffer descriptors with 32-bit
+// offsets: the bytes from a matrix's base to the end of its last row (width
+// rounded up to 8 elements) must stay below 4 GiB.
+bool bf16_extent_ok(int64_t rows, int64_t ld, int64_t width) {
+  constexpr int64_t kMaxElems = int64_t(0xffffffff) / 2;
+  if (rows > 1 && ld > kMaxElems / (rows - 1)) return false;
+  return (rows - 1) * ld + round_up(width, 8) <= kMaxElems;
+}
+
 // Matrix operand: [rows][ld] with `width` used columns.  Rows are validated
-// separately (bad_dim); here: ld range, ld multiple, base alignment.
-tp_status check_mat(const void* p, int64_t ld, int64_t width, int dtype) {
+// separately (bad_dim); here: ld range, extent, ld multiple, base alignment.
+tp_status check_mat(const void* p, int64_t rows, int64_t ld, int64_t width, int dtype) {
   if (ld < width || ld > (int64_t(1) << 40)) return TP_E_SHAPE;
+  if (dtype == TP_BF16 && !bf16_extent_ok(rows, ld, width)) return TP_E_SHAPE;
   if (ld % vec_elems(dtype) != 0 || !aligned16(p)) return TP_E_ALIGN;
   return TP_OK;
 }
@@ -108,11 +118,11 @@ tp_status tp_column_fwd(int dtype, int act, int64_t M, int64_t N, int64_t K, con
   if (act == TP_ACT_SWIGLU && !A2) return TP_E_NULL;
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return TP_E_SHAPE;
   TPS_TRY(check_grid(dtype, M, N));
-  TPS_TRY(check_mat(X, ldx, K, dtype));
-  TPS_TRY(check_mat(A, lda, N, dtype));
-  if (act == TP_ACT_SWIGLU) TPS_TRY(check_mat(A2, lda2, N, dtype));
-  TPS_TRY(check_mat(Y, ldy, N, dtype));
-  if (act != TP_ACT_NONE) TPS_TRY(check_mat(Pre, ldpre, act == TP_ACT_SWIGLU ? 2 * N : N, dtype));
+  TPS_TRY(check_mat(X, M, ldx, K, dtype));
+  TPS_TRY(check_mat(A, K, lda, N, dtype));
+  if (act == TP_ACT_SWIGLU) TPS_TRY(check_mat(A2, K, lda2, N, dtype));
+  TPS_TRY(check_mat(Y, M, ldy, N, dtype));
+  if (act != TP_ACT_NONE) TPS_TRY(check_mat(Pre, M, ldpre, act == TP_ACT_SWIGLU ? 2 * N : N, dtype));
   TPS_TRY(check_vec(bias));
   if (act == TP_ACT_SWIGLU) TPS_TRY(check_vec(bias2));
 
@@ -140,9 +150,9 @@ tp_status tp_row_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* Xi,
   if (!Xi || !Bi || !Zp) return TP_E_NULL;
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return TP_E_SHAPE;
   TPS_TRY(check_grid(dtype, M, N));
-  TPS_TRY(check_mat(Xi, ldx, K, dtype));
-  TPS_TRY(check_mat(Bi, ldb, N, dtype));
-  TPS_TRY(check_mat(Zp, ldz, N, dtype));
+  TPS_TRY(check_mat(Xi, M, ldx, K, dtype));
+  TPS_TRY(check_mat(Bi, K, ldb, N, dtype));
+  TPS_TRY(check_mat(Zp, M, ldz, N, dtype));
   GemmLaunch L = {};
   L.nprob = 1;
   L.p[0] = make_problem(M, N, tps::L_NN, tps::E_STORE);
@@ -157,8 +167,8 @@ tp_status tp_sum_partials(int dtype, int t, int64_t M, int64_t N, const void* pa
   if (!valid_dtype(dtype)) return TP_E_DTYPE;
   if (!parts || !out) return TP_E_NULL;
   if (t < 1 || bad_dim(M) || bad_dim(N) || part_stride < 0) return TP_E_SHAPE;
-  TPS_TRY(check_mat(parts, ld, N, dtype));
-  TPS_TRY(check_mat(out, ldo, N, dtype));
+  TPS_TRY(check_mat(parts, M, ld, N, dtype));
+  TPS_TRY(check_mat(out, M, ldo, N, dtype));
   if (part_stride % vec_elems(dtype) != 0) return TP_E_ALIGN;
   TPS_TRY(check_vec(bias));
   tps::SumArgs a = {t, M, N, parts, ld, part_stride, bias, out, ldo};
@@ -180,18 +190,30 @@ tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* dZ,
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return TP_E_SHAPE;
   TPS_TRY(check_grid(dtype, M, K));
   TPS_TRY(check_grid(dtype, K, N));
-  TPS_TRY(check_mat(dZ, lddz, N, dtype));
-  TPS_TRY(check_mat(Xi, ldx, K, dtype));
-  TPS_TRY(check_mat(Bi, ldb, N, dtype));
-  if (dXi) TPS_TRY(check_mat(dXi, lddx, K, dtype));
-  if (dBi) TPS_TRY(check_mat(dBi, lddb, N, dtype));
+  TPS_TRY(check_mat(dZ, M, lddz, N, dtype));
+  TPS_TRY(check_mat(Xi, M, ldx, K, dtype));
+  TPS_TRY(check_mat(Bi, K, ldb, N, dtype));
+  if (dXi) TPS_TRY(check_mat(dXi, M, lddx, K, dtype));
+  if (dBi) TPS_TRY(check_mat(dBi, K, lddb, N, dtype));
   TPS_TRY(check_vec(dbias));
   if (dbias) {
     if (!workspace || ws_bytes < tp_row_bwd_workspace_bytes(dtype, M, N)) return TP_E_WORKSPACE;
     if (!aligned16(workspace)) return TP_E_ALIGN;
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dXi) {   // dX_i = dZ B_i^T: NT over K' = N
+  if (dXi && dBi && dtype == TP_BF16) {   // both GEMMs in one launch (the library may share the CUs)
+    GemmLaunch L = {};
+    L.nprob = 2;
+    L.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);   // dB_i = X_i^T dZ
+    L.p[0].seg[0] = tps::Seg{Xi, dZ, ldx, lddz, M};
+    L.p[0].c = dBi;
+    L.p[0].ldc = lddb;
+    L.p[1] = make_problem(M, K, tps::L_NT, tps::E_STORE);   // dX_i = dZ B_i^T
+    L.p[1].seg[0] = tps::Seg{dZ, Bi, lddz, ldb, N};
+    L.p[1].c = dXi;
+    L.p[1].ldc = lddx;
+    if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
+  } else if (dXi) {   // dX_i = dZ B_i^T: NT over K' = N
     GemmLaunch L = {};
     L.nprob = 1;
     L.p[0] = make_problem(M, K, tps::L_NT, tps::E_STORE);
@@ -200,7 +222,7 @@ tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* dZ,
     L.p[0].ldc = lddx;
     if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
   }
-  if (dBi) {   // dB_i = X_i^T dZ: TN over K' = M
+  if (dBi && !(dXi && dtype == TP_BF16)) {   // dB_i = X_i^T dZ: TN over K' = M
     GemmLaunch L = {};
     L.nprob = 1;
     L.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);
@@ -250,17 +272,18 @@ tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t K, con
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return TP_E_SHAPE;
   TPS_TRY(check_grid(dtype, M, K));
   TPS_TRY(check_grid(dtype, K, N));
-  TPS_TRY(check_mat(dY, lddy, N, dtype));
-  TPS_TRY(check_mat(X, ldx, K, dtype));
-  TPS_TRY(check_mat(A, lda, N, dtype));
-  if (swiglu) TPS_TRY(check_mat(A2, lda2, N, dtype));
-  if (act != TP_ACT_NONE) TPS_TRY(check_mat(Pre, ldpre, swiglu ? 2 * N : N, dtype));
-  if (dXpart) TPS_TRY(check_mat(dXpart, lddx, K, dtype));
-  if (dA) TPS_TRY(check_mat(dA, ldda, N, dtype));
-  if (swiglu && dA2) TPS_TRY(check_mat(dA2, ldda2, N, dtype));
+  TPS_TRY(check_mat(dY, M, lddy, N, dtype));
+  TPS_TRY(check_mat(X, M, ldx, K, dtype));
+  TPS_TRY(check_mat(A, K, lda, N, dtype));
+  if (swiglu) TPS_TRY(check_mat(A2, K, lda2, N, dtype));
+  if (act != TP_ACT_NONE) TPS_TRY(check_mat(Pre, M, ldpre, swiglu ? 2 * N : N, dtype));
+  if (dXpart) TPS_TRY(check_mat(dXpart, M, lddx, K, dtype));
+  if (dA) TPS_TRY(check_mat(dA, K, ldda, N, dtype));
+  if (swiglu && dA2) TPS_TRY(check_mat(dA2, K, ldda2, N, dtype));
   TPS_TRY(check_vec(dbias));
   if (swiglu) TPS_TRY(check_vec(dbias2));
   const bool want_bias = dbias || (swiglu && dbias2);
+  if (dtype == TP_BF16 && act != TP_ACT_NONE && !bf16_extent_ok(M, round_up(N, 8), N)) return TP_E_SHAPE;
   const size_t need = tp_column_bwd_workspace_bytes(dtype, act, M, N, want_bias);
   if (need > 0) {
     if (!workspace || ws_bytes < need) return TP_E_WORKSPACE;
@@ -356,8 +379,8 @@ tp_status tp_vocab_ce_partials(int dtype, int64_t M, int64_t Vr, int64_t K, cons
   if (!H || !W || !target || !out_max || !out_sumexp || !out_tgt) return TP_E_NULL;
   if (bad_dim(M) || bad_dim(Vr) || bad_dim(K)) return TP_E_SHAPE;
   TPS_TRY(check_grid(dtype, M, Vr));
-  TPS_TRY(check_mat(H, ldh, K, dtype));
-  TPS_TRY(check_mat(W, ldw, K, dtype));
+  TPS_TRY(check_mat(H, M, ldh, K, dtype));
+  TPS_TRY(check_mat(W, Vr, ldw, K, dtype));
   if (!aligned16(target) || !aligned16(out_max) || !aligned16(out_sumexp) || !aligned16(out_tgt)) return TP_E_ALIGN;
   if (!workspace || ws_bytes < tp_vocab_ce_workspace_bytes(M, Vr)) return TP_E_WORKSPACE;
   if (!aligned16(workspace)) return TP_E_ALIGN;

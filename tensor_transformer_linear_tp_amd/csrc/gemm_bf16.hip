@@ -20,9 +20,8 @@
 // Accumulator orientation.  The MFMA is issued as (B fragment, A fragment),
 // so each lane holds four consecutive output columns of one row per
 // register quad; epilogue stores are 8-byte (bf16) vectors.
+#include <algorithm>
 #include <climits>
-#include <map>
-#include <mutex>
 #include <utility>
 
 #include "device_common.hpp"
@@ -60,16 +59,19 @@ __device__ __forceinline__ int mn_off(int k, int c) { return k * ROWB + ((c ^ mn
 // lies inside the extent and is zeroed in LDS afterwards (kc_zero_tail).
 constexpr int DMA_PER_OPERAND = 4;            // copy instructions per wave per operand stage
 
-// Copy stream of one operand of one K segment of one tile.  Wave-uniform
-// scalars plus one or two per-lane byte offsets; block j of this wave adds a
-// uniform row offset at issue time.
+// Copy stream of one operand of one K segment of one piece: the address of
+// the tile's origin, the bytes from there to the end of the operand's extent
+// (operands are below 4 GiB, so 32 bits hold every offset), the bytes per K
+// stage, and this wave's per-lane byte offsets of its blocks (block j of the
+// wave is block 4 w + j of the stage; w = the wave, or for S_MN128 the wave
+// within its half).  Everything but the offsets is wave-uniform.
 enum StreamKind : int { S_KC = 0, S_MN256 = 1, S_MN128 = 2 };
 
 struct OpStream {
-  const char* base;   // stage-0 origin (bytes)
-  int64_t remain;     // bytes from base to the end of the operand's extent
-  int64_t ld;         // leading dimension (elements)
-  uint32_t lo0, lo1;  // per-lane byte offsets (lo1: odd blocks of S_MN256)
+  const char* base;
+  uint32_t nrec;
+  uint32_t step;
+  uint32_t voff[DMA_PER_OPERAND];
 };
 
 __device__ __forceinline__ int64_t extent_bytes(int64_t rows, int64_t ld, int64_t width) {
@@ -79,15 +81,20 @@ __device__ __forceinline__ int64_t extent_bytes(int64_t rows, int64_t ld, int64_
 // K-contiguous operand: tile rows [row0, row0+256) of a [rows][K] matrix.
 // Block b (16 rows) of the stage: lane L copies row 16b + L/4, logical chunk
 // (L%4) ^ kc_swz(row) -- the swizzle only depends on the row's low 4 bits.
-__device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t rows, int64_t K, int64_t row0) {
+__device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t rows, int64_t K, int64_t row0,
+                                              int wb) {
   const int lane = threadIdx.x & 63;
   OpStream s;
   s.base = static_cast<const char*>(p) + row0 * ld * 2;
-  s.remain = extent_bytes(rows, ld, K) - row0 * ld * 2;
-  s.ld = ld;
+  s.nrec = (uint32_t)(extent_bytes(rows, ld, K) - row0 * ld * 2);
+  s.step = BK * 2;
   const int r = lane >> 2;
   const int c = (lane & 3) ^ kc_swz(r);
-  s.lo0 = s.lo1 = (uint32_t)((r * ld + 8 * c) * 2);
+#pragma unroll
+  for (int j = 0; j < DMA_PER_OPERAND; ++j) {
+    const int row = 16 * (DMA_PER_OPERAND * wb + j) + r;
+    s.voff[j] = (uint32_t)((row * ld + 8 * c) * 2);
+  }
   return s;
 }
 
@@ -95,41 +102,47 @@ __device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t
 // W = 256: block b holds rows 2b, 2b+1 (lane L: row 2b + L/32, chunk L%32);
 // W = 128: block b holds rows 4b..4b+3 (lane L: row 4b + L/16, chunk L%16).
 template <int W>
-__device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t cols, int64_t K, int64_t col0) {
+__device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t cols, int64_t K, int64_t col0,
+                                              int wb) {
   const int lane = threadIdx.x & 63;
   constexpr int CHUNKS = W / 8;
+  constexpr int ROWS = 512 / W;   // rows per block
   OpStream s;
   s.base = static_cast<const char*>(p) + col0 * 2;
-  s.remain = extent_bytes(K, ld, cols) - col0 * 2;
-  s.ld = ld;
-  const int k = lane / CHUNKS;   // row within the block
-  const int c0 = (lane % CHUNKS) ^ mn_swz(k);
-  const int c1 = (lane % CHUNKS) ^ mn_swz(k + 2);   // W = 256, odd blocks start at row 2 (mod 4)
-  s.lo0 = (uint32_t)((k * ld + 8 * c0) * 2);
-  s.lo1 = (uint32_t)((k * ld + 8 * c1) * 2);
+  s.nrec = (uint32_t)(extent_bytes(K, ld, cols) - col0 * 2);
+  s.step = (uint32_t)(BK * ld * 2);
+#pragma unroll
+  for (int j = 0; j < DMA_PER_OPERAND; ++j) {
+    const int k = ROWS * (DMA_PER_OPERAND * wb + j) + lane / CHUNKS;
+    const int c = (lane % CHUNKS) ^ mn_swz(k);
+    s.voff[j] = (uint32_t)((k * ld + 8 * c) * 2);
+  }
   return s;
 }
 
-// Issue the copies of K stage `stage` of one operand into `tile` (this
-// wave's DMA_PER_OPERAND blocks).  live == false: empty range, zeros written.
-template <int KIND>
-__device__ __forceinline__ void stream_issue(const OpStream& st, int wave, int stage, bool live, TPS_LDS char* tile) {
-  const int64_t step = (KIND == S_KC) ? BK * 2 : (int64_t)BK * st.ld * 2;
-  const int64_t off = (int64_t)stage * step;
-  const int64_t rem = live ? st.remain - off : 0;
-  const uint32_t nrec = rem <= 0 ? 0u : (rem >= 0xffffffffll ? 0xffffffffu : (uint32_t)rem);
+// Issue the copies of K stage `stage` of one operand (this wave's
+// DMA_PER_OPERAND blocks; `wtile` is this wave's first block in the LDS
+// tile).  live == false: an empty range, zeros written.
+//   exact: the descriptor starts at the stage, so its range check zero-fills
+//     whatever lies past the operand's extent (rows beyond M, N or K, the
+//     last row's K tail).
+//   otherwise (the stage lies inside the operand): the descriptor stays at
+//     the tile's origin and the stage offset goes into soffset.
+__device__ __forceinline__ void stream_issue(const OpStream& st, int stage, bool live, bool exact,
+                                             TPS_LDS char* wtile) {
+  // Branch-free selects of wave-uniform values keep the descriptor in SGPRs.
+  const uint32_t off = (uint32_t)stage * st.step;
+  const uint32_t boff = (live && exact) ? off : 0u;
+  const uint32_t so = exact ? 0u : off;
+  const uint32_t n = !live ? 0u : (!exact ? st.nrec : (st.nrec > off ? st.nrec - off : 0u));
+  // The clamp has no scalar instruction, so n is computed on the vector ALU;
+  // readfirstlane brings it back (a descriptor in VGPRs would make the
+  // compiler loop over lanes around every copy).
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(live ? st.base + off : st.base), (short)0, (int)nrec, 0x00020000);
-  const int wb = (KIND == S_MN128) ? (wave & 1) : wave;
-  const int lds0 = (KIND == S_MN128) ? (wave >> 1) * (TILE_BYTES / 2) : 0;
+      const_cast<char*>(st.base + boff), (short)0, (int)__builtin_amdgcn_readfirstlane(n), 0x00020000);
 #pragma unroll
-  for (int j = 0; j < DMA_PER_OPERAND; ++j) {
-    const int b = DMA_PER_OPERAND * wb + j;
-    const int rows_before = (KIND == S_KC) ? 16 * b : (KIND == S_MN256 ? 2 * b : 4 * b);
-    const uint32_t lo = (KIND == S_MN256 && (j & 1)) ? st.lo1 : st.lo0;
-    const uint32_t v = lo + (uint32_t)(rows_before * st.ld * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(tile + lds0 + b * 1024), 16, v, 0, 0, 0);
-  }
+  for (int j = 0; j < DMA_PER_OPERAND; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(wtile + 1024 * j), 16, st.voff[j], so, 0, 0);
 }
 
 // Zero k >= kvalid (0 < kvalid < 32) of a K-contiguous [256][32] LDS tile.
@@ -247,13 +260,16 @@ __device__ __forceinline__ TPS_LDS char* ring_slot() {
 // structs) keep all of it in registers.
 struct TileStreams {
   OpStream a0, a1, b0, b1;
-  int64_t kseg0, kseg1;    // K of each segment
+  int kseg0, kseg1;        // K of each segment
   int nk0;                 // stages of segment 0
   int s0, send;            // the piece: stages [s0, send) of the tile
+  int rot;                 // the piece runs from stage s0 + rot, wrapping around to s0
   int npad;                // send - s0 rounded up to NSTAGE
 };
 
-template <int LAYOUT, bool DUAL, bool SEG2>
+// EXACT: every stage's copies are range-checked at the operand's extent
+// (edge tiles); otherwise only K-tail stages are (whole tiles).
+template <int LAYOUT, bool DUAL, bool SEG2, bool EXACT>
 struct Pipe {
   static constexpr bool A_KC = LAYOUT != L_TN;
   static constexpr bool B_KC = LAYOUT == L_NT;
@@ -261,37 +277,43 @@ struct Pipe {
   static constexpr int KB = B_KC ? S_KC : (DUAL ? S_MN128 : S_MN256);
 
   int wave, wm, wn;
+  int wlds_a, wlds_b;     // this wave's first copy block in the A / B tile (bytes)
   TileStreams cur, nxt;   // nxt.send == 0: no next piece (its copies are empty)
 
   __device__ __forceinline__ void init_wave() {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     wm = wave >> 1;
     wn = wave & 1;
+    wlds_a = 1024 * DMA_PER_OPERAND * wave;
+    wlds_b = TILE_BYTES + (KB == S_MN128 ? (wave >> 1) * (TILE_BYTES / 2) + 1024 * DMA_PER_OPERAND * (wave & 1)
+                                          : 1024 * DMA_PER_OPERAND * wave);
     init_frag_addr();
   }
 
   __device__ __forceinline__ void seg_streams(const Problem& P, int64_t m0, int64_t n0, bool use1, OpStream& sa,
-                                              OpStream& sb, int64_t& K) const {
+                                              OpStream& sb, int& Kseg) const {
     // Field-wise selection keeps the problem description in registers.
     const void* pa = use1 ? P.seg[1].a : P.seg[0].a;
     const void* pb = use1 ? P.seg[1].b : P.seg[0].b;
     const int64_t lda = use1 ? P.seg[1].lda : P.seg[0].lda;
     const int64_t ldb = use1 ? P.seg[1].ldb : P.seg[0].ldb;
-    K = use1 ? P.seg[1].K : P.seg[0].K;
-    sa = A_KC ? stream_kc(pa, lda, P.M, K, m0) : stream_mn<256>(pa, lda, P.M, K, m0);
+    const int64_t K = use1 ? P.seg[1].K : P.seg[0].K;
+    Kseg = (int)K;
+    sa = A_KC ? stream_kc(pa, lda, P.M, K, m0, wave) : stream_mn<256>(pa, lda, P.M, K, m0, wave);
     if (B_KC) {
-      sb = stream_kc(pb, ldb, P.N, K, n0);
+      sb = stream_kc(pb, ldb, P.N, K, n0, wave);
     } else if (DUAL) {   // waves 0,1 stream the gate weight, waves 2,3 the up weight
       const bool up = (wave >> 1) != 0;
-      sb = stream_mn<128>(up ? P.b_up : pb, up ? P.ldb_up : ldb, P.N, K, n0);
+      sb = stream_mn<128>(up ? P.b_up : pb, up ? P.ldb_up : ldb, P.N, K, n0, wave & 1);
     } else {
-      sb = stream_mn<256>(pb, ldb, P.N, K, n0);
+      sb = stream_mn<256>(pb, ldb, P.N, K, n0, wave);
     }
   }
 
-  // Streams of stages [s0, min(s1, stages of the tile)) of the tile at (m0, n0).
-  __device__ __forceinline__ TileStreams make_streams(const Problem& P, int64_t m0, int64_t n0, int s0,
-                                                      int s1) const {
+  // Streams of stages [s0, min(s1, stages of the tile)) of the tile at (m0, n0),
+  // started rot8/8 of the way into the range.
+  __device__ __forceinline__ TileStreams make_streams(const Problem& P, int64_t m0, int64_t n0, int s0, int s1,
+                                                      int rot8 = 0) const {
     TileStreams T;
     seg_streams(P, m0, n0, false, T.a0, T.b0, T.kseg0);
     if (SEG2) {
@@ -305,15 +327,55 @@ struct Pipe {
     const int nk = T.nk0 + (SEG2 ? (int)((T.kseg1 + BK - 1) / BK) : 0);
     T.s0 = s0;
     T.send = min(s1, nk);
+    T.rot = ((T.send - s0) * rot8) >> 3;
     T.npad = (T.send - s0 + NSTAGE - 1) / NSTAGE * NSTAGE;
+    uniform(T);
     return T;
+  }
+
+  // The stream records are wave-uniform, but parts of them are computed on
+  // the vector ALU (integer division has no scalar form); readfirstlane moves
+  // them to scalar registers once per piece, so the per-stage descriptor
+  // arithmetic is scalar.
+  static __device__ __forceinline__ uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+  static __device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
+  static __device__ __forceinline__ void uniform(OpStream& o) {
+    const uint64_t a = reinterpret_cast<uint64_t>(o.base);
+    o.base = reinterpret_cast<const char*>(((uint64_t)sgpr((uint32_t)(a >> 32)) << 32) | sgpr((uint32_t)a));
+    o.nrec = sgpr(o.nrec);
+    o.step = sgpr(o.step);
+  }
+  static __device__ __forceinline__ void uniform(TileStreams& T) {
+    uniform(T.a0);
+    uniform(T.b0);
+    if (SEG2) {
+      uniform(T.a1);
+      uniform(T.b1);
+    }
+    T.kseg0 = sgpr(T.kseg0);
+    T.kseg1 = sgpr(T.kseg1);
+    T.nk0 = sgpr(T.nk0);
+    T.s0 = sgpr(T.s0);
+    T.send = sgpr(T.send);
+    T.rot = sgpr(T.rot);
+    T.npad = sgpr(T.npad);
   }
 
   __device__ __forceinline__ void no_next() {
     nxt = cur;
     nxt.s0 = 0;
     nxt.send = 0;
+    nxt.rot = 0;
     nxt.npad = 0;
+  }
+
+  // Tile stage of step r of a piece; live == false past the piece's end.
+  static __device__ __forceinline__ int stage_of(const TileStreams& T, int r, bool& live) {
+    const int cnt = T.send - T.s0;
+    int t = r + T.rot;
+    t = t >= cnt ? t - cnt : t;
+    live = r < cnt;
+    return T.s0 + t;
   }
 
   // Issue the copies of step r of the current piece (NEXT: of the next
@@ -323,12 +385,18 @@ struct Pipe {
   template <bool NEXT>
   __device__ __forceinline__ void issue(int r, TPS_LDS char* dst) {
     const TileStreams& T = NEXT ? nxt : cur;
-    const int s = T.s0 + r;   // stage within the tile
+    bool live;
+    const int s = stage_of(T, r, live);
     const bool s1 = SEG2 && s >= T.nk0;
     const int stage = s1 ? s - T.nk0 : s;
-    const bool live = s < T.send;
-    stream_issue<KA>(s1 ? T.a1 : T.a0, wave, stage, live, dst);
-    stream_issue<KB>(s1 ? T.b1 : T.b0, wave, stage, live, dst + TILE_BYTES);
+    const bool exact = EXACT || (stage + 1) * BK > (s1 ? T.kseg1 : T.kseg0);
+    // Recompute the LDS destinations at every stage (an empty asm hides the
+    // wave offsets' value): hoisted, the 32 per-slot addresses would crowd
+    // the scalar registers.
+    int wa = wlds_a, wb = wlds_b;
+    asm volatile("" : "+s"(wa), "+s"(wb));
+    stream_issue(s1 ? T.a1 : T.a0, stage, live, exact, dst + wa);
+    stream_issue(s1 ? T.b1 : T.b0, stage, live, exact, dst + wb);
   }
 
   // Per-lane LDS byte addresses of the fragments, computed once.  A fragment
@@ -437,13 +505,14 @@ struct Pipe {
     // retires this wave's reads of the slot that is refilled below.
     waitcnt<(NSTAGE - 2) * 2 * DMA_PER_OPERAND, 0>();
     __builtin_amdgcn_s_barrier();
-    const int ka = cur.s0 + kt;   // stage within the tile
+    bool kt_live;
+    const int ka = stage_of(cur, kt, kt_live);   // stage within the tile
     const bool s1 = SEG2 && ka >= cur.nk0;
-    const int64_t kseg = s1 ? cur.kseg1 : cur.kseg0;
-    const int64_t k0 = (int64_t)(s1 ? ka - cur.nk0 : ka) * BK;
-    if ((A_KC || B_KC) && ka < cur.send && k0 + BK > kseg) {   // K tail of K-contiguous operands
-      if (A_KC) kc_zero_tail(cur_slot, (int)(kseg - k0));
-      if (B_KC) kc_zero_tail(cur_slot + TILE_BYTES, (int)(kseg - k0));
+    const int kseg = s1 ? cur.kseg1 : cur.kseg0;
+    const int k0 = (s1 ? ka - cur.nk0 : ka) * BK;
+    if ((A_KC || B_KC) && kt_live && k0 + BK > kseg) {   // K tail of K-contiguous operands
+      if (A_KC) kc_zero_tail(cur_slot, kseg - k0);
+      if (B_KC) kc_zero_tail(cur_slot + TILE_BYTES, kseg - k0);
       waitcnt<63, 0>();
       __builtin_amdgcn_s_barrier();
     }
@@ -694,7 +763,7 @@ __device__ __forceinline__ Problem pick_problem(const GemmLaunch& L, bool s) {
   TPS_PICK(nseg); TPS_PICK(layout); TPS_PICK(epi); TPS_PICK(b_up); TPS_PICK(ldb_up);
   TPS_PICK(bias); TPS_PICK(bias2); TPS_PICK(c); TPS_PICK(ldc); TPS_PICK(pre); TPS_PICK(ldpre);
   TPS_PICK(tiles_m); TPS_PICK(tiles_n); TPS_PICK(tile_begin);
-  TPS_PICK(edge_only); TPS_PICK(full_m); TPS_PICK(full_n); TPS_PICK(ustages);
+  TPS_PICK(edge_only); TPS_PICK(full_m); TPS_PICK(full_n);
 #undef TPS_PICK
   return P;
 }
@@ -723,186 +792,90 @@ __device__ __forceinline__ void locate(const GemmLaunch& L, int id, int epi, Pro
   n0 = (int64_t)tn * (epi == E_SWIGLU ? BN / 2 : BN);
 }
 
-// ---- schedule of the fast kernels -------------------------------------------------------
-// The whole tiles of a launch are laid end to end as one sequence of K work
-// units (a unit is `ustages` K stages; a tile's last unit may be short), and
-// workgroup g of G takes the units [g W / G, (g+1) W / G).  The launcher
-// picks the unit: a whole tile when there are at least half as many tiles
-// as CUs (each workgroup then runs whole tiles), else 1/s of a tile's K with
-// s = CUs / tiles and G = s * tiles (split-K: each workgroup runs one K
-// slice, and workgroups at the same K offset of neighbouring tiles share
-// operand panels in L2).
-//
-// A tile split over several workgroups is finished by the last of them to
-// arrive: each stores its fp32 part in a slot of the partial buffer and
-// counts itself in at the tile's arrival counter; the one that completes
-// the count sums the parts (in workgroup order, so the result does not
-// depend on arrival order), runs the epilogue and clears the counter.
-// Nobody waits for anybody.  Slots: workgroup g uses slot 2g for the piece
-// at the end of its range and 2g + 1 for the one at its start (a range splits
-// at most those two).  Counters: indexed by the workgroup holding the
-// tile's first unit, which no other split tile shares.
+// ---- schedule of the fast kernels ---------------------------------------------------------
+// Workgroup g of G (one per CU) runs the whole tiles [g T / G, (g+1) T / G)
+// of the launch's T tiles, with the K-stage stream running on from tile to
+// tile.  Workgroup g sits on XCD g / (G / 8), so the tiles that run at the
+// same time on one XCD are neighbours in the grouped tile order and share
+// operand panels in its L2.
+__device__ __forceinline__ int range_begin(int g, int T, int G) { return (int)((int64_t)g * T / G); }
 
-// Tile holding global unit q: its launch-wide index, first unit and units.
-__device__ __forceinline__ void unit_tile(const GemmLaunch& L, int q, int& tile, int& tq0, int& nq) {
-  const bool p1 = L.nprob > 1 && q >= L.p[1].q_begin;
-  const int qb = p1 ? L.p[1].q_begin : L.p[0].q_begin;
-  nq = p1 ? L.p[1].nq : L.p[0].nq;
-  const int local = (q - qb) / nq;
-  tile = (p1 ? L.p[1].tile_begin : L.p[0].tile_begin) + local;
-  tq0 = qb + local * nq;
-}
-
-// First unit of workgroup g's range, and the workgroup whose range holds unit q
-// (the largest g with floor(g W / G) <= q).
-__device__ __forceinline__ int range_begin(int g, int W, int G) { return (int)((int64_t)g * W / G); }
-__device__ __forceinline__ int unit_wg(int q, int W, int G) { return (int)(((int64_t)(q + 1) * G - 1) / W); }
-
-constexpr int SK_SLOT_FLOATS = BM * BN;   // one fp32 partial tile
-
-// Slot layout: chunk c (4 floats) of thread t at float 4 (256 c + t), so each
-// store/load instruction of the workgroup covers 4 KiB contiguously.  Chunk
-// c = 4 (4 i + j) + r holds registers 4r..4r+3 of accumulator block (i, j).
-//
-// Coherence across XCDs (each has its own L2): the parts are written and
-// read with device-scope cache policy (sc1), so stores reach the coherent
-// level and loads do not hit stale L2 lines; a wave's stores are complete
-// once vmcnt reaches zero.  No whole-cache write-back or invalidate is
-// needed, which would cost the other CUs of the XCD their cached operands.
-constexpr int CPOL_DEVICE = 16;   // sc1
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float* slot) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(slot), (short)0, SK_SLOT_FLOATS * 4, 0x00020000);
-}
-
-template <int I, int J>
-__device__ __forceinline__ void sk_store_block(__amdgpu_buffer_rsrc_t slot, const f32x16& a) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int c = (4 * I + J) * 4 + r;
-    const u32x4 v = {__float_as_uint(a[4 * r]), __float_as_uint(a[4 * r + 1]), __float_as_uint(a[4 * r + 2]),
-                     __float_as_uint(a[4 * r + 3])};
-    __builtin_amdgcn_raw_buffer_store_b128(v, slot, 16 * (256 * c + t), 0, CPOL_DEVICE);
-  }
-}
-
-// Each block either goes through the epilogue (whole tile) or into the slot.
-template <int EPI, int... Is>
-__device__ __forceinline__ void piece_blocks(bool whole, const Problem& P, int64_t m0, int64_t n0,
-                                             __amdgpu_buffer_rsrc_t slot,
-                                             f32x16 (&acc)[4][4], std::integer_sequence<int, Is...>) {
-  ((whole ? fast_block<EPI, Is / 4, Is % 4>(P, m0, n0, acc[Is / 4][Is % 4], acc[Is / 4][(Is % 4) ^ 2])
-          : sk_store_block<Is / 4, Is % 4>(slot, acc[Is / 4][Is % 4]),
-    __builtin_amdgcn_sched_barrier(0)),
-   ...);
-}
-
-__device__ __forceinline__ f32x16 join4(const f32x4& a, const f32x4& b, const f32x4& c, const f32x4& d) {
-  return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
-}
-
-// Sum of the parts of a split tile, block row I, then its epilogue.
-template <int EPI, int I>
-__device__ __forceinline__ void sk_reduce_row(const GemmLaunch& L, const Problem& P, int64_t m0, int64_t n0,
-                                              int gfirst, int glast, int last_slot) {
-  const int t = threadIdx.x;
-  f32x4 v[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) v[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int gp = gfirst; gp <= glast; ++gp) {
-    const __amdgpu_buffer_rsrc_t slot =
-        slot_rsrc(L.sk_part + (int64_t)(gp == glast ? last_slot : 2 * gp) * SK_SLOT_FLOATS);
-#pragma unroll
-    for (int c = 0; c < 16; ++c)
-      v[c] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(slot, 16 * (256 * (16 * I + c) + t), 0,
-                                                                               CPOL_DEVICE));
-  }
-  fast_block<EPI, I, 0>(P, m0, n0, join4(v[0], v[1], v[2], v[3]), join4(v[8], v[9], v[10], v[11]));
-  fast_block<EPI, I, 1>(P, m0, n0, join4(v[4], v[5], v[6], v[7]), join4(v[12], v[13], v[14], v[15]));
-  fast_block<EPI, I, 2>(P, m0, n0, join4(v[8], v[9], v[10], v[11]), join4(v[0], v[1], v[2], v[3]));
-  fast_block<EPI, I, 3>(P, m0, n0, join4(v[12], v[13], v[14], v[15]), join4(v[4], v[5], v[6], v[7]));
-}
-
-// Finish one piece (units [q0, q1) of the tile starting at unit tq0, nq units).
-template <int EPI>
-__device__ __forceinline__ void finish_piece(const GemmLaunch& L, int g, int qb, int tile, int tq0, int q0, int q1,
-                                             int nq, f32x16 (&acc)[4][4]) {
-  const bool whole = q0 == 0 && q1 == nq;
-  Problem P;
-  int64_t m0, n0;
-  locate<false>(L, tile, EPI, P, m0, n0);
-  const int my_slot = 2 * g + (tq0 + q1 == qb ? 0 : 1);
-  piece_blocks<EPI>(whole, P, m0, n0, slot_rsrc(L.sk_part + (int64_t)my_slot * SK_SLOT_FLOATS), acc,
-                    std::make_integer_sequence<int, 16>{});
-  if (whole) return;
-  const int G = gridDim.x, W = L.sk_W;
-  const int gfirst = unit_wg(tq0, W, G), glast = unit_wg(tq0 + nq - 1, W, G);
-  waitcnt<0, 15>();   // this wave's part is stored at device scope
-  __syncthreads();    // ... and so are the other three waves' parts
-  uint32_t old = 0;
-  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(L.sk_count + gfirst, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool last = __syncthreads_or(threadIdx.x == 0 && old == (uint32_t)(glast - gfirst));
-  if (!last) return;
-  if (threadIdx.x == 0) __hip_atomic_store(L.sk_count + gfirst, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int last_slot = 2 * glast + (range_begin(glast + 1, W, G) > tq0 + nq ? 1 : 0);
-  sk_reduce_row<EPI, 0>(L, P, m0, n0, gfirst, glast, last_slot);
-  sk_reduce_row<EPI, 1>(L, P, m0, n0, gfirst, glast, last_slot);
-  sk_reduce_row<EPI, 2>(L, P, m0, n0, gfirst, glast, last_slot);
-  sk_reduce_row<EPI, 3>(L, P, m0, n0, gfirst, glast, last_slot);
-}
-
-// Fast kernels: one per (operand layout, epilogue, K segments), so each role
-// of the shard path is a distinct kernel in traces.  Whole tiles only, no
-// bias, aligned outputs; stream-K schedule (above), one workgroup per CU,
-// with the K-stage stream running on from piece to piece.  Workgroup g sits
-// on XCD g / (G / 8), so neighbouring ranges share an L2.
+// Whole tiles [t0, t0 + count) of a launch spread over G workgroups; this is
+// workgroup g.  The K-stage stream runs on from tile to tile.  Tiles start
+// their K loop (xcd/8) of the way in, wrapping around.
 template <int LAYOUT, int EPI, bool SEG2>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch L) {
-  const int G = gridDim.x;
-  const int g = (G % 8 == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  const int W = L.sk_W;
-  const int qa = range_begin(g, W, G), qb = range_begin(g + 1, W, G);
-  if (qa >= qb) return;
+__device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count, int g, int G, int xcd) {
+  const int ta = t0 + range_begin(g, count, G), tb = t0 + range_begin(g + 1, count, G);
+  if (ta >= tb) return;
   constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
-  Pipe<LAYOUT, DUAL, SEG2> pipe;
+  Pipe<LAYOUT, DUAL, SEG2, false> pipe;
   pipe.init_wave();
-  int tile, tq0, nq;
-  unit_tile(L, qb - 1, tile, tq0, nq);
-  int q0 = max(qa, tq0) - tq0, q1 = qb - tq0;   // this piece: units [q0, q1) of the tile
+  int tile = ta;
   {
     Problem P;
     int64_t m0, n0;
     locate<false>(L, tile, EPI, P, m0, n0);
-    pipe.cur = pipe.make_streams(P, m0, n0, P.ustages * q0, P.ustages * q1);
+    pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX, xcd);
   }
   pipe.prologue();
   for (;;) {
-    const int cursor = tq0 + q0;   // first unit of this piece; the next piece ends there
-    const bool more = cursor > qa;
-    int ntile = 0, ntq0 = 0, nnq = 1;
+    const bool more = tile + 1 < tb;
     f32x16 acc[4][4];
     pipe.run_tile(acc, zero_acc, [&]() {
       if (more) {
-        unit_tile(L, cursor - 1, ntile, ntq0, nnq);
         Problem Pn;
         int64_t m0n, n0n;
-        locate<false>(L, ntile, EPI, Pn, m0n, n0n);
-        pipe.nxt = pipe.make_streams(Pn, m0n, n0n, Pn.ustages * (max(qa, ntq0) - ntq0), Pn.ustages * (cursor - ntq0));
+        locate<false>(L, tile + 1, EPI, Pn, m0n, n0n);
+        pipe.nxt = pipe.make_streams(Pn, m0n, n0n, 0, INT_MAX, xcd);
       } else {
         pipe.no_next();
       }
     });
-    finish_piece<EPI>(L, g, qb, tile, tq0, q0, q1, nq, acc);
+    {
+      Problem P;
+      int64_t m0, n0;
+      locate<false>(L, tile, EPI, P, m0, n0);
+      fast_epilogue<EPI>(P, m0, n0, acc, std::make_integer_sequence<int, 16>{});
+    }
     if (!more) break;
-    q0 = max(qa, ntq0) - ntq0;
-    q1 = cursor - ntq0;
-    tile = ntile;
-    tq0 = ntq0;
-    nq = nnq;
+    ++tile;
     pipe.cur = pipe.nxt;
   }
   waitcnt<0, 0>();   // trailing (empty) copies retire before the workgroup ends
+}
+
+// Workgroup index with the workgroups of one XCD numbered consecutively (the
+// hardware hands workgroup b to XCD b % 8), and the XCD.
+__device__ __forceinline__ int wg_index(int& xcd) {
+  const int G = gridDim.x;
+  xcd = blockIdx.x & 7;
+  return (G % 8 == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+}
+
+// Fast kernels: one per (operand layout, epilogue, K segments), so each role
+// of the shard path is a distinct kernel in traces.  Whole tiles only, no
+// bias, aligned outputs; one workgroup per CU.  Starting the K loops of the
+// XCDs at different points keeps the workgroups of one XCD in step (their
+// shared operand panels stay in its L2).
+template <int LAYOUT, int EPI, bool SEG2>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch L) {
+  int xcd;
+  const int g = wg_index(xcd);
+  tile_loop<LAYOUT, EPI, SEG2>(L, 0, L.tiles, g, gridDim.x, xcd);
+}
+
+// Two problems of different operand layouts in one launch: workgroups
+// [0, g0) run problem 0's tiles, the rest problem 1's (plain stores).  Used
+// when one problem alone cannot fill the CUs, e.g. the row-parallel backward,
+// whose weight gradient has few, long tiles and whose input gradient has
+// more, shorter ones.
+template <int LA, int LB>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_dual_kernel(const GemmLaunch L) {
+  int xcd;
+  const int g = wg_index(xcd);
+  const int t1 = L.p[1].tile_begin;
+  if (g < L.g0) tile_loop<LA, E_STORE, false>(L, 0, t1, g, L.g0, xcd);
+  else tile_loop<LB, E_STORE, false>(L, t1, L.tiles - t1, g - L.g0, (int)gridDim.x - L.g0, xcd);
 }
 
 // Generic kernels: one tile per workgroup, any shape, bias, alignment.
@@ -914,7 +887,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmL
   int64_t m0, n0;
   locate<true>(L, id, EPI, P, m0, n0);
   f32x16 acc[4][4];
-  Pipe<LAYOUT, DUAL, SEG2> pipe;
+  Pipe<LAYOUT, DUAL, SEG2, true> pipe;
   pipe.init_wave();
   pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
   pipe.prologue();
@@ -1015,7 +988,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const CEArgs a, in
   P.epi = E_STORE;
   f32x16 acc[4][4];
   {
-    Pipe<L_NT, false, false> pipe;
+    Pipe<L_NT, false, false, true> pipe;
     pipe.init_wave();
     pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
     pipe.prologue();
@@ -1099,60 +1072,66 @@ hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Stream-K partial buffers, one per (device, stream): calls on one stream are
-// ordered, so they can share one; calls on different streams must not.
-// Allocated on first use (two fp32 tile slots per CU plus one arrival
-// counter per CU, the counters zeroed once; every launch leaves them zero)
-// and kept until the process ends.
-struct SkBuffer {
-  float* part = nullptr;
-  uint32_t* count = nullptr;
-  int wgs = 0;
-};
-
-std::mutex g_sk_mu;
-std::map<std::pair<int, hipStream_t>, SkBuffer> g_sk;
-
-hipError_t sk_buffer(int dev, int wgs, hipStream_t s, float*& part, uint32_t*& count) {
-  std::lock_guard<std::mutex> lk(g_sk_mu);
-  SkBuffer& b = g_sk[{dev, s}];
-  if (b.wgs < wgs) {
-    if (b.part) {   // a larger grid than before on this stream: retire the old buffer first
-      hipError_t e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return e;
-      hipFree(b.part);
-      b = SkBuffer{};
-    }
-    const size_t part_bytes = (size_t)2 * wgs * SK_SLOT_FLOATS * sizeof(float);
-    const size_t bytes = part_bytes + (size_t)wgs * sizeof(uint32_t);
-    void* p = nullptr;
-    hipError_t e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return e;
-    e = hipMemset(static_cast<char*>(p) + part_bytes, 0, bytes - part_bytes);
-    if (e != hipSuccess) {
-      hipFree(p);
-      return e;
-    }
-    b.part = static_cast<float*>(p);
-    b.count = reinterpret_cast<uint32_t*>(static_cast<char*>(p) + part_bytes);
-    b.wgs = wgs;
-  }
-  part = b.part;
-  count = b.count;
-  return hipSuccess;
-}
-
-int stages_of(const Problem& P) {
-  int nk = (int)((P.seg[0].K + BK - 1) / BK);
-  if (P.nseg > 1) nk += (int)((P.seg[1].K + BK - 1) / BK);
-  return nk;
-}
-
 }  // namespace
 
+// Stages of a problem's tile rounded up to the ring depth (its MFMA time).
+int64_t tile_stages(const Problem& P) {
+  int64_t nk = (P.seg[0].K + BK - 1) / BK;
+  if (P.nseg > 1) nk += (P.seg[1].K + BK - 1) / BK;
+  return (nk + NSTAGE - 1) / NSTAGE * NSTAGE;
+}
+
+// Problem 0 on g0 workgroups and problem 1 on the rest of `cus`, one launch:
+// the best g0 and its makespan (in tile stages).
+int64_t dual_split(int64_t t0, int64_t s0, int64_t t1, int64_t s1, int cus, int& g0) {
+  int64_t best = INT64_MAX;
+  g0 = 1;
+  for (int g = 1; g < cus; ++g) {
+    const int64_t m = std::max((t0 + g - 1) / g * s0, (t1 + cus - g - 1) / (cus - g) * s1);
+    if (m < best) {
+      best = m;
+      g0 = g;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
-  // Problems of one launch must share the operand layout and the epilogue;
-  // otherwise split.  Only L_NN carries activation epilogues.
+  int dev = 0, cus = 256;
+  {
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  // The row-parallel backward pair (TN weight gradient, NT input gradient) in
+  // one launch, when all their tiles are whole and sharing the CUs beats
+  // running them one after the other.
+  if (L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
+      L.p[1].epi == E_STORE && L.p[0].nseg == 1 && L.p[1].nseg == 1 && fast_ok(L.p[0]) && fast_ok(L.p[1]) &&
+      L.p[0].M % BM == 0 && L.p[0].N % BN == 0 && L.p[1].M % BM == 0 && L.p[1].N % BN == 0 && cus % 8 == 0) {
+    const int64_t t0 = (L.p[0].M / BM) * (L.p[0].N / BN), t1 = (L.p[1].M / BM) * (L.p[1].N / BN);
+    const int64_t s0 = tile_stages(L.p[0]), s1 = tile_stages(L.p[1]);
+    const int64_t apart = (t0 + cus - 1) / cus * s0 + (t1 + cus - 1) / cus * s1;   // one after the other
+    int g0 = 1;
+    const int64_t together = dual_split(t0, s0, t1, s1, cus, g0);
+    if (together < apart && t0 + t1 < INT_MAX) {
+      GemmLaunch D = L;
+      for (int i = 0; i < 2; ++i) {
+        D.p[i].tiles_m = (int)(L.p[i].M / BM);
+        D.p[i].tiles_n = (int)(L.p[i].N / BN);
+        D.p[i].edge_only = 0;
+      }
+      D.p[0].tile_begin = 0;
+      D.p[1].tile_begin = (int)t0;
+      D.tiles = (int)(t0 + t1);
+      D.g0 = g0;
+      hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      return hipGetLastError();
+    }
+  }
+  // Otherwise problems of one launch must share the operand layout and the
+  // epilogue; else split.  Only L_NN carries activation epilogues.
   if (L.nprob > 1 && (L.p[0].layout != L.p[1].layout || L.p[0].epi != L.p[1].epi)) {
     GemmLaunch a = L, b = L;
     a.nprob = 1;
@@ -1166,38 +1145,15 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   GemmLaunch F = L, E = L;   // whole tiles (fast kernel), remaining tiles (generic kernel)
   int nf = 0, ne = 0;
   int64_t W = 0;
-  int cus = 256, dev = 0;
-  {
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-  }
-  int whole_tiles = 0;
-  for (int i = 0; i < L.nprob; ++i) {
-    const Problem& P = L.p[i];
-    const int64_t bn = (P.epi == E_SWIGLU) ? BN / 2 : BN;
-    if (fast) whole_tiles += (int)(P.M / BM) * (int)(P.N / bn);
-  }
-  // split factor: K slices per tile (1: whole tiles)
-  const int split = (whole_tiles > 0 && 2 * whole_tiles <= cus) ? cus / whole_tiles : 1;
   for (int i = 0; i < L.nprob; ++i) {
     const Problem& P = L.p[i];
     const int64_t bn = (P.epi == E_SWIGLU) ? BN / 2 : BN;
     const int tm = (int)((P.M + BM - 1) / BM), tn = (int)((P.N + bn - 1) / bn);
     const int fm = fast ? (int)(P.M / BM) : 0, fn = fast ? (int)(P.N / bn) : 0;
-    const int nk = std::max(1, stages_of(P));
-    const int quads = (nk + NSTAGE - 1) / NSTAGE;
-    const int s_i = std::min(split, quads);                      // at least one ring of stages per slice
-    const int uq = (quads + s_i - 1) / s_i;                      // quads per unit
     F.p[i].tiles_m = fm;
     F.p[i].tiles_n = fn;
     F.p[i].tile_begin = nf;
     F.p[i].edge_only = 0;
-    F.p[i].ustages = uq * NSTAGE;
-    F.p[i].nq = (quads + uq - 1) / uq;
-    F.p[i].q_begin = (int)W;
-    W += (int64_t)fm * fn * F.p[i].nq;
     nf += fm * fn;
     E.p[i].tiles_m = tm;
     E.p[i].tiles_n = tn;
@@ -1207,13 +1163,9 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     E.p[i].tile_begin = ne;
     ne += tm * tn - fm * fn;
   }
-  if (W >= INT_MAX) return hipErrorInvalidValue;
   if (nf > 0) {
-    const int grid = (int)std::min<int64_t>(cus, W);
-    F.sk_W = (int)W;
-    hipError_t e = sk_buffer(dev, cus, s, F.sk_part, F.sk_count);
-    if (e != hipSuccess) return e;
-    e = dispatch<true>(F, nf, grid, s);
+    F.tiles = nf;
+    hipError_t e = dispatch<true>(F, nf, std::min(nf, cus), s);
     if (e != hipSuccess) return e;
   }
   if (ne > 0) return dispatch<false>(E, ne, ne, s);

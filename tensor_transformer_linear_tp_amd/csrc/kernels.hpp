@@ -46,8 +46,6 @@ struct Problem {
   int tiles_m, tiles_n, tile_begin;
   int edge_only;         // tiles enumerate only the ragged edge (right strip, then bottom strip)
   int full_m, full_n;    // whole tiles along M and N (edge_only)
-  int nq, q_begin;       // split tiles: work units per tile, first unit of this problem
-  int ustages;           // K stages per work unit (a multiple of the LDS ring depth)
 };
 
 // Up to two independent GEMM problems share one launch (their tiles are
@@ -55,12 +53,8 @@ struct Problem {
 struct GemmLaunch {
   Problem p[2];
   int nprob;
-  // stream-K (bf16 whole-tile kernels): total work units, partial-tile
-  // slots (two per workgroup), arrival counters (one per workgroup, zero
-  // between launches)
-  int sk_W;
-  float* sk_part;
-  uint32_t* sk_count;
+  int tiles;             // bf16 whole-tile kernels: tiles of the launch
+  int g0;                // two-layout launch: workgroups of problem 0
 };
 
 struct CEArgs {

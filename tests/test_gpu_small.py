@@ -144,6 +144,24 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
     assert_close("db", host64(db), rdb, TOL[dtype])
 
 
+# Whole 256 x 256 tiles only (the persistent whole-tile kernels; for the row
+# backward, its two GEMMs share one launch).
+TILE_SHAPES = [(512, 256, 768), (768, 512, 256)]
+
+
+@pytest.mark.parametrize("shape", TILE_SHAPES)
+def test_row_bwd_whole_tiles(shape):
+    M, N, K = shape
+    dtype = syn.BF16
+    d = _inputs(dtype, M, N, K, 11 + M, "none")
+    Xi, Bi = dev(d["dY"]), dev(d["B"])
+    dX, dB, _ = ops.row_bwd(dev(d["dZ"]), Xi, Bi)
+    torch.cuda.synchronize()
+    rdX, rdB, _ = oracle.row_bwd(d["dZ"].f64, d["dY"].f64, d["B"].f64)
+    assert_close("dX", host64(dX), rdX, TOL[dtype])
+    assert_close("dB", host64(dB), rdB, TOL[dtype])
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("act", ["none", "gelu", "swiglu"])
