@@ -1,25 +1,25 @@
 // bf16 GEMM family for gfx950 (MI355X): C = A B with fp32 accumulation on
-// v_mfma_f32_32x32x16_bf16, LDS-staged double-buffered tiles and fused
-// epilogues; plus the vocab-parallel LM-head kernel whose epilogue reduces
-// logit tiles to (max, sum exp) partials without writing the logits.
+// v_mfma_f32_32x32x16_bf16, a 4-stage LDS ring filled by direct-to-LDS buffer
+// loads, and fused epilogues; plus the vocab-parallel LM-head kernel whose
+// epilogue reduces logit tiles to (max, sum exp) partials without writing the
+// logits.
 //
 // Tiling: a 256-thread workgroup (4 wave64s as 2 x 2) owns a 256 x 256 output
 // tile (SwiGLU: 256 rows x (128 gate + 128 up) columns); each wave owns
-// 128 x 128 = 4 x 4 MFMA blocks of 32 x 32.  K advances 64 per LDS stage.
+// 128 x 128 = 4 x 4 MFMA blocks of 32 x 32.  K advances 32 per LDS stage.
 //
-// LDS layouts.  Operands are copied global -> registers -> LDS in their
-// global orientation:
-//   * K-contiguous operand (A of NN/NT, B of NT): [256 rows][64 k], read as
+// LDS layouts.  Operands are copied global -> LDS in their global orientation:
+//   * K-contiguous operand (A of NN/NT, B of NT): [256 rows][32 k], read as
 //     MFMA fragments with one ds_read_b128 per lane;
-//   * MN-contiguous operand (A of TN, B of NN/TN): [64 k][256 cols], read
+//   * MN-contiguous operand (A of TN, B of NN/TN): [32 k][256 cols], read
 //     with two ds_read_b64_tr_b16 per lane, which transposes 16-bit elements
 //     across each 16-lane group on the way out of LDS.
 // Both use an XOR swizzle of the 16-byte chunk index so that fragment reads
-// and the staging writes fall into distinct banks.
+// fall into distinct banks.
 //
 // Accumulator orientation.  The MFMA is issued as (B fragment, A fragment),
 // so each lane holds four consecutive output columns of one row per
-// register quad; epilogue stores are 8-byte (bf16) vectors.
+// register quad.
 #include <algorithm>
 #include <climits>
 #include <utility>
