@@ -23,9 +23,10 @@
  *            written.  A failed launch returns TP_E_HIP (outputs undefined).
  *            A device fault surfaces at the caller's next synchronization.
  * Shapes.    M, N, K >= 1 (int64, each < 2^31); tails of any size are masked
- *            inside the kernels.  A bf16 matrix must span less than 4 GiB:
- *            ((rows - 1) * ld + width rounded up to 8) * 2 bytes < 2^32
- *            (the kernels address operands with 32-bit offsets).
+ *            inside the kernels.  A bf16 matrix must span less than 2 GiB:
+ *            ((rows - 1) * ld + width rounded up to 8) * 2 bytes < 2^31
+ *            (the kernels address operands with 32-bit offsets); otherwise
+ *            TP_E_SHAPE.
  * Alignment. Every base pointer must be 16-byte aligned and every `ld` a
  *            multiple of 8 elements for bf16 (4 for fp32), so 16-byte vector
  *            accesses are legal.  The kernels may READ each input row up to

@@ -28,10 +28,11 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 size_t align_ws(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // bf16 matrices are addressed through buffer descriptors with 32-bit
-// offsets: the bytes from a matrix's base to the end of its last row (width
-// rounded up to 8 elements) must stay below 4 GiB.
+// offsets (a lane's offset plus a stage offset): the bytes from a matrix's
+// base to the end of its last row (width rounded up to 8 elements) must stay
+// below 2 GiB.
 bool bf16_extent_ok(int64_t rows, int64_t ld, int64_t width) {
-  constexpr int64_t kMaxElems = int64_t(0xffffffff) / 2;
+  constexpr int64_t kMaxElems = int64_t(0x7fffffff) / 2;
   if (rows > 1 && ld > kMaxElems / (rows - 1)) return false;
   return (rows - 1) * ld + round_up(width, 8) <= kMaxElems;
 }

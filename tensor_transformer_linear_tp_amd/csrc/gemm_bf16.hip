@@ -61,7 +61,7 @@ constexpr int DMA_PER_OPERAND = 4;            // copy instructions per wave per 
 
 // Copy stream of one operand of one K segment of one piece: the address of
 // the tile's origin, the bytes from there to the end of the operand's extent
-// (operands are below 4 GiB, so 32 bits hold every offset), the bytes per K
+// (operands are below 2 GiB, so 32 bits hold every offset), the bytes per K
 // stage, and this wave's per-lane byte offsets of its blocks (block j of the
 // wave is block 4 w + j of the stage; w = the wave, or for S_MN128 the wave
 // within its half).  Everything but the offsets is wave-uniform.
@@ -122,27 +122,19 @@ __device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t
 
 // Issue the copies of K stage `stage` of one operand (this wave's
 // DMA_PER_OPERAND blocks; `wtile` is this wave's first block in the LDS
-// tile).  live == false: an empty range, zeros written.
-//   exact: the descriptor starts at the stage, so its range check zero-fills
-//     whatever lies past the operand's extent (rows beyond M, N or K, the
-//     last row's K tail).
-//   otherwise (the stage lies inside the operand): the descriptor stays at
-//     the tile's origin and the stage offset goes into soffset.
-__device__ __forceinline__ void stream_issue(const OpStream& st, int stage, bool live, bool exact,
-                                             TPS_LDS char* wtile) {
-  // Branch-free selects of wave-uniform values keep the descriptor in SGPRs.
-  const uint32_t off = (uint32_t)stage * st.step;
-  const uint32_t boff = (live && exact) ? off : 0u;
-  const uint32_t so = exact ? 0u : off;
-  const uint32_t n = !live ? 0u : (!exact ? st.nrec : (st.nrec > off ? st.nrec - off : 0u));
-  // The clamp has no scalar instruction, so n is computed on the vector ALU;
-  // readfirstlane brings it back (a descriptor in VGPRs would make the
-  // compiler loop over lanes around every copy).
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(st.base + boff), (short)0, (int)__builtin_amdgcn_readfirstlane(n), 0x00020000);
+// tile).  The descriptor stays at the tile's origin with the operand's
+// remaining extent as its range; the stage offset goes into each lane's
+// voffset, which the range check covers, so whatever lies past the extent
+// (rows beyond M, N or K, the last row's K tail) reads as zero.  live ==
+// false: every lane is sent past the range, so the stage is all zeros.
+// (Operands below 2 GiB keep voffset + offset inside 32 bits.)
+__device__ __forceinline__ void stream_issue(const OpStream& st, int stage, bool live, TPS_LDS char* wtile) {
+  const uint32_t off = live ? (uint32_t)stage * st.step : st.nrec;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(st.base), (short)0, (int)st.nrec, 0x00020000);
 #pragma unroll
   for (int j = 0; j < DMA_PER_OPERAND; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(wtile + 1024 * j), 16, st.voff[j], so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(wtile + 1024 * j), 16, st.voff[j] + off, 0, 0, 0);
 }
 
 // Zero k >= kvalid (0 < kvalid < 32) of a K-contiguous [256][32] LDS tile.
@@ -267,9 +259,7 @@ struct TileStreams {
   int npad;                // send - s0 rounded up to NSTAGE
 };
 
-// EXACT: every stage's copies are range-checked at the operand's extent
-// (edge tiles); otherwise only K-tail stages are (whole tiles).
-template <int LAYOUT, bool DUAL, bool SEG2, bool EXACT>
+template <int LAYOUT, bool DUAL, bool SEG2>
 struct Pipe {
   static constexpr bool A_KC = LAYOUT != L_TN;
   static constexpr bool B_KC = LAYOUT == L_NT;
@@ -389,14 +379,13 @@ struct Pipe {
     const int s = stage_of(T, r, live);
     const bool s1 = SEG2 && s >= T.nk0;
     const int stage = s1 ? s - T.nk0 : s;
-    const bool exact = EXACT || (stage + 1) * BK > (s1 ? T.kseg1 : T.kseg0);
     // Recompute the LDS destinations at every stage (an empty asm hides the
     // wave offsets' value): hoisted, the 32 per-slot addresses would crowd
     // the scalar registers.
     int wa = wlds_a, wb = wlds_b;
     asm volatile("" : "+s"(wa), "+s"(wb));
-    stream_issue(s1 ? T.a1 : T.a0, stage, live, exact, dst + wa);
-    stream_issue(s1 ? T.b1 : T.b0, stage, live, exact, dst + wb);
+    stream_issue(s1 ? T.a1 : T.a0, stage, live, dst + wa);
+    stream_issue(s1 ? T.b1 : T.b0, stage, live, dst + wb);
   }
 
   // Per-lane LDS byte addresses of the fragments, computed once.  A fragment
@@ -808,7 +797,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
   const int ta = t0 + range_begin(g, count, G), tb = t0 + range_begin(g + 1, count, G);
   if (ta >= tb) return;
   constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
-  Pipe<LAYOUT, DUAL, SEG2, false> pipe;
+  Pipe<LAYOUT, DUAL, SEG2> pipe;
   pipe.init_wave();
   int tile = ta;
   {
@@ -887,7 +876,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmL
   int64_t m0, n0;
   locate<true>(L, id, EPI, P, m0, n0);
   f32x16 acc[4][4];
-  Pipe<LAYOUT, DUAL, SEG2, true> pipe;
+  Pipe<LAYOUT, DUAL, SEG2> pipe;
   pipe.init_wave();
   pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
   pipe.prologue();
@@ -988,7 +977,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const CEArgs a, in
   P.epi = E_STORE;
   f32x16 acc[4][4];
   {
-    Pipe<L_NT, false, false, true> pipe;
+    Pipe<L_NT, false, false> pipe;
     pipe.init_wave();
     pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
     pipe.prologue();
