@@ -81,6 +81,7 @@ __device__ __forceinline__ int64_t extent_bytes(int64_t rows, int64_t ld, int64_
 // K-contiguous operand: tile rows [row0, row0+256) of a [rows][K] matrix.
 // Block b (16 rows) of the stage: lane L copies row 16b + L/4, logical chunk
 // (L%4) ^ kc_swz(row) -- the swizzle only depends on the row's low 4 bits.
+template <int NB = DMA_PER_OPERAND>
 __device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t rows, int64_t K, int64_t row0,
                                               int wb) {
   const int lane = threadIdx.x & 63;
@@ -91,8 +92,8 @@ __device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t
   const int r = lane >> 2;
   const int c = (lane & 3) ^ kc_swz(r);
 #pragma unroll
-  for (int j = 0; j < DMA_PER_OPERAND; ++j) {
-    const int row = 16 * (DMA_PER_OPERAND * wb + j) + r;
+  for (int j = 0; j < NB; ++j) {
+    const int row = 16 * (NB * wb + j) + r;
     s.voff[j] = (uint32_t)((row * ld + 8 * c) * 2);
   }
   return s;
@@ -128,12 +129,13 @@ __device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t
 // (rows beyond M, N or K, the last row's K tail) reads as zero.  live ==
 // false: every lane is sent past the range, so the stage is all zeros.
 // (Operands below 2 GiB keep voffset + offset inside 32 bits.)
+template <int NB = DMA_PER_OPERAND>
 __device__ __forceinline__ void stream_issue(const OpStream& st, int stage, bool live, TPS_LDS char* wtile) {
   const uint32_t off = live ? (uint32_t)stage * st.step : st.nrec;
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(st.base), (short)0, (int)st.nrec, 0x00020000);
 #pragma unroll
-  for (int j = 0; j < DMA_PER_OPERAND; ++j)
+  for (int j = 0; j < NB; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(wtile + 1024 * j), 16, st.voff[j] + off, 0, 0, 0);
 }
 
@@ -259,10 +261,15 @@ struct TileStreams {
   int npad;                // send - s0 rounded up to NSTAGE
 };
 
-template <int LAYOUT, bool DUAL, bool SEG2>
+// MI: 32-row MFMA blocks per wave along M (4: 256-row tiles; 2: 128-row
+// tiles, K-contiguous A only).
+template <int LAYOUT, bool DUAL, bool SEG2, int MI = 4>
 struct Pipe {
   static constexpr bool A_KC = LAYOUT != L_TN;
   static constexpr bool B_KC = LAYOUT == L_NT;
+  static_assert(MI == 4 || (MI == 2 && A_KC), "128-row tiles need a K-contiguous A");
+  static constexpr int NBA = DMA_PER_OPERAND * MI / 4;   // A copies per wave per stage
+  static constexpr int NCOPY = NBA + DMA_PER_OPERAND;   // copies per wave per stage
   static constexpr int KA = A_KC ? S_KC : S_MN256;
   static constexpr int KB = B_KC ? S_KC : (DUAL ? S_MN128 : S_MN256);
 
@@ -274,7 +281,7 @@ struct Pipe {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     wm = wave >> 1;
     wn = wave & 1;
-    wlds_a = 1024 * DMA_PER_OPERAND * wave;
+    wlds_a = 1024 * NBA * wave;
     wlds_b = TILE_BYTES + (KB == S_MN128 ? (wave >> 1) * (TILE_BYTES / 2) + 1024 * DMA_PER_OPERAND * (wave & 1)
                                           : 1024 * DMA_PER_OPERAND * wave);
     init_frag_addr();
@@ -289,7 +296,7 @@ struct Pipe {
     const int64_t ldb = use1 ? P.seg[1].ldb : P.seg[0].ldb;
     const int64_t K = use1 ? P.seg[1].K : P.seg[0].K;
     Kseg = (int)K;
-    sa = A_KC ? stream_kc(pa, lda, P.M, K, m0, wave) : stream_mn<256>(pa, lda, P.M, K, m0, wave);
+    sa = A_KC ? stream_kc<NBA>(pa, lda, P.M, K, m0, wave) : stream_mn<256>(pa, lda, P.M, K, m0, wave);
     if (B_KC) {
       sb = stream_kc(pb, ldb, P.N, K, n0, wave);
     } else if (DUAL) {   // waves 0,1 stream the gate weight, waves 2,3 the up weight
@@ -384,7 +391,7 @@ struct Pipe {
     // the scalar registers.
     int wa = wlds_a, wb = wlds_b;
     asm volatile("" : "+s"(wa), "+s"(wb));
-    stream_issue(s1 ? T.a1 : T.a0, stage, live, dst + wa);
+    stream_issue<NBA>(s1 ? T.a1 : T.a0, stage, live, dst + wa);
     stream_issue(s1 ? T.b1 : T.b0, stage, live, dst + wb);
   }
 
@@ -403,7 +410,7 @@ struct Pipe {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       if (A_KC) {
-        const int r = 128 * wm + (lane & 31);
+        const int r = 32 * MI * wm + (lane & 31);
         adA[x] = kc_off(r, 2 * (x & 1) + hi32);
       } else {
         const int col = 128 * wm + 32 * x + 16 * (h & 1) + 4 * (q & 3);
@@ -440,7 +447,7 @@ struct Pipe {
 
   __device__ __forceinline__ void load(const TPS_LDS char* base, int kk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
       af[kk][i] = A_KC ? rd_kc(base + adA[kk] + 2048 * i) : rd_mn(base + adA[i] + 16 * kk * 512, 512);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -450,9 +457,9 @@ struct Pipe {
     }
   }
 
-  __device__ __forceinline__ void mma(int r, f32x16 (&acc)[4][4]) {
+  __device__ __forceinline__ void mma(int r, f32x16 (&acc)[MI][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[r][j], af[r][i], acc[i][j], 0, 0, 0);
@@ -469,13 +476,13 @@ struct Pipe {
   // Ask the scheduler to alternate one MFMA with one LDS read (and, in the
   // first phase of a step, one global->LDS copy), instead of loading each
   // fragment just before its first use.
-  static constexpr int READS = (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
+  static constexpr int READS = (A_KC ? MI : 8) + (B_KC ? 4 : 8);
   static __device__ __forceinline__ void interleave(bool with_copies) {
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < 4 * MI; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
       if (g < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // DS read
-      if (with_copies && g < 2 * DMA_PER_OPERAND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+      if (with_copies && g < NCOPY) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -487,12 +494,12 @@ struct Pipe {
   // LAST: one of the piece's last NSTAGE steps, which issue the next piece's
   // first stages (all but the first of them).
   template <int S, bool LAST>
-  __device__ __forceinline__ void step(int kt, f32x16 (&acc)[4][4]) {
+  __device__ __forceinline__ void step(int kt, f32x16 (&acc)[MI][4]) {
     TPS_LDS char* cur_slot = ring_slot<S>();
     // Stage kt's copies are complete once only the later NSTAGE-2 stages'
-    // copies (2 * DMA_PER_OPERAND each) remain outstanding; lgkmcnt(0)
+    // copies (NCOPY each) remain outstanding; lgkmcnt(0)
     // retires this wave's reads of the slot that is refilled below.
-    waitcnt<(NSTAGE - 2) * 2 * DMA_PER_OPERAND, 0>();
+    waitcnt<(NSTAGE - 2) * NCOPY, 0>();
     __builtin_amdgcn_s_barrier();
     bool kt_live;
     const int ka = stage_of(cur, kt, kt_live);   // stage within the tile
@@ -521,7 +528,7 @@ struct Pipe {
   // `next` is called before the last NSTAGE steps and must set nxt (or call
   // no_next()); those steps issue the next piece's first stages.
   template <class InitFn, class NextFn>
-  __device__ __forceinline__ void run_tile(f32x16 (&acc)[4][4], InitFn&& init, NextFn&& next) {
+  __device__ __forceinline__ void run_tile(f32x16 (&acc)[MI][4], InitFn&& init, NextFn&& next) {
     init(acc);
     zero_set1();              // the first step's deferred sub-step multiplies zeros
     int kt = 0;
@@ -546,9 +553,10 @@ struct Pipe {
   }
 };
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+template <int MI>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MI][4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0.f};
 }
@@ -585,13 +593,13 @@ __device__ __forceinline__ void store_pk(uint16_t* p, const uint32_t (&pk)[8]) {
   *reinterpret_cast<u32x4*>(p + 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
 }
 
-template <int EPI, int I, int J>
+template <int EPI, int MI, int I, int J>
 __device__ __forceinline__ void fast_block(const Problem& P, int64_t m0, int64_t n0, const f32x16& a,
                                            const f32x16& b) {
   constexpr bool dual = EPI == E_SWIGLU;
   if (dual && J >= 2) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  const int64_t m = m0 + 128 * wm + 32 * I + (lane & 31);
+  const int64_t m = m0 + 32 * MI * wm + 32 * I + (lane & 31);
   const int64_t n = n0 + (dual ? 64 * wn + 32 * (J & 1) : 128 * wn + 32 * J) + 8 * (lane >> 5);
   uint32_t py[8], pg[8], pu[8];
 #pragma unroll
@@ -622,10 +630,10 @@ __device__ __forceinline__ void fast_block(const Problem& P, int64_t m0, int64_t
   }
 }
 
-template <int EPI, int... Is>
-__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[4][4],
+template <int EPI, int MI, int... Is>
+__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[MI][4],
                                               std::integer_sequence<int, Is...>) {
-  ((fast_block<EPI, Is / 4, Is % 4>(P, m0, n0, acc[Is / 4][Is % 4], acc[Is / 4][(Is % 4) ^ 2]),
+  ((fast_block<EPI, MI, Is / 4, Is % 4>(P, m0, n0, acc[Is / 4][Is % 4], acc[Is / 4][(Is % 4) ^ 2]),
     __builtin_amdgcn_sched_barrier(0)),
    ...);
 }
@@ -792,29 +800,42 @@ __device__ __forceinline__ int range_begin(int g, int T, int G) { return (int)((
 // Whole tiles [t0, t0 + count) of a launch spread over G workgroups; this is
 // workgroup g.  The K-stage stream runs on from tile to tile.  Tiles start
 // their K loop (xcd/8) of the way in, wrapping around.
-template <int LAYOUT, int EPI, bool SEG2>
+// Tile `tile` of a whole-tile launch; with MI == 2 the launch's tiles are
+// the two 128-row halves of the 256-row tiles from L.half_base on.
+template <int MI>
+__device__ __forceinline__ void locate_mi(const GemmLaunch& L, int tile, int epi, Problem& P, int64_t& m0,
+                                          int64_t& n0) {
+  if (MI == 4) {
+    locate<false>(L, tile, epi, P, m0, n0);
+  } else {
+    locate<false>(L, L.half_base + (tile >> 1), epi, P, m0, n0);
+    m0 += (tile & 1) * (BM / 2);
+  }
+}
+
+template <int LAYOUT, int EPI, bool SEG2, int MI = 4>
 __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count, int g, int G, int xcd) {
   const int ta = t0 + range_begin(g, count, G), tb = t0 + range_begin(g + 1, count, G);
   if (ta >= tb) return;
   constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
-  Pipe<LAYOUT, DUAL, SEG2> pipe;
+  Pipe<LAYOUT, DUAL, SEG2, MI> pipe;
   pipe.init_wave();
   int tile = ta;
   {
     Problem P;
     int64_t m0, n0;
-    locate<false>(L, tile, EPI, P, m0, n0);
+    locate_mi<MI>(L, tile, EPI, P, m0, n0);
     pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX, xcd);
   }
   pipe.prologue();
   for (;;) {
     const bool more = tile + 1 < tb;
-    f32x16 acc[4][4];
-    pipe.run_tile(acc, zero_acc, [&]() {
+    f32x16 acc[MI][4];
+    pipe.run_tile(acc, zero_acc<MI>, [&]() {
       if (more) {
         Problem Pn;
         int64_t m0n, n0n;
-        locate<false>(L, tile + 1, EPI, Pn, m0n, n0n);
+        locate_mi<MI>(L, tile + 1, EPI, Pn, m0n, n0n);
         pipe.nxt = pipe.make_streams(Pn, m0n, n0n, 0, INT_MAX, xcd);
       } else {
         pipe.no_next();
@@ -823,8 +844,8 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
     {
       Problem P;
       int64_t m0, n0;
-      locate<false>(L, tile, EPI, P, m0, n0);
-      fast_epilogue<EPI>(P, m0, n0, acc, std::make_integer_sequence<int, 16>{});
+      locate_mi<MI>(L, tile, EPI, P, m0, n0);
+      fast_epilogue<EPI, MI>(P, m0, n0, acc, std::make_integer_sequence<int, 4 * MI>{});
     }
     if (!more) break;
     ++tile;
@@ -846,11 +867,11 @@ __device__ __forceinline__ int wg_index(int& xcd) {
 // bias, aligned outputs; one workgroup per CU.  Starting the K loops of the
 // XCDs at different points keeps the workgroups of one XCD in step (their
 // shared operand panels stay in its L2).
-template <int LAYOUT, int EPI, bool SEG2>
+template <int LAYOUT, int EPI, bool SEG2, int MI>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch L) {
   int xcd;
   const int g = wg_index(xcd);
-  tile_loop<LAYOUT, EPI, SEG2>(L, 0, L.tiles, g, gridDim.x, xcd);
+  tile_loop<LAYOUT, EPI, SEG2, MI>(L, 0, L.tiles, g, gridDim.x, xcd);
 }
 
 // Two problems of different operand layouts in one launch: workgroups
@@ -880,7 +901,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmL
   pipe.init_wave();
   pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
   pipe.prologue();
-  pipe.run_tile(acc, zero_acc, [&]() { pipe.no_next(); });
+  pipe.run_tile(acc, zero_acc<4>, [&]() { pipe.no_next(); });
   waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
   __syncthreads();
   generic_epilogue(P, m0, n0, acc);
@@ -981,7 +1002,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const CEArgs a, in
     pipe.init_wave();
     pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
     pipe.prologue();
-    pipe.run_tile(acc, zero_acc, [&]() { pipe.no_next(); });
+    pipe.run_tile(acc, zero_acc<4>, [&]() { pipe.no_next(); });
     waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
     __syncthreads();
   }
@@ -1041,15 +1062,19 @@ bool fast_ok(const Problem& P) {
   return true;
 }
 
-template <bool FAST>
+// FAST: whole tiles (HALF: the 128-row halves of the tiles from half_base on;
+// layouts with a K-contiguous A and one K segment only); else edge tiles.
+template <bool FAST, bool HALF = false>
 hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
   const dim3 g(grid), block(NTHREADS);
   const int layout = L.p[0].layout, epi = L.p[0].epi;
   const bool seg2 = L.p[0].nseg > 1 || (L.nprob > 1 && L.p[1].nseg > 1);
-#define TPS_LAUNCH(LY, EP, S2)                                                           \
-  do {                                                                                   \
-    if (FAST) hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2>), g, block, 0, s, L);     \
-    else hipLaunchKernelGGL((gemm_bf16_edge_kernel<LY, EP, S2>), g, block, 0, s, L, total); \
+#define TPS_LAUNCH(LY, EP, S2)                                                                    \
+  do {                                                                                            \
+    if (FAST && HALF && LY != L_TN && !S2)                                                        \
+      hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, (LY != L_TN && !S2) ? 2 : 4>), g, block, 0, s, L); \
+    else if (FAST) hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, 4>), g, block, 0, s, L);     \
+    else hipLaunchKernelGGL((gemm_bf16_edge_kernel<LY, EP, S2>), g, block, 0, s, L, total);      \
   } while (0)
   if (layout == L_NN && epi == E_SWIGLU) TPS_LAUNCH(L_NN, E_SWIGLU, false);
   else if (layout == L_NN && epi == E_GELU) TPS_LAUNCH(L_NN, E_GELU, false);
@@ -1153,9 +1178,21 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     ne += tm * tn - fm * fn;
   }
   if (nf > 0) {
-    F.tiles = nf;
-    hipError_t e = dispatch<true>(F, nf, std::min(nf, cus), s);
+    // A last round that would leave over half the CUs idle runs as 128-row
+    // half tiles instead (layouts with a K-contiguous A and one segment).
+    const bool half_ok = L.p[0].layout != L_TN && L.p[0].nseg == 1 && (L.nprob == 1 || L.p[1].nseg == 1);
+    const int rem = nf % cus;
+    const int tail = (half_ok && nf > cus && rem > 0 && 2 * rem <= cus) ? rem : 0;
+    F.tiles = nf - tail;
+    hipError_t e = dispatch<true>(F, F.tiles, std::min(F.tiles, cus), s);
     if (e != hipSuccess) return e;
+    if (tail > 0) {
+      GemmLaunch H = F;
+      H.tiles = 2 * tail;
+      H.half_base = nf - tail;
+      e = dispatch<true, true>(H, H.tiles, H.tiles, s);
+      if (e != hipSuccess) return e;
+    }
   }
   if (ne > 0) return dispatch<false>(E, ne, ne, s);
   return hipSuccess;

@@ -55,6 +55,7 @@ struct GemmLaunch {
   int nprob;
   int tiles;             // bf16 whole-tile kernels: tiles of the launch
   int g0;                // two-layout launch: workgroups of problem 0
+  int half_base;         // half-tile launch: first (256-row) tile it splits
 };
 
 struct CEArgs {

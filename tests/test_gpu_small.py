@@ -149,6 +149,21 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
 TILE_SHAPES = [(512, 256, 768), (768, 512, 256)]
 
 
+@pytest.mark.parametrize("act", ["none", "swiglu"])
+def test_column_fwd_half_tile_tail_round(act):
+    # 17 x 17 = 289 whole tiles on 256 CUs: the last 33 run as 128-row halves.
+    M, K = 17 * 256, 64
+    N = 17 * (128 if act == "swiglu" else 256)
+    dtype = syn.BF16
+    d = _inputs(dtype, M, N, K, 5, act)
+    Y, Pre = ops.column_fwd(dev(d["X"]), dev(d["A"]), act, A2=dev(d["A2"]) if act == "swiglu" else None)
+    torch.cuda.synchronize()
+    Yr, Prer = oracle.column_fwd(d["X"].f64, d["A"].f64, act, A2=d["A2"].f64 if act == "swiglu" else None)
+    assert_close("Y", host64(Y), Yr, TOL[dtype])
+    if act != "none":
+        assert_close("Pre", host64(Pre), Prer, TOL[dtype])
+
+
 @pytest.mark.parametrize("shape", TILE_SHAPES)
 def test_row_bwd_whole_tiles(shape):
     M, N, K = shape
