@@ -27,4 +27,5 @@ from .tp_oracle import (  # noqa: F401
     wgrad,
     vocab_ce_partials,
     lse_recombine,
+    vocab_ce_bwd,
 )

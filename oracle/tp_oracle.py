@@ -274,3 +274,31 @@ def lse_recombine(parts):
     lse = mstar + np.log(sstar)
     tgt = ts.sum(axis=0)
     return lse, tgt, lse - tgt
+
+
+def vocab_ce_bwd(H, W, target, v0, lse, gscale=None):
+    """Backward of the vocab-parallel cross entropy for one vocab shard.
+
+    [TP/SP] "Embedding and LM head: split by vocab": each rank owns the
+    logits z = H W_r^T of its vocab rows; with the per-token log-sum-exp
+    recombined over all shards (lse, as lse_recombine returns it), the
+    gradient of the per-token loss lse - z[target] w.r.t. the shard's logits
+    is softmax(z) - onehot(target), the onehot entry present only on the shard
+    that owns the target.  gscale [M] (default 1) is the upstream gradient of
+    each token's loss.  The shard's weight gradient dW_r = dz^T H completes
+    locally; dH_r = dz W_r is this shard's partial of dH (summed over shards).
+    Returns (dz [M, V_r], dH_r [M, K], dW_r [V_r, K]), float64.
+    """
+    H, W = _f64(H), _f64(W)
+    lse = _f64(lse)
+    target = np.asarray(target, dtype=np.int64)
+    g = np.ones(H.shape[0]) if gscale is None else _f64(gscale)
+    z = H @ W.T
+    dz = np.exp(z - lse[:, None])
+    vr = W.shape[0]
+    owned = (target >= v0) & (target < v0 + vr)
+    rows = np.nonzero(owned)[0]
+    dz[rows, target[rows] - v0] -= 1.0
+    dz *= g[:, None]
+    return dz, dz @ W, dz.T @ H
+

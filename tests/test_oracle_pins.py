@@ -338,3 +338,80 @@ def test_ce_large_logits_do_not_overflow():
     assert m[0] == 900.0 and np.isfinite(s).all()
     lse, _, _ = oracle.lse_recombine([(m, s, np.zeros(2))])
     assert lse[0] == pytest.approx(900.0 + math.log(1 + math.exp(-30.0) + math.exp(-1050.0)), rel=1e-15)
+
+
+# ---- vocab-parallel CE backward -------------------------------------------------------------
+
+def _full_loss(H, Ws, target, g):
+    """Sum_m g_m (lse_m - z_m[target_m]) over the full vocabulary, written out directly."""
+    z = np.concatenate([H @ W.T for W in Ws], axis=1)
+    out = 0.0
+    for m in range(H.shape[0]):
+        row = z[m]
+        mx = max(row)
+        lse = mx + math.log(sum(math.exp(v - mx) for v in row))
+        out += g[m] * (lse - row[target[m]])
+    return out
+
+
+def test_ce_bwd_hand_example():
+    # z = [0, ln 2]: softmax (1/3, 2/3); target 1 -> dz = (1/3, -1/3)
+    H = np.array([[1.0]])
+    W = np.array([[0.0], [math.log(2.0)]])
+    lse = np.array([math.log(3.0)])
+    dz, dH, dW = oracle.vocab_ce_bwd(H, W, [1], 0, lse)
+    assert np.allclose(dz, [[1 / 3, -1 / 3]], atol=1e-15)
+    assert np.allclose(dH, [[-math.log(2.0) / 3]], atol=1e-15)
+    assert np.allclose(dW, [[1 / 3], [-1 / 3]], atol=1e-15)
+
+
+def test_ce_bwd_finite_differences_over_shards():
+    rng = np.random.default_rng(7)
+    M, K, vr, R = 3, 4, 5, 3
+    H = rng.standard_normal((M, K))
+    Ws = [rng.standard_normal((vr, K)) * 0.7 for _ in range(R)]
+    target = np.array([2, 9, 14])          # owned by shards 0, 1, 2
+    g = np.array([0.5, 1.0, 2.0])
+    parts = [oracle.vocab_ce_partials(H, W, target, r * vr) for r, W in enumerate(Ws)]
+    lse, _, _ = oracle.lse_recombine(parts)
+    outs = [oracle.vocab_ce_bwd(H, W, target, r * vr, lse, g) for r, W in enumerate(Ws)]
+    dH = sum(o[1] for o in outs)
+    eps = 1e-6
+    num_dH = np.zeros_like(H)
+    for idx in np.ndindex(H.shape):
+        Hp, Hm = H.copy(), H.copy()
+        Hp[idx] += eps
+        Hm[idx] -= eps
+        num_dH[idx] = (_full_loss(Hp, Ws, target, g) - _full_loss(Hm, Ws, target, g)) / (2 * eps)
+    assert np.allclose(dH, num_dH, atol=1e-7)
+    for r in range(R):
+        num_dW = np.zeros_like(Ws[r])
+        for idx in np.ndindex(Ws[r].shape):
+            Wp = [W.copy() for W in Ws]
+            Wm = [W.copy() for W in Ws]
+            Wp[r][idx] += eps
+            Wm[r][idx] -= eps
+            num_dW[idx] = (_full_loss(H, Wp, target, g) - _full_loss(H, Wm, target, g)) / (2 * eps)
+        assert np.allclose(outs[r][2], num_dW, atol=1e-7)
+
+
+def test_ce_bwd_rows_sum_to_zero_and_loops():
+    rng = np.random.default_rng(8)
+    M, K, vr, R = 4, 3, 6, 2
+    H = rng.standard_normal((M, K))
+    Ws = [rng.standard_normal((vr, K)) for _ in range(R)]
+    target = np.array([0, 7, 11, -3])      # the last token's target is owned by no shard
+    parts = [oracle.vocab_ce_partials(H, W, target, r * vr) for r, W in enumerate(Ws)]
+    lse, _, _ = oracle.lse_recombine(parts)
+    outs = [oracle.vocab_ce_bwd(H, W, target, r * vr, lse) for r, W in enumerate(Ws)]
+    rowsum = sum(o[0].sum(axis=1) for o in outs)
+    # softmax sums to one; the onehot subtracts one where some shard owns the target
+    assert np.allclose(rowsum, [0.0, 0.0, 0.0, 1.0], atol=1e-12)
+    for r, (dz, dH, dW) in enumerate(outs):
+        for m in range(M):
+            for k in range(K):
+                assert abs(dH[m, k] - sum(dz[m, j] * Ws[r][j, k] for j in range(vr))) < 1e-12
+        for j in range(vr):
+            for k in range(K):
+                assert abs(dW[j, k] - sum(dz[m, j] * H[m, k] for m in range(M))) < 1e-12
+
