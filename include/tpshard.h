@@ -197,6 +197,32 @@ TP_API tp_status tp_vocab_ce_partials(int dtype, int64_t M, int64_t Vr, int64_t 
                                void* workspace, size_t ws_bytes, void* stream);
 TP_API size_t tp_vocab_ce_workspace_bytes(int64_t M, int64_t Vr);
 
+/*
+ * Backward of the vocab-parallel cross entropy for shard [v0, v0+Vr).
+ * [TP/SP] "Embedding and LM head: split by vocab": with the per-token
+ * log-sum-exp recombined over all shards, each rank differentiates its own
+ * logits locally; its weight gradient completes locally and its input
+ * gradient is a partial summed over the shards (like the column-parallel dX).
+ *
+ *   z  = H W^T, recomputed tile by tile (the forward stored no logits)
+ *   dz = gscale[m] * (exp(z[m,j] - lse[m]) - [j == target[m]-v0])
+ *   dH = dz W    [M, K]: this shard's partial (nullable: not computed)
+ *   dW = dz^T H  [Vr, K]: the shard's weight gradient (nullable)
+ * lse: fp32 [M], the recombined lse (M* + ln S* over all shards).
+ * gscale: fp32 [M], upstream gradient of each token's loss; NULL means 1.
+ * target: int32 [M]; a target outside [v0, v0+Vr) (negative included) adds
+ * no onehot term on this shard.  dz is stored as bf16 in the workspace
+ * (>= tp_vocab_ce_bwd_workspace_bytes(M, Vr)) between its two GEMMs; exp
+ * and the subtraction are fp32.  Outputs take the input dtype.  Only TP_BF16
+ * is supported (TP_FP32 returns TP_E_DTYPE).
+ */
+TP_API tp_status tp_vocab_ce_bwd(int dtype, int64_t M, int64_t Vr, int64_t K,
+                                 const void* H, int64_t ldh, const void* W, int64_t ldw,
+                                 const int32_t* target, int64_t v0, const float* lse, const float* gscale,
+                                 void* dH, int64_t lddh, void* dW, int64_t lddw,
+                                 void* workspace, size_t ws_bytes, void* stream);
+TP_API size_t tp_vocab_ce_bwd_workspace_bytes(int64_t M, int64_t Vr);
+
 #ifdef __cplusplus
 }
 #endif

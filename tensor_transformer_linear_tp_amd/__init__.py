@@ -23,7 +23,7 @@ __all__ = [
     "TP_FP32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU", "TP_ACT_SWIGLU", "TPError", "LIB_PATH",
     "tp_abi_version", "tp_status_str", "tp_column_fwd", "tp_row_fwd", "tp_sum_partials", "tp_row_bwd",
     "tp_row_bwd_workspace_bytes", "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_vocab_ce_partials",
-    "tp_vocab_ce_workspace_bytes", "EXPORTED_SYMBOLS",
+    "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -50,6 +50,9 @@ _SIGS = {
     "tp_vocab_ce_partials": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                     _sz, _vp]),
     "tp_vocab_ce_workspace_bytes": (_sz, [_i64, _i64]),
+    "tp_vocab_ce_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp,
+                               _i64, _vp, _sz, _vp]),
+    "tp_vocab_ce_bwd_workspace_bytes": (_sz, [_i64, _i64]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -165,3 +168,14 @@ def tp_vocab_ce_partials(dtype, M, Vr, K, H, ldh, W, ldw, target, v0, out_max, o
 
 def tp_vocab_ce_workspace_bytes(M, Vr) -> int:
     return _load().tp_vocab_ce_workspace_bytes(M, Vr)
+
+
+def tp_vocab_ce_bwd(dtype, M, Vr, K, H, ldh, W, ldw, target, v0, lse, gscale, dH, lddh, dW, lddw, workspace,
+                    ws_bytes, stream=None):
+    _check("tp_vocab_ce_bwd", _load().tp_vocab_ce_bwd(
+        dtype, M, Vr, K, _ptr(H), ldh, _ptr(W), ldw, _ptr(target), v0, _ptr(lse), _ptr(gscale), _ptr(dH), lddh,
+        _ptr(dW), lddw, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_vocab_ce_bwd_workspace_bytes(M, Vr) -> int:
+    return _load().tp_vocab_ce_bwd_workspace_bytes(M, Vr)

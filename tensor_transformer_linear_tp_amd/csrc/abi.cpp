@@ -389,4 +389,65 @@ tp_status tp_vocab_ce_partials(int dtype, int64_t M, int64_t Vr, int64_t K, cons
   return tps::launch_ce_partials(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
 }
 
+size_t tp_vocab_ce_bwd_workspace_bytes(int64_t M, int64_t Vr) {
+  if (bad_dim(M) || bad_dim(Vr)) return 0;
+  return align_ws((size_t)M * (size_t)round_up(Vr, 8) * 2);
+}
+
+tp_status tp_vocab_ce_bwd(int dtype, int64_t M, int64_t Vr, int64_t K, const void* H, int64_t ldh, const void* W,
+                          int64_t ldw, const int32_t* target, int64_t v0, const float* lse, const float* gscale,
+                          void* dH, int64_t lddh, void* dW, int64_t lddw, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  if (dtype != TP_BF16) return TP_E_DTYPE;
+  if (!H || !W || !target || !lse) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(Vr) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_grid(dtype, M, Vr));
+  TPS_TRY(check_grid(dtype, M, K));
+  TPS_TRY(check_grid(dtype, Vr, K));
+  TPS_TRY(check_mat(H, M, ldh, K, dtype));
+  TPS_TRY(check_mat(W, Vr, ldw, K, dtype));
+  if (dH) TPS_TRY(check_mat(dH, M, lddh, K, dtype));
+  if (dW) TPS_TRY(check_mat(dW, Vr, lddw, K, dtype));
+  const int64_t lddz = round_up(Vr, 8);
+  if (!bf16_extent_ok(M, lddz, Vr)) return TP_E_SHAPE;
+  if (!aligned16(target) || !aligned16(lse) || (gscale && !aligned16(gscale))) return TP_E_ALIGN;
+  if (!dH && !dW) return TP_OK;
+  if (!workspace || ws_bytes < tp_vocab_ce_bwd_workspace_bytes(M, Vr)) return TP_E_WORKSPACE;
+  if (!aligned16(workspace)) return TP_E_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* dz = workspace;
+  {   // dz = gscale * (softmax(z) - onehot), z = H W^T: NT with the CE-gradient epilogue
+    GemmLaunch L = {};
+    L.nprob = 1;
+    L.p[0] = make_problem(M, Vr, tps::L_NT, tps::E_CE_GRAD);
+    L.p[0].seg[0] = tps::Seg{H, W, ldh, ldw, K};
+    L.p[0].c = dz;
+    L.p[0].ldc = lddz;
+    L.p[0].lse = lse;
+    L.p[0].gscale = gscale;
+    L.p[0].target = target;
+    L.p[0].v0 = v0;
+    if (tps::launch_gemm_bf16(L, s) != hipSuccess) return TP_E_HIP;
+  }
+  if (dH) {   // dH = dz W: NN over K' = Vr
+    GemmLaunch L = {};
+    L.nprob = 1;
+    L.p[0] = make_problem(M, K, tps::L_NN, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{dz, W, lddz, ldw, Vr};
+    L.p[0].c = dH;
+    L.p[0].ldc = lddh;
+    if (tps::launch_gemm_bf16(L, s) != hipSuccess) return TP_E_HIP;
+  }
+  if (dW) {   // dW = dz^T H: TN over K' = M
+    GemmLaunch L = {};
+    L.nprob = 1;
+    L.p[0] = make_problem(Vr, K, tps::L_TN, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{dz, H, lddz, ldh, M};
+    L.p[0].c = dW;
+    L.p[0].ldc = lddw;
+    if (tps::launch_gemm_bf16(L, s) != hipSuccess) return TP_E_HIP;
+  }
+  return TP_OK;
+}
+
 }  // extern "C"

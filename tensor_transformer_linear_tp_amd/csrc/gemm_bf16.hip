@@ -673,6 +673,12 @@ __device__ __forceinline__ void epi8(const Problem& P, int64_t m, int64_t n, int
   uint16_t* c = static_cast<uint16_t*>(P.c) + m * P.ldc + n;
   if (P.epi == E_STORE) {
     store8_bf16(c, v, nv);
+  } else if (P.epi == E_CE_GRAD) {
+    const float l = P.lse[m], g = P.gscale ? P.gscale[m] : 1.0f;
+    const int64_t t = (int64_t)P.target[m] - P.v0 - n;   // target column relative to n
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = g * (__expf(v[e] - l) - (t == e ? 1.0f : 0.0f));
+    store8_bf16(c, v, nv);
   } else if (P.epi == E_GELU) {
     float y[8];
 #pragma unroll
@@ -759,6 +765,7 @@ __device__ __forceinline__ Problem pick_problem(const GemmLaunch& L, bool s) {
   TPS_PICK(seg[1].a); TPS_PICK(seg[1].b); TPS_PICK(seg[1].lda); TPS_PICK(seg[1].ldb); TPS_PICK(seg[1].K);
   TPS_PICK(nseg); TPS_PICK(layout); TPS_PICK(epi); TPS_PICK(b_up); TPS_PICK(ldb_up);
   TPS_PICK(bias); TPS_PICK(bias2); TPS_PICK(c); TPS_PICK(ldc); TPS_PICK(pre); TPS_PICK(ldpre);
+  TPS_PICK(lse); TPS_PICK(gscale); TPS_PICK(target); TPS_PICK(v0);
   TPS_PICK(tiles_m); TPS_PICK(tiles_n); TPS_PICK(tile_begin);
   TPS_PICK(edge_only); TPS_PICK(full_m); TPS_PICK(full_n);
 #undef TPS_PICK
@@ -1055,7 +1062,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // Whole tiles of this problem may take the fast kernel.
 bool fast_ok(const Problem& P) {
-  if (P.bias || P.bias2) return false;
+  if (P.bias || P.bias2 || P.epi == E_CE_GRAD) return false;
   if (!aligned16(P.c) || (P.ldc & 7)) return false;
   if (P.epi != E_STORE && (!aligned16(P.pre) || (P.ldpre & 7))) return false;
   if (P.epi == E_SWIGLU && (P.N & 7)) return false;
@@ -1069,16 +1076,21 @@ hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
   const dim3 g(grid), block(NTHREADS);
   const int layout = L.p[0].layout, epi = L.p[0].epi;
   const bool seg2 = L.p[0].nseg > 1 || (L.nprob > 1 && L.p[1].nseg > 1);
-#define TPS_LAUNCH(LY, EP, S2)                                                                    \
-  do {                                                                                            \
-    if (FAST && HALF && LY != L_TN && !S2)                                                        \
-      hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, (LY != L_TN && !S2) ? 2 : 4>), g, block, 0, s, L); \
-    else if (FAST) hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, 4>), g, block, 0, s, L);     \
-    else hipLaunchKernelGGL((gemm_bf16_edge_kernel<LY, EP, S2>), g, block, 0, s, L, total);      \
+#define TPS_LAUNCH(LY, EP, S2)                                                                      \
+  do {                                                                                              \
+    if constexpr (FAST && EP != E_CE_GRAD) {                                                        \
+      if constexpr (HALF && LY != L_TN && !S2)                                                      \
+        hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, 2>), g, block, 0, s, L);                   \
+      else                                                                                          \
+        hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, 4>), g, block, 0, s, L);                   \
+    } else if constexpr (!FAST) {                                                                   \
+      hipLaunchKernelGGL((gemm_bf16_edge_kernel<LY, EP, S2>), g, block, 0, s, L, total);            \
+    }                                                                                               \
   } while (0)
   if (layout == L_NN && epi == E_SWIGLU) TPS_LAUNCH(L_NN, E_SWIGLU, false);
   else if (layout == L_NN && epi == E_GELU) TPS_LAUNCH(L_NN, E_GELU, false);
   else if (layout == L_NN) TPS_LAUNCH(L_NN, E_STORE, false);
+  else if (layout == L_NT && epi == E_CE_GRAD) TPS_LAUNCH(L_NT, E_CE_GRAD, false);
   else if (layout == L_NT && seg2) TPS_LAUNCH(L_NT, E_STORE, true);
   else if (layout == L_NT) TPS_LAUNCH(L_NT, E_STORE, false);
   else TPS_LAUNCH(L_TN, E_STORE, false);

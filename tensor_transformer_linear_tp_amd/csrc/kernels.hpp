@@ -17,7 +17,8 @@ enum Layout : int { L_NN = 0, L_NT = 1, L_TN = 2 };
 //   E_STORE : C = acc (+ bias)
 //   E_GELU  : P = acc + bias; Pre = P; C = GeLU(P)
 //   E_SWIGLU: G = acc_gate + bias, U = acc_up + bias2; Pre = [G | U]; C = silu(G) * U
-enum EpiMode : int { E_STORE = 0, E_GELU = 1, E_SWIGLU = 2 };
+//   E_CE_GRAD: C = gscale[m] * (exp(acc - lse[m]) - [n == target[m] - v0])  (CE backward)
+enum EpiMode : int { E_STORE = 0, E_GELU = 1, E_SWIGLU = 2, E_CE_GRAD = 3 };
 
 // One K-segment: C += A_seg * B_seg over K elements.  A problem may chain
 // two segments that accumulate into the same tile (the SwiGLU dgrad sums the
@@ -42,6 +43,10 @@ struct Problem {
   int64_t ldc;
   void* pre;             // E_GELU / E_SWIGLU pre-activation output
   int64_t ldpre;
+  const float* lse;      // E_CE_GRAD: per-row log-sum-exp [M]
+  const float* gscale;   // E_CE_GRAD: per-row upstream gradient [M] or nullptr (1)
+  const int32_t* target; // E_CE_GRAD: per-row target id [M]
+  int64_t v0;            // E_CE_GRAD: first column's id
   // filled by the launcher
   int tiles_m, tiles_n, tile_begin;
   int edge_only;         // tiles enumerate only the ragged edge (right strip, then bottom strip)

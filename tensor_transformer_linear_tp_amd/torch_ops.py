@@ -12,7 +12,8 @@ import torch
 
 from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_column_bwd,
                tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
-               tp_sum_partials, tp_vocab_ce_partials, tp_vocab_ce_workspace_bytes)
+               tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
+               tp_vocab_ce_workspace_bytes)
 
 ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
 
@@ -154,5 +155,23 @@ def vocab_ce_partials(H, W, target, v0):
     return m, s, tg
 
 
+def vocab_ce_bwd(H, W, target, v0, lse, gscale=None, want_dh=True, want_dw=True):
+    """(dH partial, dW) of the CE loss for the vocab shard starting at v0, given the recombined lse."""
+    H, W = aligned(H), aligned(W)
+    M, K = H.shape
+    Vr = W.shape[0]
+    target = target.to(torch.int32).contiguous()
+    lse = lse.to(torch.float32).contiguous()
+    if gscale is not None:
+        gscale = gscale.to(torch.float32).contiguous()
+    dH = empty_padded(M, K, H.dtype, H.device) if want_dh else None
+    dW = empty_padded(Vr, K, H.dtype, H.device) if want_dw else None
+    ws_n = tp_vocab_ce_bwd_workspace_bytes(M, Vr)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=H.device)
+    tp_vocab_ce_bwd(TP_BF16, M, Vr, K, H, ld(H), W, ld(W), target, v0, lse, gscale, dH,
+                    ld(dH) if dH is not None else 0, dW, ld(dW) if dW is not None else 0, ws, ws_n)
+    return dH, dW
+
+
 __all__ = ["column_fwd", "row_fwd", "stack_partials", "sum_partials", "row_bwd", "column_bwd",
-           "vocab_ce_partials", "empty_padded", "aligned", "dtype_code", "TP_FP32", "TP_BF16"]
+           "vocab_ce_partials", "vocab_ce_bwd", "empty_padded", "aligned", "dtype_code", "TP_FP32", "TP_BF16"]

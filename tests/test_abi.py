@@ -119,6 +119,35 @@ def test_ce_validation(lib):
     assert _rc("tp_vocab_ce_partials", *a) == 3
 
 
+def test_ce_bwd_validation(lib):
+    ws = tp.tp_vocab_ce_bwd_workspace_bytes(8192, 18992)
+    assert ws == 8192 * 18992 * 2                        # bf16 dz, rows padded to 8 (already)
+    assert tp.tp_vocab_ce_bwd_workspace_bytes(3, 5) == 256    # 3 x 8 x 2 bytes, rounded to 256
+    base = [tp.TP_BF16, 8192, 18992, 4096, P, 4096, P, 4096, P, 0, P, None, P, 4096, P, 4096, P, ws, None]
+    a = list(base); a[0] = tp.TP_FP32
+    assert _rc("tp_vocab_ce_bwd", *a) == 4
+    a = list(base); a[10] = None                              # lse is required
+    assert _rc("tp_vocab_ce_bwd", *a) == 1
+    a = list(base); a[17] = ws - 2
+    assert _rc("tp_vocab_ce_bwd", *a) == 6
+    a = list(base); a[11] = P + 4                             # gscale misaligned
+    assert _rc("tp_vocab_ce_bwd", *a) == 3
+    a = list(base); a[13] = 4000                              # ld(dH) < K
+    assert _rc("tp_vocab_ce_bwd", *a) == 2
+    a = list(base); a[12], a[14], a[16] = None, None, None    # nothing requested: no work, no workspace
+    assert _rc("tp_vocab_ce_bwd", *a) == 0
+
+
+def test_bf16_operands_below_2gib(lib):
+    # X [2^17, 2^13] bf16 spans exactly 2 GiB: rejected before any HIP call.
+    K = 1 << 13
+    args = [tp.TP_BF16, tp.TP_ACT_NONE, 1 << 17, 256, K, P, K, P, 256, None, 0, None, None, P, 256, None, 0, None]
+    assert _rc("tp_column_fwd", *args) == 2
+    # the same through an ld that makes a small matrix span 2 GiB
+    args = [tp.TP_BF16, tp.TP_ACT_NONE, 2, 256, 64, P, 1 << 30, P, 256, None, 0, None, None, P, 256, None, 0, None]
+    assert _rc("tp_column_fwd", *args) == 2
+
+
 def test_binding_raises_typed_errors(lib):
     with pytest.raises(tp.TPError) as ei:
         tp.tp_row_fwd(tp.TP_BF16, 0, 8, 8, P, 8, P, 8, P, 8, stream=0)

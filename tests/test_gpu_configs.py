@@ -232,6 +232,32 @@ def test_c5_shard0_full_size_sampled():
     assert_close("loss", gloss, rloss, TOL_CE)
 
 
+def test_c5_ce_backward_full_size_sampled():
+    cfg = syn.C5
+    d = syn.vocab_inputs(cfg, shard=0)
+    target = d["target"].copy()
+    ms = sample_idx(cfg.M, 48, 13)            # token rows of dH
+    js = sample_idx(cfg.Vr, 48, 14)           # vocab rows of dW
+    target[ms[::2]] = (ms[::2] * 7919) % cfg.Vr
+    # lse near the shard's own log-sum-exp (ln 18992 + 1.28^2/2 ~ 10.7), so the softmax
+    # term and the onehot term are both of order one; g: per-token upstream gradient
+    lse = (10.7 + syn.normal(cfg.seed + 30, (cfg.M,), 0.3, syn.FP32).f32).astype(np.float32)
+    g = syn.normal(cfg.seed + 31, (cfg.M,), 1.0, syn.FP32).f32
+    dH, dW = ops.vocab_ce_bwd(dev(d["H"]), dev(d["W"]), torch.from_numpy(target).cuda(), d["v0"],
+                              torch.from_numpy(lse).cuda(), torch.from_numpy(g).cuda())
+    torch.cuda.synchronize()
+    H64, W64 = d["H"].f64, d["W"].f64
+    _, rdH, _ = oracle.vocab_ce_bwd(H64[ms], W64, target[ms], d["v0"], lse[ms], g[ms])
+    assert_close("dH", host64(dH)[ms], rdH, TOL[syn.BF16])
+    # dW rows j: dz[:, j] over all tokens, from the oracle restricted to vocab rows js
+    dz_cols = np.empty((cfg.M, len(js)))
+    for c, j in enumerate(js):
+        dzc, _, _ = oracle.vocab_ce_bwd(H64, W64[j:j + 1], target, d["v0"] + j, lse, g)
+        dz_cols[:, c] = dzc[:, 0]
+    rdW = dz_cols.T @ H64
+    assert_close("dW", host64(dW)[js], rdW, TOL[syn.BF16])
+
+
 def test_c5_eight_shards_recombined():
     cfg = syn.C5
     Mt = 64

@@ -234,6 +234,26 @@ def test_vocab_ce_small(M, Vr, K):
     assert np.all(host64(tg)[~owned] == 0.0)
 
 
+@pytest.mark.parametrize("M,Vr,K,use_g", [(1, 1, 8, False), (37, 300, 72, True), (300, 600, 136, False),
+                                           (260, 1000, 64, True), (512, 768, 256, True)])
+def test_vocab_ce_bwd_small(M, Vr, K, use_g):
+    rng = np.random.default_rng(3 * M + Vr)
+    H = syn.normal(80 + M, (M, K), 1.0, syn.BF16)
+    W = syn.normal(81 + Vr, (Vr, K), 0.3, syn.BF16)
+    v0 = 500
+    target = rng.integers(v0 - 50, v0 + Vr + 50, size=M).astype(np.int32)
+    target[: min(M, 3)] = [v0, v0 + Vr - 1, -5][: min(M, 3)]
+    lse, _, _ = oracle.lse_recombine([oracle.vocab_ce_partials(H.f64, W.f64, target, v0)])
+    lse32 = lse.astype(np.float32)
+    g32 = syn.normal(82 + M, (M,), 1.0, syn.FP32).f32 if use_g else None
+    dH, dW = ops.vocab_ce_bwd(dev(H), dev(W), torch.from_numpy(target).cuda(), v0, torch.from_numpy(lse32).cuda(),
+                              torch.from_numpy(g32).cuda() if use_g else None)
+    torch.cuda.synchronize()
+    _, rdH, rdW = oracle.vocab_ce_bwd(H.f64, W.f64, target, v0, lse32, g32)
+    assert_close("dH", host64(dH), rdH, TOL[syn.BF16])
+    assert_close("dW", host64(dW), rdW, TOL[syn.BF16])
+
+
 def test_deterministic_bitwise():
     d = _inputs(syn.BF16, 520, 300, 1030, 3, "swiglu")
     outs = []
