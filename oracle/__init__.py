@@ -28,4 +28,6 @@ from .tp_oracle import (  # noqa: F401
     vocab_ce_partials,
     lse_recombine,
     vocab_ce_bwd,
+    layer_norm,
+    sp_reduce_scatter_ln,
 )

@@ -302,3 +302,34 @@ def vocab_ce_bwd(H, W, target, v0, lse, gscale=None):
     dz *= g[:, None]
     return dz, dz @ W, dz.T @ H
 
+
+def layer_norm(h, gamma=None, beta=None, eps=1e-5):
+    """LayerNorm over the last axis: (h - mean) / sqrt(var + eps) * gamma + beta, var biased (1/N)."""
+    h = _f64(h)
+    mu = h.mean(axis=-1, keepdims=True)
+    var = ((h - mu) ** 2).mean(axis=-1, keepdims=True)
+    y = (h - mu) / np.sqrt(var + eps)
+    if gamma is not None:
+        y = y * _f64(gamma)
+    if beta is not None:
+        y = y + _f64(beta)
+    return y
+
+
+def sp_reduce_scatter_ln(parts, r0, Mr, bias=None, resid=None, gamma=None, beta=None, eps=1e-5):
+    """Sequence-parallel block boundary of one rank, on one device.
+
+    [TP/SP] "Sequence Parallel": the all-reduce after the row-parallel layer
+    becomes a reduce-scatter -- each rank keeps the sum for its own block of
+    tokens -- and the residual add and LayerNorm that follow run on that
+    block only; an all-gather rebuilds the full sequence before the next
+    column-parallel layer.  Rank rows [r0, r0 + Mr):
+      h = sum_i parts[i][r0:r0+Mr] (ascending i) + bias (once) + resid
+      y = LayerNorm(h) * gamma + beta
+    resid is the rank's own [Mr, N] block.  Returns (y, h), float64.
+    """
+    h = sum_partials([_f64(p)[r0:r0 + Mr] for p in parts], bias)
+    if resid is not None:
+        h = h + _f64(resid)
+    return layer_norm(h, gamma, beta, eps), h
+

@@ -415,3 +415,55 @@ def test_ce_bwd_rows_sum_to_zero_and_loops():
             for k in range(K):
                 assert abs(dW[j, k] - sum(dz[m, j] * H[m, k] for m in range(M))) < 1e-12
 
+
+# ---- sequence-parallel reduce-scatter + residual + LayerNorm -------------------------------
+
+def test_sp_reduce_scatter_fig2_halves():
+    # Fig. 2 as a reduce-scatter over token rows: each GPU keeps the sum of its own half.
+    g = _golden("v4_fig2_allreduce.json")
+    parts = [np.array(v, float).reshape(2, 1) for v in g["gpu_inputs"]]   # one column, two token rows
+    _, h0 = oracle.sp_reduce_scatter_ln(parts, 0, 1)
+    _, h1 = oracle.sp_reduce_scatter_ln(parts, 1, 1)
+    assert h0[0, 0] == g["reduce_scatter"]["gpu0_first_half"]
+    assert h1[0, 0] == g["reduce_scatter"]["gpu1_second_half"]
+
+
+def test_layer_norm_closed_forms():
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((5, 64)) * 3 + 2
+    y = oracle.layer_norm(h, eps=0.0)
+    assert np.allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    assert np.allclose((y ** 2).mean(axis=1), 1.0, atol=1e-12)
+    # hand example: [1, 3] -> mean 2, var 1 -> [-1, 1]; gamma/beta scale and shift per column
+    y2 = oracle.layer_norm(np.array([[1.0, 3.0]]), gamma=[2.0, 3.0], beta=[0.5, -1.0], eps=0.0)
+    assert np.allclose(y2, [[-1.5, 2.0]], atol=1e-15)
+    # eps enters under the square root: [0, 2] with eps = 3 -> var 1 -> +-1/2
+    assert np.allclose(oracle.layer_norm(np.array([[0.0, 2.0]]), eps=3.0), [[-0.5, 0.5]], atol=1e-15)
+
+
+def test_layer_norm_matches_torch_cpu_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal((7, 33))
+    gam, bet = rng.standard_normal(33), rng.standard_normal(33)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(h), (33,), torch.from_numpy(gam), torch.from_numpy(bet),
+                                         1e-5).numpy()
+    assert np.allclose(oracle.layer_norm(h, gam, bet, 1e-5), ref, atol=1e-12)
+
+
+def test_sp_ranks_concatenated_equal_allreduce_then_layernorm():
+    rng = np.random.default_rng(13)
+    t, M, N = 4, 12, 16
+    parts = [rng.standard_normal((M, N)) for _ in range(t)]
+    bias, resid = rng.standard_normal(N), rng.standard_normal((M, N))
+    gam, bet = rng.standard_normal(N), rng.standard_normal(N)
+    Mr = M // t
+    ys, hs = [], []
+    for r in range(t):
+        y, h = oracle.sp_reduce_scatter_ln(parts, r * Mr, Mr, bias, resid[r * Mr:(r + 1) * Mr], gam, bet)
+        ys.append(y)
+        hs.append(h)
+    full_h = sum(parts) + bias + resid
+    assert np.allclose(np.concatenate(hs), full_h, atol=1e-12)
+    assert np.allclose(np.concatenate(ys), oracle.layer_norm(full_h, gam, bet), atol=1e-12)
+
