@@ -223,6 +223,36 @@ TP_API tp_status tp_vocab_ce_bwd(int dtype, int64_t M, int64_t Vr, int64_t K,
                                  void* workspace, size_t ws_bytes, void* stream);
 TP_API size_t tp_vocab_ce_bwd_workspace_bytes(int64_t M, int64_t Vr);
 
+/*
+ * Sequence-parallel block boundary of one rank, on one device (not a
+ * collective).  [TP/SP] section "SP: shard the activations that TP leaves
+ * whole": the all-reduce after the row-parallel layer becomes a
+ * reduce-scatter, so each rank keeps the sum for its own block of tokens, and
+ * the residual add and LayerNorm that follow are per-token work done on that
+ * block only; [TPcomm] Fig. 2 (reduce-scatter half of the all-reduce).
+ * Rank rows [r0, r0 + Mr) of the t partials parts_i [M, N] (ld; parts_i =
+ * parts + i*part_stride elements):
+ *
+ *   h[m]   = sum_{i<t} parts_i[r0 + m] (ascending i) + bias + resid[m]
+ *   out[m] = (h[m] - mean) / sqrt(var + eps) * gamma + beta
+ *
+ * mean and var (biased, 1/N) are over the N columns of h[m]; m in [0, Mr).
+ * bias, gamma, beta: [N], nullable (absent = 0, 1, 0).  resid: the rank's
+ * [Mr, N] block (ldr), nullable.  hout: [Mr, N] (ldh), nullable -- the
+ * residual stream h rounded to the dtype; hout may be exactly resid (same
+ * pointer, ldh == ldr) to update the residual stream in place.  out: [Mr, N]
+ * (ldo).  h, mean, var and the normalisation are fp32 from unrounded h.
+ * Limits: 1 <= N <= 16384 and 0 <= r0, r0 + Mr <= M; eps >= 0 and finite;
+ * otherwise TP_E_SHAPE.  part_stride: a multiple of 8 (bf16) / 4 (fp32).
+ */
+TP_API tp_status tp_sp_reduce_scatter_ln(int dtype, int t, int64_t M, int64_t N,
+                                         const void* parts, int64_t ld, int64_t part_stride,
+                                         int64_t r0, int64_t Mr, const void* bias,
+                                         const void* resid, int64_t ldr,
+                                         const void* gamma, const void* beta, float eps,
+                                         void* out, int64_t ldo, void* hout, int64_t ldh,
+                                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -319,7 +319,7 @@ def layer_norm(h, gamma=None, beta=None, eps=1e-5):
 def sp_reduce_scatter_ln(parts, r0, Mr, bias=None, resid=None, gamma=None, beta=None, eps=1e-5):
     """Sequence-parallel block boundary of one rank, on one device.
 
-    [TP/SP] "Sequence Parallel": the all-reduce after the row-parallel layer
+    [TP/SP] "SP: shard the activations that TP leaves whole": the all-reduce after the row-parallel layer
     becomes a reduce-scatter -- each rank keeps the sum for its own block of
     tokens -- and the residual add and LayerNorm that follow run on that
     block only; an all-gather rebuilds the full sequence before the next

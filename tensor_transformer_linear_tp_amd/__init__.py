@@ -23,7 +23,8 @@ __all__ = [
     "TP_FP32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU", "TP_ACT_SWIGLU", "TPError", "LIB_PATH",
     "tp_abi_version", "tp_status_str", "tp_column_fwd", "tp_row_fwd", "tp_sum_partials", "tp_row_bwd",
     "tp_row_bwd_workspace_bytes", "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_vocab_ce_partials",
-    "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
+    "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "tp_sp_reduce_scatter_ln",
+    "EXPORTED_SYMBOLS",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -53,6 +54,8 @@ _SIGS = {
     "tp_vocab_ce_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp,
                                _i64, _vp, _sz, _vp]),
     "tp_vocab_ce_bwd_workspace_bytes": (_sz, [_i64, _i64]),
+    "tp_sp_reduce_scatter_ln": (_i32, [_i32, _i32, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
+                                       ctypes.c_float, _vp, _i64, _vp, _i64, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -179,3 +182,10 @@ def tp_vocab_ce_bwd(dtype, M, Vr, K, H, ldh, W, ldw, target, v0, lse, gscale, dH
 
 def tp_vocab_ce_bwd_workspace_bytes(M, Vr) -> int:
     return _load().tp_vocab_ce_bwd_workspace_bytes(M, Vr)
+
+
+def tp_sp_reduce_scatter_ln(dtype, t, M, N, parts, ld, part_stride, r0, Mr, bias, resid, ldr, gamma, beta, eps, out,
+                            ldo, hout, ldh, stream=None):
+    _check("tp_sp_reduce_scatter_ln", _load().tp_sp_reduce_scatter_ln(
+        dtype, t, M, N, _ptr(parts), ld, part_stride, r0, Mr, _ptr(bias), _ptr(resid), ldr, _ptr(gamma), _ptr(beta),
+        float(eps), _ptr(out), ldo, _ptr(hout), ldh, _stream(stream)))

@@ -177,6 +177,29 @@ tp_status tp_sum_partials(int dtype, int t, int64_t M, int64_t N, const void* pa
                                                                                                        : TP_E_HIP;
 }
 
+tp_status tp_sp_reduce_scatter_ln(int dtype, int t, int64_t M, int64_t N, const void* parts, int64_t ld,
+                                  int64_t part_stride, int64_t r0, int64_t Mr, const void* bias, const void* resid,
+                                  int64_t ldr, const void* gamma, const void* beta, float eps, void* out, int64_t ldo,
+                                  void* hout, int64_t ldh, void* stream) {
+  if (!valid_dtype(dtype)) return TP_E_DTYPE;
+  if (!parts || !out) return TP_E_NULL;
+  if (t < 1 || bad_dim(M) || bad_dim(N) || N > tps::kSpLnMaxN || part_stride < 0) return TP_E_SHAPE;
+  if (bad_dim(Mr) || r0 < 0 || r0 > M - Mr) return TP_E_SHAPE;
+  if (!(eps >= 0.f) || !(eps <= 3.4e38f)) return TP_E_SHAPE;   // rejects NaN and inf
+  TPS_TRY(check_mat(parts, M, ld, N, dtype));
+  if (part_stride % vec_elems(dtype) != 0) return TP_E_ALIGN;
+  TPS_TRY(check_mat(out, Mr, ldo, N, dtype));
+  if (resid) TPS_TRY(check_mat(resid, Mr, ldr, N, dtype));
+  if (hout) TPS_TRY(check_mat(hout, Mr, ldh, N, dtype));
+  if (hout && hout == resid && ldh != ldr) return TP_E_SHAPE;
+  TPS_TRY(check_vec(bias));
+  TPS_TRY(check_vec(gamma));
+  TPS_TRY(check_vec(beta));
+  tps::SpLnArgs a = {t, Mr, N, parts, ld, part_stride, r0, bias, resid, ldr, gamma, beta, eps, out, ldo, hout, ldh};
+  return tps::launch_sp_rs_ln(dtype == TP_BF16, a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK
+                                                                                                   : TP_E_HIP;
+}
+
 size_t tp_row_bwd_workspace_bytes(int dtype, int64_t M, int64_t N) {
   (void)dtype;
   if (bad_dim(M) || bad_dim(N)) return 0;

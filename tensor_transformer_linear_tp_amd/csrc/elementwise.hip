@@ -1,9 +1,11 @@
 // HBM-bound kernels of the shard path: the column-epilogue backward (dP from
 // dY and the saved pre-activation, fused with fp32 column partial sums for the
-// bias gradients), the ordered reduction of those partials, and the t-way sum
-// of shard partials.  Each thread moves 8 consecutive columns with 16-byte
+// bias gradients), the ordered reduction of those partials, the t-way sum of
+// shard partials, and its sequence-parallel form fused with the residual add
+// and LayerNorm.  Each thread moves 8 consecutive columns with 16-byte
 // accesses when the row segment is whole and aligned.
 #include <algorithm>
+#include <utility>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -37,7 +39,9 @@ __device__ __forceinline__ void store8<uint16_t>(uint16_t* p, int nv, const floa
     *reinterpret_cast<u32x4*>(p) =
         u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
   } else {
-    for (int e = 0; e < nv; ++e) p[e] = f2bf(v[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < nv) p[e] = f2bf(v[e]);
   }
 }
 
@@ -62,7 +66,9 @@ __device__ __forceinline__ void store8<float>(float* p, int nv, const float (&v)
     *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
   } else {
-    for (int e = 0; e < nv; ++e) p[e] = v[e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < nv) p[e] = v[e];
   }
 }
 
@@ -162,6 +168,54 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* colpa
   out[n] = from_f<T>(s);
 }
 
+// 8 columns at p: one 16-byte-aligned vector load when FULL, else the first
+// nv elements one by one (the rest 0).  Callers pass 16-byte-aligned p when
+// FULL (base pointers, leading dimensions and strides are validated so).
+template <bool FULL, typename T>
+__device__ __forceinline__ void ld8(const T* p, int nv, float (&v)[8]) {
+  if constexpr (FULL) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = x[e];
+        v[4 + e] = y[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < nv ? to_f<T>(p[e]) : 0.f;
+  }
+}
+
+// acc = sum_{i<t} p[i * stride] over 8 columns, fp32, in ascending i.  The
+// partials are loaded G at a time before any of them is added, so a thread
+// keeps G loads in flight; past the last partial the load repeats partial t-1
+// (a cache hit) and is not added.
+template <bool FULL, typename T, int G>
+__device__ __forceinline__ void sum_parts8(const T* p, int64_t stride, int t, int nv, float (&acc)[8]) {
+  for (int i0 = 0; i0 < t; i0 += G) {
+    float v[G][8];
+#pragma unroll
+    for (int j = 0; j < G; ++j) ld8<FULL>(p + min(i0 + j, t - 1) * stride, nv, v[j]);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (i0 + j == 0) acc[e] = v[j][e];
+        else if (i0 + j < t) acc[e] += v[j][e];
+      }
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void sum_partials_kernel(const SumArgs a) {
   const int64_t cpr = (a.N + 7) / 8;
@@ -172,20 +226,138 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const SumArgs a) {
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
     const int64_t m = idx / cpr, n = (idx - m * cpr) * 8;
     const int nv = (int)min<int64_t>(8, a.N - n);
-    float acc[8], v[8];
-    load8<T>(parts + m * a.ld + n, nv, acc);
-    for (int i = 1; i < a.t; ++i) {
-      load8<T>(parts + i * a.part_stride + m * a.ld + n, nv, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += v[e];
-    }
+    float acc[8];
+    if (nv == 8) sum_parts8<true, T, 8>(parts + m * a.ld + n, a.part_stride, a.t, nv, acc);
+    else sum_parts8<false, T, 8>(parts + m * a.ld + n, a.part_stride, a.t, nv, acc);
     if (bias)
       for (int e = 0; e < nv; ++e) acc[e] += to_f<T>(bias[n + e]);
     store8<T>(out + m * a.ldo + n, nv, acc);
   }
 }
 
+// Sum of v over the 256 threads of the workgroup, the same on every thread
+// (fixed reduction tree: the result does not depend on timing).
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();   // red may still be read from a previous call
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Calls f(std::integral_constant<int, c>) for c = 0 .. CH-1, so that register
+// arrays indexed by c keep compile-time indices.
+template <typename F, int... C>
+__device__ __forceinline__ void for_each_chunk(F&& f, std::integer_sequence<int, C...>) {
+  (f(std::integral_constant<int, C>{}), ...);
+}
+
+// One workgroup per row of the rank's block; each thread holds CH chunks of 8
+// columns in registers (N <= 2048 * CH), so the row is read once.
+template <typename T, int CH>
+__global__ __launch_bounds__(256) void sp_rs_ln_kernel(const SpLnArgs a) {
+  __shared__ float red[4];
+  constexpr auto chunks = std::make_integer_sequence<int, CH>{};
+  const int64_t m = blockIdx.x;
+  const int64_t row = a.r0 + m;
+  const int64_t cpr = (a.N + 7) / 8;
+  const T* parts = static_cast<const T*>(a.parts);
+  const T* bias = static_cast<const T*>(a.bias);
+  const T* resid = static_cast<const T*>(a.resid);
+  float h[CH][8];
+  float s = 0.f;
+  for_each_chunk([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    const int64_t chunk = threadIdx.x + 256 * c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[c][e] = 0.f;
+    if (chunk < cpr) {
+      const int64_t n = chunk * 8;
+      const int nv = (int)min<int64_t>(8, a.N - n);
+      auto body = [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        // bias and residual are loaded first and added after the partials, in
+        // this order; an absent one loads partial 0 instead (no branch around
+        // the load) and is not added
+        const T* p0 = parts + row * a.ld + n;
+        float bv[8], rv[8];
+        ld8<FULL>(bias ? bias + n : p0, nv, bv);
+        ld8<FULL>(resid ? resid + m * a.ldr + n : p0, nv, rv);
+        sum_parts8<FULL, T, 8>(p0, a.part_stride, a.t, nv, h[c]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (bias) h[c][e] += bv[e];
+          if (resid) h[c][e] += rv[e];
+          s += h[c][e];   // masked columns hold 0
+        }
+      };
+      if (nv == 8) body(std::true_type{});
+      else body(std::false_type{});
+    }
+  }, chunks);
+  const float mean = block_sum256(s, red) / (float)a.N;
+  float s2 = 0.f;
+  for_each_chunk([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    const int64_t chunk = threadIdx.x + 256 * c;
+    if (chunk < cpr) {
+      const int nv = (int)min<int64_t>(8, a.N - chunk * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = h[c][e] - mean;
+        s2 += e < nv ? d * d : 0.f;
+      }
+    }
+  }, chunks);
+  const float var = block_sum256(s2, red) / (float)a.N;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  const T* gamma = static_cast<const T*>(a.gamma);
+  const T* beta = static_cast<const T*>(a.beta);
+  T* out = static_cast<T*>(a.out);
+  T* hout = static_cast<T*>(a.hout);
+  for_each_chunk([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    const int64_t chunk = threadIdx.x + 256 * c;
+    if (chunk < cpr) {
+      const int64_t n = chunk * 8;
+      const int nv = (int)min<int64_t>(8, a.N - n);
+      if (hout) store8<T>(hout + m * a.ldh + n, nv, h[c]);
+      float g[8], b[8], y[8];   // absent gamma / beta: partial 0 is loaded instead, not used
+      const T* own = parts + row * a.ld + n;
+      if (nv == 8) {
+        ld8<true>(gamma ? gamma + n : own, 8, g);
+        ld8<true>(beta ? beta + n : own, 8, b);
+      } else {
+        ld8<false>(gamma ? gamma + n : own, nv, g);
+        ld8<false>(beta ? beta + n : own, nv, b);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (h[c][e] - mean) * rstd * (gamma ? g[e] : 1.f) + (beta ? b[e] : 0.f);
+      store8<T>(out + m * a.ldo + n, nv, y);
+    }
+  }, chunks);
+}
+
 }  // namespace
+
+template <typename T>
+static void launch_sp_rs_ln_t(const SpLnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.Mr), block(256);
+  if (a.N <= 2048) hipLaunchKernelGGL((sp_rs_ln_kernel<T, 1>), grid, block, 0, s, a);
+  else if (a.N <= 4096) hipLaunchKernelGGL((sp_rs_ln_kernel<T, 2>), grid, block, 0, s, a);
+  else if (a.N <= 8192) hipLaunchKernelGGL((sp_rs_ln_kernel<T, 4>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((sp_rs_ln_kernel<T, kSpLnMaxN / 2048>), grid, block, 0, s, a);
+}
+
+hipError_t launch_sp_rs_ln(int is_bf16, const SpLnArgs& a, hipStream_t s) {
+  if (a.N < 1 || a.N > kSpLnMaxN) return hipErrorInvalidValue;
+  if (a.Mr <= 0) return hipSuccess;
+  if (is_bf16) launch_sp_rs_ln_t<uint16_t>(a, s);
+  else launch_sp_rs_ln_t<float>(a, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_act_bwd(int is_bf16, const ActBwdArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.M + kColpartRows - 1) / kColpartRows), (unsigned)((a.N + 255) / 256));

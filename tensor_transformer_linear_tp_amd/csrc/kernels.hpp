@@ -103,6 +103,27 @@ struct SumArgs {
   int64_t ldo;
 };
 
+// Sequence-parallel block boundary: reduce-scatter of the t row partials over
+// rows [r0, r0 + Mr), + bias + residual, then LayerNorm.
+struct SpLnArgs {
+  int t;
+  int64_t Mr, N;
+  const void* parts;
+  int64_t ld, part_stride, r0;
+  const void* bias;
+  const void* resid;
+  int64_t ldr;
+  const void* gamma;
+  const void* beta;
+  float eps;
+  void* out;
+  int64_t ldo;
+  void* hout;
+  int64_t ldh;
+};
+
+constexpr int kSpLnMaxN = 16384;   // row width the LayerNorm kernel holds in registers
+
 constexpr int kColpartRows = 64;   // rows per column-partial block
 
 hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s);
@@ -113,5 +134,6 @@ hipError_t launch_act_bwd(int is_bf16, const ActBwdArgs& a, hipStream_t s);
 hipError_t launch_colsum_finalize(int is_bf16, const float* colpart, int64_t nrb, int64_t ldcp,
                                   int64_t N, int part, void* out, hipStream_t s);
 hipError_t launch_sum_partials(int is_bf16, const SumArgs& a, hipStream_t s);
+hipError_t launch_sp_rs_ln(int is_bf16, const SpLnArgs& a, hipStream_t s);
 
 }  // namespace tps

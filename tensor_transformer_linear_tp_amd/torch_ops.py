@@ -12,7 +12,7 @@ import torch
 
 from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_column_bwd,
                tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
-               tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
+               tp_sp_reduce_scatter_ln, tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
                tp_vocab_ce_workspace_bytes)
 
 ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
@@ -101,6 +101,28 @@ def sum_partials(buf, N, bias=None, out=None):
         out = empty_padded(M, N, buf.dtype, buf.device)
     tp_sum_partials(dtype_code(buf), t, M, N, buf, ldp, M * ldp, bias, out, ld(out))
     return out
+
+
+def sp_reduce_scatter_ln(buf, N, r0, Mr, bias=None, resid=None, gamma=None, beta=None, eps=1e-5, want_h=True,
+                         h_inplace=False):
+    """Rank rows [r0, r0+Mr) of sum_i buf[i] + bias + resid, then LayerNorm; returns (y, h).
+
+    ``buf`` is a [t, M, ld] tensor of partials; ``resid`` is the rank's [Mr, N] block.  With
+    ``h_inplace`` the residual stream h overwrites ``resid`` (which must then satisfy the layout rule).
+    """
+    t, M, ldp = buf.shape
+    bias, gamma, beta = aligned(bias), aligned(gamma), aligned(beta)
+    if not h_inplace:
+        resid = aligned(resid)
+    y = empty_padded(Mr, N, buf.dtype, buf.device)
+    if h_inplace:
+        h = resid
+    else:
+        h = empty_padded(Mr, N, buf.dtype, buf.device) if want_h else None
+    tp_sp_reduce_scatter_ln(dtype_code(buf), t, M, N, buf, ldp, M * ldp, r0, Mr, bias, resid,
+                            ld(resid) if resid is not None else 0, gamma, beta, eps, y, ld(y), h,
+                            ld(h) if h is not None else 0)
+    return y, h
 
 
 def row_bwd(dZ, Xi, Bi, want_dx=True, want_dw=True, want_db=False):

@@ -138,6 +138,39 @@ def test_ce_bwd_validation(lib):
     assert _rc("tp_vocab_ce_bwd", *a) == 0
 
 
+def test_sp_reduce_scatter_ln_validation(lib):
+    # t=8 partials [8192, 4096], rank 3 of 8 keeps rows [3072, 4096)
+    base = [tp.TP_BF16, 8, 8192, 4096, P, 4096, 8192 * 4096, 3072, 1024, P, P, 4096, P, P, 1e-5, P, 4096, P, 4096,
+            None]
+    a = list(base); a[0] = 7
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 4
+    a = list(base); a[15] = None                              # out is required
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 1
+    a = list(base); a[3] = 16385                              # wider than the register-held row
+    a[5] = a[16] = a[11] = a[18] = 16392
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
+    a = list(base); a[7] = 7169                               # r0 + Mr > M
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
+    a = list(base); a[7] = -1
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
+    a = list(base); a[8] = 0                                  # empty block
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
+    for eps in (-1e-5, float("nan"), float("inf")):
+        a = list(base); a[14] = eps
+        assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
+    a = list(base); a[6] = 8192 * 4096 + 4                    # part_stride not a multiple of 8
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 3
+    a = list(base); a[12] = P + 2                             # gamma misaligned
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 3
+    a = list(base); a[11] = 4000                              # ld(resid) < N
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
+    a = list(base); a[18] = 4104                              # hout == resid with another ld
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
+    a = list(base); a[2] = 1 << 19                            # partials span >= 2 GiB
+    a[8] = 1 << 16
+    assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
+
+
 def test_bf16_operands_below_2gib(lib):
     # X [2^17, 2^13] bf16 spans exactly 2 GiB: rejected before any HIP call.
     K = 1 << 13

@@ -211,6 +211,32 @@ def test_c4_four_way_partial_sum_sampled():
     assert_close("Z", rows(Z, ms), ref, BF)
 
 
+def test_c2_sequence_parallel_boundary_sampled():
+    # The 8 row partials of c2's down projection [8192, 4096], reduce-scattered
+    # over token blocks of 1024 rows, + bias + residual, then LayerNorm.
+    cfg = syn.C2
+    t, M, N = cfg.t, cfg.M, cfg.H
+    Mr = M // t
+    seeded = [syn.normal(2950 + i, (M, N), 1.0, syn.BF16) for i in range(t)]
+    bias = syn.normal(2960, (N,), 0.02, syn.BF16)
+    gamma = syn.normal(2961, (N,), 1.0, syn.BF16)
+    beta = syn.normal(2962, (N,), 0.1, syn.BF16)
+    buf, n = ops.stack_partials([dev(p) for p in seeded])
+    ms = sample_idx(Mr, 48, 13)
+    part_rows = {}
+    for rank in (0, 3, t - 1):
+        r0 = rank * Mr
+        resid = syn.normal(2970 + rank, (Mr, N), 1.0, syn.BF16)
+        y, h = ops.sp_reduce_scatter_ln(buf, n, r0, Mr, dev(bias), dev(resid), dev(gamma), dev(beta), eps=1e-5)
+        torch.cuda.synchronize()
+        for i, p in enumerate(seeded):
+            part_rows[i] = p.f64[r0 + ms]
+        ry, rh = oracle.sp_reduce_scatter_ln([part_rows[i] for i in range(t)], 0, len(ms), bias.f64,
+                                             resid.f64[ms], gamma.f64, beta.f64, 1e-5)
+        assert_close(f"h rank {rank}", rows(h, ms), rh, BF)
+        assert_close(f"y rank {rank}", rows(y, ms), ry, BF)
+
+
 # ---------------------------------------------------------------------------
 # c5: vocab-parallel LM head + CE partials.
 # ---------------------------------------------------------------------------

@@ -214,6 +214,93 @@ def test_sum_partials_with_bias_once(dtype, t):
     assert_close("Z in place", host64(Zin), oracle.sum_partials([p.f64 for p in seeded]), TOL[dtype])
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_sp_fig2_halves_on_gpu(dtype):
+    # Fig. 2 as a reduce-scatter over token rows: rank 0 keeps 1 + 3, rank 1 keeps 2 + 4.
+    g = _golden("v4_fig2_allreduce.json")
+    parts = [_t(np.array(v, np.float32).reshape(2, 1), dtype) for v in g["gpu_inputs"]]
+    buf, n = ops.stack_partials(parts)
+    _, h0 = ops.sp_reduce_scatter_ln(buf, n, 0, 1)
+    _, h1 = ops.sp_reduce_scatter_ln(buf, n, 1, 1)
+    torch.cuda.synchronize()
+    _exact(h0, [[g["reduce_scatter"]["gpu0_first_half"]]])
+    _exact(h1, [[g["reduce_scatter"]["gpu1_second_half"]]])
+
+
+# (t, M, N, r0, Mr): one column, ragged widths around the 8-wide vectors and the
+# 2048-column chunk steps, the widest row, and rank blocks at both ends.
+SP_CASES = [(1, 4, 1, 0, 4), (2, 6, 7, 2, 3), (3, 40, 70, 13, 27), (8, 64, 2048, 56, 8), (4, 33, 2049, 0, 11),
+            (8, 24, 4100, 8, 8), (2, 9, 8191, 4, 5), (3, 5, 16384, 1, 3), (8, 16, 12345, 15, 1)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("t,M,N,r0,Mr", SP_CASES)
+def test_sp_reduce_scatter_ln_small(dtype, t, M, N, r0, Mr):
+    seed = 7 * t + M + N
+    seeded = [syn.normal(seed + i, (M, N), 1.0, dtype) for i in range(t)]
+    bias = syn.normal(seed + 100, (N,), 0.5, dtype)
+    resid = syn.normal(seed + 101, (Mr, N), 2.0, dtype)
+    gamma = syn.normal(seed + 102, (N,), 1.0, dtype)
+    beta = syn.normal(seed + 103, (N,), 0.5, dtype)
+    buf, n = ops.stack_partials([dev(p) for p in seeded])
+    y, h = ops.sp_reduce_scatter_ln(buf, n, r0, Mr, dev(bias), dev(resid), dev(gamma), dev(beta), eps=1e-5)
+    y0, _ = ops.sp_reduce_scatter_ln(buf, n, r0, Mr, want_h=False)
+    torch.cuda.synchronize()
+    ry, rh = oracle.sp_reduce_scatter_ln([p.f64 for p in seeded], r0, Mr, bias.f64, resid.f64, gamma.f64, beta.f64,
+                                         1e-5)
+    assert_close("h", host64(h), rh, TOL[dtype])
+    assert_close("y", host64(y), ry, TOL[dtype])
+    ry0, _ = oracle.sp_reduce_scatter_ln([p.f64 for p in seeded], r0, Mr)
+    assert_close("y (no bias/resid/gamma/beta)", host64(y0), ry0, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_sp_flow_reduce_scatter_gather_column(dtype):
+    # The SP forward between two blocks: row partials -> each rank's block (+bias +resid,
+    # LayerNorm) -> all-gather (a concatenation on one device) -> next column-parallel GEMM.
+    t, M, N, Nc = 4, 96, 136, 40
+    Mr = M // t
+    seeded = [syn.normal(90 + i, (M, N), 1.0, dtype) for i in range(t)]
+    bias = syn.normal(95, (N,), 0.5, dtype)
+    resid = syn.normal(96, (M, N), 1.0, dtype)
+    gamma = syn.normal(97, (N,), 1.0, dtype)
+    beta = syn.normal(98, (N,), 0.5, dtype)
+    A = syn.normal(99, (N, Nc), 0.2, dtype)
+    buf, n = ops.stack_partials([dev(p) for p in seeded])
+    R = dev(resid)
+    ys = [ops.sp_reduce_scatter_ln(buf, n, r * Mr, Mr, dev(bias), R[r * Mr:(r + 1) * Mr], dev(gamma), dev(beta),
+                                   eps=1e-5)[0] for r in range(t)]
+    gathered = torch.cat(ys, dim=0)
+    Y, _ = ops.column_fwd(gathered, dev(A))
+    torch.cuda.synchronize()
+    full = oracle.sum_partials([p.f64 for p in seeded], bias=bias.f64) + resid.f64
+    ref_y = oracle.layer_norm(full, gamma.f64, beta.f64, 1e-5)
+    assert_close("gathered y", host64(gathered), ref_y, TOL[dtype])
+    assert_close("column after gather", host64(Y), oracle.column_fwd(ref_y, A.f64)[0], TOL[dtype])
+
+
+def test_sp_reduce_scatter_ln_in_place_and_constant_rows():
+    dtype = syn.BF16
+    t, M, N, r0, Mr = 4, 12, 1000, 4, 4
+    seeded = [syn.normal(60 + i, (M, N), 1.0, dtype) for i in range(t)]
+    resid = syn.normal(65, (Mr, N), 1.0, dtype)
+    buf, n = ops.stack_partials([dev(p) for p in seeded])
+    r = ops.aligned(dev(resid))
+    y, h = ops.sp_reduce_scatter_ln(buf, n, r0, Mr, resid=r, eps=1e-5, h_inplace=True)
+    torch.cuda.synchronize()
+    ry, rh = oracle.sp_reduce_scatter_ln([p.f64 for p in seeded], r0, Mr, resid=resid.f64, eps=1e-5)
+    assert h.data_ptr() == r.data_ptr()
+    assert_close("h in place", host64(r), rh, TOL[dtype])
+    assert_close("y", host64(y), ry, TOL[dtype])
+    # rows whose sum is constant: variance 0, so the output is beta exactly
+    const = [syn.from_values(np.full((2, 24), v, np.float32), dtype) for v in (1.5, -0.25)]
+    beta = syn.normal(66, (24,), 1.0, dtype)
+    buf, n = ops.stack_partials([dev(p) for p in const])
+    y, _ = ops.sp_reduce_scatter_ln(buf, n, 0, 2, beta=dev(beta), eps=1e-5)
+    torch.cuda.synchronize()
+    _exact(y, np.broadcast_to(beta.f64, (2, 24)))
+
+
 @pytest.mark.parametrize("M,Vr,K", [(1, 1, 8), (37, 300, 72), (300, 600, 136), (260, 18992, 64)])
 def test_vocab_ce_small(M, Vr, K):
     rng = np.random.default_rng(M + Vr)
