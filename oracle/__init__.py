@@ -30,4 +30,6 @@ from .tp_oracle import (  # noqa: F401
     vocab_ce_bwd,
     layer_norm,
     sp_reduce_scatter_ln,
+    vocab_embed_fwd,
+    vocab_embed_bwd,
 )

@@ -333,3 +333,37 @@ def sp_reduce_scatter_ln(parts, r0, Mr, bias=None, resid=None, gamma=None, beta=
         h = h + _f64(resid)
     return layer_norm(h, gamma, beta, eps), h
 
+
+def vocab_embed_fwd(ids, E_r, v0):
+    """Vocab-parallel embedding lookup of one rank.
+
+    [TP/SP] "Embedding and LM head: split by vocab": the table is split by
+    rows (vocab ids) into t blocks; rank r holds E_r = rows [v0, v0 + Vr).
+    A token whose id falls in the block gets that row; any other token
+    (another rank's id, or an id outside the table) gets a zero row, so the
+    all-reduce (sum over ranks) leaves every token exactly its own row.
+    ids: integer [M]; E_r: [Vr, K].  Returns [M, K] float64.
+    """
+    E = _f64(E_r)
+    ids = np.asarray(ids, dtype=np.int64)
+    out = np.zeros((ids.shape[0], E.shape[1]))
+    own = (ids >= v0) & (ids < v0 + E.shape[0])
+    out[own] = E[ids[own] - v0]
+    return out
+
+
+def vocab_embed_bwd(ids, dout, v0, Vr):
+    """Gradient of the rank's table block under the lookup above.
+
+    The lookup copies row id - v0 to token m, so the block's gradient row v
+    is the sum of dout[m] over the tokens m whose id is v0 + v (added in
+    ascending m); rows no token uses are zero.  Tokens the rank does not own
+    contribute nothing.  ids: integer [M]; dout: [M, K].  Returns [Vr, K].
+    """
+    d = _f64(dout)
+    ids = np.asarray(ids, dtype=np.int64)
+    dE = np.zeros((Vr, d.shape[1]))
+    for m in range(ids.shape[0]):
+        if v0 <= ids[m] < v0 + Vr:
+            dE[ids[m] - v0] += d[m]
+    return dE

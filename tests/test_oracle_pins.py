@@ -467,3 +467,61 @@ def test_sp_ranks_concatenated_equal_allreduce_then_layernorm():
     assert np.allclose(np.concatenate(hs), full_h, atol=1e-12)
     assert np.allclose(np.concatenate(ys), oracle.layer_norm(full_h, gam, bet), atol=1e-12)
 
+
+
+# ---------------------------------------------------------------------------
+# Vocab-parallel embedding ("Embedding and LM head: split by vocab").
+# ---------------------------------------------------------------------------
+
+def test_vocab_embed_hand_example():
+    # vocab 6, K = 2, t = 2 ranks of 3 rows; row v of the table is [10v, 10v + 1]
+    E = np.array([[10.0 * v, 10.0 * v + 1] for v in range(6)])
+    ids = [4, 0, 4, 7, -1, 2]                      # 7 and -1 are outside the table
+    r0 = oracle.vocab_embed_fwd(ids, E[0:3], 0)
+    r1 = oracle.vocab_embed_fwd(ids, E[3:6], 3)
+    assert np.array_equal(r0, [[0, 0], [0, 1], [0, 0], [0, 0], [0, 0], [20, 21]])
+    assert np.array_equal(r1, [[40, 41], [0, 0], [40, 41], [0, 0], [0, 0], [0, 0]])
+    assert np.array_equal(r0 + r1, [[40, 41], [0, 1], [40, 41], [0, 0], [0, 0], [20, 21]])
+    dout = np.array([[m, -m] for m in range(6)], float)
+    assert np.array_equal(oracle.vocab_embed_bwd(ids, dout, 0, 3), [[1, -1], [0, 0], [5, -5]])
+    assert np.array_equal(oracle.vocab_embed_bwd(ids, dout, 3, 3), [[0, 0], [2, -2], [0, 0]])
+
+
+def test_vocab_embed_shards_sum_to_full_lookup():
+    rng = np.random.default_rng(21)
+    V, K, t, M = 40, 6, 4, 50
+    E = rng.standard_normal((V, K))
+    ids = rng.integers(0, V, size=M)
+    Vr = V // t
+    total = sum(oracle.vocab_embed_fwd(ids, E[r * Vr:(r + 1) * Vr], r * Vr) for r in range(t))
+    assert np.array_equal(total, np.take(E, ids, axis=0))
+    # each token is owned by exactly one rank
+    owners = [np.any(oracle.vocab_embed_fwd(ids, np.ones((Vr, 1)), r * Vr) != 0, axis=1) for r in range(t)]
+    assert np.array_equal(np.sum(owners, axis=0), np.ones(M))
+
+
+def test_vocab_embed_bwd_is_the_adjoint_and_a_onehot_product():
+    rng = np.random.default_rng(22)
+    Vr, K, M, v0 = 9, 5, 60, 100
+    ids = rng.integers(v0 - 10, v0 + Vr + 10, size=M)
+    ids[:4] = [v0, v0 + Vr - 1, v0 + 3, v0 + 3]    # both block ends and a repeated id
+    Er = rng.standard_normal((Vr, K))
+    dout = rng.standard_normal((M, K))
+    dE = oracle.vocab_embed_bwd(ids, dout, v0, Vr)
+    # <lookup(E), dout> = <E, dE> for every E: dE is the gradient of that inner product
+    assert np.isclose(np.sum(oracle.vocab_embed_fwd(ids, Er, v0) * dout), np.sum(Er * dE), rtol=1e-12)
+    onehot = np.zeros((M, Vr))
+    own = (ids >= v0) & (ids < v0 + Vr)
+    onehot[np.nonzero(own)[0], ids[own] - v0] = 1.0
+    assert np.allclose(dE, onehot.T @ dout, atol=1e-12)
+
+
+def test_vocab_embed_bwd_shards_concatenate_to_full():
+    rng = np.random.default_rng(23)
+    V, K, t, M = 24, 3, 3, 80
+    ids = rng.integers(-3, V + 3, size=M)
+    dout = rng.standard_normal((M, K))
+    Vr = V // t
+    full = oracle.vocab_embed_bwd(ids, dout, 0, V)
+    parts = np.concatenate([oracle.vocab_embed_bwd(ids, dout, r * Vr, Vr) for r in range(t)])
+    assert np.array_equal(parts, full)
