@@ -38,8 +38,9 @@
  *            Outputs take the input dtype except the CE outputs (fp32).
  * Aliasing.  Outputs must not overlap inputs or each other, except where a
  *            call states otherwise.
- * Determinism. No atomics take part in any result: two identical calls give
- *            bitwise identical outputs.
+ * Determinism. No floating-point atomics: every sum runs in a fixed order,
+ *            so two identical calls give bitwise identical outputs (the only
+ *            atomics are integer counters, exact in any order).
  */
 #ifndef TPSHARD_H
 #define TPSHARD_H
@@ -252,6 +253,42 @@ TP_API tp_status tp_sp_reduce_scatter_ln(int dtype, int t, int64_t M, int64_t N,
                                          const void* gamma, const void* beta, float eps,
                                          void* out, int64_t ldo, void* hout, int64_t ldh,
                                          void* stream);
+
+/*
+ * Vocab-parallel embedding lookup of one rank.  [TP/SP] "Embedding and LM
+ * head: split by vocab": the embedding table is split by rows (token ids)
+ * into t blocks; the rank holding rows [v0, v0 + Vr) outputs, for each
+ * token, its row when the rank owns the id and a zero row otherwise, so the
+ * all-reduce (tp_sum_partials on one device) gives every token its own row.
+ *
+ *   out[m] = E[ids[m] - v0]   if v0 <= ids[m] < v0 + Vr,   else 0
+ *
+ * ids: int32 [M] (any value; ids of other ranks, negative ids and ids past
+ * the table give zero rows).  E: the rank's block [Vr, K] (lde).  out:
+ * [M, K] (ldo).  Rows are copied bit for bit (no arithmetic).
+ */
+TP_API tp_status tp_vocab_embed_fwd(int dtype, int64_t M, int64_t Vr, int64_t K,
+                                    const int32_t* ids, int64_t v0,
+                                    const void* E, int64_t lde, void* out, int64_t ldo,
+                                    void* stream);
+
+/*
+ * Backward of tp_vocab_embed_fwd: the gradient of the rank's table block.
+ * Same section: the lookup copies row ids[m] - v0 to token m, so
+ *
+ *   dE[v] = sum of dout[m] over the tokens m with ids[m] = v0 + v
+ *
+ * added in ascending m in fp32 and rounded once; rows no token uses are
+ * written as zeros (dE [Vr, K] is overwritten completely).  dout: [M, K]
+ * (lddo).  The tokens are grouped by row through a stable counting sort in
+ * the workspace (>= tp_vocab_embed_bwd_workspace_bytes(M, Vr) bytes), so the
+ * result does not depend on scheduling; no floating-point atomics.
+ */
+TP_API tp_status tp_vocab_embed_bwd(int dtype, int64_t M, int64_t Vr, int64_t K,
+                                    const int32_t* ids, int64_t v0,
+                                    const void* dout, int64_t lddo, void* dE, int64_t ldde,
+                                    void* workspace, size_t ws_bytes, void* stream);
+TP_API size_t tp_vocab_embed_bwd_workspace_bytes(int64_t M, int64_t Vr);
 
 #ifdef __cplusplus
 }

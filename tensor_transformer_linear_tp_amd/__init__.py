@@ -24,7 +24,7 @@ __all__ = [
     "tp_abi_version", "tp_status_str", "tp_column_fwd", "tp_row_fwd", "tp_sum_partials", "tp_row_bwd",
     "tp_row_bwd_workspace_bytes", "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_vocab_ce_partials",
     "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "tp_sp_reduce_scatter_ln",
-    "EXPORTED_SYMBOLS",
+    "tp_vocab_embed_fwd", "tp_vocab_embed_bwd", "tp_vocab_embed_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -56,6 +56,9 @@ _SIGS = {
     "tp_vocab_ce_bwd_workspace_bytes": (_sz, [_i64, _i64]),
     "tp_sp_reduce_scatter_ln": (_i32, [_i32, _i32, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
                                        ctypes.c_float, _vp, _i64, _vp, _i64, _vp]),
+    "tp_vocab_embed_fwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "tp_vocab_embed_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "tp_vocab_embed_bwd_workspace_bytes": (_sz, [_i64, _i64]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -189,3 +192,18 @@ def tp_sp_reduce_scatter_ln(dtype, t, M, N, parts, ld, part_stride, r0, Mr, bias
     _check("tp_sp_reduce_scatter_ln", _load().tp_sp_reduce_scatter_ln(
         dtype, t, M, N, _ptr(parts), ld, part_stride, r0, Mr, _ptr(bias), _ptr(resid), ldr, _ptr(gamma), _ptr(beta),
         float(eps), _ptr(out), ldo, _ptr(hout), ldh, _stream(stream)))
+
+
+def tp_vocab_embed_fwd(dtype, M, Vr, K, ids, v0, E, lde, out, ldo, stream=None):
+    _check("tp_vocab_embed_fwd", _load().tp_vocab_embed_fwd(dtype, M, Vr, K, _ptr(ids), v0, _ptr(E), lde, _ptr(out),
+                                                             ldo, _stream(stream)))
+
+
+def tp_vocab_embed_bwd(dtype, M, Vr, K, ids, v0, dout, lddo, dE, ldde, workspace, ws_bytes, stream=None):
+    _check("tp_vocab_embed_bwd", _load().tp_vocab_embed_bwd(dtype, M, Vr, K, _ptr(ids), v0, _ptr(dout), lddo,
+                                                             _ptr(dE), ldde, _ptr(workspace), ws_bytes,
+                                                             _stream(stream)))
+
+
+def tp_vocab_embed_bwd_workspace_bytes(M, Vr) -> int:
+    return _load().tp_vocab_embed_bwd_workspace_bytes(M, Vr)

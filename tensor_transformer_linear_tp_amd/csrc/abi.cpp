@@ -473,4 +473,53 @@ tp_status tp_vocab_ce_bwd(int dtype, int64_t M, int64_t Vr, int64_t K, const voi
   return TP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Vocab-parallel embedding.
+// ---------------------------------------------------------------------------
+
+tp_status tp_vocab_embed_fwd(int dtype, int64_t M, int64_t Vr, int64_t K, const int32_t* ids, int64_t v0,
+                             const void* E, int64_t lde, void* out, int64_t ldo, void* stream) {
+  if (!valid_dtype(dtype)) return TP_E_DTYPE;
+  if (!ids || !E || !out) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(Vr) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_mat(E, Vr, lde, K, dtype));
+  TPS_TRY(check_mat(out, M, ldo, K, dtype));
+  if (!aligned16(ids)) return TP_E_ALIGN;
+  const tps::EmbArgs a = {M, Vr, K, ids, v0, E, lde, out, ldo};
+  return tps::launch_emb_fwd(dtype == TP_BF16, a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK
+                                                                                                : TP_E_HIP;
+}
+
+size_t tp_vocab_embed_bwd_workspace_bytes(int64_t M, int64_t Vr) {
+  if (bad_dim(M) || bad_dim(Vr)) return 0;
+  // row counts [Vr], block totals, row starts [Vr + 1], token order [M]: int32 each
+  return align_ws((size_t)Vr * 4) + align_ws((size_t)tps::emb_bwd_count_blocks(Vr) * 4) +
+         align_ws((size_t)(Vr + 1) * 4) + align_ws((size_t)M * 4);
+}
+
+tp_status tp_vocab_embed_bwd(int dtype, int64_t M, int64_t Vr, int64_t K, const int32_t* ids, int64_t v0,
+                             const void* dout, int64_t lddo, void* dE, int64_t ldde, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return TP_E_DTYPE;
+  if (!ids || !dout || !dE) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(Vr) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_mat(dout, M, lddo, K, dtype));
+  TPS_TRY(check_mat(dE, Vr, ldde, K, dtype));
+  if (!aligned16(ids)) return TP_E_ALIGN;
+  if (!workspace || ws_bytes < tp_vocab_embed_bwd_workspace_bytes(M, Vr)) return TP_E_WORKSPACE;
+  if (!aligned16(workspace)) return TP_E_ALIGN;
+  char* w = static_cast<char*>(workspace);
+  const size_t cnt_bytes = align_ws((size_t)Vr * 4);
+  const size_t btot_bytes = align_ws((size_t)tps::emb_bwd_count_blocks(Vr) * 4);
+  const size_t start_bytes = align_ws((size_t)(Vr + 1) * 4);
+  int32_t* cnt = reinterpret_cast<int32_t*>(w);
+  int32_t* btot = reinterpret_cast<int32_t*>(w + cnt_bytes);
+  int32_t* start = reinterpret_cast<int32_t*>(w + cnt_bytes + btot_bytes);
+  int32_t* order = reinterpret_cast<int32_t*>(w + cnt_bytes + btot_bytes + start_bytes);
+  const tps::EmbArgs a = {M, Vr, K, ids, v0, dout, lddo, dE, ldde};
+  const hipError_t e =
+      tps::launch_emb_bwd(dtype == TP_BF16, a, cnt, btot, start, order, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TP_OK : TP_E_HIP;
+}
+
 }  // extern "C"

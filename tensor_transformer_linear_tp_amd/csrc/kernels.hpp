@@ -122,6 +122,18 @@ struct SpLnArgs {
   int64_t ldh;
 };
 
+// Vocab-parallel embedding: forward src = the rank's table block E [Vr, K]
+// (lds), dst = out [M, K] (ldd); backward src = dout [M, K], dst = dE [Vr, K].
+struct EmbArgs {
+  int64_t M, Vr, K;
+  const int32_t* ids;
+  int64_t v0;
+  const void* src;
+  int64_t lds;
+  void* dst;
+  int64_t ldd;
+};
+
 constexpr int kSpLnMaxN = 16384;   // row width the LayerNorm kernel holds in registers
 
 constexpr int kColpartRows = 64;   // rows per column-partial block
@@ -135,5 +147,11 @@ hipError_t launch_colsum_finalize(int is_bf16, const float* colpart, int64_t nrb
                                   int64_t N, int part, void* out, hipStream_t s);
 hipError_t launch_sum_partials(int is_bf16, const SumArgs& a, hipStream_t s);
 hipError_t launch_sp_rs_ln(int is_bf16, const SpLnArgs& a, hipStream_t s);
+hipError_t launch_emb_fwd(int is_bf16, const EmbArgs& a, hipStream_t s);
+int64_t emb_bwd_count_blocks(int64_t Vr);
+// cnt [Vr], btot [emb_bwd_count_blocks(Vr)], start [Vr + 1] and order [M]
+// int32 come from the caller's workspace.
+hipError_t launch_emb_bwd(int is_bf16, const EmbArgs& a, int32_t* cnt, int32_t* btot, int32_t* start,
+                          int32_t* order, hipStream_t s);
 
 }  // namespace tps

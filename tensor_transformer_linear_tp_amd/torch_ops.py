@@ -12,7 +12,8 @@ import torch
 
 from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_column_bwd,
                tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
-               tp_sp_reduce_scatter_ln, tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
+               tp_sp_reduce_scatter_ln, tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_embed_bwd,
+               tp_vocab_embed_bwd_workspace_bytes, tp_vocab_embed_fwd, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
                tp_vocab_ce_workspace_bytes)
 
 ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
@@ -197,3 +198,29 @@ def vocab_ce_bwd(H, W, target, v0, lse, gscale=None, want_dh=True, want_dw=True)
 
 __all__ = ["column_fwd", "row_fwd", "stack_partials", "sum_partials", "row_bwd", "column_bwd",
            "vocab_ce_partials", "vocab_ce_bwd", "empty_padded", "aligned", "dtype_code", "TP_FP32", "TP_BF16"]
+
+
+def _ids(ids: torch.Tensor) -> torch.Tensor:
+    if ids.dtype != torch.int32:
+        raise TypeError("token ids must be int32")
+    return ids if (ids.is_contiguous() and ids.data_ptr() % 16 == 0) else ids.clone()
+
+
+def vocab_embed_fwd(ids, E, v0):
+    """Rows of the rank's table block E [Vr, K] for owned ids, zero rows otherwise; returns [M, K]."""
+    ids, E = _ids(ids), aligned(E)
+    M, (Vr, K) = ids.shape[0], E.shape
+    out = empty_padded(M, K, E.dtype, E.device)
+    tp_vocab_embed_fwd(dtype_code(E), M, Vr, K, ids, v0, E, ld(E), out, ld(out))
+    return out
+
+
+def vocab_embed_bwd(ids, dout, v0, Vr):
+    """Gradient of the rank's table block [Vr, K] from dout [M, K]."""
+    ids, dout = _ids(ids), aligned(dout)
+    M, K = dout.shape
+    dE = empty_padded(Vr, K, dout.dtype, dout.device)
+    n = tp_vocab_embed_bwd_workspace_bytes(M, Vr)
+    ws = torch.empty(n, dtype=torch.uint8, device=dout.device)
+    tp_vocab_embed_bwd(dtype_code(dout), M, Vr, K, ids, v0, dout, ld(dout), dE, ld(dE), ws, n)
+    return dE

@@ -171,6 +171,36 @@ def test_sp_reduce_scatter_ln_validation(lib):
     assert _rc("tp_sp_reduce_scatter_ln", *a) == 2
 
 
+def test_vocab_embed_validation(lib):
+    ws = tp.tp_vocab_embed_bwd_workspace_bytes(8192, 18992)
+    assert ws == 76032 + 512 + 76032 + 32768                 # counts, 75 block totals, starts (Vr + 1), order
+    assert tp.tp_vocab_embed_bwd_workspace_bytes(0, 5) == 0
+    fwd = [tp.TP_BF16, 8192, 18992, 4096, P, 0, P, 4096, P, 4096, None]
+    a = list(fwd); a[0] = 9
+    assert _rc("tp_vocab_embed_fwd", *a) == 4
+    a = list(fwd); a[4] = None                                # ids required
+    assert _rc("tp_vocab_embed_fwd", *a) == 1
+    a = list(fwd); a[4] = P + 4                               # ids not 16-byte aligned
+    assert _rc("tp_vocab_embed_fwd", *a) == 3
+    a = list(fwd); a[7] = 4000                                # lde < K
+    assert _rc("tp_vocab_embed_fwd", *a) == 2
+    a = list(fwd); a[9] = 4100                                # ldo not a multiple of 8
+    assert _rc("tp_vocab_embed_fwd", *a) == 3
+    a = list(fwd); a[1] = 0
+    assert _rc("tp_vocab_embed_fwd", *a) == 2
+    bwd = [tp.TP_FP32, 8192, 18992, 4096, P, 0, P, 4096, P, 4096, P, ws, None]
+    a = list(bwd); a[11] = ws - 4
+    assert _rc("tp_vocab_embed_bwd", *a) == 6
+    a = list(bwd); a[10] = None
+    assert _rc("tp_vocab_embed_bwd", *a) == 6
+    a = list(bwd); a[10] = P + 8
+    assert _rc("tp_vocab_embed_bwd", *a) == 3
+    a = list(bwd); a[8] = None                                # dE required
+    assert _rc("tp_vocab_embed_bwd", *a) == 1
+    a = list(bwd); a[2] = 1 << 31                             # Vr out of range
+    assert _rc("tp_vocab_embed_bwd", *a) == 2
+
+
 def test_bf16_operands_below_2gib(lib):
     # X [2^17, 2^13] bf16 spans exactly 2 GiB: rejected before any HIP call.
     K = 1 << 13

@@ -284,6 +284,32 @@ def test_c5_ce_backward_full_size_sampled():
     assert_close("dW", host64(dW)[js], rdW, TOL[syn.BF16])
 
 
+def test_c5_vocab_embedding_shard_full_size():
+    # Embedding shard 0 of 8 of the 151936 x 4096 table (18992 rows), 8192 tokens with ids
+    # uniform over the full vocabulary: lookup compared in full, backward on the rows that
+    # received tokens plus sampled empty rows.
+    cfg = syn.C5
+    M, K, Vr, v0 = cfg.M, cfg.H, cfg.Vr, 0
+    ids = syn.targets(5950, M, cfg.vocab)
+    E = syn.normal(5951, (Vr, K), 0.02, syn.BF16)
+    dout = syn.normal(5952, (M, K), 1.0, syn.BF16)
+    idt = torch.from_numpy(ids).cuda()
+    out = ops.vocab_embed_fwd(idt, dev(E), v0)
+    dE = ops.vocab_embed_bwd(idt, dev(dout), v0, Vr)
+    torch.cuda.synchronize()
+    own = (ids >= v0) & (ids < v0 + Vr)
+    ms = sample_idx(M, 256, 17)
+    ms = np.unique(np.concatenate([ms, np.nonzero(own)[0][:64]]))
+    assert np.array_equal(rows(out, ms), oracle.vocab_embed_fwd(ids[ms], E.f64, v0))
+    used = np.unique(ids[own] - v0)
+    vs = np.unique(np.concatenate([used, sample_idx(Vr, 128, 18)]))
+    ref = oracle.vocab_embed_bwd(ids, dout.f64, v0, Vr)
+    assert_close("dE", rows(dE, vs), ref[vs], BF)
+    # rows no token uses are exactly zero
+    empty = np.setdiff1d(np.arange(Vr), used)
+    assert float(torch.count_nonzero(dE[torch.from_numpy(empty).cuda()]).item()) == 0.0
+
+
 def test_c5_eight_shards_recombined():
     cfg = syn.C5
     Mt = 64

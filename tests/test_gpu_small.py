@@ -341,6 +341,60 @@ def test_vocab_ce_bwd_small(M, Vr, K, use_g):
     assert_close("dW", host64(dW), rdW, TOL[syn.BF16])
 
 
+def _ids_dev(ids):
+    return torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+
+
+# (M, Vr, K, v0, kind): one row and one token, ragged widths, several 256-row blocks and
+# 256-token chunks, ids all owned / none owned / heavily repeated.
+EMB_CASES = [(1, 1, 8, 0, "uniform"), (5, 3, 7, 10, "uniform"), (300, 700, 136, 500, "uniform"),
+             (1000, 300, 13, 0, "repeated"), (777, 1030, 4100, 2000, "uniform"), (513, 257, 64, 50, "none"),
+             (2048, 600, 72, 0, "all")]
+
+
+def _emb_ids(M, Vr, v0, kind, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "none":
+        return rng.integers(v0 + Vr, v0 + Vr + 1000, size=M).astype(np.int32)
+    if kind == "all":
+        return rng.integers(v0, v0 + Vr, size=M).astype(np.int32)
+    ids = rng.integers(v0 - 2 * Vr, v0 + 3 * Vr, size=M).astype(np.int32)
+    if kind == "repeated":                                   # half the tokens on two rows
+        ids[rng.random(M) < 0.5] = v0 + min(Vr - 1, 5)
+        ids[::7] = v0
+    ids[: min(M, 3)] = [v0, v0 + Vr - 1, -1][: min(M, 3)]
+    return ids
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,Vr,K,v0,kind", EMB_CASES)
+def test_vocab_embed_fwd_bwd_small(dtype, M, Vr, K, v0, kind):
+    seed = M + 3 * Vr + K
+    ids = _emb_ids(M, Vr, v0, kind, seed)
+    E = syn.normal(seed + 1, (Vr, K), 1.0, dtype)
+    dout = syn.normal(seed + 2, (M, K), 1.0, dtype)
+    out = ops.vocab_embed_fwd(_ids_dev(ids), dev(E), v0)
+    dE = ops.vocab_embed_bwd(_ids_dev(ids), dev(dout), v0, Vr)
+    dE2 = ops.vocab_embed_bwd(_ids_dev(ids), dev(dout), v0, Vr)
+    torch.cuda.synchronize()
+    _exact(out, oracle.vocab_embed_fwd(ids, E.f64, v0))          # rows copied bit for bit
+    assert_close("dE", host64(dE), oracle.vocab_embed_bwd(ids, dout.f64, v0, Vr), TOL[dtype])
+    assert torch.equal(dE.cpu(), dE2.cpu())                        # fixed summation order
+
+
+def test_vocab_embed_shards_sum_to_full_lookup_on_gpu():
+    # t = 4 ranks' lookups summed (the all-reduce on one device) give every token its own row.
+    t, Vr, K, M = 4, 250, 72, 600
+    E = syn.normal(77, (t * Vr, K), 1.0, syn.BF16)
+    ids = np.random.default_rng(78).integers(0, t * Vr, size=M).astype(np.int32)
+    Ed = dev(E)
+    parts = [ops.vocab_embed_fwd(_ids_dev(ids), Ed[r * Vr:(r + 1) * Vr], r * Vr) for r in range(t)]
+    buf, n = ops.stack_partials(parts)
+    Z = ops.sum_partials(buf, n)
+    torch.cuda.synchronize()
+    _exact(Z, np.take(E.f64, ids, axis=0))
+
+
 def test_deterministic_bitwise():
     d = _inputs(syn.BF16, 520, 300, 1030, 3, "swiglu")
     outs = []
