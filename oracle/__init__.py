@@ -32,4 +32,6 @@ from .tp_oracle import (  # noqa: F401
     sp_reduce_scatter_ln,
     vocab_embed_fwd,
     vocab_embed_bwd,
+    attention_fwd,
+    attention_bwd,
 )

@@ -367,3 +367,75 @@ def vocab_embed_bwd(ids, dout, v0, Vr):
         if v0 <= ids[m] < v0 + Vr:
             dE[ids[m] - v0] += d[m]
     return dE
+
+
+def _attn_heads(Q, K, V, n_q, n_kv):
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    d = Q.shape[1] // n_q
+    if Q.shape[1] != n_q * d or K.shape[1] != n_kv * d or V.shape[1] != n_kv * d or n_q % n_kv != 0:
+        raise ValueError("head layout does not match")
+    return Q, K, V, d, n_q // n_kv
+
+
+def _attn_scores(Qh, Kg, causal, scale):
+    s = (Qh @ Kg.T) * scale
+    if causal:
+        S = s.shape[0]
+        s = np.where(np.arange(S)[None, :] > np.arange(S)[:, None], -np.inf, s)
+    return s
+
+
+def attention_fwd(Q, K, V, n_q, n_kv, causal=True, scale=None):
+    """Attention core of one rank's heads, between the QKV and W_O projections.
+
+    [TP/SP] "Attention: split by head": every head is computed on its own, so
+    the rank runs scaled dot-product attention for its n_q query heads; with
+    GQA (32 query / 8 KV heads at t = 8: 4 query heads and 1 KV head per rank)
+    query head h reads KV head h // (n_q / n_kv).  Per head:
+      s = Q_h K_g^T * scale (scale = 1/sqrt(d)), keys after the query masked
+      when causal, P = softmax(s) over keys, O_h = P V_g, lse = log sum exp s.
+    Q [S, n_q*d], K and V [S, n_kv*d] (head h in columns [h*d, (h+1)*d)).
+    Returns O [S, n_q*d] and lse [n_q, S], float64.
+    """
+    Q, K, V, d, group = _attn_heads(Q, K, V, n_q, n_kv)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    S = Q.shape[0]
+    O = np.zeros((S, n_q * d))
+    lse = np.zeros((n_q, S))
+    for h in range(n_q):
+        g = h // group
+        s = _attn_scores(Q[:, h * d:(h + 1) * d], K[:, g * d:(g + 1) * d], causal, scale)
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - mx)
+        tot = e.sum(axis=1, keepdims=True)
+        O[:, h * d:(h + 1) * d] = (e / tot) @ V[:, g * d:(g + 1) * d]
+        lse[h] = (mx + np.log(tot))[:, 0]
+    return O, lse
+
+
+def attention_bwd(Q, K, V, dO, n_q, n_kv, causal=True, scale=None):
+    """Gradients of the attention core above (the pages print no backward).
+
+    Textbook softmax-attention gradients per head, with P recomputed from s:
+      dV_g += P^T dO_h,  dP = dO_h V_g^T,
+      dS = P * (dP - rowsum(P * dP)),
+      dQ_h = dS K_g * scale,  dK_g += dS^T Q_h * scale.
+    A KV head's gradient sums over the query heads that read it (ascending h).
+    Returns dQ [S, n_q*d], dK, dV [S, n_kv*d], float64.
+    """
+    Q, K, V, d, group = _attn_heads(Q, K, V, n_q, n_kv)
+    dO = _f64(dO)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for h in range(n_q):
+        g = h // group
+        qs, ks = slice(h * d, (h + 1) * d), slice(g * d, (g + 1) * d)
+        s = _attn_scores(Q[:, qs], K[:, ks], causal, scale)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        P = e / e.sum(axis=1, keepdims=True)
+        dV[:, ks] += P.T @ dO[:, qs]
+        dP = dO[:, qs] @ V[:, ks].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dQ[:, qs] = dS @ K[:, ks] * scale
+        dK[:, ks] += dS.T @ Q[:, qs] * scale
+    return dQ, dK, dV

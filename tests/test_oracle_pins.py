@@ -525,3 +525,120 @@ def test_vocab_embed_bwd_shards_concatenate_to_full():
     full = oracle.vocab_embed_bwd(ids, dout, 0, V)
     parts = np.concatenate([oracle.vocab_embed_bwd(ids, dout, r * Vr, Vr) for r in range(t)])
     assert np.array_equal(parts, full)
+
+
+# ---------------------------------------------------------------------------
+# Attention core ("Attention: split by head"), GQA.
+# ---------------------------------------------------------------------------
+
+def _attn_loops(Q, K, V, n_q, n_kv, causal, scale):
+    """Pure-Python triple loops: softmax attention written element by element."""
+    S, d = len(Q), len(Q[0]) // n_q
+    group = n_q // n_kv
+    O = [[0.0] * (n_q * d) for _ in range(S)]
+    for h in range(n_q):
+        g = h // group
+        for i in range(S):
+            keys = range(i + 1) if causal else range(S)
+            sc = [sum(Q[i][h * d + c] * K[j][g * d + c] for c in range(d)) * scale for j in keys]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            z = sum(w)
+            for c in range(d):
+                O[i][h * d + c] = sum(w[t] * V[j][g * d + c] for t, j in enumerate(keys)) / z
+    return O
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_matches_loops(causal):
+    rng = np.random.default_rng(31)
+    S, d, n_q, n_kv = 5, 3, 4, 2
+    Q = rng.standard_normal((S, n_q * d))
+    K = rng.standard_normal((S, n_kv * d))
+    V = rng.standard_normal((S, n_kv * d))
+    O, lse = oracle.attention_fwd(Q, K, V, n_q, n_kv, causal=causal, scale=0.7)
+    ref = _attn_loops(Q.tolist(), K.tolist(), V.tolist(), n_q, n_kv, causal, 0.7)
+    assert np.allclose(O, ref, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(32)
+    S, d = 6, 4
+    V = rng.standard_normal((S, d))
+    K = rng.standard_normal((S, d))
+    Z = np.zeros((S, d))
+    # zero queries: uniform weights -> causal rows are prefix means, lse = log(i + 1)
+    O, lse = oracle.attention_fwd(Z, K, V, 1, 1, causal=True)
+    assert np.allclose(O, np.cumsum(V, axis=0) / np.arange(1, S + 1)[:, None], atol=1e-12)
+    assert np.allclose(lse[0], np.log(np.arange(1, S + 1)), atol=1e-12)
+    O, lse = oracle.attention_fwd(Z, K, V, 1, 1, causal=False)
+    assert np.allclose(O, np.broadcast_to(V.mean(axis=0), (S, d)), atol=1e-12)
+    # first row under the causal mask sees only key 0: O = V[0], lse = q.k * scale
+    Q = rng.standard_normal((S, d))
+    O, lse = oracle.attention_fwd(Q, K, V, 1, 1, causal=True)
+    assert np.allclose(O[0], V[0], atol=1e-12)
+    assert np.isclose(lse[0, 0], Q[0] @ K[0] / 2.0)          # default scale 1/sqrt(4)
+
+
+def test_attention_matches_torch_sdpa_fp64():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    rng = np.random.default_rng(33)
+    S, d, n_q, n_kv = 9, 8, 4, 1
+    Q = rng.standard_normal((S, n_q * d))
+    K = rng.standard_normal((S, n_kv * d))
+    V = rng.standard_normal((S, n_kv * d))
+    dO = rng.standard_normal((S, n_q * d))
+    for causal in (True, False):
+        q = torch.tensor(Q.reshape(S, n_q, d).transpose(1, 0, 2), requires_grad=True)
+        k = torch.tensor(K.reshape(S, n_kv, d).transpose(1, 0, 2), requires_grad=True)
+        v = torch.tensor(V.reshape(S, n_kv, d).transpose(1, 0, 2), requires_grad=True)
+        kr = k.repeat_interleave(n_q // n_kv, dim=0)
+        vr = v.repeat_interleave(n_q // n_kv, dim=0)
+        o = F.scaled_dot_product_attention(q, kr, vr, is_causal=causal)
+        o.backward(torch.tensor(dO.reshape(S, n_q, d).transpose(1, 0, 2)))
+        O, _ = oracle.attention_fwd(Q, K, V, n_q, n_kv, causal=causal)
+        assert np.allclose(O, o.detach().numpy().transpose(1, 0, 2).reshape(S, n_q * d), atol=1e-12)
+        dQ, dK, dV = oracle.attention_bwd(Q, K, V, dO, n_q, n_kv, causal=causal)
+        assert np.allclose(dQ, q.grad.numpy().transpose(1, 0, 2).reshape(S, -1), atol=1e-12)
+        assert np.allclose(dK, k.grad.numpy().transpose(1, 0, 2).reshape(S, -1), atol=1e-12)
+        assert np.allclose(dV, v.grad.numpy().transpose(1, 0, 2).reshape(S, -1), atol=1e-12)
+
+
+def test_attention_bwd_finite_differences():
+    rng = np.random.default_rng(34)
+    S, d, n_q, n_kv = 4, 3, 2, 1
+    Q = rng.standard_normal((S, n_q * d))
+    K = rng.standard_normal((S, n_kv * d))
+    V = rng.standard_normal((S, n_kv * d))
+    dO = rng.standard_normal((S, n_q * d))
+    grads = oracle.attention_bwd(Q, K, V, dO, n_q, n_kv, causal=True)
+
+    def loss(q, k, v):
+        return float(np.sum(oracle.attention_fwd(q, k, v, n_q, n_kv, causal=True)[0] * dO))
+
+    eps = 1e-6
+    for which, X in enumerate((Q, K, V)):
+        for idx in [(0, 0), (S - 1, X.shape[1] - 1), (2, 1)]:
+            args = [Q.copy(), K.copy(), V.copy()]
+            args[which][idx] += eps
+            up = loss(*args)
+            args[which][idx] -= 2 * eps
+            dn = loss(*args)
+            assert np.isclose(grads[which][idx], (up - dn) / (2 * eps), rtol=1e-6, atol=1e-8)
+
+
+def test_attention_gqa_equals_replicated_kv():
+    rng = np.random.default_rng(35)
+    S, d, n_q = 7, 4, 4
+    Q = rng.standard_normal((S, n_q * d))
+    K = rng.standard_normal((S, d))
+    V = rng.standard_normal((S, d))
+    dO = rng.standard_normal((S, n_q * d))
+    O1, l1 = oracle.attention_fwd(Q, K, V, n_q, 1)
+    O4, l4 = oracle.attention_fwd(Q, np.tile(K, 4), np.tile(V, 4), n_q, n_q)
+    assert np.allclose(O1, O4, atol=1e-12) and np.allclose(l1, l4, atol=1e-12)
+    _, dK1, dV1 = oracle.attention_bwd(Q, K, V, dO, n_q, 1)
+    _, dK4, dV4 = oracle.attention_bwd(Q, np.tile(K, 4), np.tile(V, 4), dO, n_q, n_q)
+    assert np.allclose(dK1, dK4.reshape(S, 4, d).sum(axis=1), atol=1e-12)
+    assert np.allclose(dV1, dV4.reshape(S, 4, d).sum(axis=1), atol=1e-12)
