@@ -290,6 +290,34 @@ TP_API tp_status tp_vocab_embed_bwd(int dtype, int64_t M, int64_t Vr, int64_t K,
                                     void* workspace, size_t ws_bytes, void* stream);
 TP_API size_t tp_vocab_embed_bwd_workspace_bytes(int64_t M, int64_t Vr);
 
+/*
+ * Attention core of one rank's heads, between the column-parallel QKV
+ * projection and the row-parallel W_O.  [TP/SP] "Attention: split by head":
+ * each head is computed on its own, so the rank attends with its n_q query
+ * heads locally, without communication; with GQA (32 query / 8 KV heads at
+ * t = 8: 4 query heads and 1 KV head per rank) query head h reads KV head
+ * h / (n_q / n_kv).  Per head, over the keys of its sequence:
+ *
+ *   O_h = softmax(Q_h K_g^T * scale  [+ causal mask: key > query -> -inf]) V_g
+ *   lse[b][h][i] = log sum_j exp(s_ij)       (natural log, fp32, masked keys excluded)
+ *
+ * B sequences of S tokens are stacked by rows (sequence b = rows
+ * [b S, b S + S)).  Q [B S, n_q * 128] (ldq), K and V [B S, n_kv * 128]
+ * (ldk, ldv); head h in columns [128 h, 128 h + 128).  The packed QKV output
+ * of tp_column_fwd is passed as Q = qkv, K = qkv + 128 n_q, V = qkv +
+ * 128 (n_q + n_kv), all with ld = 128 (n_q + 2 n_kv).  O [B S, n_q * 128]
+ * (ldo), the W_O input; lse fp32 [B][n_q][S] (kept for the backward).
+ * head_dim must be 128; n_q / n_kv must divide 4 or be a multiple of 4;
+ * scale > 0 (1/sqrt(128) for the usual attention); causal is 0 or 1.
+ * Scores, softmax and accumulation are fp32; the probabilities enter the
+ * second product as bf16.  Only TP_BF16.
+ */
+TP_API tp_status tp_attention_fwd(int dtype, int64_t B, int64_t S, int n_q, int n_kv, int head_dim,
+                                  int causal, float scale,
+                                  const void* Q, int64_t ldq, const void* K, int64_t ldk,
+                                  const void* V, int64_t ldv, void* O, int64_t ldo, float* lse,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -522,4 +522,55 @@ tp_status tp_vocab_embed_bwd(int dtype, int64_t M, int64_t Vr, int64_t K, const 
   return e == hipSuccess ? TP_OK : TP_E_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Attention core.
+// ---------------------------------------------------------------------------
+
+namespace {
+// Head layout shared by the attention entry points; fills the common fields.
+tp_status attn_check(int dtype, int64_t B, int64_t S, int n_q, int n_kv, int head_dim, int causal, float scale,
+                     const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv,
+                     tps::AttnArgs& a) {
+  if (dtype != TP_BF16) return TP_E_DTYPE;
+  if (!Q || !K || !V) return TP_E_NULL;
+  if (head_dim != 128 || bad_dim(B) || B > 65535 || bad_dim(S) || bad_dim(B * S) || B * S > kMaxDim) return TP_E_SHAPE;
+  if (n_q < 1 || n_kv < 1 || n_q > 65535 || n_q % n_kv != 0) return TP_E_SHAPE;
+  const int group = n_q / n_kv;
+  if (!(group % 4 == 0 || 4 % group == 0)) return TP_E_SHAPE;
+  if (causal != 0 && causal != 1) return TP_E_SHAPE;
+  if (!(scale > 0.f) || !(scale <= 3.4e38f)) return TP_E_SHAPE;
+  TPS_TRY(check_mat(Q, B * S, ldq, (int64_t)n_q * head_dim, dtype));
+  TPS_TRY(check_mat(K, B * S, ldk, (int64_t)n_kv * head_dim, dtype));
+  TPS_TRY(check_mat(V, B * S, ldv, (int64_t)n_kv * head_dim, dtype));
+  a = tps::AttnArgs{};
+  a.B = B;
+  a.S = S;
+  a.n_q = n_q;
+  a.n_kv = n_kv;
+  a.causal = causal;
+  a.scale = scale;
+  a.q = Q;
+  a.ldq = ldq;
+  a.k = K;
+  a.ldk = ldk;
+  a.v = V;
+  a.ldv = ldv;
+  return TP_OK;
+}
+}  // namespace
+
+tp_status tp_attention_fwd(int dtype, int64_t B, int64_t S, int n_q, int n_kv, int head_dim, int causal, float scale,
+                           const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv,
+                           void* O, int64_t ldo, float* lse, void* stream) {
+  tps::AttnArgs a;
+  TPS_TRY(attn_check(dtype, B, S, n_q, n_kv, head_dim, causal, scale, Q, ldq, K, ldk, V, ldv, a));
+  if (!O || !lse) return TP_E_NULL;
+  TPS_TRY(check_mat(O, B * S, ldo, (int64_t)n_q * head_dim, dtype));
+  if (!aligned16(lse)) return TP_E_ALIGN;
+  a.o = O;
+  a.ldo = ldo;
+  a.lse = lse;
+  return tps::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
+}
+
 }  // extern "C"

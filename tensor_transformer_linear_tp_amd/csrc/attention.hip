@@ -1,0 +1,282 @@
+// Attention core of one tensor-parallel rank's heads on gfx950: scaled
+// dot-product attention with an online (streaming) softmax, GQA (several query
+// heads read one KV head), optional causal mask, head dim 128, bf16 in, fp32
+// softmax and accumulation.
+//
+// Work split.  A 256-thread workgroup (4 wave64s) takes one KV head and 128
+// query rows that all read it: 32 tokens x 4 query heads when 4 or more query
+// heads share the KV head (one head per wave), else 32 x 4/group tokens of
+// each of its `group` heads.  Every wave owns 32 query rows, so the KV tiles
+// staged in LDS are read by 128 query rows.
+//
+// Orientation.  Scores are computed transposed, S^T = K Q^T, as
+// v_mfma_f32_32x32x16_bf16 with K as the A operand: a lane then holds one
+// query row (lane % 32) and 32 of the 64 keys of a tile, so the row max and
+// row sum are in-lane plus one exchange with lane ^ 32.  The output is
+// accumulated transposed too, O^T += V^T P^T (V as the MN-contiguous A
+// operand read with ds_read_b64_tr_b16, P^T as the B operand after one
+// v_permlane32_swap per register pair puts each lane's keys in MFMA order).
+//
+// KV tiles of 64 keys (K 16 KiB + V 16 KiB) go global -> LDS with
+// buffer_load_dwordx4 ... lds into a 2-stage ring; rows past the sequence read
+// as zero and are masked.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace tps {
+namespace {
+
+constexpr int AT_D = 128;                       // head dim
+constexpr int AT_KT = 64;                       // keys per tile
+constexpr int AT_TILE = AT_KT * AT_D * 2;       // bytes of one K or V tile (16 KiB)
+constexpr int AT_NSTAGE = 2;
+constexpr float AT_LOG2E = 1.4426950408889634f;
+
+typedef __attribute__((ext_vector_type(4))) short at_i16x4;
+typedef __attribute__((ext_vector_type(8))) short at_i16x8;
+
+// K tile [64 keys][128 d], 256-byte rows of 16 chunks; chunk c of row r sits
+// at c ^ (r % 16), so 8 consecutive rows reading one logical chunk hit
+// distinct banks.
+__device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+// V tile [64 keys][128 d]: rows k % 4 = 0,1,2,3 XOR the chunk with 0,6,10,12
+// (the pattern ds_read_b64_tr_b16 reads without bank conflicts).
+__device__ __forceinline__ int v_swz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }
+__device__ __forceinline__ int v_off(int k, int c) { return k * 256 + ((c ^ v_swz(k)) << 4); }
+
+// A-operand fragment of K for S^T: key row kb + lane % 32, d = 16 kk + 8 (lane / 32) .. +7.
+__device__ __forceinline__ bf16x8 frag_k(const TPS_LDS char* s, int kb, int kk) {
+  const int lane = threadIdx.x & 63;
+  const int r = kb + (lane & 31);
+  return *reinterpret_cast<const TPS_LDS bf16x8*>(s + k_off(r, 2 * kk + (lane >> 5)));
+}
+
+// A-operand fragment of V^T: d column db + lane % 32, keys 16 kk + 8 (lane / 32) .. +7,
+// from the [key][d] tile through the transposing LDS read (within each 16-lane
+// group, lane i gets element i % 4 of the 8-byte loads of lanes i/4, 4 + i/4, ...).
+__device__ __forceinline__ bf16x8 frag_v(const TPS_LDS char* s, int db, int kk) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 4, q = lane & 15;
+  const int col = db + 16 * (h & 1) + 4 * (q & 3);
+  const int k0 = 16 * kk + 8 * (h >> 1) + (q >> 2);
+  const int c = col >> 3, byte_in = (col & 7) * 2;
+  const at_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS at_i16x4*)(s + v_off(k0, c) + byte_in));
+  const at_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS at_i16x4*)(s + v_off(k0 + 4, c) + byte_in));
+  const at_i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Per-lane byte offsets (relative to a tile's first key row) of this wave's 4
+// copy blocks of one 64 x 128 tile: block 4 w + j covers rows 4 (4 w + j) .. +3;
+// lane L writes LDS bytes [16 L, 16 L + 16) of the block = row 4 B + L / 16,
+// physical chunk L % 16.
+template <bool V>
+__device__ __forceinline__ void tile_voffs(int64_t ld, uint32_t (&vo)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * (4 * wave + j) + (lane >> 4);
+    const int p = lane & 15;
+    const int c = V ? (p ^ v_swz(row)) : (p ^ (row & 15));
+    vo[j] = (uint32_t)((row * ld + 8 * c) * 2);
+  }
+}
+
+__device__ __forceinline__ void issue_tile(const __amdgpu_buffer_rsrc_t& r, const uint32_t (&vo)[4], uint32_t off,
+                                           TPS_LDS char* dst) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(dst + 1024 * (4 * wave + j)), 16, vo[j] + off, 0, 0,
+                                             0);
+}
+
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(VM | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf2(lo, hi); }
+
+// LDS ring: stage s holds the K tile at s * 2 * AT_TILE and the V tile after it.
+__shared__ __attribute__((aligned(1024))) char at_ring[AT_NSTAGE * 2 * AT_TILE];
+
+__device__ __forceinline__ TPS_LDS char* ring_k(int stage) { return (TPS_LDS char*)at_ring + stage * 2 * AT_TILE; }
+__device__ __forceinline__ TPS_LDS char* ring_v(int stage) { return ring_k(stage) + AT_TILE; }
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int group = a.n_q / a.n_kv;
+  const int hpw = group < 4 ? group : 4;              // query heads per workgroup
+  const int tq = 32 * (4 / hpw);                       // tokens per workgroup
+  const int nquad = group / hpw;
+  const int64_t nqb = (a.S + tq - 1) / tq;
+  const int64_t qb = nqb - 1 - (int64_t)blockIdx.x;    // longest causal blocks first
+  const int g = (int)blockIdx.y / nquad, quad = (int)blockIdx.y % nquad;
+  const int64_t b = blockIdx.z;
+  const int head = g * group + quad * hpw + (wave % hpw);
+  const int64_t tok0 = qb * tq + 32 * (wave / hpw);    // this wave's first token
+  const int64_t row0 = b * a.S;                        // the sequence's first row
+
+  // Q fragments (B operand of S^T): row tok0 + lane % 32, d = 16 kk + 8 (lane / 32) .. +7
+  bf16x8 qf[8];
+  {
+    const int64_t t = min<int64_t>(tok0 + (lane & 31), a.S - 1);
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (row0 + t) * a.ldq + (int64_t)head * AT_D + 8 * (lane >> 5);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(q + 16 * kk);
+  }
+
+  // KV range of the workgroup and copy streams (descriptor at the head's first row)
+  const int64_t kv_end = a.causal ? min<int64_t>(a.S, qb * tq + tq) : a.S;
+  const int nt = (int)((kv_end + AT_KT - 1) / AT_KT);
+  const char* kbase = static_cast<const char*>(a.k) + (row0 * a.ldk + (int64_t)g * AT_D) * 2;
+  const char* vbase = static_cast<const char*>(a.v) + (row0 * a.ldv + (int64_t)g * AT_D) * 2;
+  const uint32_t knrec = (uint32_t)(((a.S - 1) * a.ldk + AT_D) * 2);
+  const uint32_t vnrec = (uint32_t)(((a.S - 1) * a.ldv + AT_D) * 2);
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)knrec,
+                                                                      0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)vnrec,
+                                                                      0x00020000);
+  uint32_t kvo[4], vvo[4];
+  tile_voffs<false>(a.ldk, kvo);
+  tile_voffs<true>(a.ldv, vvo);
+  const uint32_t kstep = (uint32_t)(AT_KT * a.ldk * 2), vstep = (uint32_t)(AT_KT * a.ldv * 2);
+
+  issue_tile(kr, kvo, 0, ring_k(0));
+  issue_tile(vr, vvo, 0, ring_v(0));
+
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{0.f};
+  float m = -INFINITY, l = 0.f;
+  const float c = a.scale * AT_LOG2E;
+  const int64_t my_tok = tok0 + (lane & 31);
+
+  for (int t = 0; t < nt; ++t) {
+    wait_vm<0>();
+    __syncthreads();   // tile t visible to all waves; stage (t+1)%2 free
+    if (t + 1 < nt) {
+      issue_tile(kr, kvo, (uint32_t)(t + 1) * kstep, ring_k((t + 1) & 1));
+      issue_tile(vr, vvo, (uint32_t)(t + 1) * vstep, ring_v((t + 1) & 1));
+    }
+    const TPS_LDS char* ks = ring_k(t & 1);
+    const TPS_LDS char* vs = ring_v(t & 1);
+
+    // S^T for the tile's two 32-key blocks
+    f32x16 st[2] = {f32x16{0.f}, f32x16{0.f}};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_k(ks, 32 * kb, kk), qf[kk], st[kb], 0, 0, 0);
+    }
+
+    // scale into the log2 domain; mask keys past the query (causal) or past the sequence
+    const int64_t key0 = (int64_t)t * AT_KT;
+    const bool need_mask = (key0 + AT_KT > a.S) || (a.causal && key0 + AT_KT - 1 > tok0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = st[kb][r] * c;
+        if (need_mask) {
+          const int64_t key = key0 + 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (key >= a.S || (a.causal && key > my_tok)) x = -INFINITY;
+        }
+        st[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    float rs = 0.f;
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(st[kb][r] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(st[kb][r + 1] - m_use);
+        rs += p0 + p1;
+        pk[kb][r >> 1] = pack2(p0, p1);
+      }
+    rs += __shfl_xor(rs, 32);
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+
+    // P^T fragments: k-step s covers keys 16 s .. 16 s + 15 = register groups
+    // q0 = 2 (s % 2), q0 + 1 of block s / 2; lanes < 32 hold keys +0..3 / +8..11,
+    // lanes >= 32 keys +4..7 / +12..15; one swap gives MFMA order (+0..7 | +8..15).
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kb = s >> 1, q0 = 2 * (s & 1);
+      uint32_t f[4];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(pk[kb][2 * q0 + w], pk[kb][2 * q0 + 2 + w], false, false);
+        f[w] = sw[0];
+        f[2 + w] = sw[1];
+      }
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{f[0], f[1], f[2], f[3]});
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_v(vs, 32 * db, s), pf, o[db], 0, 0, 0);
+    }
+  }
+
+  // O = O^T / l: lane holds row my_tok, d = 32 db + 8 (r / 4) + 4 (lane / 32) + r % 4;
+  // one swap per register pair gives each lane 8 consecutive d for 16-byte stores.
+  const float inv = 1.0f / l;
+  if (my_tok < a.S) {
+    if (lane < 32) {
+      float* lse = a.lse + ((int64_t)b * a.n_q + head) * a.S + my_tok;
+      *lse = (m + __log2f(l)) * 0.69314718055994531f;
+    }
+  }
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + (row0 + min<int64_t>(my_tok, a.S - 1)) * a.ldo +
+                   (int64_t)head * AT_D + 8 * (lane >> 5);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    uint32_t pk[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pk[q] = pack2(o[db][2 * q] * inv, o[db][2 * q + 1] * inv);
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const auto r = __builtin_amdgcn_permlane32_swap(pk[4 * pr + w], pk[4 * pr + 2 + w], false, false);
+        pk[4 * pr + w] = r[0];
+        pk[4 * pr + 2 + w] = r[1];
+      }
+    if (my_tok < a.S) {
+      *reinterpret_cast<u32x4*>(orow + 32 * db) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      *reinterpret_cast<u32x4*>(orow + 32 * db + 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
+  const int group = a.n_q / a.n_kv;
+  const int hpw = group < 4 ? group : 4;
+  const int tq = 32 * (4 / hpw);
+  const int64_t nqb = (a.S + tq - 1) / tq;
+  const dim3 grid((unsigned)nqb, (unsigned)(a.n_kv * (group / hpw)), (unsigned)a.B);
+  hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tps

@@ -134,6 +134,24 @@ struct EmbArgs {
   int64_t ldd;
 };
 
+// Attention core: B sequences of S tokens stacked by rows; head h of Q/O in
+// columns [128 h, 128 h + 128), KV head g of K/V likewise; lse fp32 [B][n_q][S].
+struct AttnArgs {
+  int64_t B, S;
+  int n_q, n_kv;
+  int causal;
+  float scale;
+  const void* q;
+  int64_t ldq;
+  const void* k;
+  int64_t ldk;
+  const void* v;
+  int64_t ldv;
+  void* o;
+  int64_t ldo;
+  float* lse;
+};
+
 constexpr int kSpLnMaxN = 16384;   // row width the LayerNorm kernel holds in registers
 
 constexpr int kColpartRows = 64;   // rows per column-partial block
@@ -148,6 +166,7 @@ hipError_t launch_colsum_finalize(int is_bf16, const float* colpart, int64_t nrb
 hipError_t launch_sum_partials(int is_bf16, const SumArgs& a, hipStream_t s);
 hipError_t launch_sp_rs_ln(int is_bf16, const SpLnArgs& a, hipStream_t s);
 hipError_t launch_emb_fwd(int is_bf16, const EmbArgs& a, hipStream_t s);
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 int64_t emb_bwd_count_blocks(int64_t Vr);
 // cnt [Vr], btot [emb_bwd_count_blocks(Vr)], start [Vr + 1] and order [M]
 // int32 come from the caller's workspace.

@@ -13,7 +13,7 @@ import torch
 from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_column_bwd,
                tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
                tp_sp_reduce_scatter_ln, tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_embed_bwd,
-               tp_vocab_embed_bwd_workspace_bytes, tp_vocab_embed_fwd, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
+               tp_vocab_embed_bwd_workspace_bytes, tp_vocab_embed_fwd, tp_attention_fwd, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
                tp_vocab_ce_workspace_bytes)
 
 ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
@@ -224,3 +224,15 @@ def vocab_embed_bwd(ids, dout, v0, Vr):
     ws = torch.empty(n, dtype=torch.uint8, device=dout.device)
     tp_vocab_embed_bwd(dtype_code(dout), M, Vr, K, ids, v0, dout, ld(dout), dE, ld(dE), ws, n)
     return dE
+
+
+def attention_fwd(q, k, v, n_q, n_kv, causal=True, scale=None, B=1):
+    """Attention core on views q [B S, 128 n_q], k / v [B S, 128 n_kv] (views of a packed QKV are
+    passed as they are); returns (O [B S, 128 n_q], lse [B, n_q, S] fp32)."""
+    rows = q.shape[0]
+    S = rows // B
+    scale = 1.0 / 128 ** 0.5 if scale is None else scale
+    o = empty_padded(rows, 128 * n_q, q.dtype, q.device)
+    lse = torch.empty(B, n_q, S, dtype=torch.float32, device=q.device)
+    tp_attention_fwd(dtype_code(q), B, S, n_q, n_kv, 128, causal, scale, q, ld(q), k, ld(k), v, ld(v), o, ld(o), lse)
+    return o, lse

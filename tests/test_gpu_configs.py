@@ -284,6 +284,22 @@ def test_c5_ce_backward_full_size_sampled():
     assert_close("dW", host64(dW)[js], rdW, TOL[syn.BF16])
 
 
+def test_c3_attention_core_full_size():
+    # The rank's 4 query heads and 1 KV head over one 8192-token sequence, causal, read
+    # straight from the packed QKV projection output [8192, 768].
+    cfg = syn.C3
+    S, n_q, n_kv = cfg.M, 4, 1
+    qkv = syn.normal(3950, (S, cfg.n_qkv), 1.0, syn.BF16)
+    d = dev(qkv)
+    O, lse = ops.attention_fwd(d[:, :512], d[:, 512:640], d[:, 640:], n_q, n_kv, causal=True)
+    torch.cuda.synchronize()
+    X = qkv.f64
+    ro, rl = oracle.attention_fwd(X[:, :512], X[:, 512:640], X[:, 640:], n_q, n_kv, causal=True)
+    ms = sample_idx(S, 256, 19)
+    assert_close("O", rows(O, ms), ro[ms], BF)
+    assert_close("lse", host64(lse[0])[:, ms], rl[:, ms], 1e-3)
+
+
 def test_c5_vocab_embedding_shard_full_size():
     # Embedding shard 0 of 8 of the 151936 x 4096 table (18992 rows), 8192 tokens with ids
     # uniform over the full vocabulary: lookup compared in full, backward on the rows that

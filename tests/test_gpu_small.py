@@ -395,6 +395,31 @@ def test_vocab_embed_shards_sum_to_full_lookup_on_gpu():
     _exact(Z, np.take(E.f64, ids, axis=0))
 
 
+# (B, S, n_q, n_kv, causal): one token, ragged tails of the 64-key tiles and 32-row blocks,
+# GQA groups 4 / 2 / 1 / 8, several sequences.
+ATTN_CASES = [(1, 1, 1, 1, True), (1, 37, 4, 1, True), (1, 64, 4, 1, False), (1, 200, 4, 1, True),
+              (1, 300, 2, 1, True), (1, 130, 2, 2, False), (1, 256, 8, 1, True), (3, 100, 4, 1, True),
+              (2, 129, 4, 1, False)]
+
+
+@pytest.mark.parametrize("B,S,n_q,n_kv,causal", ATTN_CASES)
+def test_attention_fwd_small(B, S, n_q, n_kv, causal):
+    seed = 11 * S + n_q + 3 * B
+    width = 128 * (n_q + 2 * n_kv)
+    qkv = syn.normal(seed, (B * S, width), 1.0, syn.BF16)       # packed [q heads | k | v] like the QKV output
+    d = dev(qkv)
+    q, k, v = d[:, :128 * n_q], d[:, 128 * n_q:128 * (n_q + n_kv)], d[:, 128 * (n_q + n_kv):]
+    O, lse = ops.attention_fwd(q, k, v, n_q, n_kv, causal=causal, B=B)
+    torch.cuda.synchronize()
+    X = qkv.f64
+    for b in range(B):
+        rs = slice(b * S, (b + 1) * S)
+        ro, rl = oracle.attention_fwd(X[rs, :128 * n_q], X[rs, 128 * n_q:128 * (n_q + n_kv)],
+                                      X[rs, 128 * (n_q + n_kv):], n_q, n_kv, causal=causal)
+        assert_close(f"O seq {b}", host64(O[rs]), ro, TOL[syn.BF16])
+        assert_close(f"lse seq {b}", host64(lse[b]), rl, 1e-3)
+
+
 def test_deterministic_bitwise():
     d = _inputs(syn.BF16, 520, 300, 1030, 3, "swiglu")
     outs = []
