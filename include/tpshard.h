@@ -310,13 +310,18 @@ TP_API size_t tp_vocab_embed_bwd_workspace_bytes(int64_t M, int64_t Vr);
  * head_dim must be 128; n_q / n_kv must divide 4 or be a multiple of 4;
  * scale > 0 (1/sqrt(128) for the usual attention); causal is 0 or 1.
  * Scores, softmax and accumulation are fp32; the probabilities enter the
- * second product as bf16.  Only TP_BF16.
+ * second product as bf16.  Only TP_BF16.  Long key ranges are cut into
+ * chunks run by separate workgroups and merged in a fixed order; their
+ * partial results need a workspace of tp_attention_fwd_workspace_bytes()
+ * bytes (0 = none needed; workspace may then be NULL).
  */
 TP_API tp_status tp_attention_fwd(int dtype, int64_t B, int64_t S, int n_q, int n_kv, int head_dim,
                                   int causal, float scale,
                                   const void* Q, int64_t ldq, const void* K, int64_t ldk,
                                   const void* V, int64_t ldv, void* O, int64_t ldo, float* lse,
-                                  void* stream);
+                                  void* workspace, size_t ws_bytes, void* stream);
+/* Workspace of tp_attention_fwd for this shape (head_dim 128); 0 for an invalid shape. */
+TP_API size_t tp_attention_fwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int causal);
 
 #ifdef __cplusplus
 }

@@ -559,17 +559,29 @@ tp_status attn_check(int dtype, int64_t B, int64_t S, int n_q, int n_kv, int hea
 }
 }  // namespace
 
+size_t tp_attention_fwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int causal) {
+  if (bad_dim(B) || bad_dim(S) || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return 0;
+  const int group = n_q / n_kv;
+  if (!(group % 4 == 0 || 4 % group == 0)) return 0;
+  return align_ws(tps::attn_fwd_workspace_bytes(B, S, n_q, n_kv, causal != 0));
+}
+
 tp_status tp_attention_fwd(int dtype, int64_t B, int64_t S, int n_q, int n_kv, int head_dim, int causal, float scale,
                            const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv,
-                           void* O, int64_t ldo, float* lse, void* stream) {
+                           void* O, int64_t ldo, float* lse, void* workspace, size_t ws_bytes, void* stream) {
   tps::AttnArgs a;
   TPS_TRY(attn_check(dtype, B, S, n_q, n_kv, head_dim, causal, scale, Q, ldq, K, ldk, V, ldv, a));
   if (!O || !lse) return TP_E_NULL;
   TPS_TRY(check_mat(O, B * S, ldo, (int64_t)n_q * head_dim, dtype));
   if (!aligned16(lse)) return TP_E_ALIGN;
+  const size_t need = tp_attention_fwd_workspace_bytes(B, S, n_q, n_kv, causal);
+  if (need > 0 && (!workspace || ws_bytes < need)) return TP_E_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return TP_E_ALIGN;
   a.o = O;
   a.ldo = ldo;
   a.lse = lse;
+  tps::attn_chunking(B, S, n_q, n_kv, causal, a.chunk_tiles, a.max_chunks);
+  a.ws = static_cast<float*>(workspace);
   return tps::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
 }
 

@@ -20,8 +20,19 @@
 // KV tiles of 64 keys (K 16 KiB + V 16 KiB) go global -> LDS with
 // buffer_load_dwordx4 ... lds into a 2-stage ring; rows past the sequence read
 // as zero and are masked.
+//
+// Split KV.  Under the causal mask the work of a query block grows with its
+// position, so a block's key range is cut into chunks of chunk_tiles tiles,
+// each run by its own workgroup (two fit on a CU).  A block with one chunk
+// writes O and lse directly; otherwise every chunk writes its unnormalized
+// O, running max and sum (fp32) to the workspace and attn_combine_kernel
+// merges the chunks in ascending order (a fixed order: the result does not
+// depend on scheduling).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
+#include <climits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -108,15 +119,48 @@ __shared__ __attribute__((aligned(1024))) char at_ring[AT_NSTAGE * 2 * AT_TILE];
 __device__ __forceinline__ TPS_LDS char* ring_k(int stage) { return (TPS_LDS char*)at_ring + stage * 2 * AT_TILE; }
 __device__ __forceinline__ TPS_LDS char* ring_v(int stage) { return ring_k(stage) + AT_TILE; }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
+// Query-block geometry shared by the attention kernels.
+struct AttnGeo {
+  int group, hpw, tq, nquad;
+  int64_t nqb;
+};
 
+__device__ __forceinline__ AttnGeo attn_geo(const AttnArgs& a) {
+  AttnGeo q;
+  q.group = a.n_q / a.n_kv;
+  q.hpw = q.group < 4 ? q.group : 4;   // query heads per workgroup
+  q.tq = 32 * (4 / q.hpw);             // tokens per workgroup
+  q.nquad = q.group / q.hpw;
+  q.nqb = (a.S + q.tq - 1) / q.tq;
+  return q;
+}
+
+// Key tiles of query block qb, and the chunks they are cut into.
+__device__ __forceinline__ int attn_tiles(const AttnArgs& a, const AttnGeo& q, int64_t qb) {
+  const int64_t kv_end = a.causal ? min<int64_t>(a.S, qb * q.tq + q.tq) : a.S;
+  return (int)((kv_end + AT_KT - 1) / AT_KT);
+}
+
+// Workspace slot of one chunk: O [128 rows][128] then m [128] and l [128], fp32.
+constexpr int64_t AT_SLOT = 128 * 128 + 2 * 128;
+
+__device__ __forceinline__ float* attn_slot(const AttnArgs& a, const AttnGeo& q, int64_t qb, int chunk) {
+  const int64_t idx = (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * q.nqb + qb) * a.max_chunks + chunk;
+  return a.ws + idx * AT_SLOT;
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int group = a.n_q / a.n_kv;
-  const int hpw = group < 4 ? group : 4;              // query heads per workgroup
-  const int tq = 32 * (4 / hpw);                       // tokens per workgroup
-  const int nquad = group / hpw;
-  const int64_t nqb = (a.S + tq - 1) / tq;
-  const int64_t qb = nqb - 1 - (int64_t)blockIdx.x;    // longest causal blocks first
+  const AttnGeo geo = attn_geo(a);
+  const int group = geo.group, hpw = geo.hpw, tq = geo.tq, nquad = geo.nquad;
+  const int64_t nqb = geo.nqb;
+  const int chunk = (int)(blockIdx.x / nqb);
+  const int64_t qb = nqb - 1 - (int64_t)(blockIdx.x % nqb);   // longest causal blocks first
+  const int nt_all = attn_tiles(a, geo, qb);
+  const int nchunks = (nt_all + a.chunk_tiles - 1) / a.chunk_tiles;
+  if (chunk >= nchunks) return;                                // (uniform: before any barrier)
+  const int t_begin = chunk * a.chunk_tiles;
+  const int nt = min(nt_all, t_begin + a.chunk_tiles) - t_begin;
   const int g = (int)blockIdx.y / nquad, quad = (int)blockIdx.y % nquad;
   const int64_t b = blockIdx.z;
   const int head = g * group + quad * hpw + (wave % hpw);
@@ -132,9 +176,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
     for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(q + 16 * kk);
   }
 
-  // KV range of the workgroup and copy streams (descriptor at the head's first row)
-  const int64_t kv_end = a.causal ? min<int64_t>(a.S, qb * tq + tq) : a.S;
-  const int nt = (int)((kv_end + AT_KT - 1) / AT_KT);
+  // copy streams (descriptor at the head's first row)
   const char* kbase = static_cast<const char*>(a.k) + (row0 * a.ldk + (int64_t)g * AT_D) * 2;
   const char* vbase = static_cast<const char*>(a.v) + (row0 * a.ldv + (int64_t)g * AT_D) * 2;
   const uint32_t knrec = (uint32_t)(((a.S - 1) * a.ldk + AT_D) * 2);
@@ -148,8 +190,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
   tile_voffs<true>(a.ldv, vvo);
   const uint32_t kstep = (uint32_t)(AT_KT * a.ldk * 2), vstep = (uint32_t)(AT_KT * a.ldv * 2);
 
-  issue_tile(kr, kvo, 0, ring_k(0));
-  issue_tile(vr, vvo, 0, ring_v(0));
+  issue_tile(kr, kvo, (uint32_t)t_begin * kstep, ring_k(0));
+  issue_tile(vr, vvo, (uint32_t)t_begin * vstep, ring_v(0));
 
   f32x16 o[4];
 #pragma unroll
@@ -162,8 +204,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
     wait_vm<0>();
     __syncthreads();   // tile t visible to all waves; stage (t+1)%2 free
     if (t + 1 < nt) {
-      issue_tile(kr, kvo, (uint32_t)(t + 1) * kstep, ring_k((t + 1) & 1));
-      issue_tile(vr, vvo, (uint32_t)(t + 1) * vstep, ring_v((t + 1) & 1));
+      issue_tile(kr, kvo, (uint32_t)(t_begin + t + 1) * kstep, ring_k((t + 1) & 1));
+      issue_tile(vr, vvo, (uint32_t)(t_begin + t + 1) * vstep, ring_v((t + 1) & 1));
     }
     const TPS_LDS char* ks = ring_k(t & 1);
     const TPS_LDS char* vs = ring_v(t & 1);
@@ -177,24 +219,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
         st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_k(ks, 32 * kb, kk), qf[kk], st[kb], 0, 0, 0);
     }
 
-    // scale into the log2 domain; mask keys past the query (causal) or past the sequence
-    const int64_t key0 = (int64_t)t * AT_KT;
+    // mask keys past the query (causal) or past the sequence; the scale (and
+    // log2 e) enters once, in the exponent's fused multiply-add (c > 0)
+    const int64_t key0 = (int64_t)(t_begin + t) * AT_KT;
     const bool need_mask = (key0 + AT_KT > a.S) || (a.causal && key0 + AT_KT - 1 > tok0);
+    if (need_mask) {
+      const int kmax = (int)min<int64_t>(a.causal ? my_tok - key0 : INT_MAX, a.S - 1 - key0);   // last visible key
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) > kmax) st[kb][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = st[kb][r] * c;
-        if (need_mask) {
-          const int64_t key = key0 + 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (key >= a.S || (a.causal && key > my_tok)) x = -INFINITY;
-        }
-        st[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
+    const float m_new = fmaxf(m, mx * c);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m - m_use);
     float rs = 0.f;
@@ -203,18 +246,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(st[kb][r] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(st[kb][r + 1] - m_use);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r + 1], c, -m_use));
         rs += p0 + p1;
         pk[kb][r >> 1] = pack2(p0, p1);
       }
     rs += __shfl_xor(rs, 32);
     l = l * alpha + rs;
     m = m_new;
+    if (__ballot(alpha != 1.0f)) {   // some row's max moved
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
 
     // P^T fragments: k-step s covers keys 16 s .. 16 s + 15 = register groups
     // q0 = 2 (s % 2), q0 + 1 of block s / 2; lanes < 32 hold keys +0..3 / +8..11,
@@ -234,6 +279,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
       for (int db = 0; db < 4; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_v(vs, 32 * db, s), pf, o[db], 0, 0, 0);
     }
+  }
+
+  if (nchunks > 1) {   // partial: unnormalized O^T rows, running max (log2 domain) and sum
+    float* slot = attn_slot(a, geo, qb, chunk);
+    const int row = 32 * wave + (lane & 31);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(slot + row * 128 + 32 * db + 8 * q + 4 * (lane >> 5)) =
+            f32x4{o[db][4 * q], o[db][4 * q + 1], o[db][4 * q + 2], o[db][4 * q + 3]};
+    if (lane < 32) {
+      slot[128 * 128 + row] = m;
+      slot[128 * 128 + 128 + row] = l;
+    }
+    return;
   }
 
   // O = O^T / l: lane holds row my_tok, d = 32 db + 8 (r / 4) + 4 (lane / 32) + r % 4;
@@ -267,15 +328,90 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
   }
 }
 
+// Merge of the chunks of every split query block: for each of the block's 128
+// rows, M = max m_c, L = sum l_c 2^(m_c - M), O = sum O_c 2^(m_c - M) / L in
+// ascending chunk order; lse = (M + log2 L) ln 2.  32 threads per row, 4 d each.
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
+  const AttnGeo geo = attn_geo(a);
+  const int64_t qb = blockIdx.x;
+  const int nchunks = (attn_tiles(a, geo, qb) + a.chunk_tiles - 1) / a.chunk_tiles;
+  if (nchunks <= 1) return;
+  const int g = (int)blockIdx.y / geo.nquad, quad = (int)blockIdx.y % geo.nquad;
+  const int64_t b = blockIdx.z;
+  const int d4 = 4 * (threadIdx.x & 31);
+  for (int pass = 0; pass < 16; ++pass) {
+    const int row = 8 * pass + (threadIdx.x >> 5);
+    const int w = row >> 5;
+    const int head = g * geo.group + quad * geo.hpw + (w % geo.hpw);
+    const int64_t tok = qb * geo.tq + 32 * (w / geo.hpw) + (row & 31);
+    if (tok >= a.S) continue;
+    float M = -INFINITY;
+    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, attn_slot(a, geo, qb, c)[128 * 128 + row]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nchunks; ++c) {
+      const float* slot = attn_slot(a, geo, qb, c);
+      const float wgt = __builtin_amdgcn_exp2f(slot[128 * 128 + row] - Mu);
+      L += slot[128 * 128 + 128 + row] * wgt;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * 128 + d4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[e] * wgt;
+    }
+    const float inv = 1.0f / L;
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + (b * a.S + tok) * a.ldo + (int64_t)head * AT_D + d4;
+    *reinterpret_cast<u32x2*>(orow) = u32x2{pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv)};
+    if (d4 == 0) a.lse[((int64_t)b * a.n_q + head) * a.S + tok] = (M + __log2f(L)) * 0.69314718055994531f;
+  }
+}
+
 }  // namespace
+
+// Chunking (a function of the shape only, so the workspace size is known
+// without a device): causal key ranges are cut into chunks of 16 tiles (1024
+// keys); without the mask every block has the same work, and the range is cut
+// only when there are fewer than 512 workgroups (two per CU of an MI355X).
+constexpr int64_t AT_TARGET_WGS = 512;
+
+void attn_chunking(int64_t B, int64_t S, int n_q, int n_kv, int causal, int& chunk_tiles, int& max_chunks) {
+  const int group = n_q / n_kv;
+  const int hpw = group < 4 ? group : 4;
+  const int tq = 32 * (4 / hpw);
+  const int64_t nqb = (S + tq - 1) / tq;
+  const int64_t nt_max = (S + AT_KT - 1) / AT_KT;
+  int64_t c;
+  if (causal) {
+    c = 16;
+  } else {
+    const int64_t blocks = nqb * n_kv * (group / hpw) * B;
+    const int64_t want = std::max<int64_t>(1, (AT_TARGET_WGS + blocks - 1) / blocks);
+    c = (nt_max + want - 1) / want;
+  }
+  c = std::max<int64_t>(1, std::min<int64_t>(c, nt_max));
+  chunk_tiles = (int)c;
+  max_chunks = (int)((nt_max + c - 1) / c);
+}
+
+size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int causal) {
+  int ct, mc;
+  attn_chunking(B, S, n_q, n_kv, causal, ct, mc);
+  if (mc <= 1) return 0;
+  const int group = n_q / n_kv;
+  const int hpw = group < 4 ? group : 4;
+  const int tq = 32 * (4 / hpw);
+  const int64_t nqb = (S + tq - 1) / tq;
+  return (size_t)(B * n_kv * (group / hpw) * nqb * mc * AT_SLOT * 4);
+}
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
   const int group = a.n_q / a.n_kv;
   const int hpw = group < 4 ? group : 4;
   const int tq = 32 * (4 / hpw);
   const int64_t nqb = (a.S + tq - 1) / tq;
-  const dim3 grid((unsigned)nqb, (unsigned)(a.n_kv * (group / hpw)), (unsigned)a.B);
-  hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(256), 0, s, a);
+  const unsigned gy = (unsigned)(a.n_kv * (group / hpw));
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)(nqb * a.max_chunks), gy, (unsigned)a.B), dim3(256), 0, s, a);
+  if (a.max_chunks > 1)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)nqb, gy, (unsigned)a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

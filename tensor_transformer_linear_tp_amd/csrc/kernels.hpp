@@ -150,6 +150,9 @@ struct AttnArgs {
   void* o;
   int64_t ldo;
   float* lse;
+  int chunk_tiles;   // key tiles (64 keys) per workgroup along a query block's key range
+  int max_chunks;    // chunks of the longest query block; > 1 needs ws
+  float* ws;         // per-chunk partial results (attn_fwd_workspace_bytes)
 };
 
 constexpr int kSpLnMaxN = 16384;   // row width the LayerNorm kernel holds in registers
@@ -166,6 +169,8 @@ hipError_t launch_colsum_finalize(int is_bf16, const float* colpart, int64_t nrb
 hipError_t launch_sum_partials(int is_bf16, const SumArgs& a, hipStream_t s);
 hipError_t launch_sp_rs_ln(int is_bf16, const SpLnArgs& a, hipStream_t s);
 hipError_t launch_emb_fwd(int is_bf16, const EmbArgs& a, hipStream_t s);
+void attn_chunking(int64_t B, int64_t S, int n_q, int n_kv, int causal, int& chunk_tiles, int& max_chunks);
+size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int causal);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 int64_t emb_bwd_count_blocks(int64_t Vr);
 // cnt [Vr], btot [emb_bwd_count_blocks(Vr)], start [Vr + 1] and order [M]

@@ -13,7 +13,8 @@ import torch
 from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_column_bwd,
                tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
                tp_sp_reduce_scatter_ln, tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_embed_bwd,
-               tp_vocab_embed_bwd_workspace_bytes, tp_vocab_embed_fwd, tp_attention_fwd, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
+               tp_vocab_embed_bwd_workspace_bytes, tp_vocab_embed_fwd, tp_attention_fwd,
+               tp_attention_fwd_workspace_bytes, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
                tp_vocab_ce_workspace_bytes)
 
 ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
@@ -234,5 +235,8 @@ def attention_fwd(q, k, v, n_q, n_kv, causal=True, scale=None, B=1):
     scale = 1.0 / 128 ** 0.5 if scale is None else scale
     o = empty_padded(rows, 128 * n_q, q.dtype, q.device)
     lse = torch.empty(B, n_q, S, dtype=torch.float32, device=q.device)
-    tp_attention_fwd(dtype_code(q), B, S, n_q, n_kv, 128, causal, scale, q, ld(q), k, ld(k), v, ld(v), o, ld(o), lse)
+    n = tp_attention_fwd_workspace_bytes(B, S, n_q, n_kv, causal)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    tp_attention_fwd(dtype_code(q), B, S, n_q, n_kv, 128, causal, scale, q, ld(q), k, ld(k), v, ld(v), o, ld(o), lse,
+                     ws, n)
     return o, lse

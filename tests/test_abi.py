@@ -201,6 +201,44 @@ def test_vocab_embed_validation(lib):
     assert _rc("tp_vocab_embed_bwd", *a) == 2
 
 
+def test_attention_validation(lib):
+    sc = 1.0 / 128 ** 0.5
+    # packed QKV [8192, 768]: 4 query heads, 1 KV head
+    ws = tp.tp_attention_fwd_workspace_bytes(1, 8192, 4, 1, 1)
+    # 256 query blocks of 32 tokens x 4 heads, up to 8 chunks of 1024 keys, 130 x 128 floats per chunk
+    assert ws == 256 * 8 * (128 * 128 + 256) * 4
+    assert tp.tp_attention_fwd_workspace_bytes(1, 1024, 4, 1, 1) == 0          # one chunk: no workspace
+    assert tp.tp_attention_fwd_workspace_bytes(1, 8192, 4, 3, 1) == 0          # invalid shape
+    base = [tp.TP_BF16, 1, 8192, 4, 1, 128, 1, sc, P, 768, P + 1024, 768, P + 1280, 768, P, 512, P, P, ws, None]
+    a = list(base); a[18] = ws - 1
+    assert _rc("tp_attention_fwd", *a) == 6
+    a = list(base); a[17] = None
+    assert _rc("tp_attention_fwd", *a) == 6
+    a = list(base); a[0] = tp.TP_FP32
+    assert _rc("tp_attention_fwd", *a) == 4
+    a = list(base); a[5] = 64                                 # head dim other than 128
+    assert _rc("tp_attention_fwd", *a) == 2
+    a = list(base); a[3], a[4] = 6, 2                         # group 3: neither divides nor is divided by 4
+    assert _rc("tp_attention_fwd", *a) == 2
+    a = list(base); a[3], a[4] = 4, 3                         # n_q not a multiple of n_kv
+    assert _rc("tp_attention_fwd", *a) == 2
+    a = list(base); a[6] = 2
+    assert _rc("tp_attention_fwd", *a) == 2
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        a = list(base); a[7] = bad
+        assert _rc("tp_attention_fwd", *a) == 2
+    a = list(base); a[16] = None                              # lse required
+    assert _rc("tp_attention_fwd", *a) == 1
+    a = list(base); a[16] = P + 4
+    assert _rc("tp_attention_fwd", *a) == 3
+    a = list(base); a[9] = 500                                # ldq < 4 x 128
+    assert _rc("tp_attention_fwd", *a) == 2
+    a = list(base); a[10] = P + 1026                          # K not 16-byte aligned
+    assert _rc("tp_attention_fwd", *a) == 3
+    a = list(base); a[1] = 1 << 16                            # more sequences than the grid takes
+    assert _rc("tp_attention_fwd", *a) == 2
+
+
 def test_bf16_operands_below_2gib(lib):
     # X [2^17, 2^13] bf16 spans exactly 2 GiB: rejected before any HIP call.
     K = 1 << 13

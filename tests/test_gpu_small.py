@@ -399,7 +399,8 @@ def test_vocab_embed_shards_sum_to_full_lookup_on_gpu():
 # GQA groups 4 / 2 / 1 / 8, several sequences.
 ATTN_CASES = [(1, 1, 1, 1, True), (1, 37, 4, 1, True), (1, 64, 4, 1, False), (1, 200, 4, 1, True),
               (1, 300, 2, 1, True), (1, 130, 2, 2, False), (1, 256, 8, 1, True), (3, 100, 4, 1, True),
-              (2, 129, 4, 1, False)]
+              (2, 129, 4, 1, False), (1, 1100, 4, 1, True), (1, 2100, 2, 1, True), (2, 700, 8, 2, False)]
+# (causal ranges beyond 1024 keys and short non-causal ones are cut into chunks merged afterwards)
 
 
 @pytest.mark.parametrize("B,S,n_q,n_kv,causal", ATTN_CASES)
