@@ -323,6 +323,32 @@ TP_API tp_status tp_attention_fwd(int dtype, int64_t B, int64_t S, int n_q, int 
 /* Workspace of tp_attention_fwd for this shape (head_dim 128); 0 for an invalid shape. */
 TP_API size_t tp_attention_fwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int causal);
 
+/*
+ * Backward of tp_attention_fwd (the pages print no backward; the textbook
+ * gradients of softmax attention).  With P = softmax(s) recomputed from the
+ * forward's lse, per head:
+ *
+ *   dV_g += P^T dO_h        dP = dO_h V_g^T        dS = P * (dP - D),
+ *   D_i  = sum_j P_ij dP_ij = sum_d dO_h[i] O_h[i]   (fp32, from O and dO)
+ *   dQ_h  = dS K_g * scale  dK_g += dS^T Q_h * scale
+ *
+ * A KV head's dK, dV sum over the query heads that read it.  Shapes and
+ * layouts as tp_attention_fwd; O and lse are that call's outputs, dO is
+ * [B S, n_q * 128] (lddo); dQ [B S, n_q * 128], dK and dV [B S, n_kv * 128]
+ * are written completely.  Products in bf16 with fp32 accumulation; partial
+ * results (key chunks for dQ, query heads and query chunks for dK and dV)
+ * live in the workspace (>= tp_attention_bwd_workspace_bytes()) and are
+ * summed in a fixed order: no atomics.  Only TP_BF16.
+ */
+TP_API tp_status tp_attention_bwd(int dtype, int64_t B, int64_t S, int n_q, int n_kv, int head_dim,
+                                  int causal, float scale,
+                                  const void* Q, int64_t ldq, const void* K, int64_t ldk,
+                                  const void* V, int64_t ldv, const void* O, int64_t ldo,
+                                  const float* lse, const void* dO, int64_t lddo,
+                                  void* dQ, int64_t lddq, void* dK, int64_t lddk, void* dV, int64_t lddv,
+                                  void* workspace, size_t ws_bytes, void* stream);
+TP_API size_t tp_attention_bwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int causal);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ __all__ = [
     "tp_row_bwd_workspace_bytes", "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_vocab_ce_partials",
     "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "tp_sp_reduce_scatter_ln",
     "tp_vocab_embed_fwd", "tp_vocab_embed_bwd", "tp_vocab_embed_bwd_workspace_bytes", "tp_attention_fwd",
-    "tp_attention_fwd_workspace_bytes", "EXPORTED_SYMBOLS",
+    "tp_attention_fwd_workspace_bytes", "tp_attention_bwd", "tp_attention_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
 
 TP_FP32, TP_BF16 = 0, 1
@@ -63,6 +63,9 @@ _SIGS = {
     "tp_attention_fwd": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _i64, _vp, _i64, _vp,
                                 _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
     "tp_attention_fwd_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32]),
+    "tp_attention_bwd": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, ctypes.c_float, _vp, _i64, _vp, _i64, _vp,
+                                _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "tp_attention_bwd_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -222,3 +225,15 @@ def tp_attention_fwd(dtype, B, S, n_q, n_kv, head_dim, causal, scale, Q, ldq, K,
 
 def tp_attention_fwd_workspace_bytes(B, S, n_q, n_kv, causal) -> int:
     return _load().tp_attention_fwd_workspace_bytes(B, S, n_q, n_kv, int(causal))
+
+
+def tp_attention_bwd(dtype, B, S, n_q, n_kv, head_dim, causal, scale, Q, ldq, K, ldk, V, ldv, O, ldo, lse, dO, lddo,
+                     dQ, lddq, dK, lddk, dV, lddv, workspace, ws_bytes, stream=None):
+    _check("tp_attention_bwd", _load().tp_attention_bwd(
+        dtype, B, S, n_q, n_kv, head_dim, int(causal), float(scale), _ptr(Q), ldq, _ptr(K), ldk, _ptr(V), ldv, _ptr(O),
+        ldo, _ptr(lse), _ptr(dO), lddo, _ptr(dQ), lddq, _ptr(dK), lddk, _ptr(dV), lddv, _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def tp_attention_bwd_workspace_bytes(B, S, n_q, n_kv, causal) -> int:
+    return _load().tp_attention_bwd_workspace_bytes(B, S, n_q, n_kv, int(causal))

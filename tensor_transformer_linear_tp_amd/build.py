@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libtpshard.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "embedding.hip", "attention.hip"]
+SOURCES = ["abi.cpp", "gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "embedding.hip", "attention.hip",
+           "attention_bwd.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

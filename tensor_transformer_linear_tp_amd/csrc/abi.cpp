@@ -585,4 +585,55 @@ tp_status tp_attention_fwd(int dtype, int64_t B, int64_t S, int n_q, int n_kv, i
   return tps::launch_attn_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
 }
 
+size_t tp_attention_bwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int causal) {
+  if (bad_dim(B) || bad_dim(S) || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return 0;
+  const int group = n_q / n_kv;
+  if (!(group % 4 == 0 || 4 % group == 0)) return 0;
+  tps::AttnBwdLayout L;
+  tps::attn_bwd_layout(B, S, n_q, n_kv, causal != 0, L);
+  return L.ld_bytes + L.dq_bytes + L.kv_bytes;
+}
+
+tp_status tp_attention_bwd(int dtype, int64_t B, int64_t S, int n_q, int n_kv, int head_dim, int causal, float scale,
+                           const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv,
+                           const void* O, int64_t ldo, const float* lse, const void* dO, int64_t lddo, void* dQ,
+                           int64_t lddq, void* dK, int64_t lddk, void* dV, int64_t lddv, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  tps::AttnBwdArgs p = {};
+  TPS_TRY(attn_check(dtype, B, S, n_q, n_kv, head_dim, causal, scale, Q, ldq, K, ldk, V, ldv, p.f));
+  if (!O || !lse || !dO || !dQ || !dK || !dV) return TP_E_NULL;
+  const int64_t rows = B * S, wq = (int64_t)n_q * head_dim, wkv = (int64_t)n_kv * head_dim;
+  TPS_TRY(check_mat(O, rows, ldo, wq, dtype));
+  TPS_TRY(check_mat(dO, rows, lddo, wq, dtype));
+  TPS_TRY(check_mat(dQ, rows, lddq, wq, dtype));
+  TPS_TRY(check_mat(dK, rows, lddk, wkv, dtype));
+  TPS_TRY(check_mat(dV, rows, lddv, wkv, dtype));
+  if (!aligned16(lse)) return TP_E_ALIGN;
+  const size_t need = tp_attention_bwd_workspace_bytes(B, S, n_q, n_kv, causal);
+  if (!workspace || ws_bytes < need) return TP_E_WORKSPACE;
+  if (!aligned16(workspace)) return TP_E_ALIGN;
+  tps::AttnBwdLayout L;
+  tps::attn_bwd_layout(B, S, n_q, n_kv, causal, L);
+  char* w = static_cast<char*>(workspace);
+  p.f.o = const_cast<void*>(O);
+  p.f.ldo = ldo;
+  p.f.lse = const_cast<float*>(lse);
+  p.f.chunk_tiles = L.chunk_tiles;
+  p.f.max_chunks = L.max_chunks;
+  p.dout = dO;
+  p.ldg = lddo;
+  p.dq = dQ;
+  p.lddq = lddq;
+  p.dk = dK;
+  p.lddk = lddk;
+  p.dv = dV;
+  p.lddv = lddv;
+  p.ld = reinterpret_cast<float*>(w);
+  p.dq_ws = reinterpret_cast<float*>(w + L.ld_bytes);
+  p.kv_ws = reinterpret_cast<float*>(w + L.ld_bytes + L.dq_bytes);
+  p.kv_chunk_tiles = L.kv_chunk_tiles;
+  p.kv_max_chunks = L.kv_max_chunks;
+  return tps::launch_attn_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
+}
+
 }  // extern "C"

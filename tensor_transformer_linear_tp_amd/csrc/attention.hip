@@ -34,82 +34,20 @@
 #include <algorithm>
 #include <climits>
 
+#include "attention_common.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace tps {
 namespace {
 
-constexpr int AT_D = 128;                       // head dim
+using namespace attn;
+
+constexpr int AT_D = HD;
 constexpr int AT_KT = 64;                       // keys per tile
 constexpr int AT_TILE = AT_KT * AT_D * 2;       // bytes of one K or V tile (16 KiB)
 constexpr int AT_NSTAGE = 2;
-constexpr float AT_LOG2E = 1.4426950408889634f;
-
-typedef __attribute__((ext_vector_type(4))) short at_i16x4;
-typedef __attribute__((ext_vector_type(8))) short at_i16x8;
-
-// K tile [64 keys][128 d], 256-byte rows of 16 chunks; chunk c of row r sits
-// at c ^ (r % 16), so 8 consecutive rows reading one logical chunk hit
-// distinct banks.
-__device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
-// V tile [64 keys][128 d]: rows k % 4 = 0,1,2,3 XOR the chunk with 0,6,10,12
-// (the pattern ds_read_b64_tr_b16 reads without bank conflicts).
-__device__ __forceinline__ int v_swz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }
-__device__ __forceinline__ int v_off(int k, int c) { return k * 256 + ((c ^ v_swz(k)) << 4); }
-
-// A-operand fragment of K for S^T: key row kb + lane % 32, d = 16 kk + 8 (lane / 32) .. +7.
-__device__ __forceinline__ bf16x8 frag_k(const TPS_LDS char* s, int kb, int kk) {
-  const int lane = threadIdx.x & 63;
-  const int r = kb + (lane & 31);
-  return *reinterpret_cast<const TPS_LDS bf16x8*>(s + k_off(r, 2 * kk + (lane >> 5)));
-}
-
-// A-operand fragment of V^T: d column db + lane % 32, keys 16 kk + 8 (lane / 32) .. +7,
-// from the [key][d] tile through the transposing LDS read (within each 16-lane
-// group, lane i gets element i % 4 of the 8-byte loads of lanes i/4, 4 + i/4, ...).
-__device__ __forceinline__ bf16x8 frag_v(const TPS_LDS char* s, int db, int kk) {
-  const int lane = threadIdx.x & 63;
-  const int h = lane >> 4, q = lane & 15;
-  const int col = db + 16 * (h & 1) + 4 * (q & 3);
-  const int k0 = 16 * kk + 8 * (h >> 1) + (q >> 2);
-  const int c = col >> 3, byte_in = (col & 7) * 2;
-  const at_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS at_i16x4*)(s + v_off(k0, c) + byte_in));
-  const at_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS at_i16x4*)(s + v_off(k0 + 4, c) + byte_in));
-  const at_i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// Per-lane byte offsets (relative to a tile's first key row) of this wave's 4
-// copy blocks of one 64 x 128 tile: block 4 w + j covers rows 4 (4 w + j) .. +3;
-// lane L writes LDS bytes [16 L, 16 L + 16) of the block = row 4 B + L / 16,
-// physical chunk L % 16.
-template <bool V>
-__device__ __forceinline__ void tile_voffs(int64_t ld, uint32_t (&vo)[4]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 4 * (4 * wave + j) + (lane >> 4);
-    const int p = lane & 15;
-    const int c = V ? (p ^ v_swz(row)) : (p ^ (row & 15));
-    vo[j] = (uint32_t)((row * ld + 8 * c) * 2);
-  }
-}
-
-__device__ __forceinline__ void issue_tile(const __amdgpu_buffer_rsrc_t& r, const uint32_t (&vo)[4], uint32_t off,
-                                           TPS_LDS char* dst) {
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(dst + 1024 * (4 * wave + j)), 16, vo[j] + off, 0, 0,
-                                             0);
-}
-
-template <int VM>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(VM >= 0 && VM < 16, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(VM | (7 << 4) | (15 << 8));
-}
+constexpr float AT_LOG2E = LOG2E;
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf2(lo, hi); }
 
@@ -186,8 +124,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)vnrec,
                                                                       0x00020000);
   uint32_t kvo[4], vvo[4];
-  tile_voffs<false>(a.ldk, kvo);
-  tile_voffs<true>(a.ldv, vvo);
+  tile_voffs<true, 4>(a.ldk, kvo);    // K: row layout (read as rows)
+  tile_voffs<false, 4>(a.ldv, vvo);   // V: column layout (read transposed)
   const uint32_t kstep = (uint32_t)(AT_KT * a.ldk * 2), vstep = (uint32_t)(AT_KT * a.ldv * 2);
 
   issue_tile(kr, kvo, (uint32_t)t_begin * kstep, ring_k(0));
@@ -216,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
     for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_k(ks, 32 * kb, kk), qf[kk], st[kb], 0, 0, 0);
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<true>(ks, 32 * kb, kk), qf[kk], st[kb], 0, 0, 0);
     }
 
     // mask keys past the query (causal) or past the sequence; the scale (and
@@ -261,35 +199,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     }
 
-    // P^T fragments: k-step s covers keys 16 s .. 16 s + 15 = register groups
-    // q0 = 2 (s % 2), q0 + 1 of block s / 2; lanes < 32 hold keys +0..3 / +8..11,
-    // lanes >= 32 keys +4..7 / +12..15; one swap gives MFMA order (+0..7 | +8..15).
+    // P^T fragments: k-step s covers keys 16 s .. 16 s + 15 of block s / 2
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int kb = s >> 1, q0 = 2 * (s & 1);
-      uint32_t f[4];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(pk[kb][2 * q0 + w], pk[kb][2 * q0 + 2 + w], false, false);
-        f[w] = sw[0];
-        f[2 + w] = sw[1];
-      }
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{f[0], f[1], f[2], f[3]});
+      const bf16x8 pf = pk_frag(pk[s >> 1], s & 1);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_v(vs, 32 * db, s), pf, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<false>(vs, 32 * db, s), pf, o[db], 0, 0, 0);
     }
   }
 
   if (nchunks > 1) {   // partial: unnormalized O^T rows, running max (log2 domain) and sum
     float* slot = attn_slot(a, geo, qb, chunk);
     const int row = 32 * wave + (lane & 31);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(slot + row * 128 + 32 * db + 8 * q + 4 * (lane >> 5)) =
-            f32x4{o[db][4 * q], o[db][4 * q + 1], o[db][4 * q + 2], o[db][4 * q + 3]};
+    store_rows_f32(o, 1.f, slot + row * 128);
     if (lane < 32) {
       slot[128 * 128 + row] = m;
       slot[128 * 128 + 128 + row] = l;
@@ -306,26 +229,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
       *lse = (m + __log2f(l)) * 0.69314718055994531f;
     }
   }
-  uint16_t* orow = static_cast<uint16_t*>(a.o) + (row0 + min<int64_t>(my_tok, a.S - 1)) * a.ldo +
-                   (int64_t)head * AT_D + 8 * (lane >> 5);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    uint32_t pk[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) pk[q] = pack2(o[db][2 * q] * inv, o[db][2 * q + 1] * inv);
-#pragma unroll
-    for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const auto r = __builtin_amdgcn_permlane32_swap(pk[4 * pr + w], pk[4 * pr + 2 + w], false, false);
-        pk[4 * pr + w] = r[0];
-        pk[4 * pr + 2 + w] = r[1];
-      }
-    if (my_tok < a.S) {
-      *reinterpret_cast<u32x4*>(orow + 32 * db) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-      *reinterpret_cast<u32x4*>(orow + 32 * db + 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
-    }
-  }
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + (row0 + min<int64_t>(my_tok, a.S - 1)) * a.ldo + (int64_t)head * AT_D;
+  store_rows_bf16(o, inv, orow, my_tok < a.S);
 }
 
 // Merge of the chunks of every split query block: for each of the block's 128

@@ -155,6 +155,31 @@ struct AttnArgs {
   float* ws;         // per-chunk partial results (attn_fwd_workspace_bytes)
 };
 
+// Attention backward: the forward's arguments (o = the forward output, lse)
+// plus dO and the three gradients; ld, dq_ws and kv_ws point into the
+// workspace (attn_bwd_layout).
+struct AttnBwdArgs {
+  AttnArgs f;
+  const void* dout;
+  int64_t ldg;
+  void* dq;
+  int64_t lddq;
+  void* dk;
+  int64_t lddk;
+  void* dv;
+  int64_t lddv;
+  float* ld;        // [B][n_q][S] pairs (lse * log2 e, sum_d dO * O)
+  float* dq_ws;     // per-chunk partial dQ (when the forward chunking splits)
+  float* kv_ws;     // per (query head, query chunk) partial dK, dV
+  int kv_chunk_tiles;
+  int kv_max_chunks;
+};
+
+struct AttnBwdLayout {
+  int chunk_tiles, max_chunks, kv_chunk_tiles, kv_max_chunks;
+  size_t ld_bytes, dq_bytes, kv_bytes;
+};
+
 constexpr int kSpLnMaxN = 16384;   // row width the LayerNorm kernel holds in registers
 
 constexpr int kColpartRows = 64;   // rows per column-partial block
@@ -172,6 +197,8 @@ hipError_t launch_emb_fwd(int is_bf16, const EmbArgs& a, hipStream_t s);
 void attn_chunking(int64_t B, int64_t S, int n_q, int n_kv, int causal, int& chunk_tiles, int& max_chunks);
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int causal);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+void attn_bwd_layout(int64_t B, int64_t S, int n_q, int n_kv, int causal, AttnBwdLayout& L);
+hipError_t launch_attn_bwd(const AttnBwdArgs& p, hipStream_t s);
 int64_t emb_bwd_count_blocks(int64_t Vr);
 // cnt [Vr], btot [emb_bwd_count_blocks(Vr)], start [Vr + 1] and order [M]
 // int32 come from the caller's workspace.

@@ -14,7 +14,7 @@ from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_col
                tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
                tp_sp_reduce_scatter_ln, tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_embed_bwd,
                tp_vocab_embed_bwd_workspace_bytes, tp_vocab_embed_fwd, tp_attention_fwd,
-               tp_attention_fwd_workspace_bytes, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
+               tp_attention_fwd_workspace_bytes, tp_attention_bwd, tp_attention_bwd_workspace_bytes, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
                tp_vocab_ce_workspace_bytes)
 
 ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
@@ -240,3 +240,19 @@ def attention_fwd(q, k, v, n_q, n_kv, causal=True, scale=None, B=1):
     tp_attention_fwd(dtype_code(q), B, S, n_q, n_kv, 128, causal, scale, q, ld(q), k, ld(k), v, ld(v), o, ld(o), lse,
                      ws, n)
     return o, lse
+
+
+def attention_bwd(q, k, v, o, lse, do, n_q, n_kv, causal=True, scale=None, B=1):
+    """Gradients (dQ, dK, dV) of attention_fwd from its outputs o, lse and the output gradient do."""
+    rows = q.shape[0]
+    S = rows // B
+    scale = 1.0 / 128 ** 0.5 if scale is None else scale
+    do = aligned(do)
+    dq = empty_padded(rows, 128 * n_q, q.dtype, q.device)
+    dk = empty_padded(rows, 128 * n_kv, q.dtype, q.device)
+    dv = empty_padded(rows, 128 * n_kv, q.dtype, q.device)
+    n = tp_attention_bwd_workspace_bytes(B, S, n_q, n_kv, causal)
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    tp_attention_bwd(dtype_code(q), B, S, n_q, n_kv, 128, causal, scale, q, ld(q), k, ld(k), v, ld(v), o, ld(o), lse,
+                     do, ld(do), dq, ld(dq), dk, ld(dk), dv, ld(dv), ws, n)
+    return dq, dk, dv

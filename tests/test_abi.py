@@ -239,6 +239,29 @@ def test_attention_validation(lib):
     assert _rc("tp_attention_fwd", *a) == 2
 
 
+def test_attention_bwd_validation(lib):
+    sc = 1.0 / 128 ** 0.5
+    ws = tp.tp_attention_bwd_workspace_bytes(1, 8192, 4, 1, 1)
+    ld = 4 * 8192 * 8                                          # (lse2, D) pairs
+    dq = 256 * 8 * 128 * 128 * 4                               # dQ partials: 256 blocks x 8 key chunks
+    kv = 64 * 4 * 4 * 128 * 256 * 4                            # dK/dV partials: 64 key blocks x 4 heads x 4 chunks
+    assert ws == ld + dq + kv
+    assert tp.tp_attention_bwd_workspace_bytes(1, 8192, 4, 3, 1) == 0
+    base = [tp.TP_BF16, 1, 8192, 4, 1, 128, 1, sc, P, 768, P + 1024, 768, P + 1280, 768, P, 512, P, P, 512,
+            P, 512, P, 128, P, 128, P, ws, None]
+    a = list(base); a[0] = tp.TP_FP32
+    assert _rc("tp_attention_bwd", *a) == 4
+    for i in (14, 16, 17, 19, 21, 23):                         # O, lse, dO, dQ, dK, dV are required
+        a = list(base); a[i] = None
+        assert _rc("tp_attention_bwd", *a) == 1
+    a = list(base); a[26] = ws - 1
+    assert _rc("tp_attention_bwd", *a) == 6
+    a = list(base); a[22] = 120                                # ld(dK) < 128
+    assert _rc("tp_attention_bwd", *a) == 2
+    a = list(base); a[16] = P + 8                              # lse not 16-byte aligned
+    assert _rc("tp_attention_bwd", *a) == 3
+
+
 def test_bf16_operands_below_2gib(lib):
     # X [2^17, 2^13] bf16 spans exactly 2 GiB: rejected before any HIP call.
     K = 1 << 13

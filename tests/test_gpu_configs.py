@@ -300,6 +300,25 @@ def test_c3_attention_core_full_size():
     assert_close("lse", host64(lse[0])[:, ms], rl[:, ms], 1e-3)
 
 
+def test_c3_attention_backward_full_size():
+    # Backward of the rank's attention core over the 8192-token sequence (causal, GQA 4:1).
+    cfg = syn.C3
+    S, n_q, n_kv = cfg.M, 4, 1
+    qkv = syn.normal(3960, (S, cfg.n_qkv), 1.0, syn.BF16)
+    dO = syn.normal(3961, (S, 512), 1.0, syn.BF16)
+    d = dev(qkv)
+    q, k, v = d[:, :512], d[:, 512:640], d[:, 640:]
+    O, lse = ops.attention_fwd(q, k, v, n_q, n_kv, causal=True)
+    dq, dk, dv = ops.attention_bwd(q, k, v, O, lse, dev(dO), n_q, n_kv, causal=True)
+    torch.cuda.synchronize()
+    X = qkv.f64
+    rq, rk, rv = oracle.attention_bwd(X[:, :512], X[:, 512:640], X[:, 640:], dO.f64, n_q, n_kv, causal=True)
+    ms = sample_idx(S, 512, 21)
+    assert_close("dQ", rows(dq, ms), rq[ms], BF)
+    assert_close("dK", rows(dk, ms), rk[ms], BF)
+    assert_close("dV", rows(dv, ms), rv[ms], BF)
+
+
 def test_c5_vocab_embedding_shard_full_size():
     # Embedding shard 0 of 8 of the 151936 x 4096 table (18992 rows), 8192 tokens with ids
     # uniform over the full vocabulary: lookup compared in full, backward on the rows that

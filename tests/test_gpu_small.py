@@ -421,6 +421,37 @@ def test_attention_fwd_small(B, S, n_q, n_kv, causal):
         assert_close(f"lse seq {b}", host64(lse[b]), rl, 1e-3)
 
 
+ATTN_BWD_CASES = [(1, 1, 1, 1, True), (1, 37, 4, 1, True), (1, 200, 4, 1, True), (1, 300, 2, 1, True),
+                  (1, 130, 2, 2, False), (1, 256, 8, 1, True), (2, 100, 4, 1, True), (1, 1100, 4, 1, True),
+                  (1, 2200, 4, 1, True), (2, 700, 8, 2, False)]
+# (beyond 1024 keys the dQ pass is cut into key chunks; beyond 2048 queries the dK/dV pass into
+# query chunks)
+
+
+@pytest.mark.parametrize("B,S,n_q,n_kv,causal", ATTN_BWD_CASES)
+def test_attention_bwd_small(B, S, n_q, n_kv, causal):
+    seed = 13 * S + n_q + 5 * B
+    width = 128 * (n_q + 2 * n_kv)
+    qkv = syn.normal(seed, (B * S, width), 1.0, syn.BF16)
+    dO = syn.normal(seed + 1, (B * S, 128 * n_q), 1.0, syn.BF16)
+    d = dev(qkv)
+    q, k, v = d[:, :128 * n_q], d[:, 128 * n_q:128 * (n_q + n_kv)], d[:, 128 * (n_q + n_kv):]
+    O, lse = ops.attention_fwd(q, k, v, n_q, n_kv, causal=causal, B=B)
+    dq, dk, dv = ops.attention_bwd(q, k, v, O, lse, dev(dO), n_q, n_kv, causal=causal, B=B)
+    dq2, dk2, dv2 = ops.attention_bwd(q, k, v, O, lse, dev(dO), n_q, n_kv, causal=causal, B=B)
+    torch.cuda.synchronize()
+    X, G = qkv.f64, dO.f64
+    for b in range(B):
+        rs = slice(b * S, (b + 1) * S)
+        rq, rk, rv = oracle.attention_bwd(X[rs, :128 * n_q], X[rs, 128 * n_q:128 * (n_q + n_kv)],
+                                          X[rs, 128 * (n_q + n_kv):], G[rs], n_q, n_kv, causal=causal)
+        assert_close(f"dQ seq {b}", host64(dq[rs]), rq, TOL[syn.BF16])
+        assert_close(f"dK seq {b}", host64(dk[rs]), rk, TOL[syn.BF16])
+        assert_close(f"dV seq {b}", host64(dv[rs]), rv, TOL[syn.BF16])
+    for x, y in ((dq, dq2), (dk, dk2), (dv, dv2)):                  # fixed summation order
+        assert torch.equal(x.cpu(), y.cpu())
+
+
 def test_deterministic_bitwise():
     d = _inputs(syn.BF16, 520, 300, 1030, 3, "swiglu")
     outs = []
