@@ -235,39 +235,59 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
 
 // Merge of the chunks of every split query block: for each of the block's 128
 // rows, M = max m_c, L = sum l_c 2^(m_c - M), O = sum O_c 2^(m_c - M) / L in
-// ascending chunk order; lse = (M + log2 L) ln 2.  32 threads per row, 4 d each.
+// ascending chunk order; lse = (M + log2 L) ln 2.  A workgroup takes 8 rows of
+// one block (32 threads per row, 4 columns each); the chunks' values are loaded
+// 8 at a time before they are combined (past the last chunk the load repeats
+// it and is not used).
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   const AttnGeo geo = attn_geo(a);
-  const int64_t qb = blockIdx.x;
+  const int64_t qb = blockIdx.x >> 4;
   const int nchunks = (attn_tiles(a, geo, qb) + a.chunk_tiles - 1) / a.chunk_tiles;
   if (nchunks <= 1) return;
   const int g = (int)blockIdx.y / geo.nquad, quad = (int)blockIdx.y % geo.nquad;
   const int64_t b = blockIdx.z;
   const int d4 = 4 * (threadIdx.x & 31);
-  for (int pass = 0; pass < 16; ++pass) {
-    const int row = 8 * pass + (threadIdx.x >> 5);
-    const int w = row >> 5;
-    const int head = g * geo.group + quad * geo.hpw + (w % geo.hpw);
-    const int64_t tok = qb * geo.tq + 32 * (w / geo.hpw) + (row & 31);
-    if (tok >= a.S) continue;
-    float M = -INFINITY;
-    for (int c = 0; c < nchunks; ++c) M = fmaxf(M, attn_slot(a, geo, qb, c)[128 * 128 + row]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nchunks; ++c) {
-      const float* slot = attn_slot(a, geo, qb, c);
-      const float wgt = __builtin_amdgcn_exp2f(slot[128 * 128 + row] - Mu);
-      L += slot[128 * 128 + 128 + row] * wgt;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * 128 + d4);
+  const int row = 8 * (blockIdx.x & 15) + (threadIdx.x >> 5);
+  const int w = row >> 5;
+  const int head = g * geo.group + quad * geo.hpw + (w % geo.hpw);
+  const int64_t tok = qb * geo.tq + 32 * (w / geo.hpw) + (row & 31);
+  if (tok >= a.S) return;
+  const float* s0 = attn_slot(a, geo, qb, 0);
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < nchunks; c0 += 8) {
+    float mc[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += v[e] * wgt;
-    }
-    const float inv = 1.0f / L;
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + (b * a.S + tok) * a.ldo + (int64_t)head * AT_D + d4;
-    *reinterpret_cast<u32x2*>(orow) = u32x2{pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv)};
-    if (d4 == 0) a.lse[((int64_t)b * a.n_q + head) * a.S + tok] = (M + __log2f(L)) * 0.69314718055994531f;
+    for (int j = 0; j < 8; ++j) mc[j] = s0[min(c0 + j, nchunks - 1) * AT_SLOT + 128 * 128 + row];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) M = fmaxf(M, mc[j]);   // repeats of the last chunk change nothing
   }
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nchunks; c0 += 8) {
+    float mc[8], lc[8];
+    f32x4 oc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float* sl = s0 + min(c0 + j, nchunks - 1) * AT_SLOT;
+      mc[j] = sl[128 * 128 + row];
+      lc[j] = sl[128 * 128 + 128 + row];
+      oc[j] = *reinterpret_cast<const f32x4*>(sl + row * 128 + d4);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (c0 + j < nchunks) {
+        const float wgt = __builtin_amdgcn_exp2f(mc[j] - Mu);
+        L += lc[j] * wgt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += oc[j][e] * wgt;
+      }
+    }
+  }
+  const float inv = 1.0f / L;
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + (b * a.S + tok) * a.ldo + (int64_t)head * AT_D + d4;
+  *reinterpret_cast<u32x2*>(orow) = u32x2{pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv)};
+  if (d4 == 0) a.lse[((int64_t)b * a.n_q + head) * a.S + tok] = (M + __log2f(L)) * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -316,7 +336,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
   const unsigned gy = (unsigned)(a.n_kv * (group / hpw));
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)(nqb * a.max_chunks), gy, (unsigned)a.B), dim3(256), 0, s, a);
   if (a.max_chunks > 1)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)nqb, gy, (unsigned)a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(nqb * 16), gy, (unsigned)a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

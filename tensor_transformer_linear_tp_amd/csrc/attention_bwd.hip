@@ -196,32 +196,39 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const AttnBwdArgs p
   store_rows_bf16(dq, a.scale, out, my_tok < a.S);
 }
 
-// Ordered sum of the key chunks of every split query block, times scale.
+// Ordered sum of the key chunks of every split query block, times scale: a
+// workgroup takes 8 rows of one block (32 threads per row, 4 columns each) and
+// loads 8 chunks' values before adding them.
 __global__ __launch_bounds__(256) void attn_bwd_dq_combine_kernel(const AttnBwdArgs p) {
   const AttnArgs& a = p.f;
   const Geo geo = geo_of(a);
-  const int64_t qb = blockIdx.x;
+  const int64_t qb = blockIdx.x >> 4;
   const int nchunks = (key_tiles(a, geo, qb) + a.chunk_tiles - 1) / a.chunk_tiles;
   if (nchunks <= 1) return;
   const int g = (int)blockIdx.y / geo.nquad, quad = (int)blockIdx.y % geo.nquad;
   const int64_t b = blockIdx.z;
   const int d4 = 4 * (threadIdx.x & 31);
-  for (int pass = 0; pass < 16; ++pass) {
-    const int row = 8 * pass + (threadIdx.x >> 5);
-    const int w = row >> 5;
-    const int head = g * geo.group + quad * geo.hpw + (w % geo.hpw);
-    const int64_t tok = qb * geo.tq + 32 * (w / geo.hpw) + (row & 31);
-    if (tok >= a.S) continue;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(dq_slot(p, geo, qb, 0) + row * 128 + d4);
-    for (int ch = 1; ch < nchunks; ++ch) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(dq_slot(p, geo, qb, ch) + row * 128 + d4);
+  const int row = 8 * (blockIdx.x & 15) + (threadIdx.x >> 5);
+  const int w = row >> 5;
+  const int head = g * geo.group + quad * geo.hpw + (w % geo.hpw);
+  const int64_t tok = qb * geo.tq + 32 * (w / geo.hpw) + (row & 31);
+  if (tok >= a.S) return;
+  const float* s0 = dq_slot(p, geo, qb, 0) + row * 128 + d4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nchunks; c0 += 8) {
+    f32x4 v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += v[e];
-    }
-    uint16_t* out = static_cast<uint16_t*>(p.dq) + (b * a.S + tok) * p.lddq + (int64_t)head * HD + d4;
-    *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf2(acc[0] * a.scale, acc[1] * a.scale),
-                                           pack_bf2(acc[2] * a.scale, acc[3] * a.scale)};
+    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const f32x4*>(s0 + min(c0 + j, nchunks - 1) * DQ_SLOT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < nchunks) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += v[j][e];
+      }
   }
+  uint16_t* out = static_cast<uint16_t*>(p.dq) + (b * a.S + tok) * p.lddq + (int64_t)head * HD + d4;
+  *reinterpret_cast<u32x2*>(out) =
+      u32x2{pack_bf2(acc[0] * a.scale, acc[1] * a.scale), pack_bf2(acc[2] * a.scale, acc[3] * a.scale)};
 }
 
 // ---- dK, dV -------------------------------------------------------------------------
@@ -366,31 +373,40 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
 }
 
 // dK, dV rows of every key block: ordered sum over the query heads of the group
-// and their query chunks, rounded to bf16.  64 threads per row, 4 columns each.
+// and their query chunks (head-major), rounded to bf16.  A workgroup takes 4
+// rows (64 threads per row, 4 of the 256 [dK | dV] columns each) and loads 8
+// partials before adding them.
 __global__ __launch_bounds__(256) void attn_bwd_dkv_combine_kernel(const AttnBwdArgs p) {
   const AttnArgs& a = p.f;
-  const int64_t kbk = blockIdx.x;
+  const int64_t kbk = blockIdx.x >> 5;
   const int g = (int)blockIdx.y;
   const int64_t b = blockIdx.z;
   const int group = a.n_q / a.n_kv;
   const int nchunks = (query_tiles(a, kbk) + p.kv_chunk_tiles - 1) / p.kv_chunk_tiles;
   const int col = 4 * (threadIdx.x & 63);   // 0..252 over [dK | dV]
-  for (int pass = 0; pass < 32; ++pass) {
-    const int row = 4 * pass + (threadIdx.x >> 6);
-    const int64_t key = 128 * kbk + row;
-    if (key >= a.S) continue;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int hg = 0; hg < group; ++hg)
-      for (int ch = 0; ch < nchunks; ++ch) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(kv_slot(p, b, g, kbk, hg, ch) + row * 256 + col);
+  const int row = 4 * (blockIdx.x & 31) + (threadIdx.x >> 6);
+  const int64_t key = 128 * kbk + row;
+  if (key >= a.S) return;
+  const int n = group * nchunks;            // partial j = (head j / nchunks, chunk j % nchunks)
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < n; j0 += 8) {
+    f32x4 v[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    for (int j = 0; j < 8; ++j) {
+      const int jj = min(j0 + j, n - 1);
+      v[j] = *reinterpret_cast<const f32x4*>(kv_slot(p, b, g, kbk, jj / nchunks, jj % nchunks) + row * 256 + col);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j0 + j < n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += v[j][e];
       }
-    const bool is_k = col < 128;
-    uint16_t* out = is_k ? static_cast<uint16_t*>(p.dk) + (b * a.S + key) * p.lddk + (int64_t)g * HD + col
-                         : static_cast<uint16_t*>(p.dv) + (b * a.S + key) * p.lddv + (int64_t)g * HD + (col - 128);
-    *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
   }
+  const bool is_k = col < 128;
+  uint16_t* out = is_k ? static_cast<uint16_t*>(p.dk) + (b * a.S + key) * p.lddk + (int64_t)g * HD + col
+                       : static_cast<uint16_t*>(p.dv) + (b * a.S + key) * p.lddv + (int64_t)g * HD + (col - 128);
+  *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
 }
 
 }  // namespace
@@ -427,11 +443,11 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)(nqb * a.max_chunks), gy, (unsigned)a.B), dim3(256), 0, s, p);
   if (a.max_chunks > 1)
-    hipLaunchKernelGGL(attn_bwd_dq_combine_kernel, dim3((unsigned)nqb, gy, (unsigned)a.B), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_bwd_dq_combine_kernel, dim3((unsigned)(nqb * 16), gy, (unsigned)a.B), dim3(256), 0, s, p);
   hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)(nkb * p.kv_max_chunks), (unsigned)a.n_q, (unsigned)a.B),
                      dim3(256), 0, s, p);
-  hipLaunchKernelGGL(attn_bwd_dkv_combine_kernel, dim3((unsigned)nkb, (unsigned)a.n_kv, (unsigned)a.B), dim3(256), 0,
-                     s, p);
+  hipLaunchKernelGGL(attn_bwd_dkv_combine_kernel, dim3((unsigned)(nkb * 32), (unsigned)a.n_kv, (unsigned)a.B),
+                     dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
