@@ -21,6 +21,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "attention_common.hpp"
 #include "device_common.hpp"
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const AttnBwdArgs p
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int key = 32 * kb + 8 * ((r + e) >> 2) + 4 * (lane >> 5) + ((r + e) & 3);
-          const float pr = key > kmax ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(st[r + e], c, -lse2));
+          const float pr = __builtin_amdgcn_exp2f(key > kmax ? -INFINITY : __builtin_fmaf(st[r + e], c, -lse2));
           ds[e] = pr * (dp[r + e] - Dv);
         }
         pk[kb][r >> 1] = pack_bf2(ds[0], ds[1]);
@@ -232,7 +233,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_combine_kernel(const AttnBwdA
 }
 
 // ---- dK, dV -------------------------------------------------------------------------
-__shared__ __attribute__((aligned(1024))) char bkv_ring[2 * QSTAGE];
+constexpr int KV_NSTAGE = 2;
+
+__shared__ __attribute__((aligned(1024))) char bkv_ring[KV_NSTAGE * QSTAGE];
 
 __device__ __forceinline__ TPS_LDS char* bkv_q(int st) { return (TPS_LDS char*)bkv_ring + st * QSTAGE; }
 __device__ __forceinline__ TPS_LDS char* bkv_g(int st) { return bkv_q(st) + QTILE; }
@@ -306,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (TPS_LDS void*)bkv_l(st), 4, (uint32_t)(qt * 8 + 4 * lane), 0, 0,
                                                0);
   };
-  issue(0, 0);
+  for (int t = 0; t < KV_NSTAGE - 1 && t < nt; ++t) issue(t, t);
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -318,43 +321,55 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
 
   for (int t = 0; t < nt; ++t) {
     wait_vm<0>();
-    __syncthreads();
-    if (t + 1 < nt) issue(t + 1, (t + 1) & 1);
-    const TPS_LDS char* qs = bkv_q(t & 1);
-    const TPS_LDS char* gs = bkv_g(t & 1);
-    const TPS_LDS float* ls = (const TPS_LDS float*)bkv_l(t & 1);
+    __syncthreads();   // tile t visible to all waves; the other stage is free
+    if (t + KV_NSTAGE - 1 < nt) issue(t + KV_NSTAGE - 1, (t + KV_NSTAGE - 1) % KV_NSTAGE);
+    const TPS_LDS char* qs = bkv_q(t % KV_NSTAGE);
+    const TPS_LDS char* gs = bkv_g(t % KV_NSTAGE);
+    const TPS_LDS float* ls = (const TPS_LDS float*)bkv_l(t % KV_NSTAGE);
 
-    f32x16 s = f32x16{0.f}, dp = f32x16{0.f};
+    f32x16 s = f32x16{0.f}, dp = f32x16{0.f};   // two independent chains, interleaved
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<true>(qs, 0, kk), kf[kk], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<true>(gs, 0, kk), vf[kk], dp, 0, 0, 0);
     }
-    // lane: key my_key, queries qt + 8 (r / 4) + 4 (lane / 32) + r % 4
+    // lane: key my_key, queries qt + 8 (r / 4) + 4 (lane / 32) + r % 4.  Every pair of the
+    // tile is live when its queries lie inside the sequence, the wave's keys do, and (causal)
+    // its first query is not before the wave's last key; otherwise mask per element.
     const int64_t qt = q_begin + (int64_t)(t_begin + t) * QT;
-    const int64_t lim = a.S - 1 - qt;                           // last query of the sequence, tile-relative
-    const int64_t first = a.causal ? my_key - qt : INT_MIN;    // first query that sees this key
+    const bool full = qt + QT <= a.S && key_w + 32 <= a.S && (!a.causal || qt >= key_w + 31);
+    const int lim = (int)min<int64_t>(a.S - 1 - qt, INT_MAX);                       // last query, tile-relative
+    const int first = a.causal ? (int)max<int64_t>(min<int64_t>(my_key - qt, INT_MAX), INT_MIN) : INT_MIN;
+    const bool key_ok = my_key < a.S;
     uint32_t pp[8], pd[8];
+    // P = 2^(S c - lse2) (masked pairs: 2^-inf = 0), dS = P (dP - D); two straight-line
+    // versions, chosen per tile, so that unmasked tiles carry no per-element tests
+    auto softmax_grad = [&](auto masked) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int qi = 8 * q + 4 * (lane >> 5);
-      const f32x4 l01 = *reinterpret_cast<const TPS_LDS f32x4*>(ls + 2 * qi);
-      const f32x4 l23 = *reinterpret_cast<const TPS_LDS f32x4*>(ls + 2 * qi + 4);
-      const float lse2[4] = {l01[0], l01[2], l23[0], l23[2]};
-      const float dd[4] = {l01[1], l01[3], l23[1], l23[3]};
-      float pv[4], dsv[4];
+      for (int q = 0; q < 4; ++q) {
+        const int qi = 8 * q + 4 * (lane >> 5);
+        const f32x4 l01 = *reinterpret_cast<const TPS_LDS f32x4*>(ls + 2 * qi);
+        const f32x4 l23 = *reinterpret_cast<const TPS_LDS f32x4*>(ls + 2 * qi + 4);
+        const float lse2[4] = {l01[0], l01[2], l23[0], l23[2]};
+        const float dd[4] = {l01[1], l01[3], l23[1], l23[3]};
+        float pv[4], dsv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q + e;
-        const bool live = (qi + e) <= lim && (qi + e) >= first && my_key < a.S;
-        pv[e] = live ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2[e])) : 0.f;
-        dsv[e] = pv[e] * (dp[r] - dd[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q + e;
+          float x = __builtin_fmaf(s[r], c, -lse2[e]);
+          if constexpr (decltype(masked)::value)
+            x = ((qi + e) <= lim && (qi + e) >= first && key_ok) ? x : -INFINITY;
+          pv[e] = __builtin_amdgcn_exp2f(x);
+          dsv[e] = pv[e] * (dp[r] - dd[e]);
+        }
+        pp[2 * q] = pack_bf2(pv[0], pv[1]);
+        pp[2 * q + 1] = pack_bf2(pv[2], pv[3]);
+        pd[2 * q] = pack_bf2(dsv[0], dsv[1]);
+        pd[2 * q + 1] = pack_bf2(dsv[2], dsv[3]);
       }
-      pp[2 * q] = pack_bf2(pv[0], pv[1]);
-      pp[2 * q + 1] = pack_bf2(pv[2], pv[3]);
-      pd[2 * q] = pack_bf2(dsv[0], dsv[1]);
-      pd[2 * q + 1] = pack_bf2(dsv[2], dsv[3]);
-    }
+    };
+    if (full) softmax_grad(std::false_type{});
+    else softmax_grad(std::true_type{});
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
       const bf16x8 pf = pk_frag(pp, ss);
