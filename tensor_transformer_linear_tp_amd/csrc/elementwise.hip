@@ -5,6 +5,7 @@
 // and LayerNorm.  Each thread moves 8 consecutive columns with 16-byte
 // accesses when the row segment is whole and aligned.
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 #include "device_common.hpp"
@@ -86,6 +87,104 @@ __device__ __forceinline__ float to_f<uint16_t>(uint16_t x) { return bf2f(x); }
 template <>
 __device__ __forceinline__ float to_f<float>(float x) { return x; }
 
+// 8 columns at p: one 16-byte-aligned vector load when FULL, else the first
+// nv elements one by one (the rest 0).  Callers pass 16-byte-aligned p when
+// FULL (base pointers, leading dimensions and strides are validated so).
+template <bool FULL, typename T>
+__device__ __forceinline__ void ld8(const T* p, int nv, float (&v)[8]) {
+  if constexpr (FULL) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = x[e];
+        v[4 + e] = y[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < nv ? to_f<T>(p[e]) : 0.f;
+  }
+}
+
+// Store of 8 columns at p: one 16-byte vector store when FULL (p 16-byte
+// aligned), else the first nv elements.
+template <bool FULL, typename T>
+__device__ __forceinline__ void st8(T* p, int nv, const float (&v)[8]) {
+  if constexpr (FULL && sizeof(T) == 2) {
+    *reinterpret_cast<u32x4*>(p) =
+        u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+  } else if constexpr (FULL) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < nv) p[e] = from_f<T>(v[e]);
+  }
+}
+
+// Rows ty, ty + 8, ... (64 rows) of row block rb at columns n .. n + 7 of the
+// activation backward, RB rows at a time with all their loads issued first
+// (past the matrix the row index repeats the last row: loaded, not used);
+// column sums of dP accumulate into cg (gate or single) and cu (up).
+template <bool FULL, typename T>
+__device__ __forceinline__ void act_rows(const ActBwdArgs& a, int64_t rb, int ty, int64_t n, int nv, float (&cg)[8],
+                                         float (&cu)[8]) {
+  constexpr int RB = 4;
+  const bool swiglu = a.act == E_SWIGLU;
+  const T* dY = static_cast<const T*>(a.dY);
+  // Without an activation there is no Pre (it may be NULL): the pre-activation
+  // loads then read dY again (values unused), so every load is unconditional.
+  const bool has_pre = a.act != E_STORE;
+  const T* pre = has_pre ? static_cast<const T*>(a.pre) : dY;
+  const int64_t ldpre = has_pre ? a.ldpre : a.lddy;
+#pragma unroll
+  for (int q0 = 0; q0 < kColpartRows / 8; q0 += RB) {
+    float dy[RB][8], gg[RB][8], uu[RB][8];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int64_t m = min<int64_t>(rb * kColpartRows + ty + 8 * (q0 + j), a.M - 1);
+      ld8<FULL>(dY + m * a.lddy + n, nv, dy[j]);
+      ld8<FULL>(pre + m * ldpre + n, nv, gg[j]);
+      ld8<FULL>(pre + m * ldpre + (swiglu ? a.N : 0) + n, nv, uu[j]);   // up half (SwiGLU only)
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int64_t m = rb * kColpartRows + ty + 8 * (q0 + j);
+      const bool live = m < a.M;
+      float g[8], u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (a.act == E_STORE) {
+          g[e] = dy[j][e];
+          u[e] = 0.f;
+        } else if (a.act == E_GELU) {
+          g[e] = dy[j][e] * gelu_grad_f(gg[j][e]);
+          u[e] = 0.f;
+        } else {
+          const float sg = sigmoid_f(gg[j][e]);
+          g[e] = dy[j][e] * uu[j][e] * (sg * (1.0f + gg[j][e] * (1.0f - sg)));
+          u[e] = dy[j][e] * (gg[j][e] * sg);
+        }
+        cg[e] += live ? g[e] : 0.f;
+        cu[e] += live ? u[e] : 0.f;
+      }
+      if (live && a.dp) {
+        st8<FULL>(static_cast<T*>(a.dp) + m * a.lddp + n, nv, g);
+        if (swiglu) st8<FULL>(static_cast<T*>(a.dp_up) + m * a.lddp + n, nv, u);
+      }
+    }
+  }
+}
+
 // Block (x = row block, y = column block): 32 column-threads x 8 row-threads
 // over [64 rows] x [256 columns].
 template <typename T>
@@ -102,40 +201,8 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(const ActBwdArgs a) {
     const int nv = (int)min<int64_t>(8, a.N - n);
     const T* dY = static_cast<const T*>(a.dY);
     const T* pre = static_cast<const T*>(a.pre);
-    for (int q = 0; q < kColpartRows / 8; ++q) {
-      const int64_t m = rb * kColpartRows + ty + 8 * q;
-      if (m >= a.M) break;
-      float dy[8], g[8], u[8];
-      load8<T>(dY + m * a.lddy + n, nv, dy);
-      if (a.act == E_STORE) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) g[e] = dy[e];
-      } else if (a.act == E_GELU) {
-        float p[8];
-        load8<T>(pre + m * a.ldpre + n, nv, p);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) g[e] = dy[e] * gelu_grad_f(p[e]);
-      } else {
-        float gg[8], uu[8];
-        load8<T>(pre + m * a.ldpre + n, nv, gg);
-        load8<T>(pre + m * a.ldpre + a.N + n, nv, uu);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float s = sigmoid_f(gg[e]);
-          g[e] = dy[e] * uu[e] * (s * (1.0f + gg[e] * (1.0f - s)));
-          u[e] = dy[e] * (gg[e] * s);
-        }
-      }
-      if (a.dp) {
-        store8<T>(static_cast<T*>(a.dp) + m * a.lddp + n, nv, g);
-        if (swiglu) store8<T>(static_cast<T*>(a.dp_up) + m * a.lddp + n, nv, u);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        cg[e] += g[e];
-        if (swiglu) cu[e] += u[e];
-      }
-    }
+    if (nv == 8) act_rows<true, T>(a, rb, ty, n, nv, cg, cu);
+    else act_rows<false, T>(a, rb, ty, n, nv, cg, cu);
   }
   if (!a.colpart) return;   // uniform across the block
 #pragma unroll
@@ -166,33 +233,6 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* colpa
   float s = 0.f;
   for (int64_t rb = 0; rb < nrb; ++rb) s += colpart[(rb * 2 + part) * ldcp + n];
   out[n] = from_f<T>(s);
-}
-
-// 8 columns at p: one 16-byte-aligned vector load when FULL, else the first
-// nv elements one by one (the rest 0).  Callers pass 16-byte-aligned p when
-// FULL (base pointers, leading dimensions and strides are validated so).
-template <bool FULL, typename T>
-__device__ __forceinline__ void ld8(const T* p, int nv, float (&v)[8]) {
-  if constexpr (FULL) {
-    if constexpr (sizeof(T) == 2) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = __uint_as_float(w[e] << 16);
-        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-      }
-    } else {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = x[e];
-        v[4 + e] = y[e];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = e < nv ? to_f<T>(p[e]) : 0.f;
-  }
 }
 
 // acc = sum_{i<t} p[i * stride] over 8 columns, fp32, in ascending i.  The
