@@ -293,9 +293,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
 }  // namespace
 
 // Chunking (a function of the shape only, so the workspace size is known
-// without a device): causal key ranges are cut into chunks of 16 tiles (1024
-// keys); without the mask every block has the same work, and the range is cut
-// only when there are fewer than 512 workgroups (two per CU of an MI355X).
+// without a device).  Causal: the blocks' key ranges differ in length, so
+// they are cut into chunks of about 1.2x the mean work per workgroup slot
+// (512 slots: two workgroups on each CU of an MI355X), which keeps the number
+// of workgroups near one round of slots and lets the short chunks fill the
+// gaps.  Without the mask every block has the same work, and the range is cut
+// only when there are fewer than 512 workgroups.
 constexpr int64_t AT_TARGET_WGS = 512;
 
 void attn_chunking(int64_t B, int64_t S, int n_q, int n_kv, int causal, int& chunk_tiles, int& max_chunks) {
@@ -306,7 +309,11 @@ void attn_chunking(int64_t B, int64_t S, int n_q, int n_kv, int causal, int& chu
   const int64_t nt_max = (S + AT_KT - 1) / AT_KT;
   int64_t c;
   if (causal) {
-    c = 16;
+    int64_t tiles = 0;   // key tiles over all query blocks of one (sequence, head group)
+    for (int64_t qb = 0; qb < nqb; ++qb) tiles += (std::min<int64_t>(S, (qb + 1) * tq) + AT_KT - 1) / AT_KT;
+    const int64_t groups = (int64_t)n_kv * (group / hpw) * B;
+    c = (12 * tiles * groups + 10 * AT_TARGET_WGS - 1) / (10 * AT_TARGET_WGS);
+    c = std::max<int64_t>(c, 8);
   } else {
     const int64_t blocks = nqb * n_kv * (group / hpw) * B;
     const int64_t want = std::max<int64_t>(1, (AT_TARGET_WGS + blocks - 1) / blocks);

@@ -205,9 +205,10 @@ def test_attention_validation(lib):
     sc = 1.0 / 128 ** 0.5
     # packed QKV [8192, 768]: 4 query heads, 1 KV head
     ws = tp.tp_attention_fwd_workspace_bytes(1, 8192, 4, 1, 1)
-    # 256 query blocks of 32 tokens x 4 heads, up to 8 chunks of 1024 keys, 130 x 128 floats per chunk
-    assert ws == 256 * 8 * (128 * 128 + 256) * 4
-    assert tp.tp_attention_fwd_workspace_bytes(1, 1024, 4, 1, 1) == 0          # one chunk: no workspace
+    # 256 query blocks of 32 tokens x 4 heads; causal chunks of ceil(1.2 x 16512 key tiles / 512) = 39
+    # tiles, so up to 4 chunks per block; 130 x 128 floats per chunk
+    assert ws == 256 * 4 * (128 * 128 + 256) * 4
+    assert tp.tp_attention_fwd_workspace_bytes(1, 512, 4, 1, 1) == 0           # one chunk: no workspace
     assert tp.tp_attention_fwd_workspace_bytes(1, 8192, 4, 3, 1) == 0          # invalid shape
     base = [tp.TP_BF16, 1, 8192, 4, 1, 128, 1, sc, P, 768, P + 1024, 768, P + 1280, 768, P, 512, P, P, ws, None]
     a = list(base); a[18] = ws - 1
@@ -243,7 +244,7 @@ def test_attention_bwd_validation(lib):
     sc = 1.0 / 128 ** 0.5
     ws = tp.tp_attention_bwd_workspace_bytes(1, 8192, 4, 1, 1)
     ld = 4 * 8192 * 8                                          # (lse2, D) pairs
-    dq = 256 * 8 * 128 * 128 * 4                               # dQ partials: 256 blocks x 8 key chunks
+    dq = 256 * 4 * 128 * 128 * 4                               # dQ partials: 256 blocks x 4 key chunks
     kv = 64 * 4 * 4 * 128 * 256 * 4                            # dK/dV partials: 64 key blocks x 4 heads x 4 chunks
     assert ws == ld + dq + kv
     assert tp.tp_attention_bwd_workspace_bytes(1, 8192, 4, 3, 1) == 0
