@@ -124,8 +124,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)vnrec,
                                                                       0x00020000);
   uint32_t kvo[4], vvo[4];
-  tile_voffs<true, 4>(a.ldk, kvo);    // K: row layout (read as rows)
-  tile_voffs<false, 4>(a.ldv, vvo);   // V: column layout (read transposed)
+  tile_voffs<LAY_ROW, 4>(a.ldk, kvo);   // K: read as rows
+  tile_voffs<LAY_COL, 4>(a.ldv, vvo);   // V: read transposed
   const uint32_t kstep = (uint32_t)(AT_KT * a.ldk * 2), vstep = (uint32_t)(AT_KT * a.ldv * 2);
 
   issue_tile(kr, kvo, (uint32_t)t_begin * kstep, ring_k(0));
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
     for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<true>(ks, 32 * kb, kk), qf[kk], st[kb], 0, 0, 0);
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<LAY_ROW>(ks, 32 * kb, kk), qf[kk], st[kb], 0, 0, 0);
     }
 
     // mask keys past the query (causal) or past the sequence; the scale (and
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
       const bf16x8 pf = pk_frag(pk[s >> 1], s & 1);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<false>(vs, 32 * db, s), pf, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<LAY_COL>(vs, 32 * db, s), pf, o[db], 0, 0, 0);
     }
   }
 

@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const AttnBwdArgs p
   const __amdgpu_buffer_rsrc_t kr = rsrc(kbase, (uint32_t)(((a.S - 1) * a.ldk + HD) * 2));
   const __amdgpu_buffer_rsrc_t vr = rsrc(vbase, (uint32_t)(((a.S - 1) * a.ldv + HD) * 2));
   uint32_t kvo[4], vvo[4];
-  tile_voffs<true, 4>(a.ldk, kvo);   // K: read as rows (S^T) and as columns (dQ)
-  tile_voffs<true, 4>(a.ldv, vvo);   // V: read as rows (dP^T)
+  tile_voffs<LAY_BOTH, 4>(a.ldk, kvo);   // K: read as rows (S^T) and as columns (dQ)
+  tile_voffs<LAY_ROW, 4>(a.ldv, vvo);    // V: read as rows (dP^T)
   const uint32_t kstep = (uint32_t)(KT * a.ldk * 2), vstep = (uint32_t)(KT * a.ldv * 2);
   issue_tile(kr, kvo, (uint32_t)t_begin * kstep, bq_k(0));
   issue_tile(vr, vvo, (uint32_t)t_begin * vstep, bq_v(0));
@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const AttnBwdArgs p
       f32x16 st = f32x16{0.f}, dp = f32x16{0.f};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<true>(ks, 32 * kb, kk), qf[kk], st, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<true>(vs, 32 * kb, kk), gf[kk], dp, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<LAY_BOTH>(ks, 32 * kb, kk), qf[kk], st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<LAY_ROW>(vs, 32 * kb, kk), gf[kk], dp, 0, 0, 0);
       }
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const AttnBwdArgs p
       const bf16x8 df = pk_frag(pk[s >> 1], s & 1);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<true>(ks, 32 * db, s), df, dq[db], 0, 0, 0);
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<LAY_BOTH>(ks, 32 * db, s), df, dq[db], 0, 0, 0);
     }
   }
 
@@ -296,8 +296,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
   const __amdgpu_buffer_rsrc_t gr = rsrc(gbase, (uint32_t)(((a.S - 1) * p.ldg + HD) * 2));
   const __amdgpu_buffer_rsrc_t lr = rsrc(lbase, (uint32_t)(a.S * 8));
   uint32_t qvo[2], gvo[2];
-  tile_voffs<true, 2>(a.ldq, qvo);
-  tile_voffs<true, 2>(p.ldg, gvo);
+  tile_voffs<LAY_BOTH, 2>(a.ldq, qvo);
+  tile_voffs<LAY_BOTH, 2>(p.ldg, gvo);
   const uint32_t qstep = (uint32_t)(QT * a.ldq * 2), gstep = (uint32_t)(QT * p.ldg * 2);
 
   auto issue = [&](int t, int st) {
@@ -330,8 +330,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
     f32x16 s = f32x16{0.f}, dp = f32x16{0.f};   // two independent chains, interleaved
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<true>(qs, 0, kk), kf[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<true>(gs, 0, kk), vf[kk], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<LAY_BOTH>(qs, 0, kk), kf[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<LAY_BOTH>(gs, 0, kk), vf[kk], dp, 0, 0, 0);
     }
     // lane: key my_key, queries qt + 8 (r / 4) + 4 (lane / 32) + r % 4.  Every pair of the
     // tile is live when its queries lie inside the sequence, the wave's keys do, and (causal)
@@ -376,8 +376,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
       const bf16x8 df = pk_frag(pd, ss);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<true>(gs, 32 * db, ss), pf, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<true>(qs, 32 * db, ss), df, dk[db], 0, 0, 0);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<LAY_BOTH>(gs, 32 * db, ss), pf, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<LAY_BOTH>(qs, 32 * db, ss), df, dk[db], 0, 0, 0);
       }
     }
   }

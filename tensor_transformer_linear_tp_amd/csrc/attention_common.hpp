@@ -23,42 +23,52 @@ constexpr float LN2 = 0.69314718055994531f;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 
-// [rows][128] bf16 tiles, 256-byte rows of 16 chunks of 16 bytes.
-// Row layout (ROWSWZ): chunk c of row r at c ^ (r % 16): 8 consecutive rows
-// reading one logical chunk (ds_read_b128) hit distinct banks.
-// Column layout (!ROWSWZ): rows r % 4 = 0,1,2,3 XOR the chunk with 0,6,10,12,
-// the pattern the transposing read uses without bank conflicts.
-template <bool ROWSWZ>
+// [rows][128] bf16 tiles, 256-byte rows of 16 chunks of 16 bytes; chunk c of
+// row r sits at c ^ swz(r).  Layouts:
+//   LAY_ROW:  swz = r % 16 -- 16 consecutive rows reading one logical chunk
+//             (ds_read_b128) hit distinct banks;
+//   LAY_COL:  rows r % 4 = 0,1,2,3 XOR with 0,6,10,12 -- the pattern the
+//             transposing read uses without bank conflicts;
+//   LAY_BOTH: swz = 2 (r % 8) + (r / 8) % 2 -- distinct over 16 consecutive
+//             rows (row reads), and over the 4 rows x 2 neighbouring chunks a
+//             16-lane group of the transposing read touches (an even swz set
+//             maps the even chunk to even slots and the odd one to odd slots),
+//             for tiles that are read both ways.
+enum : int { LAY_ROW = 0, LAY_COL = 1, LAY_BOTH = 2 };
+
+template <int LAY>
 __device__ __forceinline__ int swz(int r) {
-  return ROWSWZ ? (r & 15) : ((0xCA60 >> ((r & 3) * 4)) & 15);
+  if constexpr (LAY == LAY_ROW) return r & 15;
+  else if constexpr (LAY == LAY_COL) return (0xCA60 >> ((r & 3) * 4)) & 15;
+  else return ((r & 7) << 1) | ((r >> 3) & 1);
 }
-template <bool ROWSWZ>
+template <int LAY>
 __device__ __forceinline__ int toff(int r, int c) {
-  return r * 256 + ((c ^ swz<ROWSWZ>(r)) << 4);
+  return r * 256 + ((c ^ swz<LAY>(r)) << 4);
 }
 
 // Fragment with the tile's rows as MFMA rows/columns: row rb + lane % 32,
 // k = columns 16 kk + 8 (lane / 32) .. +7.
-template <bool ROWSWZ>
+template <int LAY>
 __device__ __forceinline__ bf16x8 frag_rows(const TPS_LDS char* s, int rb, int kk) {
   const int lane = threadIdx.x & 63;
   const int r = rb + (lane & 31);
-  return *reinterpret_cast<const TPS_LDS bf16x8*>(s + toff<ROWSWZ>(r, 2 * kk + (lane >> 5)));
+  return *reinterpret_cast<const TPS_LDS bf16x8*>(s + toff<LAY>(r, 2 * kk + (lane >> 5)));
 }
 
 // Fragment with the tile's columns as MFMA rows/columns: column cb + lane % 32,
 // k = rows 16 kk + 8 (lane / 32) .. +7, through ds_read_b64_tr_b16 (within
 // each 16-lane group, lane i gets element i % 4 of the 8-byte loads of lanes
 // i/4, 4 + i/4, 8 + i/4, 12 + i/4).
-template <bool ROWSWZ>
+template <int LAY>
 __device__ __forceinline__ bf16x8 frag_cols(const TPS_LDS char* s, int cb, int kk) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 4, q = lane & 15;
   const int col = cb + 16 * (h & 1) + 4 * (q & 3);
   const int k0 = 16 * kk + 8 * (h >> 1) + (q >> 2);
   const int c = col >> 3, byte_in = (col & 7) * 2;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS i16x4*)(s + toff<ROWSWZ>(k0, c) + byte_in));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS i16x4*)(s + toff<ROWSWZ>(k0 + 4, c) + byte_in));
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS i16x4*)(s + toff<LAY>(k0, c) + byte_in));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS i16x4*)(s + toff<LAY>(k0 + 4, c) + byte_in));
   const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -66,13 +76,13 @@ __device__ __forceinline__ bf16x8 frag_cols(const TPS_LDS char* s, int cb, int k
 // Per-lane byte offsets of this wave's NB copy blocks of a [16 NB][128] tile
 // (block NB w + j = rows 4 (NB w + j) .. +3; lane L writes bytes [16 L, 16 L + 16)
 // of the block = row 4 B + L / 16, physical chunk L % 16).
-template <bool ROWSWZ, int NB>
+template <int LAY, int NB>
 __device__ __forceinline__ void tile_voffs(int64_t ld, uint32_t (&vo)[NB]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int row = 4 * (NB * wave + j) + (lane >> 4);
-    const int c = (lane & 15) ^ swz<ROWSWZ>(row);
+    const int c = (lane & 15) ^ swz<LAY>(row);
     vo[j] = (uint32_t)((row * ld + 8 * c) * 2);
   }
 }
