@@ -87,7 +87,7 @@ __device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t
   const int lane = threadIdx.x & 63;
   OpStream s;
   s.base = static_cast<const char*>(p) + row0 * ld * 2;
-  s.nrec = (uint32_t)(extent_bytes(rows, ld, K) - row0 * ld * 2);
+  s.nrec = (uint32_t)(extent_bytes(rows, ld, K) - row0 * ld * 2);   // row0 < rows: every tile starts inside
   s.step = BK * 2;
   const int r = lane >> 2;
   const int c = (lane & 3) ^ kc_swz(r);
@@ -110,7 +110,7 @@ __device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t
   constexpr int ROWS = 512 / W;   // rows per block
   OpStream s;
   s.base = static_cast<const char*>(p) + col0 * 2;
-  s.nrec = (uint32_t)(extent_bytes(K, ld, cols) - col0 * 2);
+  s.nrec = (uint32_t)(extent_bytes(K, ld, cols) - col0 * 2);   // col0 < cols: every tile starts inside
   s.step = (uint32_t)(BK * ld * 2);
 #pragma unroll
   for (int j = 0; j < DMA_PER_OPERAND; ++j) {
@@ -588,9 +588,11 @@ __device__ __forceinline__ void swap_halves(uint32_t (&pk)[8]) {
     }
 }
 
-__device__ __forceinline__ void store_pk(uint16_t* p, const uint32_t (&pk)[8]) {
-  *reinterpret_cast<u32x4*>(p) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-  *reinterpret_cast<u32x4*>(p + 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+// The lane's two 8-column chunks after swap_halves: columns [0, 8) and
+// [16, 24) from p, each stored only when its flag is set.
+__device__ __forceinline__ void store_pk(uint16_t* p, const uint32_t (&pk)[8], bool lo, bool hi) {
+  if (lo) *reinterpret_cast<u32x4*>(p) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  if (hi) *reinterpret_cast<u32x4*>(p + 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
 }
 
 template <int EPI, int MI, int I, int J>
@@ -600,13 +602,33 @@ __device__ __forceinline__ void fast_block(const Problem& P, int64_t m0, int64_t
   if (dual && J >= 2) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m = m0 + 32 * MI * wm + 32 * I + (lane & 31);
-  const int64_t n = n0 + (dual ? 64 * wn + 32 * (J & 1) : 128 * wn + 32 * J) + 8 * (lane >> 5);
+  const int64_t nb = n0 + (dual ? 64 * wn + 32 * (J & 1) : 128 * wn + 32 * J);   // the block's first column
+  const int64_t n = nb + 8 * (lane >> 5);
+  // A tile may overhang the matrix (rows past M; columns past N when N is a
+  // multiple of 8): the lane's row holds two 8-column chunks, at n and n + 16,
+  // each stored only inside the matrix.  (The test is per tile first, so whole
+  // tiles store without per-lane compares.)
+  const int64_t bw = dual ? BN / 2 : BN;
+  const bool whole = m0 + 32 * MI * 2 <= P.M && n0 + bw <= P.N;   // wave-uniform
+  float ce_l = 0.f, ce_g = 0.f;
+  int64_t ce_t = 0;
+  if (EPI == E_CE_GRAD) {   // per-row loss terms; the target column relative to this lane's first column
+    const int64_t mr = m < P.M ? m : P.M - 1;
+    ce_l = P.lse[mr];
+    ce_g = P.gscale ? P.gscale[mr] : 1.0f;
+    ce_t = (int64_t)P.target[mr] - P.v0 - (nb + 4 * (lane >> 5));
+  }
   uint32_t py[8], pg[8], pu[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const float v0 = a[2 * q], v1 = a[2 * q + 1];
     if (EPI == E_STORE) {
       py[q] = pack_bf2(v0, v1);
+    } else if (EPI == E_CE_GRAD) {
+      // register r = 2 q (+1) holds column 8 (r / 4) + r % 4 past the lane's first column
+      const int c0 = 8 * (q >> 1) + 2 * (q & 1);
+      py[q] = pack_bf2(ce_g * (__expf(v0 - ce_l) - (ce_t == c0 ? 1.0f : 0.0f)),
+                       ce_g * (__expf(v1 - ce_l) - (ce_t == c0 + 1 ? 1.0f : 0.0f)));
     } else if (EPI == E_GELU) {
       pg[q] = pack_bf2(v0, v1);
       py[q] = pack_bf2(gelu_f(v0), gelu_f(v1));
@@ -618,16 +640,17 @@ __device__ __forceinline__ void fast_block(const Problem& P, int64_t m0, int64_t
     }
   }
   swap_halves(py);
-  store_pk(static_cast<uint16_t*>(P.c) + m * P.ldc + n, py);
-  if (EPI != E_STORE) {
-    swap_halves(pg);
-    uint16_t* pre = static_cast<uint16_t*>(P.pre) + m * P.ldpre;
-    store_pk(pre + n, pg);
-    if (dual) {
-      swap_halves(pu);
-      store_pk(pre + P.N + n, pu);
-    }
-  }
+  if (EPI == E_GELU || EPI == E_SWIGLU) swap_halves(pg);
+  if (dual) swap_halves(pu);
+  uint16_t* c = static_cast<uint16_t*>(P.c) + m * P.ldc + n;
+  uint16_t* pre = (EPI == E_GELU || EPI == E_SWIGLU) ? static_cast<uint16_t*>(P.pre) + m * P.ldpre + n : nullptr;
+  auto stores = [&](bool lo, bool hi) {
+    store_pk(c, py, lo, hi);
+    if (EPI == E_GELU || EPI == E_SWIGLU) store_pk(pre, pg, lo, hi);
+    if (dual) store_pk(pre + P.N, pu, lo, hi);
+  };
+  if (whole) stores(true, true);
+  else stores(m < P.M && n < P.N, m < P.M && n + 16 < P.N);
 }
 
 template <int EPI, int MI, int... Is>
@@ -870,7 +893,8 @@ __device__ __forceinline__ int wg_index(int& xcd) {
 }
 
 // Fast kernels: one per (operand layout, epilogue, K segments), so each role
-// of the shard path is a distinct kernel in traces.  Whole tiles only, no
+// of the shard path is a distinct kernel in traces.  Tiles overhanging the
+// matrix are masked at the stores (rows; columns in 8-wide chunks); no
 // bias, aligned outputs; one workgroup per CU.  Starting the K loops of the
 // XCDs at different points keeps the workgroups of one XCD in step (their
 // shared operand panels stay in its L2).
@@ -1060,16 +1084,17 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Whole tiles of this problem may take the fast kernel.
+// The tiles of this problem may take the fast kernel (no bias, 16-byte
+// aligned outputs).
 bool fast_ok(const Problem& P) {
-  if (P.bias || P.bias2 || P.epi == E_CE_GRAD) return false;
+  if (P.bias || P.bias2) return false;
   if (!aligned16(P.c) || (P.ldc & 7)) return false;
   if (P.epi != E_STORE && (!aligned16(P.pre) || (P.ldpre & 7))) return false;
   if (P.epi == E_SWIGLU && (P.N & 7)) return false;
   return true;
 }
 
-// FAST: whole tiles (HALF: the 128-row halves of the tiles from half_base on;
+// FAST: the fast kernel's tiles (HALF: the 128-row halves of the tiles from half_base on;
 // layouts with a K-contiguous A and one K segment only); else edge tiles.
 template <bool FAST, bool HALF = false>
 hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
@@ -1078,7 +1103,7 @@ hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
   const bool seg2 = L.p[0].nseg > 1 || (L.nprob > 1 && L.p[1].nseg > 1);
 #define TPS_LAUNCH(LY, EP, S2)                                                                      \
   do {                                                                                              \
-    if constexpr (FAST && EP != E_CE_GRAD) {                                                        \
+    if constexpr (FAST) {                                                                           \
       if constexpr (HALF && LY != L_TN && !S2)                                                      \
         hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, 2>), g, block, 0, s, L);                   \
       else                                                                                          \
@@ -1168,14 +1193,16 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   bool fast = true;
   for (int i = 0; i < L.nprob; ++i) fast = fast && fast_ok(L.p[i]);
-  GemmLaunch F = L, E = L;   // whole tiles (fast kernel), remaining tiles (generic kernel)
+  GemmLaunch F = L, E = L;   // fast-kernel tiles, remaining tiles (generic kernel)
   int nf = 0, ne = 0;
   int64_t W = 0;
   for (int i = 0; i < L.nprob; ++i) {
     const Problem& P = L.p[i];
     const int64_t bn = (P.epi == E_SWIGLU) ? BN / 2 : BN;
     const int tm = (int)((P.M + BM - 1) / BM), tn = (int)((P.N + bn - 1) / bn);
-    const int fm = fast ? (int)(P.M / BM) : 0, fn = fast ? (int)(P.N / bn) : 0;
+    // The fast kernel masks rows past M, and columns past N in whole 8-column
+    // chunks: every tile row, and the last tile column when N % 8 == 0.
+    const int fm = fast ? tm : 0, fn = fast ? ((P.N & 7) == 0 ? tn : (int)(P.N / bn)) : 0;
     F.p[i].tiles_m = fm;
     F.p[i].tiles_n = fn;
     F.p[i].tile_begin = nf;
@@ -1191,8 +1218,10 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   if (nf > 0) {
     // A last round that would leave over half the CUs idle runs as 128-row
-    // half tiles instead (layouts with a K-contiguous A and one segment).
-    const bool half_ok = L.p[0].layout != L_TN && L.p[0].nseg == 1 && (L.nprob == 1 || L.p[1].nseg == 1);
+    // half tiles instead (layouts with a K-contiguous A and one segment; M a
+    // multiple of 256, so that no half tile starts past the last row).
+    bool half_ok = L.p[0].layout != L_TN && L.p[0].nseg == 1 && (L.nprob == 1 || L.p[1].nseg == 1);
+    for (int i = 0; i < L.nprob; ++i) half_ok = half_ok && L.p[i].M % BM == 0;
     const int rem = nf % cus;
     const int tail = (half_ok && nf > cus && rem > 0 && 2 * rem <= cus) ? rem : 0;
     F.tiles = nf - tail;
