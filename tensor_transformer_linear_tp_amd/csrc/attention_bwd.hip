@@ -233,7 +233,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_combine_kernel(const AttnBwdA
 }
 
 // ---- dK, dV -------------------------------------------------------------------------
-constexpr int KV_NSTAGE = 2;
+// Ring of 32-query tiles.  Iteration t finishes tile t (dV, dK) and forms tile t + 1's S and
+// dP; while its MFMAs run, it reads from LDS the operands of iteration t + 1 (tile t + 2's row
+// fragments, tile t + 1's (lse2, D)), so that every iteration starts on operands already in
+// registers.  The waves meet at a barrier every KV_WIN = 2
+// iterations: at the barrier of an even t, tiles up to t + 3 have landed (the window reads up
+// to tile t + 3), tiles t - 2 and t - 1 are finished, and their stages take tiles t + 6, t + 7.
+constexpr int KV_NSTAGE = 8;
+constexpr int KV_WIN = 2;
 
 __shared__ __attribute__((aligned(1024))) char bkv_ring[KV_NSTAGE * QSTAGE];
 
@@ -277,18 +284,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
   const int64_t kc = min<int64_t>(my_key, a.S - 1);
   const int64_t q_begin = kv_q_begin(a, kbk);
 
-  // K and V rows of this lane's key (B operands of S = Q K^T and dP = dO V^T)
-  bf16x8 kf[8], vf[8];
-  {
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (row0 + kc) * a.ldk + (int64_t)g * HD + 8 * (lane >> 5);
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (row0 + kc) * a.ldv + (int64_t)g * HD + 8 * (lane >> 5);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
-      vf[kk] = *reinterpret_cast<const bf16x8*>(vp + 16 * kk);
-    }
-  }
-
   const char* qbase = static_cast<const char*>(a.q) + (row0 * a.ldq + (int64_t)h * HD) * 2;
   const char* gbase = static_cast<const char*>(p.dout) + (row0 * p.ldg + (int64_t)h * HD) * 2;
   const char* lbase = reinterpret_cast<const char*>(p.ld + 2 * (((int64_t)b * a.n_q + h) * a.S));
@@ -305,11 +300,26 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
     const uint32_t tq = (uint32_t)(qt / QT);
     issue_tile(qr, qvo, tq * qstep, bkv_q(st));
     issue_tile(gr, gvo, tq * gstep, bkv_g(st));
-    if (wave == 0)   // 32 (lse2, D) pairs: 256 bytes, 4 per lane
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (TPS_LDS void*)bkv_l(st), 4, (uint32_t)(qt * 8 + 4 * lane), 0, 0,
-                                               0);
+    // 32 (lse2, D) pairs: 256 bytes, 4 per lane.  Every wave issues the same copy (identical
+    // bytes to the same place), so that every wave counts 5 copies per tile.
+    lds_copy4(lr, (uint32_t)(qt * 8 + 4 * lane), bkv_l(st));
   };
-  for (int t = 0; t < KV_NSTAGE - 1 && t < nt; ++t) issue(t, t);
+  for (int t = 0; t < 4 && t < nt; ++t) issue(t, t);
+  // K and V rows of this lane's key (B operands of S = Q K^T and dP = dO V^T)
+  bf16x8 kf[8], vf[8];
+  {
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (row0 + kc) * a.ldk + (int64_t)g * HD + 8 * (lane >> 5);
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (row0 + kc) * a.ldv + (int64_t)g * HD + 8 * (lane >> 5);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(kp + 16 * kk);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(vp + 16 * kk);
+    }
+  }
+  // Tiles 0 .. 3 and the K, V rows; waited for here, explicitly, so that the compiler's own
+  // wait for the K, V registers does not also wait for the copies queued after them.
+  wait_vm<0>();
+  for (int t = 4; t < KV_NSTAGE && t < nt; ++t) issue(t, t);
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -319,67 +329,170 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(const AttnBwdArgs 
   }
   const float c = a.scale * LOG2E;
 
-  for (int t = 0; t < nt; ++t) {
-    wait_vm<0>();
-    __syncthreads();   // tile t visible to all waves; the other stage is free
-    if (t + KV_NSTAGE - 1 < nt) issue(t + KV_NSTAGE - 1, (t + KV_NSTAGE - 1) % KV_NSTAGE);
-    const TPS_LDS char* qs = bkv_q(t % KV_NSTAGE);
-    const TPS_LDS char* gs = bkv_g(t % KV_NSTAGE);
-    const TPS_LDS float* ls = (const TPS_LDS float*)bkv_l(t % KV_NSTAGE);
-
-    f32x16 s = f32x16{0.f}, dp = f32x16{0.f};   // two independent chains, interleaved
+  // Row fragments of the tile in ring stage st: A operands of S = Q K^T and dP = dO V^T.
+  auto load_rows = [&](int st, bf16x8 (&qa)[8], bf16x8 (&ga)[8]) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<LAY_BOTH>(qs, 0, kk), kf[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<LAY_BOTH>(gs, 0, kk), vf[kk], dp, 0, 0, 0);
+      qa[kk] = frag_rows<LAY_BOTH>(bkv_q(st), 0, kk);
+      ga[kk] = frag_rows<LAY_BOTH>(bkv_g(st), 0, kk);
     }
+  };
+  // Column fragments of k-step ss: A operands of dV += dO^T P and dK += Q^T dS.
+  auto load_cols = [&](int st, int ss, bf16x8 (&cq)[4], bf16x8 (&cg)[4]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      cg[db] = frag_cols<LAY_BOTH>(bkv_g(st), 32 * db, ss);
+      cq[db] = frag_cols<LAY_BOTH>(bkv_q(st), 32 * db, ss);
+    }
+  };
+  // (lse2, D) of this lane's 16 queries: pairs 8 q + 4 (lane / 32) + 0..3 as two f32x4 per q
+  auto load_ld = [&](int st, f32x4 (&lv)[8]) {
+    const TPS_LDS float* ls = (const TPS_LDS float*)bkv_l(st);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int qi = 8 * q + 4 * (lane >> 5);
+      lv[2 * q] = *reinterpret_cast<const TPS_LDS f32x4*>(ls + 2 * qi);
+      lv[2 * q + 1] = *reinterpret_cast<const TPS_LDS f32x4*>(ls + 2 * qi + 4);
+    }
+  };
+
+  __syncthreads();   // tiles 0 .. 3 visible to every wave
+  // Operands rotate through registers: at the top of iteration t, ra, rg hold tile t + 1's row
+  // fragments and lv tile t's (lse2, D).
+  // Reads of tiles past the chunk's end hit stale ring stages; those values are never used.
+  bf16x8 ra[8], rg[8], cq0[4], cg0[4];
+  f32x4 lv[8];
+  f32x16 s_cur = f32x16{0.f}, dp_cur = f32x16{0.f};
+  load_rows(0, ra, rg);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[kk], kf[kk], s_cur, 0, 0, 0);
+    dp_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rg[kk], vf[kk], dp_cur, 0, 0, 0);
+  }
+  load_rows(1, ra, rg);
+  load_ld(0, lv);
+
+  for (int t = 0; t < nt; ++t) {
+    if (t > 0 && t % KV_WIN == 0) {
+      // tiles up to t + 5 issued (5 copies each); tiles up to t + 3 must have landed
+      switch (max(0, min(nt, t + 6) - (t + 4))) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<5>(); break;
+        default: wait_vm<10>(); break;
+      }
+      __syncthreads();
+      if (t + 6 < nt) issue(t + 6, (t + 6) % KV_NSTAGE);
+      if (t + 7 < nt) issue(t + 7, (t + 7) % KV_NSTAGE);
+    }
+    const int st = t % KV_NSTAGE;
+    __builtin_amdgcn_sched_barrier(0);
+
     // lane: key my_key, queries qt + 8 (r / 4) + 4 (lane / 32) + r % 4.  Every pair of the
     // tile is live when its queries lie inside the sequence, the wave's keys do, and (causal)
     // its first query is not before the wave's last key; otherwise mask per element.
-    const int64_t qt = q_begin + (int64_t)(t_begin + t) * QT;
-    const bool full = qt + QT <= a.S && key_w + 32 <= a.S && (!a.causal || qt >= key_w + 31);
-    const int lim = (int)min<int64_t>(a.S - 1 - qt, INT_MAX);                       // last query, tile-relative
-    const int first = a.causal ? (int)max<int64_t>(min<int64_t>(my_key - qt, INT_MAX), INT_MIN) : INT_MIN;
+    // (positions fit in 32 bits: a bf16 operand holds under 2^30 elements, so B S < 2^23)
+    const int qt = (int)q_begin + (t_begin + t) * QT;
+    const int S32 = (int)a.S, kw = (int)key_w;
+    const bool full = qt + QT <= S32 && kw + 32 <= S32 && (!a.causal || qt >= kw + 31);
+    const int lim = S32 - 1 - qt;                           // last query, tile-relative
+    const int first = a.causal ? (int)my_key - qt : INT_MIN;  // first query that sees my_key
     const bool key_ok = my_key < a.S;
     uint32_t pp[8], pd[8];
-    // P = 2^(S c - lse2) (masked pairs: 2^-inf = 0), dS = P (dP - D); two straight-line
+    f32x16 s_nxt = f32x16{0.f}, dp_nxt = f32x16{0.f};
+    // S and dP of tile t + 1 on the matrix cores while the vector unit forms tile t's
+    // P = 2^(S c - lse2) (masked pairs: 2^-inf = 0) and dS = P (dP - D); two straight-line
     // versions, chosen per tile, so that unmasked tiles carry no per-element tests
-    auto softmax_grad = [&](auto masked) {
+    auto step = [&](auto masked) {
+      load_cols(st, 0, cq0, cg0);   // this tile's first column fragments, needed after the step
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[kk], kf[kk], s_nxt, 0, 0, 0);
+        dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rg[kk], vf[kk], dp_nxt, 0, 0, 0);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int qi = 8 * q + 4 * (lane >> 5);
-        const f32x4 l01 = *reinterpret_cast<const TPS_LDS f32x4*>(ls + 2 * qi);
-        const f32x4 l23 = *reinterpret_cast<const TPS_LDS f32x4*>(ls + 2 * qi + 4);
+        const f32x4 l01 = lv[2 * q], l23 = lv[2 * q + 1];
         const float lse2[4] = {l01[0], l01[2], l23[0], l23[2]};
         const float dd[4] = {l01[1], l01[3], l23[1], l23[3]};
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * q + e;
-          float x = __builtin_fmaf(s[r], c, -lse2[e]);
-          if constexpr (decltype(masked)::value)
-            x = ((qi + e) <= lim && (qi + e) >= first && key_ok) ? x : -INFINITY;
-          pv[e] = __builtin_amdgcn_exp2f(x);
-          dsv[e] = pv[e] * (dp[r] - dd[e]);
+          if constexpr (decltype(masked)::value) {
+            // the mask acts on the operands (S -> -inf, dP -> D), so that neither path shares
+            // an instruction with the other that the compiler would hoist out of the MFMA mix
+            const bool ok = (qi + e) <= lim && (qi + e) >= first && key_ok;
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(ok ? s_cur[r] : -INFINITY, c, -lse2[e]));
+            dsv[e] = pv[e] * ((ok ? dp_cur[r] : dd[e]) - dd[e]);
+          } else {
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], c, -lse2[e]));
+            dsv[e] = pv[e] * (dp_cur[r] - dd[e]);
+          }
         }
         pp[2 * q] = pack_bf2(pv[0], pv[1]);
         pp[2 * q + 1] = pack_bf2(pv[2], pv[3]);
         pd[2 * q] = pack_bf2(dsv[0], dsv[1]);
         pd[2 * q + 1] = pack_bf2(dsv[2], dsv[3]);
       }
-    };
-    if (full) softmax_grad(std::false_type{});
-    else softmax_grad(std::true_type{});
+      // one MFMA, then a slice of the vector work, so that the vector unit runs while the
+      // matrix core is busy (one wave per SIMD: nothing else would fill those cycles)
+      // (group masks: 0x008 MFMA, 0x002 | 0x400 vector ALU and transcendental, 0x100 LDS read)
+      if constexpr (decltype(masked)::value) {
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const bf16x8 pf = pk_frag(pp, ss);
-      const bf16x8 df = pk_frag(pd, ss);
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+        }
+      }
+    };
+    if (full) step(std::false_type{});
+    else step(std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+
+    // dV, dK in two k-steps of 8 MFMAs; under each, the LDS reads for what comes next: the
+    // second column fragments and the next iteration's (lse2, D), then its rows
+    bf16x8 cq1[4], cg1[4];
+    {
+      const bf16x8 pf = pk_frag(pp, 0), df = pk_frag(pd, 0);
+      load_cols(st, 1, cq1, cg1);
+      load_ld((t + 1) % KV_NSTAGE, lv);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<LAY_BOTH>(gs, 32 * db, ss), pf, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_cols<LAY_BOTH>(qs, 32 * db, ss), df, dk[db], 0, 0, 0);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cg0[db], pf, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cq0[db], df, dk[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const bf16x8 pf = pk_frag(pp, 1), df = pk_frag(pd, 1);
+      load_rows((t + 2) % KV_NSTAGE, ra, rg);   // the next iteration's S, dP operands
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cg1[db], pf, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cq1[db], df, dk[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s_cur = s_nxt;
+    dp_cur = dp_nxt;
   }
 
   float* slot = kv_slot(p, b, g, kbk, h % group, chunk) + (32 * wave + (lane & 31)) * 256;

@@ -87,24 +87,40 @@ __device__ __forceinline__ void tile_voffs(int64_t ld, uint32_t (&vo)[NB]) {
   }
 }
 
+// Global -> LDS copies (buffer_load ... lds): lane i's 16 (4) bytes from byte offset voff of
+// the buffer land at dst + 16 i (dst + 4 i); dst must be wave-uniform.  Written as inline
+// assembly on purpose: for the builtin form the compiler makes every later transposing LDS
+// read (ds_read_b64_tr_b16) wait for all outstanding copies, including the ones just issued
+// for later tiles, which serialises the copy-ahead ring.  The kernels order copies and reads
+// themselves (wait_vm on their own copies, then a workgroup barrier).
+__device__ __forceinline__ void lds_copy16(const __amdgpu_buffer_rsrc_t& r, uint32_t voff, TPS_LDS char* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void lds_copy4(const __amdgpu_buffer_rsrc_t& r, uint32_t voff, TPS_LDS char* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+}
+
 template <int NB>
 __device__ __forceinline__ void issue_tile(const __amdgpu_buffer_rsrc_t& r, const uint32_t (&vo)[NB], uint32_t off,
                                            TPS_LDS char* dst) {
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(dst + 1024 * (NB * wave + j)), 16, vo[j] + off, 0, 0,
-                                             0);
+  for (int j = 0; j < NB; ++j) lds_copy16(r, vo[j] + off, dst + 1024 * (NB * wave + j));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t nrec) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec, 0x00020000);
 }
 
+// s_waitcnt vmcnt(VM): at most VM of this wave's vector memory operations (loads, LDS
+// copies) still outstanding.  The 6-bit count is split over immediate bits 3:0 and 15:14;
+// expcnt and lgkmcnt are left at their maxima (no wait).
 template <int VM>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(VM >= 0 && VM < 16, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(VM | (7 << 4) | (15 << 8));
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // B-operand fragment of k-step s from a 32 x 32 accumulator-shaped block
