@@ -45,6 +45,18 @@ def sample_idx(n, k, seed):
     return np.unique(np.concatenate([np.array(fixed, dtype=np.int64), extra.astype(np.int64)]))
 
 
+def tile_sample_idx(n, tile, seed, per_tile=1):
+    """Sorted sample with `per_tile` random indices inside every `tile`-sized block of [0, n)
+    (the last, partial block included) plus both ends, so that every tile of a tiled kernel's
+    output is checked."""
+    rng = np.random.default_rng(seed)
+    idx = [0, n - 1]
+    for t0 in range(0, n, tile):
+        t1 = min(n, t0 + tile)
+        idx += list(rng.integers(t0, t1, size=per_tile))
+    return np.unique(np.array(idx, dtype=np.int64))
+
+
 def rows(t, idx):
     """float64 copy of the selected rows of a device matrix."""
     import torch

@@ -8,7 +8,7 @@ import pytest
 import oracle
 import synthetic as syn
 
-from .gpu_util import TOL, TOL_CE, assert_close, cols, dev, host64, rows, sample_idx
+from .gpu_util import TOL, TOL_CE, assert_close, cols, dev, host64, rows, sample_idx, tile_sample_idx
 
 pytestmark = pytest.mark.gpu
 
@@ -245,8 +245,8 @@ def test_c5_shard0_full_size_sampled():
     cfg = syn.C5
     d = syn.vocab_inputs(cfg, shard=0)
     target = d["target"].copy()
-    # make sure a good number of sampled tokens have their target in shard 0
-    ms = sample_idx(cfg.M, 64, 12)
+    # two tokens in every 256-row tile; half of them get their target in shard 0
+    ms = tile_sample_idx(cfg.M, 256, 12, per_tile=2)
     target[ms[::2]] = (ms[::2] * 7919) % cfg.Vr
     m, s, tg = ops.vocab_ce_partials(dev(d["H"]), dev(d["W"]), torch.from_numpy(target).cuda(), d["v0"])
     torch.cuda.synchronize()
@@ -262,8 +262,10 @@ def test_c5_ce_backward_full_size_sampled():
     cfg = syn.C5
     d = syn.vocab_inputs(cfg, shard=0)
     target = d["target"].copy()
-    ms = sample_idx(cfg.M, 48, 13)            # token rows of dH
-    js = sample_idx(cfg.Vr, 48, 14)           # vocab rows of dW
+    # token rows of dH and vocab rows of dW: two in every 256-row block (the GEMM tile), so that
+    # every tile of the dz workspace and of both products enters the check
+    ms = tile_sample_idx(cfg.M, 256, 13, per_tile=2)
+    js = tile_sample_idx(cfg.Vr, 256, 14, per_tile=2)
     target[ms[::2]] = (ms[::2] * 7919) % cfg.Vr
     # lse near the shard's own log-sum-exp (ln 18992 + 1.28^2/2 ~ 10.7), so the softmax
     # term and the onehot term are both of order one; g: per-token upstream gradient
