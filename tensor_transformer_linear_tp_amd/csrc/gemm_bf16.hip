@@ -102,7 +102,11 @@ __device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t
 // MN-contiguous operand: columns [col0, col0 + W) of a [K][cols] matrix.
 // W = 256: block b holds rows 2b, 2b+1 (lane L: row 2b + L/32, chunk L%32);
 // W = 128: block b holds rows 4b..4b+3 (lane L: row 4b + L/16, chunk L%16).
-template <int W>
+// Only the first VALID chunks of each row are wanted (a 192-wide tile kept
+// in the 256-wide layout): lanes holding a later chunk are sent past the
+// range, so they fetch nothing and fill their LDS slot with zeros.
+constexpr uint32_t kDeadLane = 0x80000000u;   // above any extent (< 2 GiB), below 2^32 with any stage offset
+template <int W, int VALID = W / 8>
 __device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t cols, int64_t K, int64_t col0,
                                               int wb) {
   const int lane = threadIdx.x & 63;
@@ -116,7 +120,7 @@ __device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t
   for (int j = 0; j < DMA_PER_OPERAND; ++j) {
     const int k = ROWS * (DMA_PER_OPERAND * wb + j) + lane / CHUNKS;
     const int c = (lane % CHUNKS) ^ mn_swz(k);
-    s.voff[j] = (uint32_t)((k * ld + 8 * c) * 2);
+    s.voff[j] = (VALID < CHUNKS && c >= VALID) ? kDeadLane : (uint32_t)((k * ld + 8 * c) * 2);
   }
   return s;
 }
@@ -261,15 +265,20 @@ struct TileStreams {
   int npad;                // send - s0 rounded up to NSTAGE
 };
 
-// MI: 32-row MFMA blocks per wave along M (4: 256-row tiles; 2: 128-row
-// tiles, K-contiguous A only).
-template <int LAYOUT, bool DUAL, bool SEG2, int MI = 4>
+// MI, NI: 32 x 32 MFMA blocks per wave along M and N; the tile is
+// (64 MI) x (64 NI).  MI = 4, 3 or 2 (2: K-contiguous A only), NI = 4 or 3
+// (SwiGLU: 4).  A K-contiguous operand of 64 MI rows is copied as MI blocks
+// of 16 rows per wave; an MN-contiguous one always fills the 256-wide LDS
+// layout (192-wide tiles leave its last 64 columns zero).
+template <int LAYOUT, bool DUAL, bool SEG2, int MI = 4, int NI = 4>
 struct Pipe {
   static constexpr bool A_KC = LAYOUT != L_TN;
   static constexpr bool B_KC = LAYOUT == L_NT;
-  static_assert(MI == 4 || (MI == 2 && A_KC), "128-row tiles need a K-contiguous A");
-  static constexpr int NBA = DMA_PER_OPERAND * MI / 4;   // A copies per wave per stage
-  static constexpr int NCOPY = NBA + DMA_PER_OPERAND;   // copies per wave per stage
+  static_assert(MI == 4 || MI == 3 || (MI == 2 && A_KC), "128-row tiles need a K-contiguous A");
+  static_assert(NI == 4 || (NI == 3 && !DUAL), "tile widths: 256, or 192 without the SwiGLU pairing");
+  static constexpr int NBA = A_KC ? MI : DMA_PER_OPERAND;   // A copies per wave per stage
+  static constexpr int NBB = B_KC ? NI : DMA_PER_OPERAND;   // B copies per wave per stage
+  static constexpr int NCOPY = NBA + NBB;                   // copies per wave per stage
   static constexpr int KA = A_KC ? S_KC : S_MN256;
   static constexpr int KB = B_KC ? S_KC : (DUAL ? S_MN128 : S_MN256);
 
@@ -283,7 +292,7 @@ struct Pipe {
     wn = wave & 1;
     wlds_a = 1024 * NBA * wave;
     wlds_b = TILE_BYTES + (KB == S_MN128 ? (wave >> 1) * (TILE_BYTES / 2) + 1024 * DMA_PER_OPERAND * (wave & 1)
-                                          : 1024 * DMA_PER_OPERAND * wave);
+                                          : 1024 * NBB * wave);
     init_frag_addr();
   }
 
@@ -296,14 +305,14 @@ struct Pipe {
     const int64_t ldb = use1 ? P.seg[1].ldb : P.seg[0].ldb;
     const int64_t K = use1 ? P.seg[1].K : P.seg[0].K;
     Kseg = (int)K;
-    sa = A_KC ? stream_kc<NBA>(pa, lda, P.M, K, m0, wave) : stream_mn<256>(pa, lda, P.M, K, m0, wave);
+    sa = A_KC ? stream_kc<NBA>(pa, lda, P.M, K, m0, wave) : stream_mn<256, 8 * MI>(pa, lda, P.M, K, m0, wave);
     if (B_KC) {
-      sb = stream_kc(pb, ldb, P.N, K, n0, wave);
+      sb = stream_kc<NBB>(pb, ldb, P.N, K, n0, wave);
     } else if (DUAL) {   // waves 0,1 stream the gate weight, waves 2,3 the up weight
       const bool up = (wave >> 1) != 0;
       sb = stream_mn<128>(up ? P.b_up : pb, up ? P.ldb_up : ldb, P.N, K, n0, wave & 1);
     } else {
-      sb = stream_mn<256>(pb, ldb, P.N, K, n0, wave);
+      sb = stream_mn<256, 8 * NI>(pb, ldb, P.N, K, n0, wave);
     }
   }
 
@@ -392,7 +401,7 @@ struct Pipe {
     int wa = wlds_a, wb = wlds_b;
     asm volatile("" : "+s"(wa), "+s"(wb));
     stream_issue<NBA>(s1 ? T.a1 : T.a0, stage, live, dst + wa);
-    stream_issue(s1 ? T.b1 : T.b0, stage, live, dst + wb);
+    stream_issue<NBB>(s1 ? T.b1 : T.b0, stage, live, dst + wb);
   }
 
   // Per-lane LDS byte addresses of the fragments, computed once.  A fragment
@@ -413,19 +422,19 @@ struct Pipe {
         const int r = 32 * MI * wm + (lane & 31);
         adA[x] = kc_off(r, 2 * (x & 1) + hi32);
       } else {
-        const int col = 128 * wm + 32 * x + 16 * (h & 1) + 4 * (q & 3);
+        const int col = 32 * MI * wm + 32 * x + 16 * (h & 1) + 4 * (q & 3);
         const int k = 8 * (h >> 1) + (q >> 2);
         adA[x] = mn_off<512>(k, col >> 3) + (col & 7) * 2;
       }
       if (B_KC) {
-        const int r = 128 * wn + (lane & 31);
+        const int r = 32 * NI * wn + (lane & 31);
         adB[x] = TILE_BYTES + kc_off(r, 2 * (x & 1) + hi32);
       } else if (DUAL) {
         const int col = 64 * wn + 32 * (x & 1) + 16 * (h & 1) + 4 * (q & 3);
         const int k = 8 * (h >> 1) + (q >> 2);
         adB[x] = TILE_BYTES + (x >> 1) * (TILE_BYTES / 2) + mn_off<256>(k, col >> 3) + (col & 7) * 2;
       } else {
-        const int col = 128 * wn + 32 * x + 16 * (h & 1) + 4 * (q & 3);
+        const int col = 32 * NI * wn + 32 * x + 16 * (h & 1) + 4 * (q & 3);
         const int k = 8 * (h >> 1) + (q >> 2);
         adB[x] = TILE_BYTES + mn_off<512>(k, col >> 3) + (col & 7) * 2;
       }
@@ -450,18 +459,18 @@ struct Pipe {
     for (int i = 0; i < MI; ++i)
       af[kk][i] = A_KC ? rd_kc(base + adA[kk] + 2048 * i) : rd_mn(base + adA[i] + 16 * kk * 512, 512);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NI; ++j) {
       if (B_KC) bfr[kk][j] = rd_kc(base + adB[kk] + 2048 * j);
       else if (DUAL) bfr[kk][j] = rd_mn(base + adB[j] + 16 * kk * 256, 256);
       else bfr[kk][j] = rd_mn(base + adB[j] + 16 * kk * 512, 512);
     }
   }
 
-  __device__ __forceinline__ void mma(int r, f32x16 (&acc)[MI][4]) {
+  __device__ __forceinline__ void mma(int r, f32x16 (&acc)[MI][NI]) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NI; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[r][j], af[r][i], acc[i][j], 0, 0, 0);
   }
 
@@ -476,11 +485,12 @@ struct Pipe {
   // Ask the scheduler to alternate one MFMA with one LDS read (and, in the
   // first phase of a step, one global->LDS copy), instead of loading each
   // fragment just before its first use.
-  static constexpr int READS = (A_KC ? MI : 8) + (B_KC ? 4 : 8);
+  static constexpr int READS = (A_KC ? MI : 2 * MI) + (B_KC ? NI : 2 * NI);
+  static constexpr int GROUPS = std::max(MI * NI, READS);
   static __device__ __forceinline__ void interleave(bool with_copies) {
 #pragma unroll
-    for (int g = 0; g < 4 * MI; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+    for (int g = 0; g < GROUPS; ++g) {
+      if (g < MI * NI) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
       if (g < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // DS read
       if (with_copies && g < NCOPY) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
     }
@@ -494,7 +504,7 @@ struct Pipe {
   // LAST: one of the piece's last NSTAGE steps, which issue the next piece's
   // first stages (all but the first of them).
   template <int S, bool LAST>
-  __device__ __forceinline__ void step(int kt, f32x16 (&acc)[MI][4]) {
+  __device__ __forceinline__ void step(int kt, f32x16 (&acc)[MI][NI]) {
     TPS_LDS char* cur_slot = ring_slot<S>();
     // Stage kt's copies are complete once only the later NSTAGE-2 stages'
     // copies (NCOPY each) remain outstanding; lgkmcnt(0)
@@ -528,7 +538,7 @@ struct Pipe {
   // `next` is called before the last NSTAGE steps and must set nxt (or call
   // no_next()); those steps issue the next piece's first stages.
   template <class InitFn, class NextFn>
-  __device__ __forceinline__ void run_tile(f32x16 (&acc)[MI][4], InitFn&& init, NextFn&& next) {
+  __device__ __forceinline__ void run_tile(f32x16 (&acc)[MI][NI], InitFn&& init, NextFn&& next) {
     init(acc);
     zero_set1();              // the first step's deferred sub-step multiplies zeros
     int kt = 0;
@@ -553,12 +563,12 @@ struct Pipe {
   }
 };
 
-template <int MI>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MI][4]) {
+template <int MI, int NI = 4>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MI][NI]) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0.f};
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x16{0.f};
 }
 
 // ---- GEMM epilogue -------------------------------------------------------------------
@@ -595,20 +605,20 @@ __device__ __forceinline__ void store_pk(uint16_t* p, const uint32_t (&pk)[8], b
   if (hi) *reinterpret_cast<u32x4*>(p + 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
 }
 
-template <int EPI, int MI, int I, int J>
+template <int EPI, int MI, int NI, int I, int J>
 __device__ __forceinline__ void fast_block(const Problem& P, int64_t m0, int64_t n0, const f32x16& a,
                                            const f32x16& b) {
   constexpr bool dual = EPI == E_SWIGLU;
   if (dual && J >= 2) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m = m0 + 32 * MI * wm + 32 * I + (lane & 31);
-  const int64_t nb = n0 + (dual ? 64 * wn + 32 * (J & 1) : 128 * wn + 32 * J);   // the block's first column
+  const int64_t nb = n0 + (dual ? 64 * wn + 32 * (J & 1) : 32 * NI * wn + 32 * J);   // the block's first column
   const int64_t n = nb + 8 * (lane >> 5);
   // A tile may overhang the matrix (rows past M; columns past N when N is a
   // multiple of 8): the lane's row holds two 8-column chunks, at n and n + 16,
   // each stored only inside the matrix.  (The test is per tile first, so whole
   // tiles store without per-lane compares.)
-  const int64_t bw = dual ? BN / 2 : BN;
+  const int64_t bw = dual ? BN / 2 : 64 * NI;
   const bool whole = m0 + 32 * MI * 2 <= P.M && n0 + bw <= P.N;   // wave-uniform
   float ce_l = 0.f, ce_g = 0.f;
   int64_t ce_t = 0;
@@ -653,10 +663,12 @@ __device__ __forceinline__ void fast_block(const Problem& P, int64_t m0, int64_t
   else stores(m < P.M && n < P.N, m < P.M && n + 16 < P.N);
 }
 
-template <int EPI, int MI, int... Is>
-__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[MI][4],
+template <int EPI, int MI, int NI, int... Is>
+__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[MI][NI],
                                               std::integer_sequence<int, Is...>) {
-  ((fast_block<EPI, MI, Is / 4, Is % 4>(P, m0, n0, acc[Is / 4][Is % 4], acc[Is / 4][(Is % 4) ^ 2]),
+  // SwiGLU (NI = 4): block J's up values are block J ^ 2.
+  ((fast_block<EPI, MI, NI, Is / NI, Is % NI>(P, m0, n0, acc[Is / NI][Is % NI],
+                                              acc[Is / NI][EPI == E_SWIGLU ? (Is % NI) ^ 2 : Is % NI]),
     __builtin_amdgcn_sched_barrier(0)),
    ...);
 }
@@ -795,8 +807,9 @@ __device__ __forceinline__ Problem pick_problem(const GemmLaunch& L, bool s) {
   return P;
 }
 
-// Tile of a launch: its problem (selected field-wise) and its origin.
-template <bool EDGE>
+// Tile of a launch: its problem (selected field-wise) and its origin; tiles
+// are (64 MI) x (64 NI) (SwiGLU: 128 columns of Y).
+template <bool EDGE, int MI = 4, int NI = 4>
 __device__ __forceinline__ void locate(const GemmLaunch& L, int id, int epi, Problem& P, int64_t& m0, int64_t& n0) {
   P = pick_problem(L, L.nprob > 1 && id >= L.p[1].tile_begin);
   P.epi = epi;
@@ -815,8 +828,8 @@ __device__ __forceinline__ void locate(const GemmLaunch& L, int id, int epi, Pro
   } else {
     tile_coords(local, P.tiles_m, P.tiles_n, tm, tn);
   }
-  m0 = (int64_t)tm * BM;
-  n0 = (int64_t)tn * (epi == E_SWIGLU ? BN / 2 : BN);
+  m0 = (int64_t)tm * (64 * MI);
+  n0 = (int64_t)tn * (epi == E_SWIGLU ? BN / 2 : 64 * NI);
 }
 
 // ---- schedule of the fast kernels ---------------------------------------------------------
@@ -830,42 +843,44 @@ __device__ __forceinline__ int range_begin(int g, int T, int G) { return (int)((
 // Whole tiles [t0, t0 + count) of a launch spread over G workgroups; this is
 // workgroup g.  The K-stage stream runs on from tile to tile.  Tiles start
 // their K loop (xcd/8) of the way in, wrapping around.
-// Tile `tile` of a whole-tile launch; with MI == 2 the launch's tiles are
-// the two 128-row halves of the 256-row tiles from L.half_base on.
-template <int MI>
+// Tile `tile` of a whole-tile launch.  In a half-tile tail launch
+// (L.half_tail, MI == 2) the launch's tiles are the two 128-row halves of
+// the 256-row tiles from L.half_base on; otherwise the problems' tile grids
+// are in (64 MI) x (64 NI) tiles.
+template <int MI, int NI>
 __device__ __forceinline__ void locate_mi(const GemmLaunch& L, int tile, int epi, Problem& P, int64_t& m0,
                                           int64_t& n0) {
-  if (MI == 4) {
-    locate<false>(L, tile, epi, P, m0, n0);
-  } else {
+  if (MI == 2 && NI == 4 && L.half_tail) {
     locate<false>(L, L.half_base + (tile >> 1), epi, P, m0, n0);
     m0 += (tile & 1) * (BM / 2);
+  } else {
+    locate<false, MI, NI>(L, tile, epi, P, m0, n0);
   }
 }
 
-template <int LAYOUT, int EPI, bool SEG2, int MI = 4>
+template <int LAYOUT, int EPI, bool SEG2, int MI = 4, int NI = 4>
 __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count, int g, int G, int xcd) {
   const int ta = t0 + range_begin(g, count, G), tb = t0 + range_begin(g + 1, count, G);
   if (ta >= tb) return;
   constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
-  Pipe<LAYOUT, DUAL, SEG2, MI> pipe;
+  Pipe<LAYOUT, DUAL, SEG2, MI, NI> pipe;
   pipe.init_wave();
   int tile = ta;
   {
     Problem P;
     int64_t m0, n0;
-    locate_mi<MI>(L, tile, EPI, P, m0, n0);
+    locate_mi<MI, NI>(L, tile, EPI, P, m0, n0);
     pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX, xcd);
   }
   pipe.prologue();
   for (;;) {
     const bool more = tile + 1 < tb;
-    f32x16 acc[MI][4];
-    pipe.run_tile(acc, zero_acc<MI>, [&]() {
+    f32x16 acc[MI][NI];
+    pipe.run_tile(acc, zero_acc<MI, NI>, [&]() {
       if (more) {
         Problem Pn;
         int64_t m0n, n0n;
-        locate_mi<MI>(L, tile + 1, EPI, Pn, m0n, n0n);
+        locate_mi<MI, NI>(L, tile + 1, EPI, Pn, m0n, n0n);
         pipe.nxt = pipe.make_streams(Pn, m0n, n0n, 0, INT_MAX, xcd);
       } else {
         pipe.no_next();
@@ -874,8 +889,8 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
     {
       Problem P;
       int64_t m0, n0;
-      locate_mi<MI>(L, tile, EPI, P, m0, n0);
-      fast_epilogue<EPI, MI>(P, m0, n0, acc, std::make_integer_sequence<int, 4 * MI>{});
+      locate_mi<MI, NI>(L, tile, EPI, P, m0, n0);
+      fast_epilogue<EPI, MI, NI>(P, m0, n0, acc, std::make_integer_sequence<int, MI * NI>{});
     }
     if (!more) break;
     ++tile;
@@ -898,11 +913,11 @@ __device__ __forceinline__ int wg_index(int& xcd) {
 // bias, aligned outputs; one workgroup per CU.  Starting the K loops of the
 // XCDs at different points keeps the workgroups of one XCD in step (their
 // shared operand panels stay in its L2).
-template <int LAYOUT, int EPI, bool SEG2, int MI>
+template <int LAYOUT, int EPI, bool SEG2, int MI, int NI = 4>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch L) {
   int xcd;
   const int g = wg_index(xcd);
-  tile_loop<LAYOUT, EPI, SEG2, MI>(L, 0, L.tiles, g, gridDim.x, xcd);
+  tile_loop<LAYOUT, EPI, SEG2, MI, NI>(L, 0, L.tiles, g, gridDim.x, xcd);
 }
 
 // Two problems of different operand layouts in one launch: workgroups
@@ -1157,7 +1172,10 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   // The row-parallel backward pair (TN weight gradient, NT input gradient) in
   // one launch, when all their tiles are whole and sharing the CUs beats
-  // running them one after the other.
+  // running them one after the other.  (Smaller tiles that would balance the
+  // c2 pair exactly -- 192 x 256 weight-gradient tiles beside 128 x 256
+  // input-gradient tiles, 1.5 tile-times per CU instead of 2 -- ran it
+  // slower: a stage's barrier and copies are paid for fewer MFMAs.)
   if (L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
       L.p[1].epi == E_STORE && L.p[0].nseg == 1 && L.p[1].nseg == 1 && fast_ok(L.p[0]) && fast_ok(L.p[1]) &&
       L.p[0].M % BM == 0 && L.p[0].N % BN == 0 && L.p[1].M % BM == 0 && L.p[1].N % BN == 0 && cus % 8 == 0) {
@@ -1177,6 +1195,7 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
       D.p[1].tile_begin = (int)t0;
       D.tiles = (int)(t0 + t1);
       D.g0 = g0;
+      D.half_tail = 0;
       hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT>), dim3(cus), dim3(NTHREADS), 0, s, D);
       return hipGetLastError();
     }
@@ -1193,6 +1212,38 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   bool fast = true;
   for (int i = 0; i < L.nprob; ++i) fast = fast && fast_ok(L.p[i]);
+  // Weight gradients (TN) may take 256 x 192 tiles when those fill the CUs
+  // in fewer 256 x 256-tile times (the c2 column backward: two 4096 x 1536
+  // problems are 192 whole tiles, 75 % of 256 CUs, or 256 tiles of
+  // 256 x 192, one round of three quarters the length).  Every tile then
+  // takes the fast kernel (columns past N are masked in 8-column chunks).
+  if (fast && L.p[0].layout == L_TN && L.p[0].epi == E_STORE && L.p[0].nseg == 1 &&
+      (L.nprob == 1 || L.p[1].nseg == 1)) {
+    bool n8 = true;
+    int64_t n44 = 0, n43 = 0;
+    for (int i = 0; i < L.nprob; ++i) {
+      const Problem& P = L.p[i];
+      n8 = n8 && (P.N & 7) == 0;
+      n44 += (P.M + BM - 1) / BM * ((P.N + BN - 1) / BN);
+      n43 += (P.M + BM - 1) / BM * ((P.N + 191) / 192);
+    }
+    if (n8 && n43 < INT_MAX && (n43 + cus - 1) / cus * 12 < (n44 + cus - 1) / cus * 16) {
+      GemmLaunch G = L;
+      int nt = 0;
+      for (int i = 0; i < L.nprob; ++i) {
+        G.p[i].tiles_m = (int)((L.p[i].M + BM - 1) / BM);
+        G.p[i].tiles_n = (int)((L.p[i].N + 191) / 192);
+        G.p[i].tile_begin = nt;
+        G.p[i].edge_only = 0;
+        nt += G.p[i].tiles_m * G.p[i].tiles_n;
+      }
+      G.tiles = nt;
+      G.half_tail = 0;
+      hipLaunchKernelGGL((gemm_bf16_kernel<L_TN, E_STORE, false, 4, 3>), dim3(std::min(nt, cus)), dim3(NTHREADS), 0,
+                         s, G);
+      return hipGetLastError();
+    }
+  }
   GemmLaunch F = L, E = L;   // fast-kernel tiles, remaining tiles (generic kernel)
   int nf = 0, ne = 0;
   int64_t W = 0;
@@ -1225,12 +1276,14 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     const int rem = nf % cus;
     const int tail = (half_ok && nf > cus && rem > 0 && 2 * rem <= cus) ? rem : 0;
     F.tiles = nf - tail;
+    F.half_tail = 0;
     hipError_t e = dispatch<true>(F, F.tiles, std::min(F.tiles, cus), s);
     if (e != hipSuccess) return e;
     if (tail > 0) {
       GemmLaunch H = F;
       H.tiles = 2 * tail;
       H.half_base = nf - tail;
+      H.half_tail = 1;
       e = dispatch<true, true>(H, H.tiles, H.tiles, s);
       if (e != hipSuccess) return e;
     }

@@ -61,6 +61,7 @@ struct GemmLaunch {
   int tiles;             // bf16 whole-tile kernels: tiles of the launch
   int g0;                // two-layout launch: workgroups of problem 0
   int half_base;         // half-tile launch: first (256-row) tile it splits
+  int half_tail;         // 1: a half-tile tail launch (tiles are halves from half_base on)
 };
 
 struct CEArgs {

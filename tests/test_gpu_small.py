@@ -146,7 +146,7 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
 
 # Whole 256 x 256 tiles only (the persistent whole-tile kernels; for the row
 # backward, its two GEMMs share one launch).
-TILE_SHAPES = [(512, 256, 768), (768, 512, 256)]
+TILE_SHAPES = [(512, 256, 768), (768, 512, 256), (2048, 1024, 768)]
 
 
 @pytest.mark.parametrize("act", ["none", "swiglu"])
@@ -175,6 +175,26 @@ def test_row_bwd_whole_tiles(shape):
     rdX, rdB, _ = oracle.row_bwd(d["dZ"].f64, d["dY"].f64, d["B"].f64)
     assert_close("dX", host64(dX), rdX, TOL[dtype])
     assert_close("dB", host64(dB), rdB, TOL[dtype])
+
+
+@pytest.mark.parametrize("act", ["none", "swiglu"])
+def test_column_bwd_wgrad_narrow_tiles_two_rounds(act):
+    # Weight gradient [2560, 7680] (per problem): 300 tiles of 256 x 256 or
+    # 400 of 256 x 192 on 256 CUs -- two rounds either way, so the narrow
+    # tiles are taken and workgroups run one or two tiles in a row.
+    M, N, K = 64, 7680 // (2 if act == "swiglu" else 1), 2560
+    dtype = syn.BF16
+    d = _inputs(dtype, M, N, K, 23, act)
+    sw = act == "swiglu"
+    dX, dA, dA2, _, _ = ops.column_bwd(dev(d["dY"]), dev(d["X"]), dev(d["A"]),
+                                       Pre=dev(d["Pre"]) if sw else None, act=act, A2=dev(d["A2"]) if sw else None)
+    torch.cuda.synchronize()
+    r = oracle.column_bwd(d["dY"].f64, d["X"].f64, d["A"].f64, d["Pre"].f64 if sw else None, act,
+                          d["A2"].f64 if sw else None)
+    assert_close("dXpart", host64(dX), r[0], TOL[dtype])
+    assert_close("dA", host64(dA), r[1], TOL[dtype])
+    if sw:
+        assert_close("dA2", host64(dA2), r[2], TOL[dtype])
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
