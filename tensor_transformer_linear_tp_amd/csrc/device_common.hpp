@@ -38,7 +38,10 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
   return cdf + x * pdf;
 }
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Logistic function; the reciprocal is gfx950's v_rcp_f32 (1 ulp) rather than
+// an IEEE division (a ten-instruction sequence per element).  Large |x| gives
+// exactly 0 or 1.
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
 

@@ -135,15 +135,15 @@ __device__ __forceinline__ void st8(T* p, int nv, const float (&v)[8]) {
 // activation backward, RB rows at a time with all their loads issued first
 // (past the matrix the row index repeats the last row: loaded, not used);
 // column sums of dP accumulate into cg (gate or single) and cu (up).
-template <bool FULL, typename T>
+template <bool FULL, int ACT, typename T>
 __device__ __forceinline__ void act_rows(const ActBwdArgs& a, int64_t rb, int ty, int64_t n, int nv, float (&cg)[8],
                                          float (&cu)[8]) {
   constexpr int RB = 4;
-  const bool swiglu = a.act == E_SWIGLU;
+  constexpr bool swiglu = ACT == E_SWIGLU;
   const T* dY = static_cast<const T*>(a.dY);
   // Without an activation there is no Pre (it may be NULL): the pre-activation
   // loads then read dY again (values unused), so every load is unconditional.
-  const bool has_pre = a.act != E_STORE;
+  constexpr bool has_pre = ACT != E_STORE;
   const T* pre = has_pre ? static_cast<const T*>(a.pre) : dY;
   const int64_t ldpre = has_pre ? a.ldpre : a.lddy;
 #pragma unroll
@@ -163,10 +163,10 @@ __device__ __forceinline__ void act_rows(const ActBwdArgs& a, int64_t rb, int ty
       float g[8], u[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (a.act == E_STORE) {
+        if (ACT == E_STORE) {
           g[e] = dy[j][e];
           u[e] = 0.f;
-        } else if (a.act == E_GELU) {
+        } else if (ACT == E_GELU) {
           g[e] = dy[j][e] * gelu_grad_f(gg[j][e]);
           u[e] = 0.f;
         } else {
@@ -187,22 +187,20 @@ __device__ __forceinline__ void act_rows(const ActBwdArgs& a, int64_t rb, int ty
 
 // Block (x = row block, y = column block): 32 column-threads x 8 row-threads
 // over [64 rows] x [256 columns].
-template <typename T>
+template <typename T, int ACT>
 __global__ __launch_bounds__(256) void act_bwd_kernel(const ActBwdArgs a) {
   __shared__ float red[8][2][256];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int64_t n = (int64_t)blockIdx.y * 256 + 8 * tx;
   const int64_t rb = blockIdx.x;
-  const bool swiglu = a.act == E_SWIGLU;
+  constexpr bool swiglu = ACT == E_SWIGLU;
   float cg[8], cu[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) cg[e] = cu[e] = 0.f;
   if (n < a.N) {
     const int nv = (int)min<int64_t>(8, a.N - n);
-    const T* dY = static_cast<const T*>(a.dY);
-    const T* pre = static_cast<const T*>(a.pre);
-    if (nv == 8) act_rows<true, T>(a, rb, ty, n, nv, cg, cu);
-    else act_rows<false, T>(a, rb, ty, n, nv, cg, cu);
+    if (nv == 8) act_rows<true, ACT, T>(a, rb, ty, n, nv, cg, cu);
+    else act_rows<false, ACT, T>(a, rb, ty, n, nv, cg, cu);
   }
   if (!a.colpart) return;   // uniform across the block
 #pragma unroll
@@ -401,8 +399,15 @@ hipError_t launch_sp_rs_ln(int is_bf16, const SpLnArgs& a, hipStream_t s) {
 
 hipError_t launch_act_bwd(int is_bf16, const ActBwdArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.M + kColpartRows - 1) / kColpartRows), (unsigned)((a.N + 255) / 256));
-  if (is_bf16) hipLaunchKernelGGL(act_bwd_kernel<uint16_t>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(act_bwd_kernel<float>, grid, dim3(256), 0, s, a);
+#define TPS_ACT_LAUNCH(T)                                                                                     \
+  do {                                                                                                        \
+    if (a.act == E_SWIGLU) hipLaunchKernelGGL((act_bwd_kernel<T, E_SWIGLU>), grid, dim3(256), 0, s, a);       \
+    else if (a.act == E_GELU) hipLaunchKernelGGL((act_bwd_kernel<T, E_GELU>), grid, dim3(256), 0, s, a);      \
+    else hipLaunchKernelGGL((act_bwd_kernel<T, E_STORE>), grid, dim3(256), 0, s, a);                          \
+  } while (0)
+  if (is_bf16) TPS_ACT_LAUNCH(uint16_t);
+  else TPS_ACT_LAUNCH(float);
+#undef TPS_ACT_LAUNCH
   return hipGetLastError();
 }
 
