@@ -921,17 +921,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch
 }
 
 // Two problems of different operand layouts in one launch: workgroups
-// [0, g0) run problem 0's tiles, the rest problem 1's (plain stores).  Used
-// when one problem alone cannot fill the CUs, e.g. the row-parallel backward,
-// whose weight gradient has few, long tiles and whose input gradient has
-// more, shorter ones.
-template <int LA, int LB>
+// [0, g0) run problem 0's tiles, the rest problem 1's (plain stores), each
+// problem in its own tile shape.  Used when one problem alone cannot fill the
+// CUs, e.g. the row-parallel backward, whose weight gradient has few, long
+// tiles and whose input gradient has more, shorter ones.
+template <int LA, int LB, int MIA = 4, int NIA = 4, int MIB = 4, int NIB = 4>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_dual_kernel(const GemmLaunch L) {
   int xcd;
   const int g = wg_index(xcd);
   const int t1 = L.p[1].tile_begin;
-  if (g < L.g0) tile_loop<LA, E_STORE, false>(L, 0, t1, g, L.g0, xcd);
-  else tile_loop<LB, E_STORE, false>(L, t1, L.tiles - t1, g - L.g0, (int)gridDim.x - L.g0, xcd);
+  if (g < L.g0) tile_loop<LA, E_STORE, false, MIA, NIA>(L, 0, t1, g, L.g0, xcd);
+  else tile_loop<LB, E_STORE, false, MIB, NIB>(L, t1, L.tiles - t1, g - L.g0, (int)gridDim.x - L.g0, xcd);
 }
 
 // Generic kernels: one tile per workgroup, any shape, bias, alignment.
@@ -1147,8 +1147,16 @@ int64_t tile_stages(const Problem& P) {
   return (nk + NSTAGE - 1) / NSTAGE * NSTAGE;
 }
 
+// Whole (64 mi) x (64 ni) tiles of a problem, or -1 if its output does not
+// divide into them.
+int64_t whole_tiles(const Problem& P, int mi, int ni) {
+  const int64_t bm = 64 * mi, bn = 64 * ni;
+  if (P.M % bm || P.N % bn) return -1;
+  return (P.M / bm) * (P.N / bn);
+}
+
 // Problem 0 on g0 workgroups and problem 1 on the rest of `cus`, one launch:
-// the best g0 and its makespan (in tile stages).
+// the best g0 and its makespan (in units of a tile's cost).
 int64_t dual_split(int64_t t0, int64_t s0, int64_t t1, int64_t s1, int cus, int& g0) {
   int64_t best = INT64_MAX;
   g0 = 1;
@@ -1172,23 +1180,43 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   // The row-parallel backward pair (TN weight gradient, NT input gradient) in
   // one launch, when all their tiles are whole and sharing the CUs beats
-  // running them one after the other.  (Smaller tiles that would balance the
-  // c2 pair exactly -- 192 x 256 weight-gradient tiles beside 128 x 256
-  // input-gradient tiles, 1.5 tile-times per CU instead of 2 -- ran it
-  // slower: a stage's barrier and copies are paid for fewer MFMAs.)
+  // running them one after the other.  Tile shapes per problem, from a short
+  // list: 256 x 256 for both, or 192 x 256 weight-gradient tiles beside
+  // 256 x 192 input-gradient tiles (at c2, 1536 x 4096 over 8192 tokens and
+  // 8192 x 1536 over 4096: 128 + 256 tiles that give every CU the same work,
+  // where 96 + 192 whole tiles leave a quarter of the CU-time idle).  A
+  // tile's cost is its stages times its MFMA blocks.  (128 x 256 input-
+  // gradient tiles balance it too but ran slower: a stage's barrier and
+  // copies then serve half the MFMAs.)
   if (L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
       L.p[1].epi == E_STORE && L.p[0].nseg == 1 && L.p[1].nseg == 1 && fast_ok(L.p[0]) && fast_ok(L.p[1]) &&
-      L.p[0].M % BM == 0 && L.p[0].N % BN == 0 && L.p[1].M % BM == 0 && L.p[1].N % BN == 0 && cus % 8 == 0) {
-    const int64_t t0 = (L.p[0].M / BM) * (L.p[0].N / BN), t1 = (L.p[1].M / BM) * (L.p[1].N / BN);
+      cus % 8 == 0) {
+    static constexpr int kGeo[2][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}};   // (MI, NI) of problem 0, of problem 1
     const int64_t s0 = tile_stages(L.p[0]), s1 = tile_stages(L.p[1]);
-    const int64_t apart = (t0 + cus - 1) / cus * s0 + (t1 + cus - 1) / cus * s1;   // one after the other
-    int g0 = 1;
-    const int64_t together = dual_split(t0, s0, t1, s1, cus, g0);
-    if (together < apart && t0 + t1 < INT_MAX) {
+    const int64_t n0 = (L.p[0].M + BM - 1) / BM * ((L.p[0].N + BN - 1) / BN);
+    const int64_t n1 = (L.p[1].M + BM - 1) / BM * ((L.p[1].N + BN - 1) / BN);
+    const int64_t apart = ((n0 + cus - 1) / cus * s0 + (n1 + cus - 1) / cus * s1) * 16;   // one after the other
+    int best = -1, g0 = 1;
+    int64_t best_cost = apart, t0 = 0, t1 = 0;
+    for (int c = 0; c < 2; ++c) {
+      const int64_t a = whole_tiles(L.p[0], kGeo[c][0], kGeo[c][1]);
+      const int64_t b = whole_tiles(L.p[1], kGeo[c][2], kGeo[c][3]);
+      if (a < 0 || b < 0 || a + b >= INT_MAX) continue;
+      int g = 1;
+      const int64_t m = dual_split(a, s0 * kGeo[c][0] * kGeo[c][1], b, s1 * kGeo[c][2] * kGeo[c][3], cus, g);
+      if (m < best_cost) {
+        best_cost = m;
+        best = c;
+        g0 = g;
+        t0 = a;
+        t1 = b;
+      }
+    }
+    if (best >= 0) {
       GemmLaunch D = L;
       for (int i = 0; i < 2; ++i) {
-        D.p[i].tiles_m = (int)(L.p[i].M / BM);
-        D.p[i].tiles_n = (int)(L.p[i].N / BN);
+        D.p[i].tiles_m = (int)(L.p[i].M / (64 * kGeo[best][2 * i]));
+        D.p[i].tiles_n = (int)(L.p[i].N / (64 * kGeo[best][2 * i + 1]));
         D.p[i].edge_only = 0;
       }
       D.p[0].tile_begin = 0;
@@ -1196,7 +1224,10 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
       D.tiles = (int)(t0 + t1);
       D.g0 = g0;
       D.half_tail = 0;
-      hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      if (best == 0)
+        hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      else
+        hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 3, 4, 4, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
       return hipGetLastError();
     }
   }

@@ -144,8 +144,10 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
     assert_close("db", host64(db), rdb, TOL[dtype])
 
 
-# Whole 256 x 256 tiles only (the persistent whole-tile kernels; for the row
-# backward, its two GEMMs share one launch).
+# Whole tiles only (the persistent whole-tile kernels; for the row backward,
+# its two GEMMs share one launch).  (768, 512, 256): 256 x 256 tiles for both
+# GEMMs; (512, 256, 768) and (2048, 1024, 768): 192 x 256 weight-gradient
+# tiles beside 256 x 192 input-gradient tiles.
 TILE_SHAPES = [(512, 256, 768), (768, 512, 256), (2048, 1024, 768)]
 
 
