@@ -858,9 +858,27 @@ __device__ __forceinline__ void locate_mi(const GemmLaunch& L, int tile, int epi
   }
 }
 
-template <int LAYOUT, int EPI, bool SEG2, int MI = 4, int NI = 4>
-__device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count, int g, int G, int xcd) {
-  const int ta = t0 + range_begin(g, count, G), tb = t0 + range_begin(g + 1, count, G);
+// The fused store epilogues of the GEMM kernels (the default of tile_loop).
+template <int EPI, int MI, int NI>
+struct StoreEpilogue {
+  __device__ __forceinline__ void operator()(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[MI][NI]) const {
+    fast_epilogue<EPI, MI, NI>(P, m0, n0, acc, std::make_integer_sequence<int, MI * NI>{});
+  }
+};
+
+// Strided (STRIDED or L.strided): workgroup g runs tiles t0 + g,
+// t0 + g + G, ... instead of a contiguous range, so that the tiles running
+// at one time are neighbours in the grouped order (share operand panels in
+// L2) however many tiles each workgroup runs; for launches of many tiles per
+// workgroup.
+template <int LAYOUT, int EPI, bool SEG2, int MI = 4, int NI = 4, bool STRIDED = false,
+          class Epi = StoreEpilogue<EPI, MI, NI>>
+__device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count, int g, int G, int xcd,
+                                          const Epi& epilogue = Epi{}) {
+  const bool strided = STRIDED || L.strided;
+  const int ta = strided ? t0 + g : t0 + range_begin(g, count, G);
+  const int tb = strided ? t0 + count : t0 + range_begin(g + 1, count, G);
+  const int stride = strided ? G : 1;
   if (ta >= tb) return;
   constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
   Pipe<LAYOUT, DUAL, SEG2, MI, NI> pipe;
@@ -874,13 +892,13 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
   }
   pipe.prologue();
   for (;;) {
-    const bool more = tile + 1 < tb;
+    const bool more = tile + stride < tb;
     f32x16 acc[MI][NI];
     pipe.run_tile(acc, zero_acc<MI, NI>, [&]() {
       if (more) {
         Problem Pn;
         int64_t m0n, n0n;
-        locate_mi<MI, NI>(L, tile + 1, EPI, Pn, m0n, n0n);
+        locate_mi<MI, NI>(L, tile + stride, EPI, Pn, m0n, n0n);
         pipe.nxt = pipe.make_streams(Pn, m0n, n0n, 0, INT_MAX, xcd);
       } else {
         pipe.no_next();
@@ -890,10 +908,10 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
       Problem P;
       int64_t m0, n0;
       locate_mi<MI, NI>(L, tile, EPI, P, m0, n0);
-      fast_epilogue<EPI, MI, NI>(P, m0, n0, acc, std::make_integer_sequence<int, MI * NI>{});
+      epilogue(P, m0, n0, acc);
     }
     if (!more) break;
-    ++tile;
+    tile += stride;
     pipe.cur = pipe.nxt;
   }
   waitcnt<0, 0>();   // trailing (empty) copies retire before the workgroup ends
@@ -953,15 +971,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmL
   generic_epilogue(P, m0, n0, acc);
 }
 
-// Row statistics of one 32-row slice (I) of a wave's 128 x 128 logit block:
-// max and sum exp(z - max) over the valid columns, the target logit if this
-// lane holds it, and the per-wave results in LDS for the cross-wave merge.
-template <int I>
-__device__ __forceinline__ void ce_rows(const CEArgs& a, f32x16 (&acc)[4][4], int64_t m0, int64_t wcol,
+// Row statistics of one 32-row slice (I) of a wave's (32 MI) x 128 logit
+// block: max and sum exp(z - max) over the valid columns, the target logit if
+// this lane holds it, and the per-wave results in LDS for the cross-wave merge.
+template <int I, int MI>
+__device__ __forceinline__ void ce_rows(const CEArgs& a, f32x16 (&acc)[MI][4], int64_t m0, int64_t wcol,
                                         int nvalid, float* ws_tgt, TPS_LDS float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5;
-  const int rl = 128 * wm + 32 * I + (lane & 31);
+  const int rl = 32 * MI * wm + 32 * I + (lane & 31);
   const int64_t m = m0 + rl;
   const int lim = nvalid - 4 * h;     // column c = 32j + 8(r/4) + (r%4) of this lane is valid iff c < lim
   float mx = -INFINITY;
@@ -1019,59 +1037,69 @@ __device__ __forceinline__ void ce_rows(const CEArgs& a, f32x16 (&acc)[4][4], in
   }
 }
 
-template <int... Is>
-__device__ __forceinline__ void ce_rows_seq(const CEArgs& a, f32x16 (&acc)[4][4], int64_t m0, int64_t wcol,
+template <int MI, int... Is>
+__device__ __forceinline__ void ce_rows_seq(const CEArgs& a, f32x16 (&acc)[MI][4], int64_t m0, int64_t wcol,
                                             int nvalid, float* ws_tgt, TPS_LDS float* red,
                                             std::integer_sequence<int, Is...>) {
-  (ce_rows<Is>(a, acc, m0, wcol, nvalid, ws_tgt, red), ...);
+  (ce_rows<Is, MI>(a, acc, m0, wcol, nvalid, ws_tgt, red), ...);
+}
+
+// Cross-wave merge buffer of the CE epilogue, [2 column waves][256 rows][max,
+// sum].  Its own array: in the persistent kernel the LDS ring is already
+// filling with the next tile's stages while the epilogue runs.
+__shared__ __attribute__((aligned(16))) float ce_red[2 * 256 * 2];
+
+// LDS-only workgroup barrier: this wave's LDS accesses are complete
+// (lgkmcnt(0)), the global->LDS copies of later stages stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---- vocab-parallel LM head: logits tile -> (max, sum exp) partials ---------------------
-// Tile (tm, tn) covers tokens [m0, m0+256) and shard vocab columns
-// [n0, n0+256).  Writes ws_ms[tn][m] = (tile max, sum exp(z - tile max)) and,
-// for the tile holding a token's target, ws_tgt[m] = z[m, target - v0].
-__global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const CEArgs a, int tiles_m, int tiles_n) {
-  const int id = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  int tm, tn;
-  tile_coords(id, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  Problem P = {};
-  P.M = a.M;
-  P.N = a.Vr;
-  P.seg[0] = Seg{a.H, a.W, a.ldh, a.ldw, a.K};
-  P.nseg = 1;
-  P.layout = L_NT;
-  P.epi = E_STORE;
-  f32x16 acc[4][4];
-  {
-    Pipe<L_NT, false, false> pipe;
-    pipe.init_wave();
-    pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
-    pipe.prologue();
-    pipe.run_tile(acc, zero_acc<4>, [&]() { pipe.no_next(); });
-    waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
-    __syncthreads();
+// Epilogue of the logit tile (tm, tn): tokens [m0, m0 + 64 MI) and shard
+// vocab columns [n0, n0 + 256).  Writes ws_ms[tn][m] = (tile max, sum
+// exp(z - tile max)) and, for the tile holding a token's target,
+// ws_tgt[m] = z[m, target - v0].  The logits never leave the registers.
+template <int MI>
+struct CeEpilogue {
+  CEArgs a;
+  int tiles_n;
+  __device__ __forceinline__ void operator()(const Problem&, int64_t m0, int64_t n0, f32x16 (&acc)[MI][4]) const {
+    const int wn = (threadIdx.x >> 6) & 1;
+    const int64_t wcol = n0 + 128 * wn;                 // first column of this wave
+    // number of valid columns of this wave, in [0, 128]
+    const int nvalid = (int)max<int64_t>(0, min<int64_t>(128, a.Vr - wcol));
+    float* ws_ms = a.ws;
+    float* ws_tgt = a.ws + 2 * (int64_t)tiles_n * a.M;
+    TPS_LDS float* red = (TPS_LDS float*)ce_red;
+    ce_rows_seq<MI>(a, acc, m0, wcol, nvalid, ws_tgt, red, std::make_integer_sequence<int, MI>{});
+    lds_barrier();
+    const int rl = threadIdx.x;
+    const int64_t m = m0 + rl;
+    const int64_t tn = n0 / BN;
+    if (rl < 64 * MI && m < a.M) {
+      const float ma = red[rl * 2], sa = red[rl * 2 + 1];
+      const float mb = red[(256 + rl) * 2], sb = red[(256 + rl) * 2 + 1];
+      const float mm = fmaxf(ma, mb);
+      const float ss = sa * __expf(ma - mm) + sb * __expf(mb - mm);
+      ws_ms[2 * (tn * a.M + m) + 0] = mm;
+      ws_ms[2 * (tn * a.M + m) + 1] = ss;
+    }
+    lds_barrier();   // red is rewritten by the next tile's epilogue
   }
+};
 
-  const int wn = (threadIdx.x >> 6) & 1;
-  const int64_t wcol = n0 + 128 * wn;                 // first column of this wave
-  // number of valid columns of this wave, in [0, 128]
-  const int nvalid = (int)max<int64_t>(0, min<int64_t>(128, a.Vr - wcol));
-  float* ws_ms = a.ws;
-  float* ws_tgt = a.ws + 2 * (int64_t)tiles_n * a.M;
-  TPS_LDS float* red = (TPS_LDS float*)ring_slot<0>();          // [2][256][2]; the main loop ended on a barrier
-  ce_rows_seq(a, acc, m0, wcol, nvalid, ws_tgt, red, std::make_integer_sequence<int, 4>{});
-  __syncthreads();
-  const int rl = threadIdx.x;
-  const int64_t m = m0 + rl;
-  if (m < a.M) {
-    const float ma = red[rl * 2], sa = red[rl * 2 + 1];
-    const float mb = red[(256 + rl) * 2], sb = red[(256 + rl) * 2 + 1];
-    const float mm = fmaxf(ma, mb);
-    const float ss = sa * __expf(ma - mm) + sb * __expf(mb - mm);
-    ws_ms[2 * ((int64_t)tn * a.M + m) + 0] = mm;
-    ws_ms[2 * ((int64_t)tn * a.M + m) + 1] = ss;
-  }
+// Persistent logit-tile kernel: workgroup g of G runs the tiles g, g + G,
+// ... of the launch (about 9 per workgroup at c5), the next tile's first
+// stages loading during this tile's epilogue (MI = 2: the 128-row halves of
+// a half-tile tail launch).
+template <int MI>
+__global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const GemmLaunch L, const CEArgs a, int tiles_n) {
+  int xcd;
+  const int g = wg_index(xcd);
+  tile_loop<L_NT, E_STORE, false, MI, 4, true>(L, 0, L.tiles, g, gridDim.x, xcd, CeEpilogue<MI>{a, tiles_n});
 }
 
 // Combine the per-tile partials of each token in ascending tile order.
@@ -1224,6 +1252,7 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
       D.tiles = (int)(t0 + t1);
       D.g0 = g0;
       D.half_tail = 0;
+      D.strided = 0;
       if (best == 0)
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT>), dim3(cus), dim3(NTHREADS), 0, s, D);
       else
@@ -1270,6 +1299,7 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
       }
       G.tiles = nt;
       G.half_tail = 0;
+      G.strided = nt >= 3 * cus;
       hipLaunchKernelGGL((gemm_bf16_kernel<L_TN, E_STORE, false, 4, 3>), dim3(std::min(nt, cus)), dim3(NTHREADS), 0,
                          s, G);
       return hipGetLastError();
@@ -1308,6 +1338,7 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     const int tail = (half_ok && nf > cus && rem > 0 && 2 * rem <= cus) ? rem : 0;
     F.tiles = nf - tail;
     F.half_tail = 0;
+    F.strided = F.tiles >= 3 * cus;   // many tiles per workgroup: keep the running tiles adjacent
     hipError_t e = dispatch<true>(F, F.tiles, std::min(F.tiles, cus), s);
     if (e != hipSuccess) return e;
     if (tail > 0) {
@@ -1315,6 +1346,7 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
       H.tiles = 2 * tail;
       H.half_base = nf - tail;
       H.half_tail = 1;
+      H.strided = 0;
       e = dispatch<true, true>(H, H.tiles, H.tiles, s);
       if (e != hipSuccess) return e;
     }
@@ -1329,11 +1361,45 @@ size_t ce_workspace_bytes(int64_t M, int64_t Vr) {
 }
 
 hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s) {
+  int dev = 0, cus = 256;
+  {
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
   const int tiles_m = (int)((a.M + BM - 1) / BM);
   const int tiles_n = (int)((a.Vr + BN - 1) / BN);
-  hipLaunchKernelGGL(ce_tile_kernel, dim3(tiles_m * tiles_n), dim3(NTHREADS), 0, s, a, tiles_m, tiles_n);
+  GemmLaunch L = {};
+  L.nprob = 1;
+  Problem& P = L.p[0];
+  P.M = a.M;
+  P.N = a.Vr;
+  P.seg[0] = Seg{a.H, a.W, a.ldh, a.ldw, a.K};
+  P.nseg = 1;
+  P.layout = L_NT;
+  P.epi = E_STORE;
+  P.tiles_m = tiles_m;
+  P.tiles_n = tiles_n;
+  const int nt = tiles_m * tiles_n;
+  // A last round that would leave over half the CUs idle runs as 128-row
+  // half tiles (M a multiple of 256, so that no half tile starts past the
+  // last row).
+  const int rem = nt % cus;
+  const int tail = (a.M % BM == 0 && nt > cus && rem > 0 && 2 * rem <= cus) ? rem : 0;
+  L.tiles = nt - tail;
+  hipLaunchKernelGGL(ce_tile_kernel<4>, dim3(std::min(L.tiles, cus)), dim3(NTHREADS), 0, s, L, a, tiles_n);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (tail > 0) {
+    GemmLaunch H = L;
+    H.tiles = 2 * tail;
+    H.half_base = nt - tail;
+    H.half_tail = 1;
+    hipLaunchKernelGGL(ce_tile_kernel<2>, dim3(H.tiles), dim3(NTHREADS), 0, s, H, a, tiles_n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)((a.M + 255) / 256)), dim3(256), 0, s, a, tiles_n);
   return hipGetLastError();
 }

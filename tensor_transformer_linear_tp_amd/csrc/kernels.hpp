@@ -62,6 +62,7 @@ struct GemmLaunch {
   int g0;                // two-layout launch: workgroups of problem 0
   int half_base;         // half-tile launch: first (256-row) tile it splits
   int half_tail;         // 1: a half-tile tail launch (tiles are halves from half_base on)
+  int strided;           // 1: workgroup g runs tiles g, g + G, ... (else a contiguous range)
 };
 
 struct CEArgs {
