@@ -1092,9 +1092,9 @@ struct CeEpilogue {
 };
 
 // Persistent logit-tile kernel: workgroup g of G runs the tiles g, g + G,
-// ... of the launch (about 9 per workgroup at c5), the next tile's first
-// stages loading during this tile's epilogue (MI = 2: the 128-row halves of
-// a half-tile tail launch).
+// ... of the launch (about 9 per workgroup for an 8192 x 18992 shard), the
+// next tile's first stages loading during this tile's epilogue (MI = 2: the
+// 128-row halves of a half-tile tail launch).
 template <int MI>
 __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const GemmLaunch L, const CEArgs a, int tiles_n) {
   int xcd;
@@ -1210,7 +1210,7 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   // one launch, when all their tiles are whole and sharing the CUs beats
   // running them one after the other.  Tile shapes per problem, from a short
   // list: 256 x 256 for both, or 192 x 256 weight-gradient tiles beside
-  // 256 x 192 input-gradient tiles (at c2, 1536 x 4096 over 8192 tokens and
+  // 256 x 192 input-gradient tiles (for 1536 x 4096 over 8192 tokens and
   // 8192 x 1536 over 4096: 128 + 256 tiles that give every CU the same work,
   // where 96 + 192 whole tiles leave a quarter of the CU-time idle).  A
   // tile's cost is its stages times its MFMA blocks.  (128 x 256 input-
@@ -1252,7 +1252,7 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
       D.tiles = (int)(t0 + t1);
       D.g0 = g0;
       D.half_tail = 0;
-      D.strided = 0;
+      D.strided = 1;   // measured faster here (one-problem launches of two tiles per CU ran slower strided)
       if (best == 0)
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT>), dim3(cus), dim3(NTHREADS), 0, s, D);
       else
@@ -1273,8 +1273,8 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   bool fast = true;
   for (int i = 0; i < L.nprob; ++i) fast = fast && fast_ok(L.p[i]);
   // Weight gradients (TN) may take 256 x 192 tiles when those fill the CUs
-  // in fewer 256 x 256-tile times (the c2 column backward: two 4096 x 1536
-  // problems are 192 whole tiles, 75 % of 256 CUs, or 256 tiles of
+  // in fewer 256 x 256-tile times (a SwiGLU column backward with two
+  // 4096 x 1536 problems: 192 whole tiles, 75 % of 256 CUs, or 256 tiles of
   // 256 x 192, one round of three quarters the length).  Every tile then
   // takes the fast kernel (columns past N are masked in 8-column chunks).
   if (fast && L.p[0].layout == L_TN && L.p[0].epi == E_STORE && L.p[0].nseg == 1 &&
