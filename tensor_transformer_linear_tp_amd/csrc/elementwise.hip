@@ -90,18 +90,23 @@ __device__ __forceinline__ float to_f<float>(float x) { return x; }
 // 8 columns at p: one 16-byte-aligned vector load when FULL, else the first
 // nv elements one by one (the rest 0).  Callers pass 16-byte-aligned p when
 // FULL (base pointers, leading dimensions and strides are validated so).
-template <bool FULL, typename T>
+// STREAM: a nontemporal load, for data read once (measured ~12 % faster on
+// the partial sums, which read 8 and write 1 buffer of 64 MiB).
+template <bool FULL, typename T, bool STREAM = false>
 __device__ __forceinline__ void ld8(const T* p, int nv, float (&v)[8]) {
   if constexpr (FULL) {
     if constexpr (sizeof(T) == 2) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+      const u32x4* q = reinterpret_cast<const u32x4*>(p);
+      const u32x4 w = STREAM ? __builtin_nontemporal_load(q) : *q;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[2 * e] = __uint_as_float(w[e] << 16);
         v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
       }
     } else {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+      const f32x4* q = reinterpret_cast<const f32x4*>(p);
+      const f32x4 x = STREAM ? __builtin_nontemporal_load(q) : q[0];
+      const f32x4 y = STREAM ? __builtin_nontemporal_load(q + 1) : q[1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[e] = x[e];
@@ -115,15 +120,22 @@ __device__ __forceinline__ void ld8(const T* p, int nv, float (&v)[8]) {
 }
 
 // Store of 8 columns at p: one 16-byte vector store when FULL (p 16-byte
-// aligned), else the first nv elements.
-template <bool FULL, typename T>
+// aligned), else the first nv elements.  STREAM: a nontemporal store.
+template <bool FULL, typename T, bool STREAM = false>
 __device__ __forceinline__ void st8(T* p, int nv, const float (&v)[8]) {
   if constexpr (FULL && sizeof(T) == 2) {
-    *reinterpret_cast<u32x4*>(p) =
-        u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+    const u32x4 w = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+    if (STREAM) __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = w;
   } else if constexpr (FULL) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    const f32x4 x = {v[0], v[1], v[2], v[3]}, y = {v[4], v[5], v[6], v[7]};
+    if (STREAM) {
+      __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+      __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(p + 4));
+    } else {
+      *reinterpret_cast<f32x4*>(p) = x;
+      *reinterpret_cast<f32x4*>(p + 4) = y;
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -152,9 +164,9 @@ __device__ __forceinline__ void act_rows(const ActBwdArgs& a, int64_t rb, int ty
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int64_t m = min<int64_t>(rb * kColpartRows + ty + 8 * (q0 + j), a.M - 1);
-      ld8<FULL>(dY + m * a.lddy + n, nv, dy[j]);
-      ld8<FULL>(pre + m * ldpre + n, nv, gg[j]);
-      ld8<FULL>(pre + m * ldpre + (swiglu ? a.N : 0) + n, nv, uu[j]);   // up half (SwiGLU only)
+      ld8<FULL, T, true>(dY + m * a.lddy + n, nv, dy[j]);
+      ld8<FULL, T, true>(pre + m * ldpre + n, nv, gg[j]);
+      ld8<FULL, T, true>(pre + m * ldpre + (swiglu ? a.N : 0) + n, nv, uu[j]);   // up half (SwiGLU only)
     }
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
@@ -242,7 +254,7 @@ __device__ __forceinline__ void sum_parts8(const T* p, int64_t stride, int t, in
   for (int i0 = 0; i0 < t; i0 += G) {
     float v[G][8];
 #pragma unroll
-    for (int j = 0; j < G; ++j) ld8<FULL>(p + min(i0 + j, t - 1) * stride, nv, v[j]);
+    for (int j = 0; j < G; ++j) ld8<FULL, T, true>(p + min(i0 + j, t - 1) * stride, nv, v[j]);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
 #pragma unroll
@@ -269,7 +281,8 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const SumArgs a) {
     else sum_parts8<false, T, 8>(parts + m * a.ld + n, a.part_stride, a.t, nv, acc);
     if (bias)
       for (int e = 0; e < nv; ++e) acc[e] += to_f<T>(bias[n + e]);
-    store8<T>(out + m * a.ldo + n, nv, acc);
+    if (nv == 8) st8<true, T, true>(out + m * a.ldo + n, nv, acc);   // 16-byte aligned: validated base and ld
+    else store8<T>(out + m * a.ldo + n, nv, acc);
   }
 }
 
