@@ -1102,19 +1102,34 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const GemmLaunch L
   tile_loop<L_NT, E_STORE, false, MI, 4, true>(L, 0, L.tiles, g, gridDim.x, xcd, CeEpilogue<MI>{a, tiles_n});
 }
 
-// Combine the per-tile partials of each token in ascending tile order.
+// Combine the per-tile partials of each token: 8 lanes per token, lane j
+// folding tiles j, j + 8, ... in ascending order, then the lanes' pairs
+// combined by a butterfly over lane ^ 1, ^ 2, ^ 4.  Max and the two-term sum
+// are commutative, so every lane ends with the same bits and the result is
+// fixed (it does not depend on scheduling).
+__device__ __forceinline__ void lse_fold(float& m, float& s, float mt, float st) {
+  const float mn = fmaxf(m, mt);
+  s = mn == -INFINITY ? 0.f : s * __expf(m - mn) + st * __expf(mt - mn);
+  m = mn;
+}
+
 __global__ __launch_bounds__(256) void ce_merge_kernel(const CEArgs a, int tiles_n) {
-  const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (m >= a.M) return;
+  const int64_t m = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+  const int j = threadIdx.x & 7;
+  const int64_t mr = m < a.M ? m : a.M - 1;   // past the end: a repeat, kept in the shuffles, not written
   const float* ws_ms = a.ws;
   const float* ws_tgt = a.ws + 2 * (int64_t)tiles_n * a.M;
-  float mm = ws_ms[2 * m], ss = ws_ms[2 * m + 1];
-  for (int t = 1; t < tiles_n; ++t) {
-    const float mt = ws_ms[2 * ((int64_t)t * a.M + m)], st = ws_ms[2 * ((int64_t)t * a.M + m) + 1];
-    const float mn = fmaxf(mm, mt);
-    ss = ss * __expf(mm - mn) + st * __expf(mt - mn);
-    mm = mn;
+  float mm = -INFINITY, ss = 0.f;
+  for (int t = j; t < tiles_n; t += 8) {
+    const float* p = ws_ms + 2 * ((int64_t)t * a.M + mr);
+    lse_fold(mm, ss, p[0], p[1]);
   }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    const float mo = __shfl_xor(mm, o), so = __shfl_xor(ss, o);
+    lse_fold(mm, ss, mo, so);
+  }
+  if (m >= a.M || j != 0) return;
   const int64_t tg = (int64_t)a.target[m] - a.v0;
   a.out_max[m] = mm;
   a.out_sumexp[m] = ss;
@@ -1400,7 +1415,7 @@ hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)((a.M + 255) / 256)), dim3(256), 0, s, a, tiles_n);
+  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)((a.M + 31) / 32)), dim3(256), 0, s, a, tiles_n);
   return hipGetLastError();
 }
 
