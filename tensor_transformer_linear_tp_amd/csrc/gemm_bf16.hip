@@ -1190,12 +1190,11 @@ int64_t tile_stages(const Problem& P) {
   return (nk + NSTAGE - 1) / NSTAGE * NSTAGE;
 }
 
-// Whole (64 mi) x (64 ni) tiles of a problem, or -1 if its output does not
-// divide into them.
-int64_t whole_tiles(const Problem& P, int mi, int ni) {
+// (64 mi) x (64 ni) tiles covering a problem's output (the last row and
+// column of tiles may overhang it).
+int64_t tiles_of(const Problem& P, int mi, int ni) {
   const int64_t bm = 64 * mi, bn = 64 * ni;
-  if (P.M % bm || P.N % bn) return -1;
-  return (P.M / bm) * (P.N / bn);
+  return (P.M + bm - 1) / bm * ((P.N + bn - 1) / bn);
 }
 
 // Problem 0 on g0 workgroups and problem 1 on the rest of `cus`, one launch:
@@ -1222,31 +1221,34 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   // The row-parallel backward pair (TN weight gradient, NT input gradient) in
-  // one launch, when all their tiles are whole and sharing the CUs beats
-  // running them one after the other.  Tile shapes per problem, from a short
-  // list: 256 x 256 for both, or 192 x 256 weight-gradient tiles beside
-  // 256 x 192 input-gradient tiles (for 1536 x 4096 over 8192 tokens and
-  // 8192 x 1536 over 4096: 128 + 256 tiles that give every CU the same work,
-  // where 96 + 192 whole tiles leave a quarter of the CU-time idle).  A
-  // tile's cost is its stages times its MFMA blocks.  (128 x 256 input-
-  // gradient tiles balance it too but ran slower: a stage's barrier and
-  // copies then serve half the MFMAs.)
+  // one launch, when sharing the CUs beats running them one after the other.
+  // Tile shapes per problem, from a short list: 256 x 256 for both; 192 x 256
+  // weight-gradient tiles beside 256 x 192 input-gradient tiles (for
+  // 1536 x 4096 over 8192 tokens and 8192 x 1536 over 4096: 128 + 256 tiles
+  // that give every CU the same work, where 96 + 192 256 x 256 tiles leave a
+  // quarter of the CU-time idle); 192 x 192 beside 128 x 192 (for a narrow
+  // 512 x 4096 weight gradient over 8192 tokens: 66 tiles instead of 32).
+  // Tiles may overhang the outputs (masked stores; N a multiple of 8).  A
+  // tile's cost is its stages times (MFMA blocks + 2), as for one-problem
+  // launches.  (128 x 256 input-gradient tiles beside 192 x 256 balance the
+  // first case too but ran slower: a stage's barrier and copies then serve
+  // half the MFMAs.)
   if (L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
       L.p[1].epi == E_STORE && L.p[0].nseg == 1 && L.p[1].nseg == 1 && fast_ok(L.p[0]) && fast_ok(L.p[1]) &&
-      cus % 8 == 0) {
-    static constexpr int kGeo[2][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}};   // (MI, NI) of problem 0, of problem 1
+      (L.p[0].N & 7) == 0 && (L.p[1].N & 7) == 0 && cus % 8 == 0) {
+    static constexpr int kGeo[3][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}};   // (MI, NI) of problem 0, 1
     const int64_t s0 = tile_stages(L.p[0]), s1 = tile_stages(L.p[1]);
-    const int64_t n0 = (L.p[0].M + BM - 1) / BM * ((L.p[0].N + BN - 1) / BN);
-    const int64_t n1 = (L.p[1].M + BM - 1) / BM * ((L.p[1].N + BN - 1) / BN);
-    const int64_t apart = ((n0 + cus - 1) / cus * s0 + (n1 + cus - 1) / cus * s1) * 16;   // one after the other
+    const int64_t n0 = tiles_of(L.p[0], 4, 4), n1 = tiles_of(L.p[1], 4, 4);
+    const int64_t apart = ((n0 + cus - 1) / cus * s0 + (n1 + cus - 1) / cus * s1) * 18;   // one after the other
     int best = -1, g0 = 1;
     int64_t best_cost = apart, t0 = 0, t1 = 0;
-    for (int c = 0; c < 2; ++c) {
-      const int64_t a = whole_tiles(L.p[0], kGeo[c][0], kGeo[c][1]);
-      const int64_t b = whole_tiles(L.p[1], kGeo[c][2], kGeo[c][3]);
-      if (a < 0 || b < 0 || a + b >= INT_MAX) continue;
+    for (int c = 0; c < 3; ++c) {
+      const int64_t a = tiles_of(L.p[0], kGeo[c][0], kGeo[c][1]);
+      const int64_t b = tiles_of(L.p[1], kGeo[c][2], kGeo[c][3]);
+      if (a + b >= INT_MAX) continue;
       int g = 1;
-      const int64_t m = dual_split(a, s0 * kGeo[c][0] * kGeo[c][1], b, s1 * kGeo[c][2] * kGeo[c][3], cus, g);
+      const int64_t w0 = s0 * (kGeo[c][0] * kGeo[c][1] + 2), w1 = s1 * (kGeo[c][2] * kGeo[c][3] + 2);
+      const int64_t m = dual_split(a, w0, b, w1, cus, g);
       if (m < best_cost) {
         best_cost = m;
         best = c;
@@ -1258,8 +1260,9 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     if (best >= 0) {
       GemmLaunch D = L;
       for (int i = 0; i < 2; ++i) {
-        D.p[i].tiles_m = (int)(L.p[i].M / (64 * kGeo[best][2 * i]));
-        D.p[i].tiles_n = (int)(L.p[i].N / (64 * kGeo[best][2 * i + 1]));
+        const int64_t bm = 64 * kGeo[best][2 * i], bn = 64 * kGeo[best][2 * i + 1];
+        D.p[i].tiles_m = (int)((L.p[i].M + bm - 1) / bm);
+        D.p[i].tiles_n = (int)((L.p[i].N + bn - 1) / bn);
         D.p[i].edge_only = 0;
       }
       D.p[0].tile_begin = 0;
@@ -1270,8 +1273,10 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
       D.strided = 1;   // measured faster here (one-problem launches of two tiles per CU ran slower strided)
       if (best == 0)
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT>), dim3(cus), dim3(NTHREADS), 0, s, D);
-      else
+      else if (best == 1)
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 3, 4, 4, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      else
+        hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 3, 3, 2, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
       return hipGetLastError();
     }
   }
@@ -1287,27 +1292,52 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   bool fast = true;
   for (int i = 0; i < L.nprob; ++i) fast = fast && fast_ok(L.p[i]);
-  // Weight gradients (TN) may take 256 x 192 tiles when those fill the CUs
-  // in fewer 256 x 256-tile times (a SwiGLU column backward with two
-  // 4096 x 1536 problems: 192 whole tiles, 75 % of 256 CUs, or 256 tiles of
-  // 256 x 192, one round of three quarters the length).  Every tile then
-  // takes the fast kernel (columns past N are masked in 8-column chunks).
-  if (fast && L.p[0].layout == L_TN && L.p[0].epi == E_STORE && L.p[0].nseg == 1 &&
-      (L.nprob == 1 || L.p[1].nseg == 1)) {
-    bool n8 = true;
-    int64_t n44 = 0, n43 = 0;
+  // Narrower tiles for plain-store launches whose 256 x 256 tiles would
+  // leave CUs idle: weight gradients (TN) in 256 x 192 or 192 x 192 tiles,
+  // NN / NT products in 128 x 192 tiles.  A launch's cost is taken as its
+  // rounds times (MFMA blocks per wave + 2), the 2 standing for a K stage's
+  // fixed barrier and copy work (256 x 256: 18; 256 x 192: 14; 192 x 192: 11;
+  // 128 x 192: 8; a 256 x 256 launch whose last round runs as 128-row halves:
+  // 18 per whole round + 10).  Examples: a SwiGLU column backward with two
+  // 4096 x 1536 weight gradients, 192 whole tiles (75 % of 256 CUs) or 256
+  // tiles of 256 x 192 in one round; an 8192 x 768 projection, 96 whole tiles
+  // or 256 tiles of 128 x 192.  Every tile then takes the fast kernel
+  // (columns past N are masked in 8-column chunks).
+  if (fast && L.p[0].epi == E_STORE && L.p[0].nseg == 1 && (L.nprob == 1 || L.p[1].nseg == 1)) {
+    const int lay = L.p[0].layout;
+    static constexpr int kTN[2][2] = {{4, 3}, {3, 3}};
+    static constexpr int kAK[1][2] = {{2, 3}};   // K-contiguous A (NN, NT)
+    const int ncand = lay == L_TN ? 2 : 1;
+    bool n8 = true, half_ok = lay != L_TN;
+    int64_t n44 = 0;
     for (int i = 0; i < L.nprob; ++i) {
       const Problem& P = L.p[i];
       n8 = n8 && (P.N & 7) == 0;
+      half_ok = half_ok && P.M % BM == 0;
       n44 += (P.M + BM - 1) / BM * ((P.N + BN - 1) / BN);
-      n43 += (P.M + BM - 1) / BM * ((P.N + 191) / 192);
     }
-    if (n8 && n43 < INT_MAX && (n43 + cus - 1) / cus * 12 < (n44 + cus - 1) / cus * 16) {
+    const int64_t rem44 = n44 % cus;
+    int64_t best_cost = (half_ok && n44 > cus && rem44 > 0 && 2 * rem44 <= cus) ? n44 / cus * 18 + 10
+                                                                                 : (n44 + cus - 1) / cus * 18;
+    int best = -1;
+    for (int c = 0; c < ncand && n8; ++c) {
+      const int mi = lay == L_TN ? kTN[c][0] : kAK[c][0], ni = lay == L_TN ? kTN[c][1] : kAK[c][1];
+      int64_t n = 0;
+      for (int i = 0; i < L.nprob; ++i)
+        n += (L.p[i].M + 64 * mi - 1) / (64 * mi) * ((L.p[i].N + 64 * ni - 1) / (64 * ni));
+      const int64_t cost = (n + cus - 1) / cus * (mi * ni + 2);
+      if (n < INT_MAX && cost < best_cost) {
+        best_cost = cost;
+        best = c;
+      }
+    }
+    if (best >= 0) {
+      const int mi = lay == L_TN ? kTN[best][0] : kAK[best][0], ni = lay == L_TN ? kTN[best][1] : kAK[best][1];
       GemmLaunch G = L;
       int nt = 0;
       for (int i = 0; i < L.nprob; ++i) {
-        G.p[i].tiles_m = (int)((L.p[i].M + BM - 1) / BM);
-        G.p[i].tiles_n = (int)((L.p[i].N + 191) / 192);
+        G.p[i].tiles_m = (int)((L.p[i].M + 64 * mi - 1) / (64 * mi));
+        G.p[i].tiles_n = (int)((L.p[i].N + 64 * ni - 1) / (64 * ni));
         G.p[i].tile_begin = nt;
         G.p[i].edge_only = 0;
         nt += G.p[i].tiles_m * G.p[i].tiles_n;
@@ -1315,8 +1345,15 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
       G.tiles = nt;
       G.half_tail = 0;
       G.strided = nt >= 3 * cus;
-      hipLaunchKernelGGL((gemm_bf16_kernel<L_TN, E_STORE, false, 4, 3>), dim3(std::min(nt, cus)), dim3(NTHREADS), 0,
-                         s, G);
+      const dim3 grid(std::min(nt, cus)), block(NTHREADS);
+      if (lay == L_TN && mi == 4)
+        hipLaunchKernelGGL((gemm_bf16_kernel<L_TN, E_STORE, false, 4, 3>), grid, block, 0, s, G);
+      else if (lay == L_TN)
+        hipLaunchKernelGGL((gemm_bf16_kernel<L_TN, E_STORE, false, 3, 3>), grid, block, 0, s, G);
+      else if (lay == L_NN)
+        hipLaunchKernelGGL((gemm_bf16_kernel<L_NN, E_STORE, false, 2, 3>), grid, block, 0, s, G);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<L_NT, E_STORE, false, 2, 3>), grid, block, 0, s, G);
       return hipGetLastError();
     }
   }
