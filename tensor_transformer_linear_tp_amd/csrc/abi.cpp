@@ -360,6 +360,23 @@ tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t K, con
         tps::launch_colsum_finalize(dtype == TP_BF16, colpart, colpart_rows(M), ldcp, N, 1, dbias2, s) != hipSuccess)
       return TP_E_HIP;
   }
+  if (dXpart && dA && !swiglu && dtype == TP_BF16) {
+    // dA = X^T dP (TN) and dX_part = dP A^T (NT) in one launch: the library
+    // may run them side by side (few long weight-gradient tiles beside many
+    // short input-gradient ones), as for the row-parallel backward.
+    GemmLaunch L = {};
+    L.nprob = 2;
+    L.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{X, dPg, ldx, ldp, M};
+    L.p[0].c = dA;
+    L.p[0].ldc = ldda;
+    L.p[1] = make_problem(M, K, tps::L_NT, tps::E_STORE);
+    L.p[1].seg[0] = tps::Seg{dPg, A, ldp, lda, N};
+    L.p[1].c = dXpart;
+    L.p[1].ldc = lddx;
+    if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
+    return TP_OK;
+  }
   if (dXpart) {   // dX_part = dP_g A^T (+ dP_u A2^T): NT over K' = N per segment
     GemmLaunch L = {};
     L.nprob = 1;
