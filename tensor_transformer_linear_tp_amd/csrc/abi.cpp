@@ -509,9 +509,8 @@ tp_status tp_vocab_embed_fwd(int dtype, int64_t M, int64_t Vr, int64_t K, const 
 
 size_t tp_vocab_embed_bwd_workspace_bytes(int64_t M, int64_t Vr) {
   if (bad_dim(M) || bad_dim(Vr)) return 0;
-  // row counts [Vr], block totals, row starts [Vr + 1], token order [M]: int32 each
-  return align_ws((size_t)Vr * 4) + align_ws((size_t)tps::emb_bwd_count_blocks(Vr) * 4) +
-         align_ws((size_t)(Vr + 1) * 4) + align_ws((size_t)M * 4);
+  // row starts [Vr + 1] and token order [M]: int32 each
+  return align_ws((size_t)(Vr + 1) * 4) + align_ws((size_t)M * 4);
 }
 
 tp_status tp_vocab_embed_bwd(int dtype, int64_t M, int64_t Vr, int64_t K, const int32_t* ids, int64_t v0,
@@ -526,16 +525,10 @@ tp_status tp_vocab_embed_bwd(int dtype, int64_t M, int64_t Vr, int64_t K, const 
   if (!workspace || ws_bytes < tp_vocab_embed_bwd_workspace_bytes(M, Vr)) return TP_E_WORKSPACE;
   if (!aligned16(workspace)) return TP_E_ALIGN;
   char* w = static_cast<char*>(workspace);
-  const size_t cnt_bytes = align_ws((size_t)Vr * 4);
-  const size_t btot_bytes = align_ws((size_t)tps::emb_bwd_count_blocks(Vr) * 4);
-  const size_t start_bytes = align_ws((size_t)(Vr + 1) * 4);
-  int32_t* cnt = reinterpret_cast<int32_t*>(w);
-  int32_t* btot = reinterpret_cast<int32_t*>(w + cnt_bytes);
-  int32_t* start = reinterpret_cast<int32_t*>(w + cnt_bytes + btot_bytes);
-  int32_t* order = reinterpret_cast<int32_t*>(w + cnt_bytes + btot_bytes + start_bytes);
+  int32_t* start = reinterpret_cast<int32_t*>(w);
+  int32_t* order = reinterpret_cast<int32_t*>(w + align_ws((size_t)(Vr + 1) * 4));
   const tps::EmbArgs a = {M, Vr, K, ids, v0, dout, lddo, dE, ldde};
-  const hipError_t e =
-      tps::launch_emb_bwd(dtype == TP_BF16, a, cnt, btot, start, order, static_cast<hipStream_t>(stream));
+  const hipError_t e = tps::launch_emb_bwd(dtype == TP_BF16, a, start, order, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TP_OK : TP_E_HIP;
 }
 

@@ -3,13 +3,12 @@
 // (per-row sums of the owned tokens' output gradients).
 //
 // The backward groups tokens by table row without atomics on any value:
-//   1. emb_count_kernel    one workgroup per 256 table rows counts the owned
-//                          tokens of each row (integer LDS counters) and of
-//                          the block;
-//   2. emb_order_kernel    one workgroup per 256 rows turns the counts into row
-//                          starts and lists each row's tokens in ascending m
-//                          (a stable counting sort of the owned tokens);
-//   3. emb_bwd_rows_kernel one workgroup per table row sums its tokens'
+//   1. emb_order_kernel    one workgroup per 256 table rows counts the owned
+//                          tokens of each of its rows (integer LDS counters)
+//                          and of all earlier rows, turns them into row starts
+//                          and lists each row's tokens in ascending m (a
+//                          stable counting sort of the owned tokens);
+//   2. emb_bwd_rows_kernel one workgroup per table row sums its tokens'
 //                          gradient rows in that order (fp32) and writes the
 //                          row once; rows without tokens are written as zeros.
 // The result is independent of scheduling: the order of every sum is fixed.
@@ -88,50 +87,46 @@ __device__ __forceinline__ void block_rows8(const EmbArgs& a, int64_t m0, int64_
   }
 }
 
-// cnt[v] = number of tokens whose id is v0 + v, for the workgroup's 256 rows;
-// btot[block] = their sum.
-__global__ __launch_bounds__(256) void emb_count_kernel(const EmbArgs a, int32_t* cnt, int32_t* btot) {
-  __shared__ int32_t c[kRowsPerBlock];
-  __shared__ int64_t tmp[256];
-  const int64_t base = (int64_t)blockIdx.x * kRowsPerBlock;
-  c[threadIdx.x] = 0;
-  __syncthreads();
-  for (int64_t m0 = 0; m0 < a.M; m0 += 256 * kIdBatch) {
-    int32_t rr[kIdBatch];
-    block_rows8(a, m0, base, rr);
-#pragma unroll
-    for (int j = 0; j < kIdBatch; ++j)
-      if (rr[j] >= 0) atomicAdd(&c[rr[j]], 1);   // integer count: order-independent
-  }
-  __syncthreads();
-  const int64_t v = base + threadIdx.x;
-  const int64_t own = v < a.Vr ? c[threadIdx.x] : 0;
-  if (v < a.Vr) cnt[v] = (int32_t)own;
-  int64_t total;
-  (void)block_excl_scan256(own, tmp, total);
-  if (threadIdx.x == 0) btot[blockIdx.x] = (int32_t)total;
-}
-
 // Row starts (start[v], start[Vr] = owned tokens) and the owned tokens listed
-// row by row, ascending m within a row.  Tokens are taken 2048 at a time: an
-// order-preserving compaction of the block's tokens into LDS, then each
-// listed token's rank among the earlier listed tokens of its row.
-__global__ __launch_bounds__(256) void emb_order_kernel(const EmbArgs a, const int32_t* cnt, const int32_t* btot,
-                                                        int32_t* start, int32_t* order) {
+// row by row, ascending m within a row.  A first pass over the ids counts
+// the tokens of each of the workgroup's rows and the owned tokens of all
+// earlier rows (every workgroup reads all ids, so no workgroup waits for
+// another).  Then tokens are taken 2048 at a time: an order-preserving
+// compaction of the block's tokens into LDS, then each listed token's rank
+// among the earlier listed tokens of its row.
+__global__ __launch_bounds__(256) void emb_order_kernel(const EmbArgs a, int32_t* start, int32_t* order) {
   constexpr int NB = 256 * kIdBatch;
   __shared__ int64_t tmp[256];
   __shared__ int32_t rstart[kRowsPerBlock];   // first slot of each row of this block
-  __shared__ int32_t running[kRowsPerBlock];  // tokens of the row already placed
+  __shared__ int32_t running[kRowsPerBlock];  // tokens of the row already placed; first the row counts
   __shared__ int32_t lrow[NB], lm[NB], upd[NB];
   __shared__ int32_t wcount[kIdBatch][4];
   const int64_t base = (int64_t)blockIdx.x * kRowsPerBlock;
   const int64_t nrows = min<int64_t>(kRowsPerBlock, a.Vr - base);
 
-  int64_t before = 0;   // owned tokens of all earlier blocks
-  for (int64_t i = threadIdx.x; i < (int64_t)blockIdx.x; i += 256) before += btot[i];
+  running[threadIdx.x] = 0;
+  __syncthreads();
+  int64_t before = 0;   // this thread's owned tokens of rows before the block
+  for (int64_t m0 = 0; m0 < a.M; m0 += NB) {
+    int32_t id[kIdBatch];
+#pragma unroll
+    for (int j = 0; j < kIdBatch; ++j) {
+      const int64_t m = m0 + threadIdx.x + 256 * j;
+      id[j] = a.ids[m < a.M ? m : a.M - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kIdBatch; ++j) {
+      const int64_t m = m0 + threadIdx.x + 256 * j;
+      const int64_t r = owned_row(id[j], a.v0, a.Vr);
+      if (m >= a.M || r < 0) continue;
+      if (r < base) ++before;
+      else if (r < base + kRowsPerBlock) atomicAdd(&running[r - base], 1);   // integer count: order-independent
+    }
+  }
+  __syncthreads();
   int64_t all_before;
   (void)block_excl_scan256(before, tmp, all_before);
-  const int64_t own = threadIdx.x < nrows ? cnt[base + threadIdx.x] : 0;
+  const int64_t own = threadIdx.x < nrows ? running[threadIdx.x] : 0;
   int64_t block_total;
   const int64_t ex = block_excl_scan256(own, tmp, block_total);
   rstart[threadIdx.x] = (int32_t)(all_before + ex);
@@ -275,13 +270,9 @@ hipError_t launch_emb_fwd(int is_bf16, const EmbArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int64_t emb_bwd_count_blocks(int64_t Vr) { return (Vr + kRowsPerBlock - 1) / kRowsPerBlock; }
-
-hipError_t launch_emb_bwd(int is_bf16, const EmbArgs& a, int32_t* cnt, int32_t* btot, int32_t* start,
-                          int32_t* order, hipStream_t s) {
-  const unsigned nb = (unsigned)emb_bwd_count_blocks(a.Vr);
-  hipLaunchKernelGGL(emb_count_kernel, dim3(nb), dim3(256), 0, s, a, cnt, btot);
-  hipLaunchKernelGGL(emb_order_kernel, dim3(nb), dim3(256), 0, s, a, cnt, btot, start, order);
+hipError_t launch_emb_bwd(int is_bf16, const EmbArgs& a, int32_t* start, int32_t* order, hipStream_t s) {
+  const unsigned nb = (unsigned)((a.Vr + kRowsPerBlock - 1) / kRowsPerBlock);
+  hipLaunchKernelGGL(emb_order_kernel, dim3(nb), dim3(256), 0, s, a, start, order);
   if (is_bf16) hipLaunchKernelGGL(emb_bwd_rows_kernel<uint16_t>, dim3((unsigned)a.Vr), dim3(256), 0, s, a, start, order);
   else hipLaunchKernelGGL(emb_bwd_rows_kernel<float>, dim3((unsigned)a.Vr), dim3(256), 0, s, a, start, order);
   return hipGetLastError();

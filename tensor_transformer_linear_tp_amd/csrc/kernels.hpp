@@ -201,10 +201,7 @@ size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int n_q, int n_kv, int cau
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
 void attn_bwd_layout(int64_t B, int64_t S, int n_q, int n_kv, int causal, AttnBwdLayout& L);
 hipError_t launch_attn_bwd(const AttnBwdArgs& p, hipStream_t s);
-int64_t emb_bwd_count_blocks(int64_t Vr);
-// cnt [Vr], btot [emb_bwd_count_blocks(Vr)], start [Vr + 1] and order [M]
-// int32 come from the caller's workspace.
-hipError_t launch_emb_bwd(int is_bf16, const EmbArgs& a, int32_t* cnt, int32_t* btot, int32_t* start,
-                          int32_t* order, hipStream_t s);
+// start [Vr + 1] and order [M] int32 come from the caller's workspace.
+hipError_t launch_emb_bwd(int is_bf16, const EmbArgs& a, int32_t* start, int32_t* order, hipStream_t s);
 
 }  // namespace tps
