@@ -52,21 +52,26 @@ __global__ __launch_bounds__(256) void emb_fwd_kernel(const EmbArgs a) {
 
 constexpr int kIdBatch = 8;   // ids per thread loaded together (2048 per workgroup)
 
-// Exclusive prefix sum of x over the 256 threads (x >= 0), fixed order;
-// total = the sum over all threads.
+// Exclusive prefix sum of x over the 256 threads (x >= 0; integers, so the
+// result does not depend on the order of the additions); total = the sum
+// over all threads.  Each wave scans its 64 values with shuffles, then the
+// four wave totals are exchanged through LDS (tmp: 4 entries).
 __device__ __forceinline__ int64_t block_excl_scan256(int64_t x, int64_t* tmp, int64_t& total) {
-  tmp[threadIdx.x] = x;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int64_t y = threadIdx.x >= (unsigned)o ? tmp[threadIdx.x - o] : 0;
-    __syncthreads();
-    tmp[threadIdx.x] += y;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(v, o);
+    if (lane >= o) v += y;
   }
-  total = tmp[255];
-  const int64_t incl = tmp[threadIdx.x];
+  if (lane == 63) tmp[wave] = v;
   __syncthreads();
-  return incl - x;
+  int64_t before = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < wave ? tmp[w] : 0;
+  total = (tmp[0] + tmp[1]) + (tmp[2] + tmp[3]);
+  __syncthreads();   // tmp may be rewritten by the next call
+  return before + v - x;
 }
 
 // Rows (relative to the block at `base`) of the 8 tokens m0 + threadIdx.x +
