@@ -111,16 +111,18 @@ __global__ __launch_bounds__(256) void emb_order_kernel(const EmbArgs a, int32_t
 
   running[threadIdx.x] = 0;
   __syncthreads();
+  // Counting pass: 32 ids per thread in flight (8192 ids per round trip).
+  constexpr int kCountBatch = 32;
   int64_t before = 0;   // this thread's owned tokens of rows before the block
-  for (int64_t m0 = 0; m0 < a.M; m0 += NB) {
-    int32_t id[kIdBatch];
+  for (int64_t m0 = 0; m0 < a.M; m0 += 256 * kCountBatch) {
+    int32_t id[kCountBatch];
 #pragma unroll
-    for (int j = 0; j < kIdBatch; ++j) {
+    for (int j = 0; j < kCountBatch; ++j) {
       const int64_t m = m0 + threadIdx.x + 256 * j;
       id[j] = a.ids[m < a.M ? m : a.M - 1];
     }
 #pragma unroll
-    for (int j = 0; j < kIdBatch; ++j) {
+    for (int j = 0; j < kCountBatch; ++j) {
       const int64_t m = m0 + threadIdx.x + 256 * j;
       const int64_t r = owned_row(id[j], a.v0, a.Vr);
       if (m >= a.M || r < 0) continue;
