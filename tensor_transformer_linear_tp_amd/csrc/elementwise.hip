@@ -305,11 +305,93 @@ __device__ __forceinline__ void for_each_chunk(F&& f, std::integer_sequence<int,
   (f(std::integral_constant<int, C>{}), ...);
 }
 
+// bf16 element e (0..7) of an 8-column chunk held as 4 raw words.
+__device__ __forceinline__ float bf16_at(const u32x4& w, int e) {
+  return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+}
+
+// The common case of sp_rs_ln_kernel (bf16, N = 2048 CH with CH <= 2 so that
+// every thread holds CH whole chunks in ~100 registers, t <= 8): every load
+// of the row -- the t partials,
+// bias, residual, gamma and beta of all CH chunks -- is issued before any is
+// used, so the row costs one round trip to memory; the raw words are kept
+// until they are added.  Same arithmetic, in the same order, as the general
+// path.  (Absent vectors load partial 0 instead and are not used.)
+template <int CH>
+__device__ __forceinline__ void sp_rs_ln_row_bf16(const SpLnArgs& a, float* red) {
+  const int64_t m = blockIdx.x;
+  const int64_t row = a.r0 + m;
+  const uint16_t* parts = static_cast<const uint16_t*>(a.parts);
+  const uint16_t* bias = static_cast<const uint16_t*>(a.bias);
+  const uint16_t* resid = static_cast<const uint16_t*>(a.resid);
+  const uint16_t* gamma = static_cast<const uint16_t*>(a.gamma);
+  const uint16_t* beta = static_cast<const uint16_t*>(a.beta);
+  u32x4 pv[CH][8], bv[CH], rv[CH], gv[CH], ev[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t n = (int64_t)(threadIdx.x + 256 * c) * 8;
+    const uint16_t* p0 = parts + row * a.ld + n;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t* pi = p0 + (int64_t)min(i, a.t - 1) * a.part_stride;
+      pv[c][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pi));
+    }
+    bv[c] = *reinterpret_cast<const u32x4*>(bias ? bias + n : p0);
+    rv[c] = *reinterpret_cast<const u32x4*>(resid ? resid + m * a.ldr + n : p0);
+    gv[c] = *reinterpret_cast<const u32x4*>(gamma ? gamma + n : p0);
+    ev[c] = *reinterpret_cast<const u32x4*>(beta ? beta + n : p0);
+  }
+  float h[CH][8];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = bf16_at(pv[c][0], e);
+#pragma unroll
+      for (int i = 1; i < 8; ++i)
+        if (i < a.t) x += bf16_at(pv[c][i], e);
+      if (bias) x += bf16_at(bv[c], e);
+      if (resid) x += bf16_at(rv[c], e);
+      h[c][e] = x;
+      s += x;
+    }
+  const float mean = block_sum256(s, red) / (float)a.N;
+  float s2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = h[c][e] - mean;
+      s2 += d * d;
+    }
+  const float var = block_sum256(s2, red) / (float)a.N;
+  const float rstd = 1.0f / sqrtf(var + a.eps);
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  uint16_t* hout = static_cast<uint16_t*>(a.hout);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t n = (int64_t)(threadIdx.x + 256 * c) * 8;
+    if (hout) store8<uint16_t>(hout + m * a.ldh + n, 8, h[c]);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      y[e] = (h[c][e] - mean) * rstd * (gamma ? bf16_at(gv[c], e) : 1.f) + (beta ? bf16_at(ev[c], e) : 0.f);
+    store8<uint16_t>(out + m * a.ldo + n, 8, y);
+  }
+}
+
 // One workgroup per row of the rank's block; each thread holds CH chunks of 8
 // columns in registers (N <= 2048 * CH), so the row is read once.
 template <typename T, int CH>
 __global__ __launch_bounds__(256) void sp_rs_ln_kernel(const SpLnArgs a) {
   __shared__ float red[4];
+  if constexpr (sizeof(T) == 2 && CH <= 2) {
+    if (a.N == 2048 * CH && a.t <= 8) {   // uniform: the whole launch takes one path
+      sp_rs_ln_row_bf16<CH>(a, red);
+      return;
+    }
+  }
   constexpr auto chunks = std::make_integer_sequence<int, CH>{};
   const int64_t m = blockIdx.x;
   const int64_t row = a.r0 + m;

@@ -251,8 +251,11 @@ def test_sp_fig2_halves_on_gpu(dtype):
 
 # (t, M, N, r0, Mr): one column, ragged widths around the 8-wide vectors and the
 # 2048-column chunk steps, the widest row, and rank blocks at both ends.
+# (8, 64, 2048, ...) and (3, 20, 4096, ...): bf16 rows of whole chunks take the kernel's
+# single-round-trip path (t <= 8 partials, 1 or 2 chunks of 8 columns per thread).
 SP_CASES = [(1, 4, 1, 0, 4), (2, 6, 7, 2, 3), (3, 40, 70, 13, 27), (8, 64, 2048, 56, 8), (4, 33, 2049, 0, 11),
-            (8, 24, 4100, 8, 8), (2, 9, 8191, 4, 5), (3, 5, 16384, 1, 3), (8, 16, 12345, 15, 1)]
+            (8, 24, 4100, 8, 8), (2, 9, 8191, 4, 5), (3, 5, 16384, 1, 3), (8, 16, 12345, 15, 1),
+            (3, 20, 4096, 5, 7)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
