@@ -939,6 +939,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch
   tile_loop<LAYOUT, EPI, SEG2, MI, NI>(L, 0, L.tiles, g, gridDim.x, xcd);
 }
 
+// Whole tiles, then the 128-row halves of the last round, in one launch: each
+// workgroup runs its whole tiles (F) and then its half tile (H, at most one
+// per workgroup), so it starts the half tile as soon as its own whole tiles
+// are done.  The second loop's first copies go to ring slots 0-2, which no
+// wave reads after the first loop's last barrier.
+template <int LAYOUT, int EPI>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tail_kernel(const GemmLaunch F, const GemmLaunch H) {
+  int xcd;
+  const int g = wg_index(xcd);
+  tile_loop<LAYOUT, EPI, false, 4, 4>(F, 0, F.tiles, g, gridDim.x, xcd);
+  tile_loop<LAYOUT, EPI, false, 2, 4>(H, 0, H.tiles, g, gridDim.x, xcd);
+}
+
 // Two problems of different operand layouts in one launch: workgroups
 // [0, g0) run problem 0's tiles, the rest problem 1's (plain stores), each
 // problem in its own tile shape.  Used when one problem alone cannot fill the
@@ -1103,6 +1116,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const GemmLaunch L
   tile_loop<L_NT, E_STORE, false, MI, 4, true>(L, 0, L.tiles, g, gridDim.x, xcd, CeEpilogue<MI>{a, tiles_n});
 }
 
+// The whole tiles (F) and then the 128-row halves of the last round (H) in
+// one launch, as gemm_bf16_tail_kernel does for the GEMMs.
+__global__ __launch_bounds__(NTHREADS, 1) void ce_tile_tail_kernel(const GemmLaunch F, const GemmLaunch H,
+                                                                   const CEArgs a, int tiles_n) {
+  int xcd;
+  const int g = wg_index(xcd);
+  tile_loop<L_NT, E_STORE, false, 4, 4, true>(F, 0, F.tiles, g, gridDim.x, xcd, CeEpilogue<4>{a, tiles_n});
+  tile_loop<L_NT, E_STORE, false, 2, 4, false>(H, 0, H.tiles, g, gridDim.x, xcd, CeEpilogue<2>{a, tiles_n});
+}
+
 // Combine the per-tile partials of each token: 8 lanes per token, lane j
 // folding tiles j, j + 8, ... in ascending order, then the lanes' pairs
 // combined by a butterfly over lane ^ 1, ^ 2, ^ 4.  Max and the two-term sum
@@ -1153,9 +1176,8 @@ bool fast_ok(const Problem& P) {
   return true;
 }
 
-// FAST: the fast kernel's tiles (HALF: the 128-row halves of the tiles from half_base on;
-// layouts with a K-contiguous A and one K segment only); else edge tiles.
-template <bool FAST, bool HALF = false>
+// FAST: the fast kernel's tiles; else edge tiles.
+template <bool FAST>
 hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
   const dim3 g(grid), block(NTHREADS);
   const int layout = L.p[0].layout, epi = L.p[0].epi;
@@ -1163,11 +1185,8 @@ hipError_t dispatch(const GemmLaunch& L, int total, int grid, hipStream_t s) {
 #define TPS_LAUNCH(LY, EP, S2)                                                                      \
   do {                                                                                              \
     if constexpr (FAST) {                                                                           \
-      if constexpr (HALF && LY != L_TN && !S2)                                                      \
-        hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, 2>), g, block, 0, s, L);                   \
-      else                                                                                          \
-        hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, 4>), g, block, 0, s, L);                   \
-    } else if constexpr (!FAST) {                                                                   \
+      hipLaunchKernelGGL((gemm_bf16_kernel<LY, EP, S2, 4>), g, block, 0, s, L);                     \
+    } else {                                                                                        \
       hipLaunchKernelGGL((gemm_bf16_edge_kernel<LY, EP, S2>), g, block, 0, s, L, total);            \
     }                                                                                               \
   } while (0)
@@ -1392,15 +1411,28 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     F.tiles = nf - tail;
     F.half_tail = 0;
     F.strided = F.tiles >= 3 * cus;   // many tiles per workgroup: keep the running tiles adjacent
-    hipError_t e = dispatch<true>(F, F.tiles, std::min(F.tiles, cus), s);
-    if (e != hipSuccess) return e;
-    if (tail > 0) {
+    if (tail > 0) {   // F.tiles >= cus: the combined launch has one workgroup per CU
       GemmLaunch H = F;
       H.tiles = 2 * tail;
       H.half_base = nf - tail;
       H.half_tail = 1;
       H.strided = 0;
-      e = dispatch<true, true>(H, H.tiles, H.tiles, s);
+      const int layout = L.p[0].layout, epi = L.p[0].epi;
+      const dim3 grid(cus), block(NTHREADS);
+      if (layout == L_NN && epi == E_SWIGLU)
+        hipLaunchKernelGGL((gemm_bf16_tail_kernel<L_NN, E_SWIGLU>), grid, block, 0, s, F, H);
+      else if (layout == L_NN && epi == E_GELU)
+        hipLaunchKernelGGL((gemm_bf16_tail_kernel<L_NN, E_GELU>), grid, block, 0, s, F, H);
+      else if (layout == L_NN)
+        hipLaunchKernelGGL((gemm_bf16_tail_kernel<L_NN, E_STORE>), grid, block, 0, s, F, H);
+      else if (epi == E_CE_GRAD)
+        hipLaunchKernelGGL((gemm_bf16_tail_kernel<L_NT, E_CE_GRAD>), grid, block, 0, s, F, H);
+      else
+        hipLaunchKernelGGL((gemm_bf16_tail_kernel<L_NT, E_STORE>), grid, block, 0, s, F, H);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else {
+      hipError_t e = dispatch<true>(F, F.tiles, std::min(F.tiles, cus), s);
       if (e != hipSuccess) return e;
     }
   }
@@ -1441,18 +1473,17 @@ hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s) {
   const int rem = nt % cus;
   const int tail = (a.M % BM == 0 && nt > cus && rem > 0 && 2 * rem <= cus) ? rem : 0;
   L.tiles = nt - tail;
-  hipLaunchKernelGGL(ce_tile_kernel<4>, dim3(std::min(L.tiles, cus)), dim3(NTHREADS), 0, s, L, a, tiles_n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (tail > 0) {
+  if (tail > 0) {   // L.tiles >= cus: one workgroup per CU runs its whole tiles, then at most one half
     GemmLaunch H = L;
     H.tiles = 2 * tail;
     H.half_base = nt - tail;
     H.half_tail = 1;
-    hipLaunchKernelGGL(ce_tile_kernel<2>, dim3(H.tiles), dim3(NTHREADS), 0, s, H, a, tiles_n);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ce_tile_tail_kernel, dim3(cus), dim3(NTHREADS), 0, s, L, H, a, tiles_n);
+  } else {
+    hipLaunchKernelGGL(ce_tile_kernel<4>, dim3(std::min(L.tiles, cus)), dim3(NTHREADS), 0, s, L, a, tiles_n);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)((a.M + 31) / 32)), dim3(256), 0, s, a, tiles_n);
   return hipGetLastError();
 }
