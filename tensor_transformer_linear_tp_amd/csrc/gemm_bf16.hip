@@ -939,16 +939,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const GemmLaunch
   tile_loop<LAYOUT, EPI, SEG2, MI, NI>(L, 0, L.tiles, g, gridDim.x, xcd);
 }
 
+// Between two tile loops of different shapes in one workgroup: the first
+// loop's last steps still issue (empty) copies into the ring, and the second
+// loop splits the ring between the waves differently (a 128-row A tile is 2
+// copy blocks per wave, a 256-row one 4), so every wave's copies must have
+// landed before any wave issues the second loop's first ones.
+__device__ __forceinline__ void ring_handover() {
+  waitcnt<0, 0>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Whole tiles, then the 128-row halves of the last round, in one launch: each
 // workgroup runs its whole tiles (F) and then its half tile (H, at most one
 // per workgroup), so it starts the half tile as soon as its own whole tiles
-// are done.  The second loop's first copies go to ring slots 0-2, which no
-// wave reads after the first loop's last barrier.
+// (and its waves' last copies) are done.
 template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tail_kernel(const GemmLaunch F, const GemmLaunch H) {
   int xcd;
   const int g = wg_index(xcd);
   tile_loop<LAYOUT, EPI, false, 4, 4>(F, 0, F.tiles, g, gridDim.x, xcd);
+  ring_handover();
   tile_loop<LAYOUT, EPI, false, 2, 4>(H, 0, H.tiles, g, gridDim.x, xcd);
 }
 
@@ -1123,6 +1134,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_tail_kernel(const GemmLau
   int xcd;
   const int g = wg_index(xcd);
   tile_loop<L_NT, E_STORE, false, 4, 4, true>(F, 0, F.tiles, g, gridDim.x, xcd, CeEpilogue<4>{a, tiles_n});
+  ring_handover();
   tile_loop<L_NT, E_STORE, false, 2, 4, false>(H, 0, H.tiles, g, gridDim.x, xcd, CeEpilogue<2>{a, tiles_n});
 }
 
