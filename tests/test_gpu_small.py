@@ -166,6 +166,19 @@ def test_column_fwd_half_tile_tail_round(act):
         assert_close("Pre", host64(Pre), Prer, TOL[dtype])
 
 
+def test_row_bwd_dx_only_half_tile_tail_round():
+    # dX = dZ B^T alone (an NT launch): 17 x 17 = 289 whole tiles on 256 CUs, so one launch runs
+    # 256 whole tiles and then the last 33 as 66 half tiles of 128 rows.
+    M, N, K = 17 * 256, 17 * 256, 64   # row input [M, N], weight [N, K], dZ [M, K]: dX [M, N] over K
+    dtype = syn.BF16
+    d = _inputs(dtype, M, N, K, 29, "none")
+    dX, dB, _ = ops.row_bwd(dev(d["dZ"]), dev(d["dY"]), dev(d["B"]), want_dw=False)
+    torch.cuda.synchronize()
+    assert dB is None
+    rdX, _, _ = oracle.row_bwd(d["dZ"].f64, d["dY"].f64, d["B"].f64)
+    assert_close("dX", host64(dX), rdX, TOL[dtype])
+
+
 @pytest.mark.parametrize("shape", TILE_SHAPES)
 def test_row_bwd_whole_tiles(shape):
     M, N, K = shape
