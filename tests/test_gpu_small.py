@@ -151,7 +151,7 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
 TILE_SHAPES = [(512, 256, 768), (768, 512, 256), (2048, 1024, 768)]
 
 
-@pytest.mark.parametrize("act", ["none", "swiglu"])
+@pytest.mark.parametrize("act", ["none", "gelu", "swiglu"])
 def test_column_fwd_half_tile_tail_round(act):
     # 17 x 17 = 289 whole tiles on 256 CUs: the last 33 run as 128-row halves.
     M, K = 17 * 256, 64
