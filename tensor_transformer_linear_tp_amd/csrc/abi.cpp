@@ -54,8 +54,10 @@ tp_status check_vec(const void* p) { return (p && !aligned16(p)) ? TP_E_ALIGN : 
     if (st_ != TP_OK) return st_;      \
   } while (0)
 
-// Tile-count limits of the launch grids (bf16: 256 x 128 smallest tile; fp32:
-// 64 x 32 tiles with the row tiles on grid.y).
+// Tile-count limits of the launch grids (bf16: counted in 256 x 128 tiles, the
+// SwiGLU tile; the launcher takes narrower tiles, down to 128 x 192, only when
+// their count also fits in an int; fp32: 64 x 32 tiles with the row tiles on
+// grid.y).
 tp_status check_grid(int dtype, int64_t M, int64_t N) {
   if (dtype == TP_BF16) {
     if (((M + 255) / 256) * ((N + 127) / 128) > kMaxDim) return TP_E_SHAPE;
