@@ -379,37 +379,34 @@ tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t K, con
     if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
     return TP_OK;
   }
-  GemmLaunch Lx = {}, Lw = {};
   if (dXpart) {   // dX_part = dP_g A^T (+ dP_u A2^T): NT over K' = N per segment
-    Lx.nprob = 1;
-    Lx.p[0] = make_problem(M, K, tps::L_NT, tps::E_STORE);
-    Lx.p[0].seg[0] = tps::Seg{dPg, A, ldp, lda, N};
+    GemmLaunch L = {};
+    L.nprob = 1;
+    L.p[0] = make_problem(M, K, tps::L_NT, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{dPg, A, ldp, lda, N};
     if (swiglu) {
-      Lx.p[0].seg[1] = tps::Seg{dPu, A2, ldp, lda2, N};
-      Lx.p[0].nseg = 2;
+      L.p[0].seg[1] = tps::Seg{dPu, A2, ldp, lda2, N};
+      L.p[0].nseg = 2;
     }
-    Lx.p[0].c = dXpart;
-    Lx.p[0].ldc = lddx;
+    L.p[0].c = dXpart;
+    L.p[0].ldc = lddx;
+    if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
   }
   if (dA) {   // dA = X^T dP_g, dA2 = X^T dP_u: TN over K' = M, one launch
-    Lw.nprob = swiglu ? 2 : 1;
-    Lw.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);
-    Lw.p[0].seg[0] = tps::Seg{X, dPg, ldx, ldp, M};
-    Lw.p[0].c = dA;
-    Lw.p[0].ldc = ldda;
+    GemmLaunch L = {};
+    L.nprob = swiglu ? 2 : 1;
+    L.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);
+    L.p[0].seg[0] = tps::Seg{X, dPg, ldx, ldp, M};
+    L.p[0].c = dA;
+    L.p[0].ldc = ldda;
     if (swiglu) {
-      Lw.p[1] = make_problem(K, N, tps::L_TN, tps::E_STORE);
-      Lw.p[1].seg[0] = tps::Seg{X, dPu, ldx, ldp, M};
-      Lw.p[1].c = dA2;
-      Lw.p[1].ldc = ldda2;
+      L.p[1] = make_problem(K, N, tps::L_TN, tps::E_STORE);
+      L.p[1].seg[0] = tps::Seg{X, dPu, ldx, ldp, M};
+      L.p[1].c = dA2;
+      L.p[1].ldc = ldda2;
     }
+    if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
   }
-  if (dXpart && dA && dtype == TP_BF16) {   // both: the library may run them as one launch
-    if (tps::launch_gemm_bf16_pair(Lx, Lw, s) != hipSuccess) return TP_E_HIP;
-    return TP_OK;
-  }
-  if (dXpart && run_gemm(dtype, Lx, s) != hipSuccess) return TP_E_HIP;
-  if (dA && run_gemm(dtype, Lw, s) != hipSuccess) return TP_E_HIP;
   return TP_OK;
 }
 

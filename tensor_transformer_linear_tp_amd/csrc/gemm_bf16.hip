@@ -963,20 +963,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tail_kernel(const GemmL
   tile_loop<LAYOUT, EPI, false, 2, 4>(H, 0, H.tiles, g, gridDim.x, xcd);
 }
 
-// Two independent launches in one (each workgroup runs its tiles of A, then
-// its tiles of B): the SwiGLU column backward's two-segment dX (NT, whole
-// 256 x 256 rounds) and its weight gradients (TN, 256 x 192), so that a
-// workgroup starts its weight-gradient tile as soon as its own dX tiles are
-// done.
-template <int LA, bool S2A, int MIA, int NIA, int LB, bool S2B, int MIB, int NIB>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_chain_kernel(const GemmLaunch A, const GemmLaunch B) {
-  int xcd;
-  const int g = wg_index(xcd);
-  tile_loop<LA, E_STORE, S2A, MIA, NIA>(A, 0, A.tiles, g, gridDim.x, xcd);
-  ring_handover();
-  tile_loop<LB, E_STORE, S2B, MIB, NIB>(B, 0, B.tiles, g, gridDim.x, xcd);
-}
-
 // Two problems of different operand layouts in one launch: workgroups
 // [0, g0) run problem 0's tiles, the rest problem 1's (plain stores), each
 // problem in its own tile shape.  Used when one problem alone cannot fill the
@@ -1258,88 +1244,6 @@ int64_t dual_split(int64_t t0, int64_t s0, int64_t t1, int64_t s1, int cus, int&
   return best;
 }
 
-// Narrower tiles for plain-store launches whose 256 x 256 tiles would leave
-// CUs idle: weight gradients (TN) in 256 x 192 or 192 x 192 tiles, NN / NT
-// products in 128 x 192 tiles.  A launch's cost is taken as its rounds times
-// (MFMA blocks per wave + 2), the 2 standing for a K stage's fixed barrier
-// and copy work (256 x 256: 18; 256 x 192: 14; 192 x 192: 11; 128 x 192: 8;
-// a 256 x 256 launch whose last round runs as 128-row halves: 18 per whole
-// round + 10).  Examples: a SwiGLU column backward with two 4096 x 1536
-// weight gradients, 192 whole tiles (75 % of 256 CUs) or 256 tiles of
-// 256 x 192 in one round; an 8192 x 768 projection, 96 whole tiles or 256
-// tiles of 128 x 192.  Every tile then takes the fast kernel (columns past N
-// are masked in 8-column chunks), so the problems must all be fast_ok.
-// Returns whether a narrower shape wins; G and (mi, ni) describe it.
-bool plan_narrow(const GemmLaunch& L, int cus, GemmLaunch& G, int& mi, int& ni) {
-  if (L.p[0].epi != E_STORE || L.p[0].nseg != 1 || (L.nprob > 1 && L.p[1].nseg != 1)) return false;
-  const int lay = L.p[0].layout;
-  static constexpr int kTN[2][2] = {{4, 3}, {3, 3}};
-  static constexpr int kAK[1][2] = {{2, 3}};   // K-contiguous A (NN, NT)
-  const int ncand = lay == L_TN ? 2 : 1;
-  bool n8 = true, half_ok = lay != L_TN;
-  int64_t n44 = 0;
-  for (int i = 0; i < L.nprob; ++i) {
-    const Problem& P = L.p[i];
-    n8 = n8 && (P.N & 7) == 0;
-    half_ok = half_ok && P.M % BM == 0;
-    n44 += (P.M + BM - 1) / BM * ((P.N + BN - 1) / BN);
-  }
-  const int64_t rem44 = n44 % cus;
-  int64_t best_cost = (half_ok && n44 > cus && rem44 > 0 && 2 * rem44 <= cus) ? n44 / cus * 18 + 10
-                                                                               : (n44 + cus - 1) / cus * 18;
-  int best = -1;
-  for (int c = 0; c < ncand && n8; ++c) {
-    const int cm = lay == L_TN ? kTN[c][0] : kAK[c][0], cn = lay == L_TN ? kTN[c][1] : kAK[c][1];
-    int64_t n = 0;
-    for (int i = 0; i < L.nprob; ++i)
-      n += (L.p[i].M + 64 * cm - 1) / (64 * cm) * ((L.p[i].N + 64 * cn - 1) / (64 * cn));
-    const int64_t cost = (n + cus - 1) / cus * (cm * cn + 2);
-    if (n < INT_MAX && cost < best_cost) {
-      best_cost = cost;
-      best = c;
-    }
-  }
-  if (best < 0) return false;
-  mi = lay == L_TN ? kTN[best][0] : kAK[best][0];
-  ni = lay == L_TN ? kTN[best][1] : kAK[best][1];
-  G = L;
-  int nt = 0;
-  for (int i = 0; i < L.nprob; ++i) {
-    G.p[i].tiles_m = (int)((L.p[i].M + 64 * mi - 1) / (64 * mi));
-    G.p[i].tiles_n = (int)((L.p[i].N + 64 * ni - 1) / (64 * ni));
-    G.p[i].tile_begin = nt;
-    G.p[i].edge_only = 0;
-    nt += G.p[i].tiles_m * G.p[i].tiles_n;
-  }
-  G.tiles = nt;
-  G.half_tail = 0;
-  G.strided = nt >= 3 * cus;
-  return true;
-}
-
-// A launch the fast kernel runs in whole rounds of 256 x 256 tiles (every
-// problem fast_ok, N a multiple of 8, the tile count a multiple of the CUs):
-// F describes it as launch_gemm_bf16 would run it.
-bool plan_whole(const GemmLaunch& L, int cus, GemmLaunch& F) {
-  F = L;
-  int64_t nf = 0;
-  for (int i = 0; i < L.nprob; ++i) {
-    const Problem& P = L.p[i];
-    if (!fast_ok(P) || (P.N & 7)) return false;
-    const int64_t bn = P.epi == E_SWIGLU ? BN / 2 : BN;
-    F.p[i].tiles_m = (int)((P.M + BM - 1) / BM);
-    F.p[i].tiles_n = (int)((P.N + bn - 1) / bn);
-    F.p[i].tile_begin = (int)nf;
-    F.p[i].edge_only = 0;
-    nf += (int64_t)F.p[i].tiles_m * F.p[i].tiles_n;
-  }
-  if (nf < cus || nf % cus != 0 || nf >= INT_MAX) return false;
-  F.tiles = (int)nf;
-  F.half_tail = 0;
-  F.strided = nf >= 3 * cus;
-  return true;
-}
-
 hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   int dev = 0, cus = 256;
   {
@@ -1420,12 +1324,60 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   bool fast = true;
   for (int i = 0; i < L.nprob; ++i) fast = fast && fast_ok(L.p[i]);
-  {
-    GemmLaunch G;
-    int mi = 0, ni = 0;
-    if (fast && plan_narrow(L, cus, G, mi, ni)) {
-      const int lay = L.p[0].layout;
-      const dim3 grid(std::min(G.tiles, cus)), block(NTHREADS);
+  // Narrower tiles for plain-store launches whose 256 x 256 tiles would
+  // leave CUs idle: weight gradients (TN) in 256 x 192 or 192 x 192 tiles,
+  // NN / NT products in 128 x 192 tiles.  A launch's cost is taken as its
+  // rounds times (MFMA blocks per wave + 2), the 2 standing for a K stage's
+  // fixed barrier and copy work (256 x 256: 18; 256 x 192: 14; 192 x 192: 11;
+  // 128 x 192: 8; a 256 x 256 launch whose last round runs as 128-row halves:
+  // 18 per whole round + 10).  Examples: a SwiGLU column backward with two
+  // 4096 x 1536 weight gradients, 192 whole tiles (75 % of 256 CUs) or 256
+  // tiles of 256 x 192 in one round; an 8192 x 768 projection, 96 whole tiles
+  // or 256 tiles of 128 x 192.  Every tile then takes the fast kernel
+  // (columns past N are masked in 8-column chunks).
+  if (fast && L.p[0].epi == E_STORE && L.p[0].nseg == 1 && (L.nprob == 1 || L.p[1].nseg == 1)) {
+    const int lay = L.p[0].layout;
+    static constexpr int kTN[2][2] = {{4, 3}, {3, 3}};
+    static constexpr int kAK[1][2] = {{2, 3}};   // K-contiguous A (NN, NT)
+    const int ncand = lay == L_TN ? 2 : 1;
+    bool n8 = true, half_ok = lay != L_TN;
+    int64_t n44 = 0;
+    for (int i = 0; i < L.nprob; ++i) {
+      const Problem& P = L.p[i];
+      n8 = n8 && (P.N & 7) == 0;
+      half_ok = half_ok && P.M % BM == 0;
+      n44 += (P.M + BM - 1) / BM * ((P.N + BN - 1) / BN);
+    }
+    const int64_t rem44 = n44 % cus;
+    int64_t best_cost = (half_ok && n44 > cus && rem44 > 0 && 2 * rem44 <= cus) ? n44 / cus * 18 + 10
+                                                                                 : (n44 + cus - 1) / cus * 18;
+    int best = -1;
+    for (int c = 0; c < ncand && n8; ++c) {
+      const int mi = lay == L_TN ? kTN[c][0] : kAK[c][0], ni = lay == L_TN ? kTN[c][1] : kAK[c][1];
+      int64_t n = 0;
+      for (int i = 0; i < L.nprob; ++i)
+        n += (L.p[i].M + 64 * mi - 1) / (64 * mi) * ((L.p[i].N + 64 * ni - 1) / (64 * ni));
+      const int64_t cost = (n + cus - 1) / cus * (mi * ni + 2);
+      if (n < INT_MAX && cost < best_cost) {
+        best_cost = cost;
+        best = c;
+      }
+    }
+    if (best >= 0) {
+      const int mi = lay == L_TN ? kTN[best][0] : kAK[best][0], ni = lay == L_TN ? kTN[best][1] : kAK[best][1];
+      GemmLaunch G = L;
+      int nt = 0;
+      for (int i = 0; i < L.nprob; ++i) {
+        G.p[i].tiles_m = (int)((L.p[i].M + 64 * mi - 1) / (64 * mi));
+        G.p[i].tiles_n = (int)((L.p[i].N + 64 * ni - 1) / (64 * ni));
+        G.p[i].tile_begin = nt;
+        G.p[i].edge_only = 0;
+        nt += G.p[i].tiles_m * G.p[i].tiles_n;
+      }
+      G.tiles = nt;
+      G.half_tail = 0;
+      G.strided = nt >= 3 * cus;
+      const dim3 grid(std::min(nt, cus)), block(NTHREADS);
       if (lay == L_TN && mi == 4)
         hipLaunchKernelGGL((gemm_bf16_kernel<L_TN, E_STORE, false, 4, 3>), grid, block, 0, s, G);
       else if (lay == L_TN)
@@ -1498,29 +1450,6 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   if (ne > 0) return dispatch<false>(E, ne, ne, s);
   return hipSuccess;
-}
-
-hipError_t launch_gemm_bf16_pair(GemmLaunch& A, GemmLaunch& B, hipStream_t s) {
-  int dev = 0, cus = 256;
-  {
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-  }
-  GemmLaunch F, G;
-  int mi = 0, ni = 0;
-  bool b_fast = true;
-  for (int i = 0; i < B.nprob; ++i) b_fast = b_fast && fast_ok(B.p[i]);
-  if (cus % 8 == 0 && A.nprob == 1 && A.p[0].layout == L_NT && A.p[0].epi == E_STORE && A.p[0].nseg == 2 &&
-      B.p[0].layout == L_TN && (B.nprob == 1 || B.p[1].layout == L_TN) && b_fast && plan_whole(A, cus, F) &&
-      plan_narrow(B, cus, G, mi, ni) && mi == 4 && ni == 3) {
-    hipLaunchKernelGGL((gemm_bf16_chain_kernel<L_NT, true, 4, 4, L_TN, false, 4, 3>), dim3(cus), dim3(NTHREADS), 0, s,
-                       F, G);
-    return hipGetLastError();
-  }
-  hipError_t e = launch_gemm_bf16(A, s);
-  return e != hipSuccess ? e : launch_gemm_bf16(B, s);
 }
 
 size_t ce_workspace_bytes(int64_t M, int64_t Vr) {

@@ -187,8 +187,6 @@ constexpr int kSpLnMaxN = 16384;   // row width the LayerNorm kernel holds in re
 constexpr int kColpartRows = 64;   // rows per column-partial block
 
 hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s);
-// A then B (independent); in one launch when their shapes allow, else as two.
-hipError_t launch_gemm_bf16_pair(GemmLaunch& A, GemmLaunch& B, hipStream_t s);
 hipError_t launch_gemm_f32(GemmLaunch& L, hipStream_t s);
 hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s);
 size_t ce_workspace_bytes(int64_t M, int64_t Vr);
