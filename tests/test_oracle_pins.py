@@ -106,6 +106,43 @@ def test_v5_row_bias_added_once():
     assert np.array_equal(wrong, oracle.sum_partials(parts, bias=b) + (len(parts) - 1) * b)
 
 
+def test_v6_bias_gradients_by_hand():
+    # Page 'v4: Tensor Parallel and Sequence Parallel', section 'Self-test':
+    # bias gradients are among the quantities compared with one device.  Hand
+    # case on the 2x2 block example split row-wise over t = 2 ranks, two
+    # tokens, upstream gradient dZ = [[1, 2], [3, 4]].  The replicated row
+    # bias b enters Z = X1 A1 + X2 A2 + b once, so dL/db = sum over tokens of
+    # dZ = [4, 6] on EVERY rank (an all-reduce of it would give t times that).
+    g = _golden("v1_block_2x2.json")
+    X = np.array(g["X"] * 2, float)          # two identical tokens [1, 2]
+    A = np.array(g["A"], float)
+    dZ = np.array([[1.0, 2.0], [3.0, 4.0]])
+    for i in range(2):
+        rs = oracle.row_slice(2, 2, i)
+        dXi, dAi, db = oracle.row_bwd(dZ, X[:, rs], A[rs, :])
+        assert np.array_equal(db, np.array([4.0, 6.0]))
+        # dX_i = dZ A_i^T, dA_i = X_i^T dZ, each entry by hand
+        a = A[rs, :][0]                      # the rank's one row of A
+        assert np.array_equal(dXi[:, 0], np.array([1 * a[0] + 2 * a[1], 3 * a[0] + 4 * a[1]]))
+        x = X[0, rs][0]
+        assert np.array_equal(dAi, np.array([[x * 4.0, x * 6.0]]))
+    # Column-split SwiGLU with one token and one column per rank, zero gate:
+    # G = 0 gives silu(0) = 0 and silu'(0) = 1/2, so with U = 3 and dY = 2 the
+    # gate-bias gradient is dY * U * 1/2 = 3 and the up-bias gradient is
+    # dY * silu(0) = 0; with G = ln 3 (sigmoid = 3/4, silu = (3/4) ln 3):
+    # up-bias gradient = 2 * (3/4) ln 3.
+    for gate, want_g, want_u in ((0.0, 3.0, 0.0),
+                                 (math.log(3.0), 2 * 3.0 * (0.75 + math.log(3.0) * 0.75 * 0.25),
+                                  2 * 0.75 * math.log(3.0))):
+        Xo = np.array([[1.0]])
+        _, Pre = oracle.column_fwd(Xo, np.array([[0.0]]), "swiglu", bias=np.array([gate]),
+                                   A2=np.array([[0.0]]), bias2=np.array([3.0]))
+        _, _, _, db, db2 = oracle.column_bwd(np.array([[2.0]]), Xo, np.array([[0.0]]), Pre, "swiglu",
+                                             np.array([[0.0]]))
+        assert db[0] == pytest.approx(want_g, rel=1e-15)
+        assert db2[0] == pytest.approx(want_u, rel=1e-15, abs=0.0)
+
+
 # ---------------------------------------------------------------------------
 # Activations: textbook values, closed forms, finite differences.
 # ---------------------------------------------------------------------------
@@ -220,7 +257,7 @@ def test_sharded_mlp_equals_unsharded(t, act, bias):
     dZ = rng.standard_normal((M, H))
 
     Yfull, _ = oracle.column_fwd(X, A, act=act, bias=ba, A2=A2, bias2=ba2)
-    zparts, dxparts, dAs, dA2s, dbs, dBs = [], [], [], [], [], []
+    zparts, dxparts, dAs, dA2s, dbs, db2s, dBs, dbrows = [], [], [], [], [], [], [], []
     for i in range(t):
         cs = oracle.column_slice(F, t, i)
         Y, Pre = oracle.column_fwd(X, A[:, cs], act=act, bias=None if ba is None else ba[cs],
@@ -230,12 +267,13 @@ def test_sharded_mlp_equals_unsharded(t, act, bias):
         zparts.append(oracle.row_fwd(Y, B[cs, :]))
         dY, dBi, dbrow = oracle.row_bwd(dZ, Y, B[cs, :])
         dBs.append(dBi)
-        np.testing.assert_allclose(dbrow, dZ.sum(axis=0), rtol=1e-12)
+        dbrows.append(dbrow)
         dXp, dA, dA2, db, db2 = oracle.column_bwd(dY, X, A[:, cs], Pre, act, None if A2 is None else A2[:, cs])
         dxparts.append(dXp)
         dAs.append(dA)
         dA2s.append(dA2)
         dbs.append(db)
+        db2s.append(db2)
     Z = oracle.sum_partials(zparts, bias=bB)
     np.testing.assert_allclose(Z, _mlp_full(X, A, A2, ba, ba2, B, bB, act), rtol=1e-11, atol=1e-11)
 
@@ -259,15 +297,40 @@ def test_sharded_mlp_equals_unsharded(t, act, bias):
         am[3, 7] -= h
         fd = (loss(A2v=ap) - loss(A2v=am)) / (2 * h)
         assert np.concatenate(dA2s, axis=1)[3, 7] == pytest.approx(fd, rel=1e-6, abs=1e-7)
+    # Bias gradients by central differences of L = <dZ, Z> over every entry
+    # of each bias.  The replicated row bias enters Z once (after the sum), so
+    # every shard's row-bias gradient must equal the full one (not 1/t of it,
+    # and not counted t times); the column biases are split with the columns.
+    def loss_b(ba_v, ba2_v, bB_v):
+        return float((dZ * _mlp_full(X, A, A2, ba_v, ba2_v, B, bB_v, act)).sum())
+
+    def fd_vec(vec, f):
+        out = np.empty_like(vec)
+        for j in range(vec.size):
+            vp, vm = vec.copy(), vec.copy()
+            vp[j] += h
+            vm[j] -= h
+            out[j] = (f(vp) - f(vm)) / (2 * h)
+        return out
+
     if bias:
-        # column bias gradient: d/db_a of L = sum over tokens of dP
-        db = np.concatenate(dbs)
-        bp, bm = ba.copy(), ba.copy()
-        bp[5] += h
-        bm[5] -= h
-        fd = (float((dZ * _mlp_full(X, A, A2, bp, ba2, B, bB, act)).sum())
-              - float((dZ * _mlp_full(X, A, A2, bm, ba2, B, bB, act)).sum())) / (2 * h)
-        assert db[5] == pytest.approx(fd, rel=1e-6, abs=1e-7)
+        fd_ba = fd_vec(ba, lambda v: loss_b(v, ba2, bB))
+        np.testing.assert_allclose(np.concatenate(dbs), fd_ba, rtol=1e-6, atol=1e-7)
+        fd_bB = fd_vec(bB, lambda v: loss_b(ba, ba2, v))
+        for dbrow in dbrows:
+            np.testing.assert_allclose(dbrow, fd_bB, rtol=1e-6, atol=1e-7)
+        if act == "swiglu":
+            fd_ba2 = fd_vec(ba2, lambda v: loss_b(ba, v, bB))
+            np.testing.assert_allclose(np.concatenate(db2s), fd_ba2, rtol=1e-6, atol=1e-7)
+        else:
+            assert all(d is None for d in db2s)
+    else:
+        # Without a row bias in the model, its gradient is still defined as the
+        # derivative of <dZ, Z + b> at b = 0; pin it the same way.
+        zero = np.zeros(H)
+        fd_b0 = fd_vec(zero, lambda v: float((dZ * (_mlp_full(X, A, A2, ba, ba2, B, None, act) + v[None, :])).sum()))
+        for dbrow in dbrows:
+            np.testing.assert_allclose(dbrow, fd_b0, rtol=1e-6, atol=1e-7)
 
 
 # ---------------------------------------------------------------------------
