@@ -199,6 +199,30 @@ TP_API tp_status tp_vocab_ce_partials(int dtype, int64_t M, int64_t Vr, int64_t 
 TP_API size_t tp_vocab_ce_workspace_bytes(int64_t M, int64_t Vr);
 
 /*
+ * Recombination of the vocab shards' cross-entropy partials: the value the
+ * all-reduce of the three per-token numbers leaves, computed on one device
+ * (not a collective).  [TP/SP] "Embedding and LM head: split by vocab": each
+ * token exchanges only its shard max, sum of e^z and target logit, and the
+ * loss follows from them:
+ *
+ *   M*[m]   = max_r max_r[m]
+ *   S*[m]   = sum_r sumexp_r[m] * exp(max_r[m] - M*[m])     (ascending r)
+ *   lse[m]  = M*[m] + ln S*[m]
+ *   tgt[m]  = sum_r tgt_r[m]            (exactly one shard owns each target)
+ *   loss[m] = lse[m] - tgt[m]
+ *
+ * R >= 1 shards; shard r's triple is maxes + r*stride, sumexps + r*stride,
+ * tgts + r*stride (fp32 [M] each, the outputs of tp_vocab_ce_partials for
+ * that shard; stride >= M, a multiple of 4, R*stride < 2^31).  Outputs lse,
+ * tgt, loss: fp32 [M] each, device, nullable (not all three NULL).  The
+ * arithmetic is fp64 with one rounding to fp32 per output; lse feeds
+ * tp_vocab_ce_bwd.  A token whose shard maxes are all -inf gets lse = -inf.
+ */
+TP_API tp_status tp_vocab_ce_combine(int R, int64_t M, const float* maxes, const float* sumexps,
+                                     const float* tgts, int64_t stride, float* lse, float* tgt, float* loss,
+                                     void* stream);
+
+/*
  * Backward of the vocab-parallel cross entropy for shard [v0, v0+Vr).
  * [TP/SP] "Embedding and LM head: split by vocab": with the per-token
  * log-sum-exp recombined over all shards, each rank differentiates its own

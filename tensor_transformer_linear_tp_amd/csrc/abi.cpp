@@ -431,6 +431,19 @@ tp_status tp_vocab_ce_partials(int dtype, int64_t M, int64_t Vr, int64_t K, cons
   return tps::launch_ce_partials(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
 }
 
+tp_status tp_vocab_ce_combine(int R, int64_t M, const float* maxes, const float* sumexps, const float* tgts,
+                              int64_t stride, float* lse, float* tgt, float* loss, void* stream) {
+  if (!maxes || !sumexps || !tgts) return TP_E_NULL;
+  if (!lse && !tgt && !loss) return TP_E_NULL;
+  if (R < 1 || bad_dim(M) || stride < M || (R > 1 && stride > kMaxDim / R)) return TP_E_SHAPE;
+  if (stride % 4 != 0 || !aligned16(maxes) || !aligned16(sumexps) || !aligned16(tgts)) return TP_E_ALIGN;
+  TPS_TRY(check_vec(lse));
+  TPS_TRY(check_vec(tgt));
+  TPS_TRY(check_vec(loss));
+  const tps::CECombineArgs a = {R, M, stride, maxes, sumexps, tgts, lse, tgt, loss};
+  return tps::launch_ce_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
+}
+
 size_t tp_vocab_ce_bwd_workspace_bytes(int64_t M, int64_t Vr) {
   if (bad_dim(M) || bad_dim(Vr)) return 0;
   return align_ws((size_t)M * (size_t)round_up(Vr, 8) * 2);

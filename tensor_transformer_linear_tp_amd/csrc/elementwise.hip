@@ -286,6 +286,28 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const SumArgs a) {
   }
 }
 
+// One token per thread: M* = max_r m_r, S* = sum_r s_r exp(m_r - M*) (shards
+// in ascending r), lse = M* + ln S*, tgt = sum_r tgt_r, loss = lse - tgt.
+// fp64 throughout (the inputs are exact in it), one rounding to fp32 per
+// output.  A token whose every shard max is -inf gets lse = -inf.
+__global__ __launch_bounds__(256) void ce_combine_kernel(const CECombineArgs a) {
+  const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (m >= a.M) return;
+  double mx = -INFINITY;
+  for (int r = 0; r < a.R; ++r) mx = fmax(mx, (double)a.maxes[(int64_t)r * a.stride + m]);
+  double s = 0.0, t = 0.0;
+  for (int r = 0; r < a.R; ++r) {
+    const int64_t i = (int64_t)r * a.stride + m;
+    const double mr = (double)a.maxes[i];
+    if (mr > -INFINITY) s += (double)a.sumexps[i] * exp(mr - mx);
+    t += (double)a.tgts[i];
+  }
+  const double lse = s > 0.0 ? mx + log(s) : -INFINITY;
+  if (a.lse) a.lse[m] = (float)lse;
+  if (a.tgt) a.tgt[m] = (float)t;
+  if (a.loss) a.loss[m] = (float)(lse - t);
+}
+
 // Sum of v over the 256 threads of the workgroup, the same on every thread
 // (fixed reduction tree: the result does not depend on timing).
 __device__ __forceinline__ float block_sum256(float v, float* red) {
@@ -515,6 +537,11 @@ hipError_t launch_colsum_finalize(int is_bf16, const float* colpart, int64_t nrb
   else
     hipLaunchKernelGGL(colsum_finalize_kernel<float>, grid, dim3(256), 0, s, colpart, nrb, ldcp, N, part,
                        static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_combine(const CECombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)((a.M + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -79,6 +79,19 @@ struct CEArgs {
   float* ws;             // [ceil(Vr/256)][M] (max,sum) pairs, then [M] target logits
 };
 
+// Log-sum-exp recombination of R vocab shards' (max, sum exp, target logit)
+// triples: shard r's arrays start at maxes / sumexps / tgts + r * stride.
+struct CECombineArgs {
+  int R;
+  int64_t M, stride;
+  const float* maxes;
+  const float* sumexps;
+  const float* tgts;
+  float* lse;            // each output [M], nullable
+  float* tgt;
+  float* loss;
+};
+
 // Elementwise backward of the column epilogue, fused with fp32 column
 // partial sums for the bias gradients.
 struct ActBwdArgs {
@@ -191,6 +204,7 @@ hipError_t launch_gemm_f32(GemmLaunch& L, hipStream_t s);
 hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s);
 size_t ce_workspace_bytes(int64_t M, int64_t Vr);
 hipError_t launch_act_bwd(int is_bf16, const ActBwdArgs& a, hipStream_t s);
+hipError_t launch_ce_combine(const CECombineArgs& a, hipStream_t s);
 hipError_t launch_colsum_finalize(int is_bf16, const float* colpart, int64_t nrb, int64_t ldcp,
                                   int64_t N, int part, void* out, hipStream_t s);
 hipError_t launch_sum_partials(int is_bf16, const SumArgs& a, hipStream_t s);

@@ -14,7 +14,7 @@ from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_col
                tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
                tp_sp_reduce_scatter_ln, tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_embed_bwd,
                tp_vocab_embed_bwd_workspace_bytes, tp_vocab_embed_fwd, tp_attention_fwd,
-               tp_attention_fwd_workspace_bytes, tp_attention_bwd, tp_attention_bwd_workspace_bytes, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_partials,
+               tp_attention_fwd_workspace_bytes, tp_attention_bwd, tp_attention_bwd_workspace_bytes, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_combine, tp_vocab_ce_partials,
                tp_vocab_ce_workspace_bytes)
 
 ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
@@ -179,6 +179,33 @@ def vocab_ce_partials(H, W, target, v0):
     return m, s, tg
 
 
+def _rows_f32(x):
+    """[R, M] fp32 device tensor whose row stride is a multiple of 4 (stacks a list of [M] tensors)."""
+    if isinstance(x, (list, tuple)):
+        x = torch.stack([v.to(torch.float32) for v in x])
+    x = x.to(torch.float32)
+    if x.dim() == 1:
+        x = x[None, :]
+    if x.stride(1) != 1 or x.stride(0) % 4 or x.data_ptr() % 16 or x.stride(0) < x.shape[1]:
+        buf = torch.empty(x.shape[0], (x.shape[1] + 3) // 4 * 4, dtype=torch.float32, device=x.device)
+        buf[:, :x.shape[1]].copy_(x)
+        x = buf[:, :x.shape[1]]
+    return x
+
+
+def vocab_ce_combine(maxes, sumexps, tgts):
+    """Recombine R shards' CE partials ([R, M] each, or lists of [M]); returns (lse, tgt, loss) fp32 [M]."""
+    ms, ss, ts = _rows_f32(maxes), _rows_f32(sumexps), _rows_f32(tgts)
+    if not (ms.shape == ss.shape == ts.shape):
+        raise ValueError("the three partial arrays must have the same shape")
+    if not (ms.stride(0) == ss.stride(0) == ts.stride(0)):
+        ms, ss, ts = (_rows_f32(v.clone()) for v in (ms, ss, ts))
+    R, M = ms.shape
+    out = [torch.empty(M, dtype=torch.float32, device=ms.device) for _ in range(3)]
+    tp_vocab_ce_combine(R, M, ms, ss, ts, ms.stride(0), *out)
+    return tuple(out)
+
+
 def vocab_ce_bwd(H, W, target, v0, lse, gscale=None, want_dh=True, want_dw=True):
     """(dH partial, dW) of the CE loss for the vocab shard starting at v0, given the recombined lse."""
     H, W = aligned(H), aligned(W)
@@ -197,7 +224,7 @@ def vocab_ce_bwd(H, W, target, v0, lse, gscale=None, want_dh=True, want_dw=True)
     return dH, dW
 
 
-__all__ = ["column_fwd", "row_fwd", "stack_partials", "sum_partials", "row_bwd", "column_bwd",
+__all__ = ["column_fwd", "row_fwd", "stack_partials", "sum_partials", "row_bwd", "column_bwd", "vocab_ce_combine",
            "vocab_ce_partials", "vocab_ce_bwd", "empty_padded", "aligned", "dtype_code", "TP_FP32", "TP_BF16"]
 
 

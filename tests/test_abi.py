@@ -119,6 +119,19 @@ def test_ce_validation(lib):
     assert _rc("tp_vocab_ce_partials", *a) == 3
 
 
+def test_ce_combine_validation(lib):
+    def call(R=8, M=64, ms=P, ss=P, ts=P, stride=64, lse=P, tgt=P, loss=P):
+        return _rc("tp_vocab_ce_combine", R, M, ms, ss, ts, stride, lse, tgt, loss, None)
+
+    assert call(ms=None) == 1 and call(ss=None) == 1 and call(ts=None) == 1
+    assert call(lse=None, tgt=None, loss=None) == 1          # nothing to write
+    assert call(R=0) == 2 and call(M=0) == 2
+    assert call(stride=32) == 2                              # stride < M
+    assert call(R=1 << 20, stride=1 << 12, M=64) == 2        # R * stride past 2^31
+    assert call(stride=66) == 3                              # not a multiple of 4 floats
+    assert call(ms=P + 4) == 3 and call(loss=P + 8) == 3
+
+
 def test_ce_bwd_validation(lib):
     ws = tp.tp_vocab_ce_bwd_workspace_bytes(8192, 18992)
     assert ws == 8192 * 18992 * 2                        # bf16 dz, rows padded to 8 (already)

@@ -92,8 +92,8 @@ def test_c2_shard_chain_sampled(c2):
     dX, dA, dA2, _, _ = ops.column_bwd(dY, Xd, Ad, Pre=Pre, act="swiglu", A2=A2d)
     torch.cuda.synchronize()
 
-    ms = sample_idx(cfg.M, 48, 1)            # token rows
-    ks = sample_idx(cfg.Fi, 40, 2)           # intermediate columns of this shard
+    ms = tile_sample_idx(cfg.M, 256, 1, per_tile=2)    # token rows: two in every 256-row tile
+    ks = tile_sample_idx(cfg.Fi, 192, 2, per_tile=2)   # intermediate columns: two per 192-wide tile
     Xf, Af, A2f, Bf, dZf = X.f64, A.f64, A2.f64, B.f64, dZ.f64
     # forward rows
     Yr, Prer = oracle.column_fwd(Xf[ms], Af, "swiglu", A2=A2f)
@@ -127,9 +127,9 @@ def test_c2_per_call_sampled(c2):
     dX, dA, dA2, dbg, dbu = ops.column_bwd(dev(dYin), dev(X), dev(A), Pre=dev(Pin), act="swiglu", A2=dev(A2),
                                            want_db=True)
     torch.cuda.synchronize()
-    ms = sample_idx(M, 48, 3)
-    ks = sample_idx(Fi, 40, 4)
-    ns = sample_idx(H, 40, 5)
+    ms = tile_sample_idx(M, 256, 3, per_tile=2)
+    ks = tile_sample_idx(Fi, 192, 4, per_tile=2)
+    ns = tile_sample_idx(H, 256, 5, per_tile=2)
     assert_close("Z", rows(Z, ms), oracle.row_fwd(Yin.f64[ms], B.f64), BF)
     assert_close("dY", rows(dYo, ms), oracle.dgrad(dZ.f64[ms], B.f64), BF)
     assert_close("dB", cols(dB, ns), oracle.wgrad(Yin.f64, dZ.f64[:, ns]), BF)
@@ -157,12 +157,12 @@ def test_c3_attention_projections_sampled():
     dAttn, dWo, _ = ops.row_bwd(dev(d["dZ"]), dev(d["attn"]), dev(d["Wo"]))
     dX, dWqkv, _, _, _ = ops.column_bwd(dev(d["dQKV"]), dev(d["X"]), dev(d["Wqkv"]), act="none")
     torch.cuda.synchronize()
-    ms = sample_idx(cfg.M, 48, 6)
+    ms = tile_sample_idx(cfg.M, 128, 6, per_tile=2)   # the narrow launches use 128-row tiles
     X, Wqkv, attn, Wo, dZ, dQKV = (d[k].f64 for k in ("X", "Wqkv", "attn", "Wo", "dZ", "dQKV"))
     assert_close("QKV", rows(QKV, ms), oracle.column_fwd(X[ms], Wqkv)[0], BF)
     assert_close("Z", rows(Z, ms), oracle.row_fwd(attn[ms], Wo), BF)
     assert_close("dAttn", rows(dAttn, ms), oracle.dgrad(dZ[ms], Wo), BF)
-    ns = sample_idx(cfg.H, 40, 7)
+    ns = tile_sample_idx(cfg.H, 192, 7, per_tile=2)
     assert_close("dWo", cols(dWo, ns), oracle.wgrad(attn, dZ[:, ns]), BF)
     assert_close("dX", rows(dX, ms), oracle.dgrad(dQKV[ms], Wqkv), BF)
     assert_close("dWqkv", host64(dWqkv), oracle.wgrad(X, dQKV), BF)
@@ -185,9 +185,9 @@ def test_c4_gelu_shard_sampled():
     dYo, dB, _ = ops.row_bwd(dev(dZ), dev(Yin), dev(B))
     dX, dA, _, _, _ = ops.column_bwd(dev(dYin), dev(X), dev(A), Pre=dev(Pin), act="gelu")
     torch.cuda.synchronize()
-    ms = sample_idx(M, 32, 8)
-    ks = sample_idx(Fi, 32, 9)
-    ns = sample_idx(H, 32, 10)
+    ms = tile_sample_idx(M, 256, 8, per_tile=2)
+    ks = tile_sample_idx(Fi, 256, 9, per_tile=1)
+    ns = tile_sample_idx(H, 256, 10, per_tile=1)
     Yr, Pr = oracle.column_fwd(X.f64[ms], A.f64, "gelu")
     assert_close("Y", rows(Y, ms), Yr, BF)
     assert_close("Pre", rows(Pre, ms), Pr, BF)
@@ -200,15 +200,82 @@ def test_c4_gelu_shard_sampled():
     assert_close("dA", cols(dA, ks), r[1], BF)
 
 
-def test_c4_four_way_partial_sum_sampled():
+def test_c4_four_shards_real_partials_summed():
+    # The pages' self-test at c4's full size: the 4 shards of one full weight
+    # (A = [A_0 .. A_3] [8192, 32768], B = [B_0; ..; B_3]) each run the GeLU
+    # column forward and the row forward on the GPU; tp_sum_partials adds their
+    # real bf16 partials, compared on tile-sampled token rows with the unsharded
+    # layer GeLU(X A) B of the oracle.
     cfg = syn.C4
-    seeded = [syn.normal(4950 + i, (cfg.M, cfg.H), 1.0, syn.BF16) for i in range(cfg.t)]
-    buf, N = ops.stack_partials([dev(p) for p in seeded])
+    shards = [syn.mlp_shard_inputs(cfg, shard=i) for i in range(cfg.t)]
+    X = shards[0]["X"]
+    Xd = dev(X)
+    zparts = []
+    for d in shards:
+        Y, _ = ops.column_fwd(Xd, dev(d["A"]), "gelu")
+        zparts.append(ops.row_fwd(Y, dev(d["B"])))
+        del Y
+    buf, N = ops.stack_partials(zparts)
+    del zparts
     Z = ops.sum_partials(buf, N)
     torch.cuda.synchronize()
-    ms = sample_idx(cfg.M, 64, 11)
-    ref = oracle.sum_partials([p.f64[ms] for p in seeded])
-    assert_close("Z", rows(Z, ms), ref, BF)
+    ms = tile_sample_idx(cfg.M, 256, 11, per_tile=2)
+    Afull = np.concatenate([d["A"].f64 for d in shards], axis=1)
+    Yr, _ = oracle.column_fwd(X.f64[ms], Afull, "gelu")
+    del Afull
+    Bfull = np.concatenate([d["B"].f64 for d in shards], axis=0)
+    assert_close("Z", rows(Z, ms), oracle.row_fwd(Yr, Bfull), BF)
+
+
+def test_c2_all_eight_shards_chain_vs_unsharded():
+    # The pages' self-test at c2's full size: the 8 shards of one full SwiGLU MLP
+    # (gate/up [4096, 12288], down [12288, 4096]) run the whole shard chain on the
+    # GPU; the forward partials and the input-gradient partials are summed with
+    # tp_sum_partials, the weight gradients are concatenated; everything is
+    # compared with the unsharded layer of the oracle (token rows: two in every
+    # 256-row tile; weight columns/rows: two in every 192-wide tile of each shard).
+    cfg = syn.C2
+    t, M, H, Fi = cfg.t, cfg.M, cfg.H, cfg.Fi
+    shards = [syn.mlp_shard_inputs(cfg, shard=i) for i in range(t)]
+    X, dZ = shards[0]["X"], shards[0]["dZ"]
+    Xd, dZd = dev(X), dev(dZ)
+    ks_local = tile_sample_idx(Fi, 192, 31, per_tile=2)
+    zparts, dxparts, dA_s, dA2_s, dB_s = [], [], [], [], []
+    for d in shards:
+        Ad, A2d, Bd = dev(d["A"]), dev(d["A2"]), dev(d["B"])
+        Y, Pre = ops.column_fwd(Xd, Ad, "swiglu", A2=A2d)
+        zparts.append(ops.row_fwd(Y, Bd))
+        dY, dB, _ = ops.row_bwd(dZd, Y, Bd)
+        dX, dA, dA2, _, _ = ops.column_bwd(dY, Xd, Ad, Pre=Pre, act="swiglu", A2=A2d)
+        dxparts.append(dX)
+        dA_s.append(cols(dA, ks_local))
+        dA2_s.append(cols(dA2, ks_local))
+        dB_s.append(rows(dB, ks_local))
+        del Y, Pre, dY, dB, dA, dA2
+    zb, n = ops.stack_partials(zparts)
+    xb, n2 = ops.stack_partials(dxparts)
+    del zparts, dxparts
+    Z = ops.sum_partials(zb, n)
+    dXs = ops.sum_partials(xb, n2)
+    torch.cuda.synchronize()
+
+    Af = np.concatenate([d["A"].f64 for d in shards], axis=1)
+    A2f = np.concatenate([d["A2"].f64 for d in shards], axis=1)
+    Bf = np.concatenate([d["B"].f64 for d in shards], axis=0)
+    Xf, dZf = X.f64, dZ.f64
+    ms = tile_sample_idx(M, 256, 30, per_tile=2)
+    Yr, Prer = oracle.column_fwd(Xf[ms], Af, "swiglu", A2=A2f)
+    assert_close("Z rows (8 partials summed)", rows(Z, ms), oracle.row_fwd(Yr, Bf), BF)
+    dYr = oracle.dgrad(dZf[ms], Bf)
+    dXr = oracle.column_bwd(dYr, Xf[ms], Af, Prer, "swiglu", A2f)[0]
+    assert_close("dX rows (8 partials summed)", rows(dXs, ms), dXr, BF)
+    ks = np.concatenate([i * Fi + ks_local for i in range(t)])   # the same local columns of every shard
+    Yk, Prek = oracle.column_fwd(Xf, Af[:, ks], "swiglu", A2=A2f[:, ks])
+    assert_close("dB rows (concatenated)", np.concatenate(dB_s, axis=0), oracle.wgrad(Yk, dZf), BF)
+    dYk = oracle.dgrad(dZf, Bf[ks, :])
+    _, dAk, dA2k, _, _ = oracle.column_bwd(dYk, Xf, Af[:, ks], Prek, "swiglu", A2f[:, ks])
+    assert_close("dA cols (concatenated)", np.concatenate(dA_s, axis=1), dAk, BF)
+    assert_close("dA2 cols (concatenated)", np.concatenate(dA2_s, axis=1), dA2k, BF)
 
 
 def test_c2_sequence_parallel_boundary_sampled():
@@ -284,6 +351,47 @@ def test_c5_ce_backward_full_size_sampled():
         dz_cols[:, c] = dzc[:, 0]
     rdW = dz_cols.T @ H64
     assert_close("dW", host64(dW)[js], rdW, TOL[syn.BF16])
+
+
+def test_c5_ce_chain_eight_shards_full_size_sampled():
+    # c5's full vocabulary (8 shards of 18992) with every intermediate made on
+    # the GPU: partials of all 8 shards -> tp_vocab_ce_combine -> each shard's
+    # backward on that lse -> dH summed over the shards.  The oracle recombines
+    # its own partials; lse, tgt, loss and dH are compared on two tokens of every
+    # 256-row tile.
+    cfg = syn.C5
+    base = syn.vocab_inputs(cfg, shard=0)
+    H, target = base["H"], base["target"]
+    g = syn.normal(cfg.seed + 40, (cfg.M,), 1.0, syn.FP32).f32
+    Hd, td, gd = dev(H), torch.from_numpy(target).cuda(), torch.from_numpy(g).cuda()
+    ms = tile_sample_idx(cfg.M, 256, 41, per_tile=2)
+    mstk = torch.empty(cfg.shards, cfg.M, dtype=torch.float32, device="cuda")
+    sstk, tstk = torch.empty_like(mstk), torch.empty_like(mstk)
+    rparts, rdH = [], np.zeros((len(ms), cfg.H))
+    Ws = []
+    for r in range(cfg.shards):
+        W = syn.vocab_inputs(cfg, shard=r, M=1)["W"]
+        m, s, tg = ops.vocab_ce_partials(Hd, dev(W), td, r * cfg.Vr)
+        mstk[r].copy_(m)
+        sstk[r].copy_(s)
+        tstk[r].copy_(tg)
+        rparts.append(oracle.vocab_ce_partials(H.f64[ms], W.f64, target[ms], r * cfg.Vr))
+        Ws.append(W)
+    lse, tgt, loss = ops.vocab_ce_combine(mstk, sstk, tstk)
+    rl, rt, rloss = oracle.lse_recombine(rparts)
+    dHs = []
+    for r, W in enumerate(Ws):
+        dH, _ = ops.vocab_ce_bwd(Hd, dev(W), td, r * cfg.Vr, lse, gd, want_dw=False)
+        dHs.append(dH)
+        rdH += oracle.vocab_ce_bwd(H.f64[ms], W.f64, target[ms], r * cfg.Vr, rl, g[ms])[1]
+    buf, n = ops.stack_partials(dHs)
+    del dHs
+    dHsum = ops.sum_partials(buf, n)
+    torch.cuda.synchronize()
+    assert_close("lse", host64(lse)[ms], rl, TOL_CE)
+    assert_close("tgt", host64(tgt)[ms], rt, TOL_CE)
+    assert_close("loss", host64(loss)[ms], rloss, TOL_CE)
+    assert_close("dH summed", rows(dHsum, ms), rdH, BF)
 
 
 def test_c3_attention_core_full_size():

@@ -383,6 +383,61 @@ def test_vocab_ce_bwd_small(M, Vr, K, use_g):
     assert_close("dW", host64(dW), rdW, TOL[syn.BF16])
 
 
+@pytest.mark.parametrize("R,M", [(1, 1), (3, 37), (8, 1000), (8, 8192)])
+def test_vocab_ce_combine_small(R, M):
+    # Seeded shard triples (max, sumexp >= 1, tgt); shard r owns token m's target
+    # when m % R == r, the others report 0.  The device combine is fp64 with one
+    # rounding to fp32, so it must agree with the float64 oracle to fp32 rounding.
+    rng = np.random.default_rng(10 * R + M)
+    mx = (rng.standard_normal((R, M)) * 3.0).astype(np.float32)
+    se = (1.0 + rng.random((R, M)) * 5000.0).astype(np.float32)
+    tg = np.zeros((R, M), dtype=np.float32)
+    own = np.arange(M) % R
+    tg[own, np.arange(M)] = (rng.standard_normal(M) * 2.0).astype(np.float32)
+    mx[:, : min(M, 2)] = 1e4 if R == 1 else mx[:, : min(M, 2)]        # large maxima: no overflow
+    lse, tgt, loss = ops.vocab_ce_combine(torch.from_numpy(mx).cuda(), torch.from_numpy(se).cuda(),
+                                          torch.from_numpy(tg).cuda())
+    torch.cuda.synchronize()
+    rl, rt, rloss = oracle.lse_recombine([(mx[r], se[r], tg[r]) for r in range(R)])
+    assert_close("lse", host64(lse), rl, 1e-6)
+    assert_close("tgt", host64(tgt), rt, 1e-6)
+    assert_close("loss", host64(loss), rloss, 1e-6)
+
+
+def test_vocab_ce_chain_eight_shards_on_gpu_outputs():
+    # The whole vocab-parallel CE path with every intermediate made on the GPU:
+    # 8 shards' partials -> device recombination (lse) -> each shard's backward on
+    # that lse -> dH summed over the shards (the all-reduce of the partial dH).
+    # Shards of 2000 vocab rows (7 whole 256-column tiles and a ragged one).
+    R, M, Vr, K = 8, 1024, 2000, 1024
+    H = syn.normal(9100, (M, K), 1.0, syn.BF16)
+    Ws = [syn.normal(9110 + r, (Vr, K), 0.05, syn.BF16) for r in range(R)]
+    target = np.random.default_rng(9120).integers(0, R * Vr, size=M).astype(np.int32)
+    g = syn.normal(9121, (M,), 1.0, syn.FP32).f32
+    Hd, td, gd = dev(H), torch.from_numpy(target).cuda(), torch.from_numpy(g).cuda()
+    parts = [ops.vocab_ce_partials(Hd, dev(Ws[r]), td, r * Vr) for r in range(R)]
+    lse, tgt, loss = ops.vocab_ce_combine([p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts])
+    dHs, dWs = [], []
+    for r in range(R):
+        dH, dW = ops.vocab_ce_bwd(Hd, dev(Ws[r]), td, r * Vr, lse, gd)
+        dHs.append(dH)
+        dWs.append(dW)
+    buf, n = ops.stack_partials(dHs)
+    dHsum = ops.sum_partials(buf, n)
+    torch.cuda.synchronize()
+    rparts = [oracle.vocab_ce_partials(H.f64, Ws[r].f64, target, r * Vr) for r in range(R)]
+    rl, rt, rloss = oracle.lse_recombine(rparts)
+    assert_close("lse", host64(lse), rl, 1e-3)
+    assert_close("tgt", host64(tgt), rt, 1e-3)
+    assert_close("loss", host64(loss), rloss, 1e-3)
+    rdH = np.zeros((M, K))
+    for r in range(R):
+        _, rdHr, rdWr = oracle.vocab_ce_bwd(H.f64, Ws[r].f64, target, r * Vr, rl, g)
+        rdH += rdHr
+        assert_close(f"dW shard {r}", host64(dWs[r]), rdWr, TOL[syn.BF16])
+    assert_close("dH summed", host64(dHsum), rdH, TOL[syn.BF16])
+
+
 def _ids_dev(ids):
     return torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
 
