@@ -13,8 +13,10 @@
  *            Y = X W: a column shard A_i is [K, N_i], a row shard B_i is
  *            [K_i, N]; the LM-head shard W_r is [V_r, K] (vocab rows).
  * Pointers.  All tensor pointers are DEVICE pointers owned by the caller.
- *            The library never allocates, frees or keeps device memory and
- *            has no global mutable state; calls are reentrant.
+ *            The library never allocates or frees device memory.  Its only
+ *            state is the per-GPU scratch array of
+ *            tp_vocab_ce_partials_noalloc (see there); every other call is
+ *            reentrant.
  * Streams.   `stream` is a hipStream_t (NULL = the null stream).  Every call
  *            validates its arguments synchronously, then only enqueues work
  *            on `stream` and returns; the caller synchronizes.
@@ -197,6 +199,29 @@ TP_API tp_status tp_vocab_ce_partials(int dtype, int64_t M, int64_t Vr, int64_t 
                                float* out_max, float* out_sumexp, float* out_tgt,
                                void* workspace, size_t ws_bytes, void* stream);
 TP_API size_t tp_vocab_ce_workspace_bytes(int64_t M, int64_t Vr);
+
+/*
+ * tp_vocab_ce_partials without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * tp_vocab_ce_partials minus the workspace: the per-tile partials live in a
+ * scratch array of TP_CE_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held until the process ends (its address is looked up on the first
+ * call on each device).  The call allocates nothing.
+ * Limit: tp_vocab_ce_workspace_bytes(M, Vr) = (2*ceil(Vr/256) + 1) * M * 4
+ * bytes must not exceed TP_CE_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. M = 8192
+ * tokens with Vr up to 65280), else TP_E_WORKSPACE and nothing is launched.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on the same GPU (other streams, other threads) race and give undefined
+ * results; calls on one stream run in order and are safe.  No part of the
+ * array needs to start at zero (every byte read is written first).
+ */
+#define TP_CE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+TP_API tp_status tp_vocab_ce_partials_noalloc(int dtype, int64_t M, int64_t Vr, int64_t K,
+                                              const void* H, int64_t ldh, const void* W, int64_t ldw,
+                                              const int32_t* target, int64_t v0,
+                                              float* out_max, float* out_sumexp, float* out_tgt,
+                                              void* stream);
 
 /*
  * Recombination of the vocab shards' cross-entropy partials: the value the

@@ -23,7 +23,7 @@ __all__ = [
     "TP_FP32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU", "TP_ACT_SWIGLU", "TPError", "LIB_PATH",
     "tp_abi_version", "tp_status_str", "tp_column_fwd", "tp_row_fwd", "tp_sum_partials", "tp_row_bwd",
     "tp_row_bwd_workspace_bytes", "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_vocab_ce_partials",
-    "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "tp_sp_reduce_scatter_ln",
+    "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_partials_noalloc", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "tp_sp_reduce_scatter_ln",
     "tp_vocab_embed_fwd", "tp_vocab_embed_bwd", "tp_vocab_embed_bwd_workspace_bytes", "tp_attention_fwd",
     "tp_attention_fwd_workspace_bytes", "tp_attention_bwd", "tp_attention_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
@@ -52,6 +52,8 @@ _SIGS = {
     "tp_vocab_ce_partials": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                     _sz, _vp]),
     "tp_vocab_ce_workspace_bytes": (_sz, [_i64, _i64]),
+    "tp_vocab_ce_partials_noalloc": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp,
+                                            _vp, _vp]),
     "tp_vocab_ce_combine": (_i32, [_i32, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp]),
     "tp_vocab_ce_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp,
                                _i64, _vp, _sz, _vp]),
@@ -182,6 +184,13 @@ def tp_vocab_ce_partials(dtype, M, Vr, K, H, ldh, W, ldw, target, v0, out_max, o
 
 def tp_vocab_ce_workspace_bytes(M, Vr) -> int:
     return _load().tp_vocab_ce_workspace_bytes(M, Vr)
+
+
+def tp_vocab_ce_partials_noalloc(dtype, M, Vr, K, H, ldh, W, ldw, target, v0, out_max, out_sumexp, out_tgt,
+                                 stream=None):
+    _check("tp_vocab_ce_partials_noalloc", _load().tp_vocab_ce_partials_noalloc(
+        dtype, M, Vr, K, _ptr(H), ldh, _ptr(W), ldw, _ptr(target), v0, _ptr(out_max), _ptr(out_sumexp),
+        _ptr(out_tgt), _stream(stream)))
 
 
 def tp_vocab_ce_combine(R, M, maxes, sumexps, tgts, stride, lse, tgt, loss, stream=None):

@@ -444,6 +444,24 @@ tp_status tp_vocab_ce_combine(int R, int64_t M, const float* maxes, const float*
   return tps::launch_ce_combine(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
 }
 
+tp_status tp_vocab_ce_partials_noalloc(int dtype, int64_t M, int64_t Vr, int64_t K, const void* H, int64_t ldh,
+                                       const void* W, int64_t ldw, const int32_t* target, int64_t v0, float* out_max,
+                                       float* out_sumexp, float* out_tgt, void* stream) {
+  static_assert(TP_CE_NOALLOC_SCRATCH_BYTES == tps::kCeScratchBytes, "header and library agree on the scratch size");
+  if (dtype != TP_BF16) return TP_E_DTYPE;
+  if (!H || !W || !target || !out_max || !out_sumexp || !out_tgt) return TP_E_NULL;
+  if (bad_dim(M) || bad_dim(Vr) || bad_dim(K)) return TP_E_SHAPE;
+  TPS_TRY(check_grid(dtype, M, Vr));
+  TPS_TRY(check_mat(H, M, ldh, K, dtype));
+  TPS_TRY(check_mat(W, Vr, ldw, K, dtype));
+  if (!aligned16(target) || !aligned16(out_max) || !aligned16(out_sumexp) || !aligned16(out_tgt)) return TP_E_ALIGN;
+  if (tps::ce_workspace_bytes(M, Vr) > tps::kCeScratchBytes) return TP_E_WORKSPACE;
+  float* ws = nullptr;
+  if (tps::ce_scratch(&ws) != hipSuccess) return TP_E_HIP;
+  tps::CEArgs a = {M, Vr, K, H, ldh, W, ldw, target, v0, out_max, out_sumexp, out_tgt, ws};
+  return tps::launch_ce_partials(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TP_OK : TP_E_HIP;
+}
+
 size_t tp_vocab_ce_bwd_workspace_bytes(int64_t M, int64_t Vr) {
   if (bad_dim(M) || bad_dim(Vr)) return 0;
   return align_ws((size_t)M * (size_t)round_up(Vr, 8) * 2);

@@ -22,6 +22,7 @@
 // register quad.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <utility>
 
 #include "device_common.hpp"
@@ -1449,6 +1450,37 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
     }
   }
   if (ne > 0) return dispatch<false>(E, ne, ne, s);
+  return hipSuccess;
+}
+
+}  // namespace tps
+
+// Scratch of the allocation-free CE entry point: the per-tile (max, sum exp)
+// pairs and target logits that tp_vocab_ce_partials keeps in the caller's
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[tps::kCeScratchBytes];
+
+namespace tps {
+
+hipError_t ce_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with `dev` current: this device's copy
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = static_cast<float*>(ptrs[dev]);
   return hipSuccess;
 }
 

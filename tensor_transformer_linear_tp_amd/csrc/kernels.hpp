@@ -202,6 +202,10 @@ constexpr int kColpartRows = 64;   // rows per column-partial block
 hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s);
 hipError_t launch_gemm_f32(GemmLaunch& L, hipStream_t s);
 hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s);
+// Size of the library's own CE scratch array (one per device), and its
+// device address on the current device (looked up once per device).
+constexpr size_t kCeScratchBytes = size_t(16) << 20;
+hipError_t ce_scratch(float** out);
 size_t ce_workspace_bytes(int64_t M, int64_t Vr);
 hipError_t launch_act_bwd(int is_bf16, const ActBwdArgs& a, hipStream_t s);
 hipError_t launch_ce_combine(const CECombineArgs& a, hipStream_t s);

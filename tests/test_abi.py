@@ -119,6 +119,26 @@ def test_ce_validation(lib):
     assert _rc("tp_vocab_ce_partials", *a) == 3
 
 
+def test_ce_noalloc_validation(lib):
+    # Same checks as tp_vocab_ce_partials, and shapes whose per-tile partials
+    # exceed the library's scratch array are rejected before any HIP call.
+    assert tp.tp_vocab_ce_workspace_bytes(8192, 18992) <= 16 << 20
+    base = [tp.TP_BF16, 8192, 18992, 4096, P, 4096, P, 4096, P, 0, P, P, P, None]
+    a = list(base); a[0] = tp.TP_FP32
+    assert _rc("tp_vocab_ce_partials_noalloc", *a) == 4
+    a = list(base); a[8] = None
+    assert _rc("tp_vocab_ce_partials_noalloc", *a) == 1
+    a = list(base); a[12] = P + 4
+    assert _rc("tp_vocab_ce_partials_noalloc", *a) == 3
+    # (2 * ceil(Vr / 256) + 1) * M * 4 bytes: Vr = 65280 is the largest that fits at M = 8192
+    assert tp.tp_vocab_ce_workspace_bytes(8192, 65280) <= 16 << 20 < tp.tp_vocab_ce_workspace_bytes(8192, 65281)
+    a = list(base); a[2] = 65281
+    assert _rc("tp_vocab_ce_partials_noalloc", *a) == 6
+    a = list(base); a[2] = 256; a[3] = 8; a[5] = 8; a[7] = 8   # one vocab tile: (2 + 1) * M * 4 bytes
+    a[1] = 1 << 21                                             # 24 MiB at 2^21 tokens
+    assert _rc("tp_vocab_ce_partials_noalloc", *a) == 6
+
+
 def test_ce_combine_validation(lib):
     def call(R=8, M=64, ms=P, ss=P, ts=P, stride=64, lse=P, tgt=P, loss=P):
         return _rc("tp_vocab_ce_combine", R, M, ms, ss, ts, stride, lse, tgt, loss, None)
