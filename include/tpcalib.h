@@ -1,0 +1,46 @@
+/*
+ * tpcalib.h -- C ABI of libtpcalib: a measurement helper, not part of the
+ * method.  It measures the bf16 MFMA rate a gfx950 GPU sustains when nothing
+ * but matrix instructions run, which is the practical ceiling the GEMM
+ * kernels of libtpshard are judged against (the nominal peak assumes the
+ * 2.4 GHz clock at every MFMA density; under a board power limit the clock
+ * drops with the power the matrix cores draw, which depends on the data).
+ */
+#ifndef TPCALIB_H
+#define TPCALIB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef TPC_API
+#define TPC_API __attribute__((visibility("default")))
+#endif
+
+/*
+ * Launches one workgroup of 4 wave64s per CU (`cus` workgroups).  Each wave
+ * loads its operand fragments (bf16, 8 per lane) from `src` once and then
+ * issues matrix instructions into independent accumulator blocks held in the
+ * 256 accumulator registers, cycling through its fragments so that
+ * consecutive instructions see different operands; no memory traffic and no
+ * LDS inside the loop.
+ *   shape 32: v_mfma_f32_32x32x16_bf16, 16 blocks, 16 fragments per wave
+ *             (wave w reads 16 KiB at src + (w % 4) * 16 KiB), 32
+ *             instructions (1048576 FLOP) per iteration;
+ *   shape 16: v_mfma_f32_16x16x32_bf16, 32 blocks, 24 fragments per wave
+ *             (24 KiB at src + (w % 4) * 24 KiB), 64 instructions
+ *             (1048576 FLOP) per iteration.
+ * src: >= 96 KiB, 16-byte aligned, device.  out: fp32 [cus * 256] (one
+ * checksum per thread, device) so the work cannot be elided.  FLOPs of one
+ * call: cus * 4 * iters * (FLOP per iteration).  Returns 0, -1 for a NULL
+ * pointer, iters < 1, cus < 1 or another shape (nothing launched), else the
+ * hipError_t of the launch.  Asynchronous on `stream` (NULL = default).
+ */
+TPC_API int tpc_mfma_loop(const void* src, float* out, int cus, int iters, int shape, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPCALIB_H */

@@ -18,6 +18,9 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libtpshard.so")
+# Measurement helper (MFMA-only calibration kernel), a library of its own: not the method.
+CALIB_PATH = os.path.join(PKG_DIR, "libtpcalib.so")
+CALIB_SOURCES = ["calib_mfma.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "embedding.hip", "attention.hip",
@@ -62,18 +65,25 @@ def _compile(src: str, hipcc: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile and link libtpshard.so; returns its path.  Always rebuilds."""
-    hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, hipcc: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile and link libtpshard.so (and the calibration library libtpcalib.so);
+    returns the path of libtpshard.so.  Always rebuilds."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, hipcc, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH, hipcc)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_PATH, hipcc)
     return LIB_PATH
 
 

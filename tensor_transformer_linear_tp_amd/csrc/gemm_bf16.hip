@@ -1,12 +1,15 @@
 // bf16 GEMM family for gfx950 (MI355X): C = A B with fp32 accumulation on
-// v_mfma_f32_32x32x16_bf16, a 4-stage LDS ring filled by direct-to-LDS buffer
+// v_mfma_f32_16x16x32_bf16, a 4-stage LDS ring filled by direct-to-LDS buffer
 // loads, and fused epilogues; plus the vocab-parallel LM-head kernel whose
 // epilogue reduces logit tiles to (max, sum exp) partials without writing the
 // logits.
 //
 // Tiling: a 256-thread workgroup (4 wave64s as 2 x 2) owns a 256 x 256 output
 // tile (SwiGLU: 256 rows x (128 gate + 128 up) columns); each wave owns
-// 128 x 128 = 4 x 4 MFMA blocks of 32 x 32.  K advances 32 per LDS stage.
+// 128 x 128 = 8 x 8 MFMA blocks of 16 x 16.  K advances 32 per LDS stage,
+// one MFMA deep.  (The 16 x 16 x 32 instruction does the same work as the
+// 32 x 32 x 16 one at a lower power per FLOP: with random operands held in
+// registers the chip sustains a ~16 % higher clock under its power limit.)
 //
 // LDS layouts.  Operands are copied global -> LDS in their global orientation:
 //   * K-contiguous operand (A of NN/NT, B of NT): [256 rows][32 k], read as
@@ -18,8 +21,8 @@
 // fall into distinct banks.
 //
 // Accumulator orientation.  The MFMA is issued as (B fragment, A fragment),
-// so each lane holds four consecutive output columns of one row per
-// register quad.
+// so in each 16 x 16 block a lane holds four consecutive output columns of
+// one row: row lane % 16, columns 4 * (lane / 16) .. +3.
 #include <algorithm>
 #include <climits>
 #include <mutex>
@@ -44,9 +47,13 @@ constexpr int GROUP_M = 8;                    // tile rows per L2 group
 // same logical chunk over all 16 chunk slots of a 256-byte bank cycle.
 __device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ kc_swz(r)) << 4); }
-// MN-contiguous [32][W]: rows of W bf16 (512 or 256 bytes); rows k%4 = 0,1,2,3
-// XOR the chunk index with 0, 6, 10, 12.
-__device__ __forceinline__ int mn_swz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }
+// MN-contiguous [32][W]: rows of W bf16 (512 or 256 bytes); row k XORs the
+// chunk index with 2 * ((k & 3) | (k & 8) >> 1): a transposing fragment read
+// covers 4 consecutive rows in each of two 16-lane groups (rows k..k+3 and
+// k+8..k+11, 32 bytes of each), and those 8 rows then hold distinct pairs of
+// chunks, all 64 banks once.  Rows k and k + 4 share the swizzle, so the
+// second read of a fragment is the first plus 4 rows.
+__device__ __forceinline__ int mn_swz(int k) { return 2 * ((k & 3) | ((k & 8) >> 1)); }
 template <int ROWB>
 __device__ __forceinline__ int mn_off(int k, int c) { return k * ROWB + ((c ^ mn_swz(k)) << 4); }
 
@@ -144,6 +151,23 @@ __device__ __forceinline__ void stream_issue(const OpStream& st, int stage, bool
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(wtile + 1024 * j), 16, st.voff[j] + off, 0, 0, 0);
 }
 
+// One of those copies: block J of this wave's blocks of the stage.
+template <int J>
+__device__ __forceinline__ void stream_issue1(const OpStream& st, int stage, bool live, TPS_LDS char* wtile) {
+  const uint32_t off = live ? (uint32_t)stage * st.step : st.nrec;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(st.base), (short)0, (int)st.nrec, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(wtile + 1024 * J), 16, st.voff[J] + off, 0, 0, 0);
+}
+
+// One 16-byte-per-lane copy into LDS at `ldst` (lane order) from `base` +
+// voff (per lane) within a range of nrec bytes (past it: zeros).
+__device__ __forceinline__ void copy16(const char* base, uint32_t nrec, uint32_t voff, TPS_LDS char* ldst) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)nrec, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)ldst, 16, voff, 0, 0, 0);
+}
+
 // Zero k >= kvalid (0 < kvalid < 32) of a K-contiguous [256][32] LDS tile.
 __device__ __forceinline__ void kc_zero_tail(TPS_LDS char* tile, int kvalid) {
   const int t = threadIdx.x;
@@ -169,37 +193,6 @@ template <int VM, int LGKM>
 __device__ __forceinline__ void waitcnt() {
   static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
-}
-
-// ---- LDS -> MFMA fragments ---------------------------------------------------
-// Operand fragment of v_mfma_f32_32x32x16_bf16: lane l holds 8 consecutive k
-// (k = 8*(l/32) + 0..7 within the 16-deep step) of row/column (l % 32).
-__device__ __forceinline__ bf16x8 frag_kc(const TPS_LDS char* s, int rb, int kk) {
-  const int lane = threadIdx.x & 63;
-  const int r = rb + (lane & 31);
-  const int c = 2 * kk + (lane >> 5);
-  return *reinterpret_cast<const TPS_LDS bf16x8*>(s + kc_off(r, c));
-}
-
-// Same fragment from an MN-contiguous tile.  ds_read_b64_tr_b16: within each
-// 16-lane group, lane i receives element (i % 4) of the 8-byte loads of
-// source lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.  Source lane s therefore
-// loads row k = base + s/4, columns c + 4*(s % 4) .. +3, and lane i ends up
-// with rows base..base+3 of column c + i.
-template <int ROWB>
-__device__ __forceinline__ bf16x8 frag_mn(const TPS_LDS char* s, int cb, int kk) {
-  const int lane = threadIdx.x & 63;
-  const int h = lane >> 4, q = lane & 15;
-  const int col = cb + 16 * (h & 1) + 4 * (q & 3);
-  const int k0 = 16 * kk + 8 * (h >> 1) + (q >> 2);
-  const int c = col >> 3, byte_in = (col & 7) * 2;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (TPS_LDS i16x4*)(s + mn_off<ROWB>(k0, c) + byte_in));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (TPS_LDS i16x4*)(s + mn_off<ROWB>(k0 + 4, c) + byte_in));
-  typedef __attribute__((ext_vector_type(8))) short i16x8;
-  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
 }
 
 // ---- scheduling --------------------------------------------------------------
@@ -264,6 +257,7 @@ struct TileStreams {
   int s0, send;            // the piece: stages [s0, send) of the tile
   int rot;                 // the piece runs from stage s0 + rot, wrapping around to s0
   int npad;                // send - s0 rounded up to NSTAGE
+  int tail;                // a K-contiguous operand's segment ends inside a stage (K % 32 != 0)
 };
 
 // MI, NI: 32 x 32 MFMA blocks per wave along M and N; the tile is
@@ -336,6 +330,7 @@ struct Pipe {
     T.send = min(s1, nk);
     T.rot = ((T.send - s0) * rot8) >> 3;
     T.npad = (T.send - s0 + NSTAGE - 1) / NSTAGE * NSTAGE;
+    T.tail = (A_KC || B_KC) && ((T.kseg0 % BK) != 0 || (SEG2 && (T.kseg1 % BK) != 0));
     uniform(T);
     return T;
   }
@@ -366,6 +361,7 @@ struct Pipe {
     T.send = sgpr(T.send);
     T.rot = sgpr(T.rot);
     T.npad = sgpr(T.npad);
+    T.tail = sgpr(T.tail);
   }
 
   __device__ __forceinline__ void no_next() {
@@ -385,59 +381,114 @@ struct Pipe {
     return T.s0 + t;
   }
 
-  // Issue the copies of step r of the current piece (NEXT: of the next
-  // piece) into `dst`.  A stage past the piece's end is issued with an empty
-  // range (zeros).  Which piece is a compile-time choice: selecting between
-  // the two at run time would put the stream records in scratch memory.
-  template <bool NEXT>
-  __device__ __forceinline__ void issue(int r, TPS_LDS char* dst) {
-    const TileStreams& T = NEXT ? nxt : cur;
-    bool live;
-    const int s = stage_of(T, r, live);
-    const bool s1 = SEG2 && s >= T.nk0;
-    const int stage = s1 ? s - T.nk0 : s;
-    // Recompute the LDS destinations at every stage (an empty asm hides the
-    // wave offsets' value): hoisted, the 32 per-slot addresses would crowd
-    // the scalar registers.
-    int wa = wlds_a, wb = wlds_b;
-    asm volatile("" : "+s"(wa), "+s"(wb));
-    stream_issue<NBA>(s1 ? T.a1 : T.a0, stage, live, dst + wa);
-    stream_issue<NBB>(s1 ? T.b1 : T.b0, stage, live, dst + wb);
+  // The copy source of step r: the current piece's step r or, past its end,
+  // the next piece's step r - npad (the next tile's first stages load during
+  // this tile's last steps and its epilogue).  Selected field-wise at run
+  // time -- scalars once per step, one vector select per copy -- so that the
+  // K loop is one uniform body (a separate block for the last steps made the
+  // register allocator move accumulators around it).
+  struct CopySrc {
+    const char* basea;      // the stage's first byte of each operand (the tile origin + the stage offset)
+    const char* baseb;
+    uint32_t nreca, nrecb;  // bytes from there to the operand's end; 0 past the piece's end (zeros)
+    bool nx, s1;
+  };
+  template <class F>
+  __device__ __forceinline__ static auto pick4(bool nx, bool s1, F c0, F c1, F n0, F n1) {
+    return nx ? (s1 ? n1 : n0) : (s1 ? c1 : c0);
+  }
+  __device__ __forceinline__ CopySrc copy_src(int r) const {
+    CopySrc c;
+    c.nx = r >= cur.npad;
+    const int rr = c.nx ? r - cur.npad : r;
+    const int s0 = c.nx ? nxt.s0 : cur.s0, send = c.nx ? nxt.send : cur.send;
+    const int rot = c.nx ? nxt.rot : cur.rot, nk0 = c.nx ? nxt.nk0 : cur.nk0;
+    const int cnt = send - s0;
+    int t = rr + rot;
+    t = t >= cnt ? t - cnt : t;
+    const bool live = rr < cnt;
+    const int st = s0 + t;
+    c.s1 = SEG2 && st >= nk0;
+    const uint32_t stage = (uint32_t)(c.s1 ? st - nk0 : st);
+    const bool x = c.nx, y = c.s1;
+    const char* ab = pick4(x, y, cur.a0.base, cur.a1.base, nxt.a0.base, nxt.a1.base);
+    const uint32_t anr = pick4(x, y, cur.a0.nrec, cur.a1.nrec, nxt.a0.nrec, nxt.a1.nrec);
+    const uint32_t ast = pick4(x, y, cur.a0.step, cur.a1.step, nxt.a0.step, nxt.a1.step);
+    const char* bb = pick4(x, y, cur.b0.base, cur.b1.base, nxt.b0.base, nxt.b1.base);
+    const uint32_t bnr = pick4(x, y, cur.b0.nrec, cur.b1.nrec, nxt.b0.nrec, nxt.b1.nrec);
+    const uint32_t bst = pick4(x, y, cur.b0.step, cur.b1.step, nxt.b0.step, nxt.b1.step);
+    const uint32_t oa = stage * ast, ob = stage * bst;
+    c.basea = ab + oa;
+    c.baseb = bb + ob;
+    c.nreca = live ? anr - oa : 0u;   // a stage past the piece's end reads past the range: zeros
+    c.nrecb = live ? bnr - ob : 0u;
+    return c;
   }
 
+  // Copy C of a step into `dst`: copies [0, NBA) are A's blocks, [NBA, NCOPY)
+  // B's.  Each writes 1 KiB of LDS in lane order at the wave's block.
+  template <int C>
+  __device__ __forceinline__ void issue1(const CopySrc& c, TPS_LDS char* dst) {
+    if constexpr (C < NBA) {
+      const uint32_t v = pick4(c.nx, c.s1, cur.a0.voff[C], cur.a1.voff[C], nxt.a0.voff[C], nxt.a1.voff[C]);
+      copy16(c.basea, c.nreca, v, dst + wlds_a + 1024 * C);
+    } else {
+      constexpr int J = C - NBA;
+      const uint32_t v = pick4(c.nx, c.s1, cur.b0.voff[J], cur.b1.voff[J], nxt.b0.voff[J], nxt.b1.voff[J]);
+      copy16(c.baseb, c.nrecb, v, dst + wlds_b + 1024 * J);
+    }
+  }
+  template <int... Cs>
+  __device__ __forceinline__ void issue_all(const CopySrc& c, TPS_LDS char* dst, std::integer_sequence<int, Cs...>) {
+    (issue1<Cs>(c, dst), ...);
+  }
+  __device__ __forceinline__ void issue(int r, TPS_LDS char* dst) {
+    issue_all(copy_src(r), dst, std::make_integer_sequence<int, NCOPY>{});
+  }
+
+  // 16 x 16 MFMA blocks per wave along M and N; acc[i][j] is block (i, j).
+  static constexpr int BI = 2 * MI, BJ = 2 * NI;
+  typedef f32x4 Acc[BI][BJ];
+
   // Per-lane LDS byte addresses of the fragments, computed once.  A fragment
-  // read is then addr + a compile-time offset (K sub-step, block), which the
-  // ds_read instruction's offset field absorbs.
-  //   K-contiguous operand: one base per 16-deep K sub-step (the swizzle
-  //   mixes k into the chunk index); blocks are +32 rows = +2048 bytes.
-  //   MN-contiguous operand: one base per 32-wide block (the swizzle mixes
-  //   the column into the chunk index); K sub-steps are +16 rows.
-  int adA[4], adB[4];
+  // of v_mfma_f32_16x16x32_bf16: lane l holds 8 consecutive k (k = 8 (l/16)
+  // .. +7 of the 32-deep stage) of row/column l % 16 of its 16-wide block.
+  //   K-contiguous operand: one ds_read_b128 (row l % 16 of the block, chunk
+  //   l / 16); block b is +16 rows = +1024 bytes (the row swizzle repeats
+  //   every 16 rows), so one base address.
+  //   MN-contiguous operand: two ds_read_b64_tr_b16 (rows k and k + 4); one
+  //   address per block (the swizzle mixes the column into the chunk index).
+  //   Within each 16-lane group the transposing read gives lane i element
+  //   i % 4 of the 8-byte loads of source lanes i/4, 4 + i/4, 8 + i/4,
+  //   12 + i/4: source lane s loads row k0 + s/4, columns c + 4 (s % 4) .. +3,
+  //   and lane i ends up with rows k0 .. k0+3 of column c + i.
+  int adA[A_KC ? 1 : BI], adB[B_KC ? 1 : BJ];
 
   __device__ __forceinline__ void init_frag_addr() {
     const int lane = threadIdx.x & 63;
-    const int h = lane >> 4, q = lane & 15, hi32 = lane >> 5;
+    const int h = lane >> 4, q = lane & 15;
+    const int k = 8 * h + (q >> 2);   // first row of this lane's transposing read
+    if constexpr (A_KC) {
+      adA[0] = kc_off(32 * MI * wm + q, h);
+    } else {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      if (A_KC) {
-        const int r = 32 * MI * wm + (lane & 31);
-        adA[x] = kc_off(r, 2 * (x & 1) + hi32);
-      } else {
-        const int col = 32 * MI * wm + 32 * x + 16 * (h & 1) + 4 * (q & 3);
-        const int k = 8 * (h >> 1) + (q >> 2);
-        adA[x] = mn_off<512>(k, col >> 3) + (col & 7) * 2;
+      for (int i = 0; i < (A_KC ? 1 : BI); ++i) {
+        const int col = 32 * MI * wm + 16 * i + 4 * (q & 3);
+        adA[i] = mn_off<512>(k, col >> 3) + (col & 7) * 2;
       }
-      if (B_KC) {
-        const int r = 32 * NI * wn + (lane & 31);
-        adB[x] = TILE_BYTES + kc_off(r, 2 * (x & 1) + hi32);
-      } else if (DUAL) {
-        const int col = 64 * wn + 32 * (x & 1) + 16 * (h & 1) + 4 * (q & 3);
-        const int k = 8 * (h >> 1) + (q >> 2);
-        adB[x] = TILE_BYTES + (x >> 1) * (TILE_BYTES / 2) + mn_off<256>(k, col >> 3) + (col & 7) * 2;
-      } else {
-        const int col = 32 * NI * wn + 32 * x + 16 * (h & 1) + 4 * (q & 3);
-        const int k = 8 * (h >> 1) + (q >> 2);
-        adB[x] = TILE_BYTES + mn_off<512>(k, col >> 3) + (col & 7) * 2;
+    }
+    if constexpr (B_KC) {
+      adB[0] = TILE_BYTES + kc_off(32 * NI * wn + q, h);
+    } else {
+#pragma unroll
+      for (int j = 0; j < (B_KC ? 1 : BJ); ++j) {
+        if (DUAL) {   // blocks 0-3: gate columns 64 wn .. +63, blocks 4-7: the same up columns
+          const int col = 64 * wn + 16 * (j & 3) + 4 * (q & 3);
+          adB[j] = TILE_BYTES + (j >> 2) * (TILE_BYTES / 2) + mn_off<256>(k, col >> 3) + (col & 7) * 2;
+        } else {
+          const int col = 32 * NI * wn + 16 * j + 4 * (q & 3);
+          adB[j] = TILE_BYTES + mn_off<512>(k, col >> 3) + (col & 7) * 2;
+        }
       }
     }
   }
@@ -445,247 +496,306 @@ struct Pipe {
   static __device__ __forceinline__ bf16x8 rd_kc(const TPS_LDS char* p) {
     return *reinterpret_cast<const TPS_LDS bf16x8*>(p);
   }
-  static __device__ __forceinline__ bf16x8 rd_mn(const TPS_LDS char* p, int rowb) {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS i16x4*)p);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS i16x4*)(p + 4 * rowb));
-    typedef __attribute__((ext_vector_type(8))) short i16x8;
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  static __device__ __forceinline__ i16x4 rd_tr(const TPS_LDS char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((TPS_LDS i16x4*)p);
   }
 
-  // Fragment register sets: sub-step kk of a stage lives in set kk.
-  bf16x8 af[2][4], bfr[2][4];
+  // Fragment registers.  B: one set per stage parity (the loop is unrolled
+  // over an even number of ring slots, so the parity is static): the
+  // previous stage's second half still multiplies its B while this stage's
+  // is read.  A: one set -- its first half is read after the previous stage's
+  // first half has run, its second half after the previous second half.
+  // MN-contiguous fragments are kept as their two transposed halves.
+  bf16x8 akc[BI], bkc[2][BJ];
+  i16x4 amn[BI][2], bmn[2][BJ][2];
 
-  __device__ __forceinline__ void load(const TPS_LDS char* base, int kk) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      af[kk][i] = A_KC ? rd_kc(base + adA[kk] + 2048 * i) : rd_mn(base + adA[i] + 16 * kk * 512, 512);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      if (B_KC) bfr[kk][j] = rd_kc(base + adB[kk] + 2048 * j);
-      else if (DUAL) bfr[kk][j] = rd_mn(base + adB[j] + 16 * kk * 256, 256);
-      else bfr[kk][j] = rd_mn(base + adB[j] + 16 * kk * 512, 512);
+  __device__ __forceinline__ bf16x8 fragA(int i) const {
+    if constexpr (A_KC) return akc[i];
+    else return __builtin_bit_cast(bf16x8, __builtin_shufflevector(amn[i][0], amn[i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  template <int P>
+  __device__ __forceinline__ bf16x8 fragB(int j) const {
+    if constexpr (B_KC) return bkc[P][j];
+    else return __builtin_bit_cast(bf16x8, __builtin_shufflevector(bmn[P][j][0], bmn[P][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // LDS read R of a stage (one instruction): the A fragments of block rows
+  // [I0, I1) first (MN: two reads each), then, when WITH_B, all of B.
+  static constexpr int RA_PER = A_KC ? 1 : 2, RB_PER = B_KC ? 1 : 2;
+  template <int P, int I0, int I1, bool WITH_B, int R>
+  __device__ __forceinline__ void read_op(const TPS_LDS char* base) {
+    constexpr int NRA = (I1 - I0) * RA_PER;
+    if constexpr (R < NRA) {
+      constexpr int i = I0 + R / RA_PER, h = R % RA_PER;
+      if constexpr (A_KC) akc[i] = rd_kc(base + adA[0] + 1024 * i);
+      else amn[i][h] = rd_tr(base + adA[A_KC ? 0 : i] + h * 4 * 512);
+    } else if constexpr (WITH_B) {
+      constexpr int j = (R - NRA) / RB_PER, h = (R - NRA) % RB_PER;
+      if constexpr (B_KC) bkc[P][j] = rd_kc(base + adB[0] + 1024 * j);
+      else bmn[P][j][h] = rd_tr(base + adB[B_KC ? 0 : j] + h * 4 * (DUAL ? 256 : 512));
     }
   }
 
-  __device__ __forceinline__ void mma(int r, f32x16 (&acc)[MI][NI]) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[r][j], af[r][i], acc[i][j], 0, 0, 0);
+  // One MFMA of the stage with parity P, accumulating in place: an asm
+  // statement ties the accumulator to one register tuple for the whole loop.
+  // (Written with the compiler builtin, the 16 x 16 accumulators were renamed
+  // and copied between registers every step.)  Operands as (B, A): the lane
+  // holds output row lane % 16, columns 4 (lane / 16) .. +3.
+  template <int P, int I, int J>
+  __device__ __forceinline__ void mma1(Acc& acc) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(acc[I][J])
+                 : "v"(fragB<P>(J)), "v"(fragA(I)));
   }
 
   __device__ __forceinline__ void zero_set1() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      af[1][i] = bf16x8{};
-      bfr[1][i] = bf16x8{};
+    for (int i = 0; i < BI; ++i) {
+      akc[i] = bf16x8{};
+      amn[i][0] = amn[i][1] = i16x4{};
+    }
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) {
+      bkc[1][j] = bf16x8{};
+      bmn[1][j][0] = bmn[1][j][1] = i16x4{};
     }
   }
 
-  // Ask the scheduler to alternate one MFMA with one LDS read (and, in the
-  // first phase of a step, a global->LDS copy after every second MFMA: packed
-  // one per MFMA into the first slots the step ran ~1 % slower), instead of
-  // loading each fragment just before its first use.
-  static constexpr int READS = (A_KC ? MI : 2 * MI) + (B_KC ? NI : 2 * NI);
-  static constexpr int GROUPS = std::max(MI * NI, READS);
-  static __device__ __forceinline__ void interleave(bool with_copies) {
-#pragma unroll
-    for (int g = 0; g < GROUPS; ++g) {
-      if (g < MI * NI) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
-      if (g < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // DS read
-      if (with_copies && (g & 1) == 0 && g / 2 < NCOPY) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
-    }
+  // Group G of a phase: MFMA G of the half H of the stage with parity PM
+  // (block row H*BI/2 + G/BJ, column G % BJ), then LDS read G (of the reads
+  // of block rows [I0, I1) of A and, WITH_B, all of B, for parity PR), then,
+  // with copies, copy G/2 after every second MFMA; fenced so the scheduler
+  // keeps this order.
+  static constexpr int HALF_MFMA = (BI / 2) * BJ;
+  template <int PM, int H, int PR, int I0, int I1, bool WITH_B, int NREAD, bool COPIES, int G>
+  __device__ __forceinline__ void group(Acc& acc, const TPS_LDS char* rbase, const CopySrc& cs, TPS_LDS char* cdst) {
+    if constexpr (G < HALF_MFMA) mma1<PM, H * (BI / 2) + G / BJ, G % BJ>(acc);
+    if constexpr (G < NREAD) read_op<PR, I0, I1, WITH_B, G>(rbase);
+    if constexpr (COPIES && G % COPY_EVERY == 0 && G / COPY_EVERY < NCOPY) issue1<G / COPY_EVERY>(cs, cdst);
     __builtin_amdgcn_sched_barrier(0);
   }
+  template <int PM, int H, int PR, int I0, int I1, bool WITH_B, int NREAD, bool COPIES, int... Gs>
+  __device__ __forceinline__ void phase(Acc& acc, const TPS_LDS char* rbase, const CopySrc& cs, TPS_LDS char* cdst,
+                                        std::integer_sequence<int, Gs...>) {
+    (group<PM, H, PR, I0, I1, WITH_B, NREAD, COPIES, Gs>(acc, rbase, cs, cdst), ...);
+  }
+  static constexpr int READS1 = (BI / 2) * RA_PER + BJ * RB_PER;
+  static constexpr int READS2 = (BI - BI / 2) * RA_PER;
+  static constexpr int COPY_EVERY = HALF_MFMA >= 4 * NCOPY ? 4 : 2;   // MFMAs per copy in phase 1
+  static constexpr int GROUPS1 = std::max(std::max(HALF_MFMA, READS1), COPY_EVERY * NCOPY);
+  static constexpr int GROUPS2 = std::max(HALF_MFMA, READS2);
 
   // One 32-deep K step on ring slot S (step kt of the current piece).
-  // Software pipeline: the MFMAs of the previous stage's second sub-step
-  // (operands already in register set 1) run after the barrier, covering
-  // the latency of this stage's first fragment reads.
-  // LAST: one of the piece's last NSTAGE steps, which issue the next piece's
-  // first stages (all but the first of them).
-  template <int S, bool LAST>
-  __device__ __forceinline__ void step(int kt, f32x16 (&acc)[MI][NI]) {
+  // Software pipeline: phase 1 runs the second half of the previous stage's
+  // MFMAs (operands already in registers) while this stage's first-half A
+  // and all its B are read and the copies of step kt + NSTAGE - 1 are issued;
+  // phase 2 runs this stage's first half while its second-half A is read.
+  template <int S>
+  __device__ __forceinline__ void step(int kt, Acc& acc) {
     TPS_LDS char* cur_slot = ring_slot<S>();
+    // The copy source's scalar work runs while this wave waits for the
+    // others at the barrier, not between the MFMAs.
+    const CopySrc cs = copy_src(kt + NSTAGE - 1);
+    __builtin_amdgcn_sched_barrier(0);
     // Stage kt's copies are complete once only the later NSTAGE-2 stages'
     // copies (NCOPY each) remain outstanding; lgkmcnt(0)
     // retires this wave's reads of the slot that is refilled below.
     waitcnt<(NSTAGE - 2) * NCOPY, 0>();
     __builtin_amdgcn_s_barrier();
-    bool kt_live;
-    const int ka = stage_of(cur, kt, kt_live);   // stage within the tile
-    const bool s1 = SEG2 && ka >= cur.nk0;
-    const int kseg = s1 ? cur.kseg1 : cur.kseg0;
-    const int k0 = (s1 ? ka - cur.nk0 : ka) * BK;
-    if ((A_KC || B_KC) && kt_live && k0 + BK > kseg) {   // K tail of K-contiguous operands
-      if (A_KC) kc_zero_tail(cur_slot, kseg - k0);
-      if (B_KC) kc_zero_tail(cur_slot + TILE_BYTES, kseg - k0);
-      waitcnt<63, 0>();
-      __builtin_amdgcn_s_barrier();
+    if ((A_KC || B_KC) && cur.tail) {   // K tail of K-contiguous operands: zero k past the segment's end
+      bool kt_live;
+      const int ka = stage_of(cur, kt, kt_live);   // stage within the tile
+      const bool s1 = SEG2 && ka >= cur.nk0;
+      const int kseg = s1 ? cur.kseg1 : cur.kseg0;
+      const int k0 = (s1 ? ka - cur.nk0 : ka) * BK;
+      if (kt_live && k0 + BK > kseg) {
+        if (A_KC) kc_zero_tail(cur_slot, kseg - k0);
+        if (B_KC) kc_zero_tail(cur_slot + TILE_BYTES, kseg - k0);
+        waitcnt<63, 0>();
+        __builtin_amdgcn_s_barrier();
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (LAST && S > 0) issue<true>(S - 1, ring_slot<(S + NSTAGE - 1) % NSTAGE>());
-    else issue<false>(kt + NSTAGE - 1, ring_slot<(S + NSTAGE - 1) % NSTAGE>());
-    load(cur_slot, 0);
-    mma(1, acc);              // previous stage, sub-step 1
-    interleave(true);
-    load(cur_slot, 1);
-    mma(0, acc);
-    interleave(false);
+    constexpr int PC = S & 1, PP = (S + 1) & 1;   // this stage's and the previous stage's parity
+    TPS_LDS char* cdst = ring_slot<(S + NSTAGE - 1) % NSTAGE>();
+    phase<PP, 1, PC, 0, BI / 2, true, READS1, true>(acc, cur_slot, cs, cdst,
+                                                   std::make_integer_sequence<int, GROUPS1>{});
+    phase<PC, 0, PC, BI / 2, BI, false, READS2, false>(acc, cur_slot, cs, cdst,
+                                                      std::make_integer_sequence<int, GROUPS2>{});
+  }
+
+  // The last stage's second half, after the loop: written with the compiler
+  // builtin, which the compiler's hazard checks see (outside the loop it may
+  // move accumulators between register files, and a register copy right next
+  // to an asm MFMA would be a hazard it does not know about).
+  template <int P, int H, int... Gs>
+  __device__ __forceinline__ void mma_half(Acc& acc, std::integer_sequence<int, Gs...>) {
+    ((acc[H * (BI / 2) + Gs / BJ][Gs % BJ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          fragB<P>(Gs % BJ), fragA(H * (BI / 2) + Gs / BJ), acc[H * (BI / 2) + Gs / BJ][Gs % BJ], 0, 0, 0)),
+     ...);
   }
 
   // Run the current piece.  The copies of its first NSTAGE-1 stages must
-  // already be issued.  `init` sets the accumulators' starting values.
-  // `next` is called before the last NSTAGE steps and must set nxt (or call
-  // no_next()); those steps issue the next piece's first stages.
-  template <class InitFn, class NextFn>
-  __device__ __forceinline__ void run_tile(f32x16 (&acc)[MI][NI], InitFn&& init, NextFn&& next) {
+  // already be issued, and nxt set (the next piece, or no_next()): the
+  // piece's last NSTAGE-1 steps issue the next piece's first stages.
+  // `init` sets the accumulators' starting values.
+  template <class InitFn>
+  __device__ __forceinline__ void run_tile(Acc& acc, InitFn&& init) {
+    static_assert(NSTAGE % 2 == 0, "the fragment set of a stage is its parity");
     init(acc);
-    zero_set1();              // the first step's deferred sub-step multiplies zeros
-    int kt = 0;
-    for (; kt + NSTAGE < cur.npad; kt += NSTAGE) {
-      step<0, false>(kt, acc);
-      step<1, false>(kt + 1, acc);
-      step<2, false>(kt + 2, acc);
-      step<3, false>(kt + 3, acc);
+    zero_set1();              // the first step's deferred half multiplies zeros
+    // The loop's asm MFMAs read the accumulators as written by ordinary code
+    // (the starting values) and leave them to ordinary code, neither of which
+    // sees them as MFMAs: wait states on both sides of the loop (the hazards
+    // of a register write before an MFMA reads it, and of an MFMA's result
+    // before a register read, last a few passes).
+    asm volatile("s_nop 4" ::: "memory");
+    for (int kt = 0; kt < cur.npad; kt += NSTAGE) {
+      step<0>(kt, acc);
+      step<1>(kt + 1, acc);
+      step<2>(kt + 2, acc);
+      step<3>(kt + 3, acc);
     }
-    next();
-    step<0, true>(kt, acc);
-    step<1, true>(kt + 1, acc);
-    step<2, true>(kt + 2, acc);
-    step<3, true>(kt + 3, acc);
-    mma(1, acc);              // last stage, sub-step 1
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    mma_half<(NSTAGE - 1) & 1, 1>(acc, std::make_integer_sequence<int, HALF_MFMA>{});   // last stage, second half
   }
 
   __device__ __forceinline__ void prologue() {
-    issue<false>(0, ring_slot<0>());
-    issue<false>(1, ring_slot<1>());
-    issue<false>(2, ring_slot<2>());
+    issue(0, ring_slot<0>());
+    issue(1, ring_slot<1>());
+    issue(2, ring_slot<2>());
   }
 };
 
 template <int MI, int NI = 4>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MI][NI]) {
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[2 * MI][2 * NI]) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < 2 * MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NI; ++j) acc[i][j] = f32x16{0.f};
+    for (int j = 0; j < 2 * NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // ---- GEMM epilogue -------------------------------------------------------------------
-// In a 32 x 32 accumulator block a lane holds row (lane % 32) and, for each
-// register quad r4, the four consecutive columns 8*r4 + 4*(lane / 32) .. +3.
-// SwiGLU waves hold gate blocks J = 0,1 and the matching up blocks J + 2.
+// In a 16 x 16 accumulator block a lane holds row (lane % 16) and the four
+// consecutive columns 4 (lane / 16) .. +3.  SwiGLU waves hold gate blocks
+// 0-3 and the matching up blocks 4-7 (same columns).
 //
 // Fast path (whole tile inside the output, 16-byte aligned rows, no bias;
-// the persistent kernel):
-// values are finished in fp32, packed to bf16 pairs, and one
-// v_permlane32_swap per pair of quads hands each lane eight consecutive
-// columns (lanes < 32 keep quads 0/2, lanes >= 32 take quads 1/3), written
-// with one 16-byte store.  No LDS: the ring is already filling with the next
-// tile's stages.
+// the persistent kernel): blocks are finished in pairs (j, j + 1) of
+// adjacent 16-column blocks -- values in fp32, packed to bf16 pairs, then
+// one v_permlane16_swap per packed register trades half of them between the
+// lanes of adjacent 16-lane rows, so that every lane holds eight consecutive
+// columns, written with one 16-byte store.  No LDS: the ring is already
+// filling with the next tile's stages.
 //
 // Generic path (edge tiles, bias, unaligned outputs; one tile per
 // workgroup): see generic_epilogue.
 
-__device__ __forceinline__ void swap_halves(uint32_t (&pk)[8]) {
+// p: the lane's packed block-j values (two registers), q: block j + 1's.
+// v_permlane16_swap swaps the odd 16-lane rows of its first operand with the
+// even rows of its second: afterwards a lane of row 0 or 2 holds {p, q} =
+// block j columns 4g .. 4g+7, a lane of row 1 or 3 block j+1 columns
+// 4(g-1) .. 4g+3 (g = lane / 16).
+__device__ __forceinline__ void swap_pair(uint32_t (&p)[2], uint32_t (&q)[2]) {
 #pragma unroll
-  for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const auto r = __builtin_amdgcn_permlane32_swap(pk[4 * pr + w], pk[4 * pr + 2 + w], false, false);
-      pk[4 * pr + w] = r[0];
-      pk[4 * pr + 2 + w] = r[1];
-    }
+  for (int w = 0; w < 2; ++w) {
+    const auto r = __builtin_amdgcn_permlane16_swap(p[w], q[w], false, false);
+    p[w] = r[0];
+    q[w] = r[1];
+  }
 }
 
-// The lane's two 8-column chunks after swap_halves: columns [0, 8) and
-// [16, 24) from p, each stored only when its flag is set.
-__device__ __forceinline__ void store_pk(uint16_t* p, const uint32_t (&pk)[8], bool lo, bool hi) {
-  if (lo) *reinterpret_cast<u32x4*>(p) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-  if (hi) *reinterpret_cast<u32x4*>(p + 16) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+__device__ __forceinline__ void store_pq(uint16_t* p, const uint32_t (&a)[2], const uint32_t (&b)[2]) {
+  *reinterpret_cast<u32x4*>(p) = u32x4{a[0], a[1], b[0], b[1]};
 }
 
-template <int EPI, int MI, int NI, int I, int J>
-__device__ __forceinline__ void fast_block(const Problem& P, int64_t m0, int64_t n0, const f32x16& a,
-                                           const f32x16& b) {
+// Blocks (I, 2 JP) and (I, 2 JP + 1) of the wave (a, b); for SwiGLU also the
+// up blocks (I, 2 JP + 4), (I, 2 JP + 5) (ua, ub).
+template <int EPI, int MI, int NI, int I, int JP>
+__device__ __forceinline__ void fast_pair(const Problem& P, int64_t m0, int64_t n0, const f32x4& a, const f32x4& b,
+                                          const f32x4& ua, const f32x4& ub) {
   constexpr bool dual = EPI == E_SWIGLU;
-  if (dual && J >= 2) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  const int64_t m = m0 + 32 * MI * wm + 32 * I + (lane & 31);
-  const int64_t nb = n0 + (dual ? 64 * wn + 32 * (J & 1) : 32 * NI * wn + 32 * J);   // the block's first column
-  const int64_t n = nb + 8 * (lane >> 5);
+  const int g = lane >> 4;
+  const int64_t m = m0 + 32 * MI * wm + 16 * I + (lane & 15);
+  const int64_t cj = n0 + (dual ? 64 * wn + 32 * JP : 32 * NI * wn + 32 * JP);   // first column of block 2 JP
+  const int64_t n = cj + 16 * (g & 1) + 4 * (g & 2);                             // this lane's 8 columns
   // A tile may overhang the matrix (rows past M; columns past N when N is a
-  // multiple of 8): the lane's row holds two 8-column chunks, at n and n + 16,
-  // each stored only inside the matrix.  (The test is per tile first, so whole
-  // tiles store without per-lane compares.)
+  // multiple of 8): each lane's 8-column chunk is stored only inside the
+  // matrix.  (The test is per tile first, so whole tiles store without
+  // per-lane compares.)
   const int64_t bw = dual ? BN / 2 : 64 * NI;
-  const bool whole = m0 + 32 * MI * 2 <= P.M && n0 + bw <= P.N;   // wave-uniform
+  const bool whole = m0 + 64 * MI <= P.M && n0 + bw <= P.N;   // wave-uniform
   float ce_l = 0.f, ce_g = 0.f;
   int64_t ce_t = 0;
-  if (EPI == E_CE_GRAD) {   // per-row loss terms; the target column relative to this lane's first column
+  if (EPI == E_CE_GRAD) {   // per-row loss terms; the target column relative to this lane's block-2JP columns
     const int64_t mr = m < P.M ? m : P.M - 1;
     ce_l = P.lse[mr];
     ce_g = P.gscale ? P.gscale[mr] : 1.0f;
-    ce_t = (int64_t)P.target[mr] - P.v0 - (nb + 4 * (lane >> 5));
+    ce_t = (int64_t)P.target[mr] - P.v0 - (cj + 4 * g);
   }
-  uint32_t py[8], pg[8], pu[8];
+  uint32_t py[2], qy[2], pg[2], qg[2], pu[2], qu[2];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const float v0 = a[2 * q], v1 = a[2 * q + 1];
+  for (int h = 0; h < 2; ++h) {   // packed register h: elements 2h, 2h + 1
+    const float a0 = a[2 * h], a1 = a[2 * h + 1], b0 = b[2 * h], b1 = b[2 * h + 1];
     if (EPI == E_STORE) {
-      py[q] = pack_bf2(v0, v1);
+      py[h] = pack_bf2(a0, a1);
+      qy[h] = pack_bf2(b0, b1);
     } else if (EPI == E_CE_GRAD) {
-      // register r = 2 q (+1) holds column 8 (r / 4) + r % 4 past the lane's first column
-      const int c0 = 8 * (q >> 1) + 2 * (q & 1);
-      py[q] = pack_bf2(ce_g * (__expf(v0 - ce_l) - (ce_t == c0 ? 1.0f : 0.0f)),
-                       ce_g * (__expf(v1 - ce_l) - (ce_t == c0 + 1 ? 1.0f : 0.0f)));
+      py[h] = pack_bf2(ce_g * (__expf(a0 - ce_l) - (ce_t == 2 * h ? 1.0f : 0.0f)),
+                       ce_g * (__expf(a1 - ce_l) - (ce_t == 2 * h + 1 ? 1.0f : 0.0f)));
+      qy[h] = pack_bf2(ce_g * (__expf(b0 - ce_l) - (ce_t == 16 + 2 * h ? 1.0f : 0.0f)),
+                       ce_g * (__expf(b1 - ce_l) - (ce_t == 17 + 2 * h ? 1.0f : 0.0f)));
     } else if (EPI == E_GELU) {
-      pg[q] = pack_bf2(v0, v1);
-      py[q] = pack_bf2(gelu_f(v0), gelu_f(v1));
+      pg[h] = pack_bf2(a0, a1);
+      qg[h] = pack_bf2(b0, b1);
+      py[h] = pack_bf2(gelu_f(a0), gelu_f(a1));
+      qy[h] = pack_bf2(gelu_f(b0), gelu_f(b1));
     } else {
-      const float u0 = b[2 * q], u1 = b[2 * q + 1];
-      pg[q] = pack_bf2(v0, v1);
-      pu[q] = pack_bf2(u0, u1);
-      py[q] = pack_bf2(silu_f(v0) * u0, silu_f(v1) * u1);
+      const float u0 = ua[2 * h], u1 = ua[2 * h + 1], v0 = ub[2 * h], v1 = ub[2 * h + 1];
+      pg[h] = pack_bf2(a0, a1);
+      qg[h] = pack_bf2(b0, b1);
+      pu[h] = pack_bf2(u0, u1);
+      qu[h] = pack_bf2(v0, v1);
+      py[h] = pack_bf2(silu_f(a0) * u0, silu_f(a1) * u1);
+      qy[h] = pack_bf2(silu_f(b0) * v0, silu_f(b1) * v1);
     }
   }
-  swap_halves(py);
-  if (EPI == E_GELU || EPI == E_SWIGLU) swap_halves(pg);
-  if (dual) swap_halves(pu);
-  uint16_t* c = static_cast<uint16_t*>(P.c) + m * P.ldc + n;
-  uint16_t* pre = (EPI == E_GELU || EPI == E_SWIGLU) ? static_cast<uint16_t*>(P.pre) + m * P.ldpre + n : nullptr;
-  auto stores = [&](bool lo, bool hi) {
-    store_pk(c, py, lo, hi);
-    if (EPI == E_GELU || EPI == E_SWIGLU) store_pk(pre, pg, lo, hi);
-    if (dual) store_pk(pre + P.N, pu, lo, hi);
-  };
-  if (whole) stores(true, true);
-  else stores(m < P.M && n < P.N, m < P.M && n + 16 < P.N);
+  swap_pair(py, qy);
+  if (EPI == E_GELU || EPI == E_SWIGLU) swap_pair(pg, qg);
+  if (dual) swap_pair(pu, qu);
+  if (whole || (m < P.M && n < P.N)) {
+    store_pq(static_cast<uint16_t*>(P.c) + m * P.ldc + n, py, qy);
+    if (EPI == E_GELU || EPI == E_SWIGLU) store_pq(static_cast<uint16_t*>(P.pre) + m * P.ldpre + n, pg, qg);
+    if (dual) store_pq(static_cast<uint16_t*>(P.pre) + m * P.ldpre + P.N + n, pu, qu);
+  }
 }
 
 template <int EPI, int MI, int NI, int... Is>
-__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[MI][NI],
-                                              std::integer_sequence<int, Is...>) {
-  // SwiGLU (NI = 4): block J's up values are block J ^ 2.
-  ((fast_block<EPI, MI, NI, Is / NI, Is % NI>(P, m0, n0, acc[Is / NI][Is % NI],
-                                              acc[Is / NI][EPI == E_SWIGLU ? (Is % NI) ^ 2 : Is % NI]),
+__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0,
+                                              f32x4 (&acc)[2 * MI][2 * NI], std::integer_sequence<int, Is...>) {
+  constexpr int NP = EPI == E_SWIGLU ? 2 : NI;   // block pairs per block row
+  constexpr int UP = EPI == E_SWIGLU ? 4 : 0;    // SwiGLU: block j's up values are block j + 4
+  ((fast_pair<EPI, MI, NI, Is / NP, Is % NP>(P, m0, n0, acc[Is / NP][2 * (Is % NP)], acc[Is / NP][2 * (Is % NP) + 1],
+                                             acc[Is / NP][2 * (Is % NP) + UP], acc[Is / NP][2 * (Is % NP) + 1 + UP]),
     __builtin_amdgcn_sched_barrier(0)),
    ...);
 }
 
 // Generic path: the ring is drained, and each wave stages 32-row slices of
-// its 32 x 128 accumulator rows in its own ring slot, then finishes eight
-// columns at a time with every bound checked.
+// its 128 x 128 accumulator (two block rows) in its own ring slot, then
+// finishes eight columns at a time with every bound checked.
 constexpr int EPI_LD = 132;                       // floats per staged row (128 + 4 padding)
 
-__device__ __forceinline__ void stage_block(TPS_LDS float* w, const f32x16& a, int j) {
+template <int SL>
+__device__ __forceinline__ void stage_slice(TPS_LDS float* w, const f32x4 (&acc)[8][8]) {
   const int lane = threadIdx.x & 63;
-  TPS_LDS float* p = w + (lane & 31) * EPI_LD + 32 * j + 4 * (lane >> 5);
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4)
-    *reinterpret_cast<TPS_LDS f32x4*>(p + 8 * r4) = f32x4{a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<TPS_LDS f32x4*>(w + (16 * rb + (lane & 15)) * EPI_LD + 16 * j + 4 * (lane >> 4)) =
+          acc[2 * SL + rb][j];
 }
 
 __device__ __forceinline__ void store8_bf16(uint16_t* p, const float (&v)[8], int nv) {
@@ -773,17 +883,17 @@ __device__ __forceinline__ void store_slice(const Problem& P, const TPS_LDS floa
 
 // The ring must be drained (no copies in flight) and every wave past its
 // last fragment read.
-__device__ __forceinline__ void generic_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void generic_epilogue(const Problem& P, int64_t m0, int64_t n0, f32x4 (&acc)[8][8]) {
   const int wave = threadIdx.x >> 6;   // wave w stages in ring slot w (16.5 KiB of 32 KiB)
   TPS_LDS float* w = reinterpret_cast<TPS_LDS float*>(
       wave < 2 ? (wave == 0 ? ring_slot<0>() : ring_slot<1>()) : (wave == 2 ? ring_slot<2>() : ring_slot<3>()));
 #pragma unroll 1
   for (int i = 0; i < 4; ++i) {
     switch (i) {   // constant indices into acc keep it in registers
-      case 0: for (int j = 0; j < 4; ++j) stage_block(w, acc[0][j], j); break;
-      case 1: for (int j = 0; j < 4; ++j) stage_block(w, acc[1][j], j); break;
-      case 2: for (int j = 0; j < 4; ++j) stage_block(w, acc[2][j], j); break;
-      default: for (int j = 0; j < 4; ++j) stage_block(w, acc[3][j], j); break;
+      case 0: stage_slice<0>(w, acc); break;
+      case 1: stage_slice<1>(w, acc); break;
+      case 2: stage_slice<2>(w, acc); break;
+      default: stage_slice<3>(w, acc); break;
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staging writes are done
     store_slice(P, w, m0, n0, i);
@@ -863,8 +973,10 @@ __device__ __forceinline__ void locate_mi(const GemmLaunch& L, int tile, int epi
 // The fused store epilogues of the GEMM kernels (the default of tile_loop).
 template <int EPI, int MI, int NI>
 struct StoreEpilogue {
-  __device__ __forceinline__ void operator()(const Problem& P, int64_t m0, int64_t n0, f32x16 (&acc)[MI][NI]) const {
-    fast_epilogue<EPI, MI, NI>(P, m0, n0, acc, std::make_integer_sequence<int, MI * NI>{});
+  __device__ __forceinline__ void operator()(const Problem& P, int64_t m0, int64_t n0,
+                                            f32x4 (&acc)[2 * MI][2 * NI]) const {
+    fast_epilogue<EPI, MI, NI>(P, m0, n0, acc,
+                               std::make_integer_sequence<int, 2 * MI * (EPI == E_SWIGLU ? 2 : NI)>{});
   }
 };
 
@@ -895,17 +1007,16 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
   pipe.prologue();
   for (;;) {
     const bool more = tile + stride < tb;
-    f32x16 acc[MI][NI];
-    pipe.run_tile(acc, zero_acc<MI, NI>, [&]() {
-      if (more) {
-        Problem Pn;
-        int64_t m0n, n0n;
-        locate_mi<MI, NI>(L, tile + stride, EPI, Pn, m0n, n0n);
-        pipe.nxt = pipe.make_streams(Pn, m0n, n0n, 0, INT_MAX, xcd);
-      } else {
-        pipe.no_next();
-      }
-    });
+    if (more) {
+      Problem Pn;
+      int64_t m0n, n0n;
+      locate_mi<MI, NI>(L, tile + stride, EPI, Pn, m0n, n0n);
+      pipe.nxt = pipe.make_streams(Pn, m0n, n0n, 0, INT_MAX, xcd);
+    } else {
+      pipe.no_next();
+    }
+    f32x4 acc[2 * MI][2 * NI];
+    pipe.run_tile(acc, zero_acc<MI, NI>);
     {
       Problem P;
       int64_t m0, n0;
@@ -986,85 +1097,84 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmL
   Problem P;
   int64_t m0, n0;
   locate<true>(L, id, EPI, P, m0, n0);
-  f32x16 acc[4][4];
+  f32x4 acc[8][8];
   Pipe<LAYOUT, DUAL, SEG2> pipe;
   pipe.init_wave();
   pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
   pipe.prologue();
-  pipe.run_tile(acc, zero_acc<4>, [&]() { pipe.no_next(); });
+  pipe.no_next();
+  pipe.run_tile(acc, zero_acc<4>);
   waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
   __syncthreads();
   generic_epilogue(P, m0, n0, acc);
 }
 
-// Row statistics of one 32-row slice (I) of a wave's (32 MI) x 128 logit
-// block: max and sum exp(z - max) over the valid columns, the target logit if
-// this lane holds it, and the per-wave results in LDS for the cross-wave merge.
+// Row statistics of one 16-row block (I) of a wave's (32 MI) x 128 logit
+// block: max and sum exp(z - max) over the valid columns (a lane holds 32 of
+// its row's columns, 16 j + 4 (lane / 16) + e; the four 16-lane rows of the
+// wave hold the rest), the target logit if this lane holds it, and the
+// per-wave results in LDS for the cross-wave merge.
 template <int I, int MI>
-__device__ __forceinline__ void ce_rows(const CEArgs& a, f32x16 (&acc)[MI][4], int64_t m0, int64_t wcol,
+__device__ __forceinline__ void ce_rows(const CEArgs& a, f32x4 (&acc)[2 * MI][8], int64_t m0, int64_t wcol,
                                         int nvalid, float* ws_tgt, TPS_LDS float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5;
-  const int rl = 32 * MI * wm + 32 * I + (lane & 31);
+  const int g = lane >> 4;
+  const int rl = 32 * MI * wm + 16 * I + (lane & 15);
   const int64_t m = m0 + rl;
-  const int lim = nvalid - 4 * h;     // column c = 32j + 8(r/4) + (r%4) of this lane is valid iff c < lim
+  const int lim = nvalid - 4 * g;     // column 16 j + 4 g + e of this lane is valid iff 16 j + e < lim
   float mx = -INFINITY;
   if (nvalid >= 128) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[I][j][r]);
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, acc[I][j][e]);
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 32 * j + 8 * (r >> 2) + (r & 3);
-        mx = fmaxf(mx, c < lim ? acc[I][j][r] : -INFINITY);
-      }
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, 16 * j + e < lim ? acc[I][j][e] : -INFINITY);
   }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   float s = 0.f;
   if (nvalid >= 128) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s += __expf(acc[I][j][r] - mx);
+      for (int e = 0; e < 4; ++e) s += __expf(acc[I][j][e] - mx);
   } else if (mx > -INFINITY) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 32 * j + 8 * (r >> 2) + (r & 3);
-        s += c < lim ? __expf(acc[I][j][r] - mx) : 0.f;
-      }
+      for (int e = 0; e < 4; ++e) s += 16 * j + e < lim ? __expf(acc[I][j][e] - mx) : 0.f;
   }
+  s += __shfl_xor(s, 16);
   s += __shfl_xor(s, 32);
   if (m < a.M) {
     const int64_t d64 = (int64_t)a.target[m] - a.v0 - wcol;   // target column relative to the wave
     if (d64 >= 0 && d64 < nvalid) {
-      const int dd = (int)d64 - 4 * h;
+      const int dd = (int)d64 - 4 * g;
       float tv = 0.f;
       bool mine = false;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool hit = (32 * j + 8 * (r >> 2) + (r & 3)) == dd;
-          tv = hit ? acc[I][j][r] : tv;
+        for (int e = 0; e < 4; ++e) {
+          const bool hit = 16 * j + e == dd;
+          tv = hit ? acc[I][j][e] : tv;
           mine = mine || hit;
         }
       if (mine) ws_tgt[m] = tv;
     }
   }
-  if (h == 0) {
+  if (g == 0) {
     red[(wn * 256 + rl) * 2 + 0] = mx;
     red[(wn * 256 + rl) * 2 + 1] = s;
   }
 }
 
 template <int MI, int... Is>
-__device__ __forceinline__ void ce_rows_seq(const CEArgs& a, f32x16 (&acc)[MI][4], int64_t m0, int64_t wcol,
+__device__ __forceinline__ void ce_rows_seq(const CEArgs& a, f32x4 (&acc)[2 * MI][8], int64_t m0, int64_t wcol,
                                             int nvalid, float* ws_tgt, TPS_LDS float* red,
                                             std::integer_sequence<int, Is...>) {
   (ce_rows<Is, MI>(a, acc, m0, wcol, nvalid, ws_tgt, red), ...);
@@ -1092,7 +1202,7 @@ template <int MI>
 struct CeEpilogue {
   CEArgs a;
   int tiles_n;
-  __device__ __forceinline__ void operator()(const Problem&, int64_t m0, int64_t n0, f32x16 (&acc)[MI][4]) const {
+  __device__ __forceinline__ void operator()(const Problem&, int64_t m0, int64_t n0, f32x4 (&acc)[2 * MI][8]) const {
     const int wn = (threadIdx.x >> 6) & 1;
     const int64_t wcol = n0 + 128 * wn;                 // first column of this wave
     // number of valid columns of this wave, in [0, 128]
@@ -1100,7 +1210,7 @@ struct CeEpilogue {
     float* ws_ms = a.ws;
     float* ws_tgt = a.ws + 2 * (int64_t)tiles_n * a.M;
     TPS_LDS float* red = (TPS_LDS float*)ce_red;
-    ce_rows_seq<MI>(a, acc, m0, wcol, nvalid, ws_tgt, red, std::make_integer_sequence<int, MI>{});
+    ce_rows_seq<MI>(a, acc, m0, wcol, nvalid, ws_tgt, red, std::make_integer_sequence<int, 2 * MI>{});
     lds_barrier();
     const int rl = threadIdx.x;
     const int64_t m = m0 + rl;
@@ -1392,7 +1502,6 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   }
   GemmLaunch F = L, E = L;   // fast-kernel tiles, remaining tiles (generic kernel)
   int nf = 0, ne = 0;
-  int64_t W = 0;
   for (int i = 0; i < L.nprob; ++i) {
     const Problem& P = L.p[i];
     const int64_t bn = (P.epi == E_SWIGLU) ? BN / 2 : BN;

@@ -36,6 +36,26 @@ def test_exports_match_header(lib):
         assert hasattr(lib, name)
 
 
+def test_calibration_library_exports_its_header():
+    # libtpcalib (the MFMA-only calibration kernel) is a measurement helper with
+    # its own header; it loads and exports exactly what include/tpcalib.h declares.
+    import ctypes
+    from tensor_transformer_linear_tp_amd import build
+    if not os.path.exists(build.CALIB_PATH):
+        build.build()
+    src = open(os.path.join(ROOT, "include", "tpcalib.h")).read()
+    declared = sorted(set(re.findall(r"^TPC_API\s+[\w\s\*]+?\b(tpc_\w+)\s*\(", src, flags=re.M)))
+    out = subprocess.run(["nm", "-D", "--defined-only", build.CALIB_PATH], capture_output=True, text=True, check=True)
+    exported = sorted(l.split()[-1] for l in out.stdout.splitlines() if " T " in l)
+    assert declared == exported == ["tpc_mfma_loop"]
+    lib = ctypes.CDLL(build.CALIB_PATH)
+    lib.tpc_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    assert lib.tpc_mfma_loop(None, None, 256, 10, 32, None) == -1      # validation only, nothing launched
+    assert lib.tpc_mfma_loop(P, P, 256, 0, 32, None) == -1
+    assert lib.tpc_mfma_loop(P, P, 256, 10, 8, None) == -1
+
+
 def test_version_and_status_strings(lib):
     assert tp.tp_abi_version() == 1
     seen = set()
