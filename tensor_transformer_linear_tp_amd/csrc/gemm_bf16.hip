@@ -67,7 +67,7 @@ __device__ __forceinline__ int mn_off(int k, int c) { return k * ROWB + ((c ^ mn
 // lies inside the extent and is zeroed in LDS afterwards (kc_zero_tail).
 constexpr int DMA_PER_OPERAND = 4;            // copy instructions per wave per operand stage
 
-// Copy stream of one operand of one K segment of one piece: the address of
+// Copy stream of one operand of one K segment of one tile: the address of
 // the tile's origin, the bytes from there to the end of the operand's extent
 // (operands are below 2 GiB, so 32 bits hold every offset), the bytes per K
 // stage, and this wave's per-lane byte offsets of its blocks (block j of the
@@ -131,33 +131,6 @@ __device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t
     s.voff[j] = (VALID < CHUNKS && c >= VALID) ? kDeadLane : (uint32_t)((k * ld + 8 * c) * 2);
   }
   return s;
-}
-
-// Issue the copies of K stage `stage` of one operand (this wave's
-// DMA_PER_OPERAND blocks; `wtile` is this wave's first block in the LDS
-// tile).  The descriptor stays at the tile's origin with the operand's
-// remaining extent as its range; the stage offset goes into each lane's
-// voffset, which the range check covers, so whatever lies past the extent
-// (rows beyond M, N or K, the last row's K tail) reads as zero.  live ==
-// false: every lane is sent past the range, so the stage is all zeros.
-// (Operands below 2 GiB keep voffset + offset inside 32 bits.)
-template <int NB = DMA_PER_OPERAND>
-__device__ __forceinline__ void stream_issue(const OpStream& st, int stage, bool live, TPS_LDS char* wtile) {
-  const uint32_t off = live ? (uint32_t)stage * st.step : st.nrec;
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(st.base), (short)0, (int)st.nrec, 0x00020000);
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(wtile + 1024 * j), 16, st.voff[j] + off, 0, 0, 0);
-}
-
-// One of those copies: block J of this wave's blocks of the stage.
-template <int J>
-__device__ __forceinline__ void stream_issue1(const OpStream& st, int stage, bool live, TPS_LDS char* wtile) {
-  const uint32_t off = live ? (uint32_t)stage * st.step : st.nrec;
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(st.base), (short)0, (int)st.nrec, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TPS_LDS void*)(wtile + 1024 * J), 16, st.voff[J] + off, 0, 0, 0);
 }
 
 // One 16-byte-per-lane copy into LDS at `ldst` (lane order) from `base` +
@@ -247,16 +220,15 @@ __device__ __forceinline__ TPS_LDS char* ring_slot() {
 // first stages, so the next tile starts with a full ring and the current
 // tile's epilogue (which does not touch LDS) overlaps those copies.
 
-// Copy streams of one piece of a tile (a range of its K stages): per K
-// segment (0, 1), one stream per operand.  Plain named members (no arrays of
-// structs) keep all of it in registers.
+// Copy streams of one tile: per K segment (0, 1), one stream per operand.
+// Plain named members (no arrays of structs) keep all of it in registers.
 struct TileStreams {
   OpStream a0, a1, b0, b1;
   int kseg0, kseg1;        // K of each segment
   int nk0;                 // stages of segment 0
-  int s0, send;            // the piece: stages [s0, send) of the tile
-  int rot;                 // the piece runs from stage s0 + rot, wrapping around to s0
-  int npad;                // send - s0 rounded up to NSTAGE
+  int nk;                  // stages of the tile (0: no tile)
+  int rot;                 // the K loop starts at stage rot, wrapping around to 0
+  int npad;                // nk rounded up to NSTAGE
   int tail;                // a K-contiguous operand's segment ends inside a stage (K % 32 != 0)
 };
 
@@ -279,7 +251,7 @@ struct Pipe {
 
   int wave, wm, wn;
   int wlds_a, wlds_b;     // this wave's first copy block in the A / B tile (bytes)
-  TileStreams cur, nxt;   // nxt.send == 0: no next piece (its copies are empty)
+  TileStreams cur, nxt;   // nxt.nk == 0: no next tile (its copies are empty)
 
   __device__ __forceinline__ void init_wave() {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -311,10 +283,8 @@ struct Pipe {
     }
   }
 
-  // Streams of stages [s0, min(s1, stages of the tile)) of the tile at (m0, n0),
-  // started rot8/8 of the way into the range.
-  __device__ __forceinline__ TileStreams make_streams(const Problem& P, int64_t m0, int64_t n0, int s0, int s1,
-                                                      int rot8 = 0) const {
+  // Streams of the tile at (m0, n0), its K loop started rot8/8 of the way in.
+  __device__ __forceinline__ TileStreams make_streams(const Problem& P, int64_t m0, int64_t n0, int rot8 = 0) const {
     TileStreams T;
     seg_streams(P, m0, n0, false, T.a0, T.b0, T.kseg0);
     if (SEG2) {
@@ -325,11 +295,9 @@ struct Pipe {
       T.kseg1 = T.kseg0;
     }
     T.nk0 = (int)((T.kseg0 + BK - 1) / BK);
-    const int nk = T.nk0 + (SEG2 ? (int)((T.kseg1 + BK - 1) / BK) : 0);
-    T.s0 = s0;
-    T.send = min(s1, nk);
-    T.rot = ((T.send - s0) * rot8) >> 3;
-    T.npad = (T.send - s0 + NSTAGE - 1) / NSTAGE * NSTAGE;
+    T.nk = T.nk0 + (SEG2 ? (int)((T.kseg1 + BK - 1) / BK) : 0);
+    T.rot = (T.nk * rot8) >> 3;
+    T.npad = (T.nk + NSTAGE - 1) / NSTAGE * NSTAGE;
     T.tail = (A_KC || B_KC) && ((T.kseg0 % BK) != 0 || (SEG2 && (T.kseg1 % BK) != 0));
     uniform(T);
     return T;
@@ -337,7 +305,7 @@ struct Pipe {
 
   // The stream records are wave-uniform, but parts of them are computed on
   // the vector ALU (integer division has no scalar form); readfirstlane moves
-  // them to scalar registers once per piece, so the per-stage descriptor
+  // them to scalar registers once per tile, so the per-stage descriptor
   // arithmetic is scalar.
   static __device__ __forceinline__ uint32_t sgpr(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
   static __device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -357,8 +325,7 @@ struct Pipe {
     T.kseg0 = sgpr(T.kseg0);
     T.kseg1 = sgpr(T.kseg1);
     T.nk0 = sgpr(T.nk0);
-    T.s0 = sgpr(T.s0);
-    T.send = sgpr(T.send);
+    T.nk = sgpr(T.nk);
     T.rot = sgpr(T.rot);
     T.npad = sgpr(T.npad);
     T.tail = sgpr(T.tail);
@@ -366,63 +333,132 @@ struct Pipe {
 
   __device__ __forceinline__ void no_next() {
     nxt = cur;
-    nxt.s0 = 0;
-    nxt.send = 0;
+    nxt.nk = 0;
     nxt.rot = 0;
     nxt.npad = 0;
   }
 
-  // Tile stage of step r of a piece; live == false past the piece's end.
+  // Tile stage of step r; live == false past the tile's last stage.
   static __device__ __forceinline__ int stage_of(const TileStreams& T, int r, bool& live) {
-    const int cnt = T.send - T.s0;
     int t = r + T.rot;
-    t = t >= cnt ? t - cnt : t;
-    live = r < cnt;
-    return T.s0 + t;
+    t = t >= T.nk ? t - T.nk : t;
+    live = r < T.nk;
+    return t;
   }
 
-  // The copy source of step r: the current piece's step r or, past its end,
-  // the next piece's step r - npad (the next tile's first stages load during
-  // this tile's last steps and its epilogue).  Selected field-wise at run
-  // time -- scalars once per step, one vector select per copy -- so that the
-  // K loop is one uniform body (a separate block for the last steps made the
-  // register allocator move accumulators around it).
+  // The copy source of step r: the current tile's step r or, past its
+  // padded end, the next tile's step r - npad (the next tile's first stages
+  // load during this tile's last steps and its epilogue).  Selected
+  // field-wise at run time -- scalars once per step, one vector select per
+  // copy -- so that the K loop is one uniform body (a separate block for the
+  // last steps made the register allocator move accumulators around it).
   struct CopySrc {
     const char* basea;      // the stage's first byte of each operand (the tile origin + the stage offset)
     const char* baseb;
-    uint32_t nreca, nrecb;  // bytes from there to the operand's end; 0 past the piece's end (zeros)
-    bool nx, s1;
+    uint32_t nreca, nrecb;  // bytes from there to the operand's end; 0 past the tile's end (zeros)
+    int nx, s1;             // masks (-1 / 0): the next tile's streams, the second K segment's
   };
   template <class F>
-  __device__ __forceinline__ static auto pick4(bool nx, bool s1, F c0, F c1, F n0, F n1) {
-    return nx ? (s1 ? n1 : n0) : (s1 ? c1 : c0);
+  __device__ __forceinline__ static auto pick4(int nx, int s1, F c0, F c1, F n0, F n1) {
+    if constexpr (SEG2) return nx ? (s1 ? n1 : n0) : (s1 ? c1 : c0);
+    else return nx ? n0 : c0;
+  }
+  // Its computation in NCALC small steps of a few scalar instructions each,
+  // so that the K loop can spread the next step's over as many MFMAs (one
+  // wave per SIMD issues about one instruction per 4 cycles, so only a few
+  // fit in the shadow of each MFMA; a run of a few dozen stalls them).  Each
+  // step ends with an empty asm statement that takes its results and the
+  // next-tile mask as read-write operands.  The compiler keeps those
+  // statements in order with the loop's MFMA statements, and a step's
+  // arithmetic depends on the previous statement's mask and feeds its own,
+  // so it stays between the two (left alone, the compiler gathers all
+  // selects on one condition into one run).  Flags are sign-splat masks,
+  // x >> sh with sh = 31 held in a register: with a literal 31 the compiler
+  // turns the shift back into a compare, whose integer value it forms on
+  // the vector unit.
+  struct CopyCalc {
+    int sh;                     // 31
+    int rr, cnt, t, live;       // live: -1 for a stage inside the tile, else 0
+    uint32_t stage, oa, ob;
+    CopySrc c;
+  };
+  static constexpr int NCALC = 12;
+  // (readfirstlane: where the compiler has kept a uniform value in a vector
+  // register, one instruction moves it to a scalar one; elsewhere it folds.)
+  static __device__ __forceinline__ int sg(int x) { return __builtin_amdgcn_readfirstlane(x); }
+  static __device__ __forceinline__ uint32_t sg(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+  static __device__ __forceinline__ const char* sg(const char* x) { return x; }
+  template <class T>
+  static __device__ __forceinline__ void pin(T& x, int& nx) {
+    x = sg(x);
+    nx = sg(nx);
+    asm volatile("" : "+s"(x), "+s"(nx));
+  }
+  __device__ __forceinline__ void calc_init(CopyCalc& w) const {
+    w.sh = 31;
+    w.c.nx = 0;
+    pin(w.sh, w.c.nx);
+  }
+  template <int I>
+  __device__ __forceinline__ void calc(CopyCalc& w, int r) const {
+    CopySrc& c = w.c;
+    if constexpr (I == 0) {
+      c.nx = ~((r - cur.npad) >> w.sh);   // r >= npad
+      w.rr = r;
+      pin(w.rr, c.nx);
+    } else if constexpr (I == 1) {
+      w.rr -= cur.npad & c.nx;
+      pin(w.rr, c.nx);
+    } else if constexpr (I == 2) {
+      w.cnt = c.nx ? nxt.nk : cur.nk;
+      pin(w.cnt, c.nx);
+    } else if constexpr (I == 3) {
+      w.t = w.rr + (c.nx ? nxt.rot : cur.rot);
+      pin(w.t, c.nx);
+    } else if constexpr (I == 4) {
+      w.live = (w.rr - w.cnt) >> w.sh;   // rr < cnt
+      pin(w.live, c.nx);
+    } else if constexpr (I == 5) {
+      const int st = w.t - (w.cnt & ~((w.t - w.cnt) >> w.sh));   // t >= cnt: wrap
+      if constexpr (SEG2) {
+        const int nk0 = c.nx ? nxt.nk0 : cur.nk0;
+        c.s1 = ~((st - nk0) >> w.sh);   // st >= nk0
+        w.stage = (uint32_t)(st - (nk0 & c.s1));
+        pin(c.s1, c.nx);
+      } else {
+        c.s1 = 0;
+        w.stage = (uint32_t)st;
+      }
+      pin(w.stage, c.nx);
+    } else if constexpr (I == 6) {
+      w.oa = w.stage * pick4(c.nx, c.s1, cur.a0.step, cur.a1.step, nxt.a0.step, nxt.a1.step);
+      pin(w.oa, c.nx);
+    } else if constexpr (I == 7) {
+      c.basea = pick4(c.nx, c.s1, cur.a0.base, cur.a1.base, nxt.a0.base, nxt.a1.base) + w.oa;
+      pin(c.basea, c.nx);
+    } else if constexpr (I == 8) {   // a stage past the tile's end reads past the range: zeros
+      c.nreca = (pick4(c.nx, c.s1, cur.a0.nrec, cur.a1.nrec, nxt.a0.nrec, nxt.a1.nrec) - w.oa) & (uint32_t)w.live;
+      pin(c.nreca, c.nx);
+    } else if constexpr (I == 9) {
+      w.ob = w.stage * pick4(c.nx, c.s1, cur.b0.step, cur.b1.step, nxt.b0.step, nxt.b1.step);
+      pin(w.ob, c.nx);
+    } else if constexpr (I == 10) {
+      c.baseb = pick4(c.nx, c.s1, cur.b0.base, cur.b1.base, nxt.b0.base, nxt.b1.base) + w.ob;
+      pin(c.baseb, c.nx);
+    } else if constexpr (I == 11) {
+      c.nrecb = (pick4(c.nx, c.s1, cur.b0.nrec, cur.b1.nrec, nxt.b0.nrec, nxt.b1.nrec) - w.ob) & (uint32_t)w.live;
+      pin(c.nrecb, c.nx);
+    }
+  }
+  template <int... Is>
+  __device__ __forceinline__ void calc_all(CopyCalc& w, int r, std::integer_sequence<int, Is...>) const {
+    (calc<Is>(w, r), ...);
   }
   __device__ __forceinline__ CopySrc copy_src(int r) const {
-    CopySrc c;
-    c.nx = r >= cur.npad;
-    const int rr = c.nx ? r - cur.npad : r;
-    const int s0 = c.nx ? nxt.s0 : cur.s0, send = c.nx ? nxt.send : cur.send;
-    const int rot = c.nx ? nxt.rot : cur.rot, nk0 = c.nx ? nxt.nk0 : cur.nk0;
-    const int cnt = send - s0;
-    int t = rr + rot;
-    t = t >= cnt ? t - cnt : t;
-    const bool live = rr < cnt;
-    const int st = s0 + t;
-    c.s1 = SEG2 && st >= nk0;
-    const uint32_t stage = (uint32_t)(c.s1 ? st - nk0 : st);
-    const bool x = c.nx, y = c.s1;
-    const char* ab = pick4(x, y, cur.a0.base, cur.a1.base, nxt.a0.base, nxt.a1.base);
-    const uint32_t anr = pick4(x, y, cur.a0.nrec, cur.a1.nrec, nxt.a0.nrec, nxt.a1.nrec);
-    const uint32_t ast = pick4(x, y, cur.a0.step, cur.a1.step, nxt.a0.step, nxt.a1.step);
-    const char* bb = pick4(x, y, cur.b0.base, cur.b1.base, nxt.b0.base, nxt.b1.base);
-    const uint32_t bnr = pick4(x, y, cur.b0.nrec, cur.b1.nrec, nxt.b0.nrec, nxt.b1.nrec);
-    const uint32_t bst = pick4(x, y, cur.b0.step, cur.b1.step, nxt.b0.step, nxt.b1.step);
-    const uint32_t oa = stage * ast, ob = stage * bst;
-    c.basea = ab + oa;
-    c.baseb = bb + ob;
-    c.nreca = live ? anr - oa : 0u;   // a stage past the piece's end reads past the range: zeros
-    c.nrecb = live ? bnr - ob : 0u;
-    return c;
+    CopyCalc w;
+    calc_init(w);
+    calc_all(w, r, std::make_integer_sequence<int, NCALC>{});
+    return w.c;
   }
 
   // Copy C of a step into `dst`: copies [0, NBA) are A's blocks, [NBA, NCOPY)
@@ -567,42 +603,48 @@ struct Pipe {
   // with copies, copy G/2 after every second MFMA; fenced so the scheduler
   // keeps this order.
   static constexpr int HALF_MFMA = (BI / 2) * BJ;
+  // COPIES: phase 1 issues the copies described by w.c; otherwise (phase 2)
+  // groups [CALC_AT, CALC_AT + NCALC) compute the next step's copy source
+  // into w, one small step each.  Phase 1's fences let scalar instructions
+  // through (the copies' M0 set-up); phase 2's let nothing through, so that
+  // the scheduler cannot gather the copy-source steps into one run.
+  static constexpr int READS2 = (BI - BI / 2) * RA_PER;
+  static constexpr int CALC_AT = READS2;
   template <int PM, int H, int PR, int I0, int I1, bool WITH_B, int NREAD, bool COPIES, int G>
-  __device__ __forceinline__ void group(Acc& acc, const TPS_LDS char* rbase, const CopySrc& cs, TPS_LDS char* cdst) {
+  __device__ __forceinline__ void group(Acc& acc, const TPS_LDS char* rbase, CopyCalc& w, TPS_LDS char* cdst,
+                                        int rnext) {
     if constexpr (G < HALF_MFMA) mma1<PM, H * (BI / 2) + G / BJ, G % BJ>(acc);
     if constexpr (G < NREAD) read_op<PR, I0, I1, WITH_B, G>(rbase);
-    if constexpr (COPIES && G % COPY_EVERY == 0 && G / COPY_EVERY < NCOPY) issue1<G / COPY_EVERY>(cs, cdst);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (COPIES && G % COPY_EVERY == 0 && G / COPY_EVERY < NCOPY) issue1<G / COPY_EVERY>(w.c, cdst);
+    if constexpr (!COPIES && G >= CALC_AT && G < CALC_AT + NCALC) calc<G - CALC_AT>(w, rnext);
+    __builtin_amdgcn_sched_barrier(COPIES ? 0x0004 : 0);
   }
   template <int PM, int H, int PR, int I0, int I1, bool WITH_B, int NREAD, bool COPIES, int... Gs>
-  __device__ __forceinline__ void phase(Acc& acc, const TPS_LDS char* rbase, const CopySrc& cs, TPS_LDS char* cdst,
-                                        std::integer_sequence<int, Gs...>) {
-    (group<PM, H, PR, I0, I1, WITH_B, NREAD, COPIES, Gs>(acc, rbase, cs, cdst), ...);
+  __device__ __forceinline__ void phase(Acc& acc, const TPS_LDS char* rbase, CopyCalc& w, TPS_LDS char* cdst,
+                                        int rnext, std::integer_sequence<int, Gs...>) {
+    (group<PM, H, PR, I0, I1, WITH_B, NREAD, COPIES, Gs>(acc, rbase, w, cdst, rnext), ...);
   }
   static constexpr int READS1 = (BI / 2) * RA_PER + BJ * RB_PER;
-  static constexpr int READS2 = (BI - BI / 2) * RA_PER;
   static constexpr int COPY_EVERY = HALF_MFMA >= 4 * NCOPY ? 4 : 2;   // MFMAs per copy in phase 1
   static constexpr int GROUPS1 = std::max(std::max(HALF_MFMA, READS1), COPY_EVERY * NCOPY);
-  static constexpr int GROUPS2 = std::max(HALF_MFMA, READS2);
+  static constexpr int GROUPS2 = std::max(HALF_MFMA, CALC_AT + NCALC);
 
-  // One 32-deep K step on ring slot S (step kt of the current piece).
+  // One 32-deep K step on ring slot S (step kt of the current tile).
   // Software pipeline: phase 1 runs the second half of the previous stage's
   // MFMAs (operands already in registers) while this stage's first-half A
   // and all its B are read and the copies of step kt + NSTAGE - 1 are issued;
   // phase 2 runs this stage's first half while its second-half A is read.
-  template <int S>
-  __device__ __forceinline__ void step(int kt, Acc& acc) {
+  // w.c: the copy source of this step (step kt + NSTAGE - 1 of the tile),
+  // replaced during phase 2 by the next step's.
+  template <int S, bool TAIL>
+  __device__ __forceinline__ void step(int kt, Acc& acc, CopyCalc& w) {
     TPS_LDS char* cur_slot = ring_slot<S>();
-    // The copy source's scalar work runs while this wave waits for the
-    // others at the barrier, not between the MFMAs.
-    const CopySrc cs = copy_src(kt + NSTAGE - 1);
-    __builtin_amdgcn_sched_barrier(0);
     // Stage kt's copies are complete once only the later NSTAGE-2 stages'
     // copies (NCOPY each) remain outstanding; lgkmcnt(0)
     // retires this wave's reads of the slot that is refilled below.
     waitcnt<(NSTAGE - 2) * NCOPY, 0>();
     __builtin_amdgcn_s_barrier();
-    if ((A_KC || B_KC) && cur.tail) {   // K tail of K-contiguous operands: zero k past the segment's end
+    if constexpr (TAIL) {   // K tail of K-contiguous operands: zero k past the segment's end
       bool kt_live;
       const int ka = stage_of(cur, kt, kt_live);   // stage within the tile
       const bool s1 = SEG2 && ka >= cur.nk0;
@@ -618,9 +660,9 @@ struct Pipe {
     __builtin_amdgcn_sched_barrier(0);
     constexpr int PC = S & 1, PP = (S + 1) & 1;   // this stage's and the previous stage's parity
     TPS_LDS char* cdst = ring_slot<(S + NSTAGE - 1) % NSTAGE>();
-    phase<PP, 1, PC, 0, BI / 2, true, READS1, true>(acc, cur_slot, cs, cdst,
+    phase<PP, 1, PC, 0, BI / 2, true, READS1, true>(acc, cur_slot, w, cdst, 0,
                                                    std::make_integer_sequence<int, GROUPS1>{});
-    phase<PC, 0, PC, BI / 2, BI, false, READS2, false>(acc, cur_slot, cs, cdst,
+    phase<PC, 0, PC, BI / 2, BI, false, READS2, false>(acc, cur_slot, w, cdst, kt + NSTAGE,
                                                       std::make_integer_sequence<int, GROUPS2>{});
   }
 
@@ -635,12 +677,21 @@ struct Pipe {
      ...);
   }
 
-  // Run the current piece.  The copies of its first NSTAGE-1 stages must
-  // already be issued, and nxt set (the next piece, or no_next()): the
-  // piece's last NSTAGE-1 steps issue the next piece's first stages.
-  // `init` sets the accumulators' starting values.
+  // Run the current tile.  The copies of its first NSTAGE-1 stages must
+  // already be issued, and nxt set (the next tile, or no_next()): the
+  // tile's last NSTAGE-1 steps issue the next tile's first stages.
+  // `init` sets the accumulators' starting values.  A tile whose
+  // K-contiguous operands end inside a stage runs a separate copy of the
+  // loop that zeroes those tails: a test inside the loop would split its
+  // body into blocks, and the compiler sinks the scalar copy bookkeeping
+  // across such splits to just after the barrier, where it stalls the MFMAs.
   template <class InitFn>
   __device__ __forceinline__ void run_tile(Acc& acc, InitFn&& init) {
+    if ((A_KC || B_KC) && cur.tail) run_loop<A_KC || B_KC>(acc, init);
+    else run_loop<false>(acc, init);
+  }
+  template <bool TAIL, class InitFn>
+  __device__ __forceinline__ void run_loop(Acc& acc, InitFn&& init) {
     static_assert(NSTAGE % 2 == 0, "the fragment set of a stage is its parity");
     init(acc);
     zero_set1();              // the first step's deferred half multiplies zeros
@@ -650,11 +701,14 @@ struct Pipe {
     // of a register write before an MFMA reads it, and of an MFMA's result
     // before a register read, last a few passes).
     asm volatile("s_nop 4" ::: "memory");
+    CopyCalc w;
+    calc_init(w);
+    calc_all(w, NSTAGE - 1, std::make_integer_sequence<int, NCALC>{});
     for (int kt = 0; kt < cur.npad; kt += NSTAGE) {
-      step<0>(kt, acc);
-      step<1>(kt + 1, acc);
-      step<2>(kt + 2, acc);
-      step<3>(kt + 3, acc);
+      step<0, TAIL>(kt, acc, w);
+      step<1, TAIL>(kt + 1, acc, w);
+      step<2, TAIL>(kt + 2, acc, w);
+      step<3, TAIL>(kt + 3, acc, w);
     }
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
     mma_half<(NSTAGE - 1) & 1, 1>(acc, std::make_integer_sequence<int, HALF_MFMA>{});   // last stage, second half
@@ -1002,7 +1056,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
     Problem P;
     int64_t m0, n0;
     locate_mi<MI, NI>(L, tile, EPI, P, m0, n0);
-    pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX, xcd);
+    pipe.cur = pipe.make_streams(P, m0, n0, xcd);
   }
   pipe.prologue();
   for (;;) {
@@ -1011,7 +1065,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
       Problem Pn;
       int64_t m0n, n0n;
       locate_mi<MI, NI>(L, tile + stride, EPI, Pn, m0n, n0n);
-      pipe.nxt = pipe.make_streams(Pn, m0n, n0n, 0, INT_MAX, xcd);
+      pipe.nxt = pipe.make_streams(Pn, m0n, n0n, xcd);
     } else {
       pipe.no_next();
     }
@@ -1100,7 +1154,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmL
   f32x4 acc[8][8];
   Pipe<LAYOUT, DUAL, SEG2> pipe;
   pipe.init_wave();
-  pipe.cur = pipe.make_streams(P, m0, n0, 0, INT_MAX);
+  pipe.cur = pipe.make_streams(P, m0, n0);
   pipe.prologue();
   pipe.no_next();
   pipe.run_tile(acc, zero_acc<4>);
