@@ -57,6 +57,17 @@ __device__ __forceinline__ int mn_swz(int k) { return 2 * ((k & 3) | ((k & 8) >>
 template <int ROWB>
 __device__ __forceinline__ int mn_off(int k, int c) { return k * ROWB + ((c ^ mn_swz(k)) << 4); }
 
+// The thread index as an opaque value.  The per-tile helpers (copy streams,
+// store epilogue) derive per-lane offsets from it; with threadIdx.x itself
+// the compiler hoists those out of the tile loop and keeps dozens of them
+// live across the K loop, which then spills.  Recomputing them per tile costs
+// a few dozen vector instructions.
+__device__ __forceinline__ int tid_opaque() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // ---- global -> LDS streaming ---------------------------------------------------
 // Each operand stage (16 KiB) is copied by 16 wave-level buffer_load_dwordx4
 // ... lds instructions, 4 per wave; each writes 1 KiB of LDS contiguously in
@@ -92,7 +103,7 @@ __device__ __forceinline__ int64_t extent_bytes(int64_t rows, int64_t ld, int64_
 template <int NB = DMA_PER_OPERAND>
 __device__ __forceinline__ OpStream stream_kc(const void* p, int64_t ld, int64_t rows, int64_t K, int64_t row0,
                                               int wb) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   OpStream s;
   s.base = static_cast<const char*>(p) + row0 * ld * 2;
   s.nrec = (uint32_t)(extent_bytes(rows, ld, K) - row0 * ld * 2);   // row0 < rows: every tile starts inside
@@ -117,7 +128,7 @@ constexpr uint32_t kDeadLane = 0x80000000u;   // above any extent (< 2 GiB), bel
 template <int W, int VALID = W / 8>
 __device__ __forceinline__ OpStream stream_mn(const void* p, int64_t ld, int64_t cols, int64_t K, int64_t col0,
                                               int wb) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   constexpr int CHUNKS = W / 8;
   constexpr int ROWS = 512 / W;   // rows per block
   OpStream s;
@@ -219,6 +230,9 @@ __device__ __forceinline__ TPS_LDS char* ring_slot() {
 // last NSTAGE-1 steps of a tile already issue the copies of the next tile's
 // first stages, so the next tile starts with a full ring and the current
 // tile's epilogue (which does not touch LDS) overlaps those copies.
+
+// Which K-loop copies a kernel carries (Pipe::run_tile).
+enum TailMode : int { TM_NONE = 0, TM_TAIL = 1, TM_ANY = 2 };
 
 // Copy streams of one tile: per K segment (0, 1), one stream per operand.
 // Plain named members (no arrays of structs) keep all of it in registers.
@@ -680,15 +694,23 @@ struct Pipe {
   // Run the current tile.  The copies of its first NSTAGE-1 stages must
   // already be issued, and nxt set (the next tile, or no_next()): the
   // tile's last NSTAGE-1 steps issue the next tile's first stages.
-  // `init` sets the accumulators' starting values.  A tile whose
-  // K-contiguous operands end inside a stage runs a separate copy of the
-  // loop that zeroes those tails: a test inside the loop would split its
-  // body into blocks, and the compiler sinks the scalar copy bookkeeping
-  // across such splits to just after the barrier, where it stalls the MFMAs.
-  template <class InitFn>
+  // `init` sets the accumulators' starting values.  Tiles whose
+  // K-contiguous operands end inside a stage (cur.tail) run a copy of the
+  // loop that zeroes those tails; TM says which copies a kernel carries:
+  // TM_NONE (the caller never passes such tiles), TM_TAIL (only such
+  // tiles), TM_ANY (both copies, chosen per tile).  A test inside the loop
+  // would split its body into blocks, and the compiler sinks the scalar copy
+  // bookkeeping across such splits to just after the barrier, where it
+  // stalls the MFMAs; two copies in one kernel hold about twice the vector
+  // registers, which the persistent kernels cannot spare without spilling.
+  template <int TM, class InitFn>
   __device__ __forceinline__ void run_tile(Acc& acc, InitFn&& init) {
-    if ((A_KC || B_KC) && cur.tail) run_loop<A_KC || B_KC>(acc, init);
-    else run_loop<false>(acc, init);
+    if constexpr (TM == TM_ANY) {
+      if ((A_KC || B_KC) && cur.tail) run_loop<A_KC || B_KC>(acc, init);
+      else run_loop<false>(acc, init);
+    } else {
+      run_loop<TM == TM_TAIL && (A_KC || B_KC)>(acc, init);
+    }
   }
   template <bool TAIL, class InitFn>
   __device__ __forceinline__ void run_loop(Acc& acc, InitFn&& init) {
@@ -763,30 +785,60 @@ __device__ __forceinline__ void store_pq(uint16_t* p, const uint32_t (&a)[2], co
   *reinterpret_cast<u32x4*>(p) = u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// A lane's output position in a tile's fast epilogue, computed once per
+// tile: block row I, column pair JP of its 8-column chunk lies at
+// c + I * rc + 32 JP elements (16 rows per block row; the pair step fits the
+// store's immediate offset), so the per-pair address work is one add per
+// block row.
+struct EpiLane {
+  uint16_t* c;     // output at (m, n)
+  uint16_t* pre;   // pre-activation output at (m, n) (GeLU, SwiGLU)
+  int64_t rc, rp;  // 16 rows of c / pre, in elements
+  int64_t m, n;    // the lane's row in block row 0, first column of its chunk in pair 0
+  int64_t cg;      // first column of the lane's 4-column group in block 0 (CE target offsets)
+  bool whole;      // the tile lies inside the output: no per-lane bounds
+};
+
+template <int EPI, int MI, int NI>
+__device__ __forceinline__ EpiLane epi_lane(const Problem& P, int64_t m0, int64_t n0) {
+  constexpr bool dual = EPI == E_SWIGLU;
+  const int tid = tid_opaque(), lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4;
+  EpiLane e;
+  e.m = m0 + 32 * MI * wm + (lane & 15);
+  const int64_t cj = n0 + (dual ? 64 * wn : 32 * NI * wn);   // first column of the wave's block 0
+  e.n = cj + 16 * (g & 1) + 4 * (g & 2);                    // this lane's 8 columns
+  e.cg = cj + 4 * g;
+  const int64_t bw = dual ? BN / 2 : 64 * NI;
+  e.whole = m0 + 64 * MI <= P.M && n0 + bw <= P.N;   // wave-uniform
+  e.c = static_cast<uint16_t*>(P.c) + e.m * P.ldc + e.n;
+  e.rc = 16 * P.ldc;
+  if (EPI == E_GELU || EPI == E_SWIGLU) {
+    e.pre = static_cast<uint16_t*>(P.pre) + e.m * P.ldpre + e.n;
+    e.rp = 16 * P.ldpre;
+  } else {
+    e.pre = nullptr;
+    e.rp = 0;
+  }
+  return e;
+}
+
 // Blocks (I, 2 JP) and (I, 2 JP + 1) of the wave (a, b); for SwiGLU also the
-// up blocks (I, 2 JP + 4), (I, 2 JP + 5) (ua, ub).
-template <int EPI, int MI, int NI, int I, int JP>
-__device__ __forceinline__ void fast_pair(const Problem& P, int64_t m0, int64_t n0, const f32x4& a, const f32x4& b,
+// up blocks (I, 2 JP + 4), (I, 2 JP + 5) (ua, ub).  A tile may overhang the
+// matrix (rows past M; columns past N when N is a multiple of 8): unless
+// WHOLE, each lane's 8-column chunk is stored only inside the matrix.
+template <int EPI, int MI, int NI, int I, int JP, bool WHOLE>
+__device__ __forceinline__ void fast_pair(const Problem& P, const EpiLane& e, const f32x4& a, const f32x4& b,
                                           const f32x4& ua, const f32x4& ub) {
   constexpr bool dual = EPI == E_SWIGLU;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  const int g = lane >> 4;
-  const int64_t m = m0 + 32 * MI * wm + 16 * I + (lane & 15);
-  const int64_t cj = n0 + (dual ? 64 * wn + 32 * JP : 32 * NI * wn + 32 * JP);   // first column of block 2 JP
-  const int64_t n = cj + 16 * (g & 1) + 4 * (g & 2);                             // this lane's 8 columns
-  // A tile may overhang the matrix (rows past M; columns past N when N is a
-  // multiple of 8): each lane's 8-column chunk is stored only inside the
-  // matrix.  (The test is per tile first, so whole tiles store without
-  // per-lane compares.)
-  const int64_t bw = dual ? BN / 2 : 64 * NI;
-  const bool whole = m0 + 64 * MI <= P.M && n0 + bw <= P.N;   // wave-uniform
+  const int64_t m = e.m + 16 * I, n = e.n + 32 * JP;
   float ce_l = 0.f, ce_g = 0.f;
   int64_t ce_t = 0;
   if (EPI == E_CE_GRAD) {   // per-row loss terms; the target column relative to this lane's block-2JP columns
     const int64_t mr = m < P.M ? m : P.M - 1;
     ce_l = P.lse[mr];
     ce_g = P.gscale ? P.gscale[mr] : 1.0f;
-    ce_t = (int64_t)P.target[mr] - P.v0 - (cj + 4 * g);
+    ce_t = (int64_t)P.target[mr] - P.v0 - (e.cg + 32 * JP);
   }
   uint32_t py[2], qy[2], pg[2], qg[2], pu[2], qu[2];
 #pragma unroll
@@ -818,22 +870,32 @@ __device__ __forceinline__ void fast_pair(const Problem& P, int64_t m0, int64_t 
   swap_pair(py, qy);
   if (EPI == E_GELU || EPI == E_SWIGLU) swap_pair(pg, qg);
   if (dual) swap_pair(pu, qu);
-  if (whole || (m < P.M && n < P.N)) {
-    store_pq(static_cast<uint16_t*>(P.c) + m * P.ldc + n, py, qy);
-    if (EPI == E_GELU || EPI == E_SWIGLU) store_pq(static_cast<uint16_t*>(P.pre) + m * P.ldpre + n, pg, qg);
-    if (dual) store_pq(static_cast<uint16_t*>(P.pre) + m * P.ldpre + P.N + n, pu, qu);
+  if (WHOLE || (m < P.M && n < P.N)) {
+    store_pq(e.c + I * e.rc + 32 * JP, py, qy);
+    if (EPI == E_GELU || EPI == E_SWIGLU) store_pq(e.pre + I * e.rp + 32 * JP, pg, qg);
+    if (dual) store_pq(e.pre + I * e.rp + P.N + 32 * JP, pu, qu);
   }
 }
 
-template <int EPI, int MI, int NI, int... Is>
-__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0,
-                                              f32x4 (&acc)[2 * MI][2 * NI], std::integer_sequence<int, Is...>) {
+template <int EPI, int MI, int NI, bool WHOLE, int... Is>
+__device__ __forceinline__ void fast_pairs(const Problem& P, const EpiLane& e, f32x4 (&acc)[2 * MI][2 * NI],
+                                           std::integer_sequence<int, Is...>) {
   constexpr int NP = EPI == E_SWIGLU ? 2 : NI;   // block pairs per block row
   constexpr int UP = EPI == E_SWIGLU ? 4 : 0;    // SwiGLU: block j's up values are block j + 4
-  ((fast_pair<EPI, MI, NI, Is / NP, Is % NP>(P, m0, n0, acc[Is / NP][2 * (Is % NP)], acc[Is / NP][2 * (Is % NP) + 1],
-                                             acc[Is / NP][2 * (Is % NP) + UP], acc[Is / NP][2 * (Is % NP) + 1 + UP]),
+  ((fast_pair<EPI, MI, NI, Is / NP, Is % NP, WHOLE>(P, e, acc[Is / NP][2 * (Is % NP)],
+                                                    acc[Is / NP][2 * (Is % NP) + 1],
+                                                    acc[Is / NP][2 * (Is % NP) + UP],
+                                                    acc[Is / NP][2 * (Is % NP) + 1 + UP]),
     __builtin_amdgcn_sched_barrier(0)),
    ...);
+}
+
+template <int EPI, int MI, int NI, class Seq>
+__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0,
+                                              f32x4 (&acc)[2 * MI][2 * NI], Seq seq) {
+  const EpiLane e = epi_lane<EPI, MI, NI>(P, m0, n0);
+  if (e.whole) fast_pairs<EPI, MI, NI, true>(P, e, acc, seq);
+  else fast_pairs<EPI, MI, NI, false>(P, e, acc, seq);
 }
 
 // Generic path: the ring is drained, and each wave stages 32-row slices of
@@ -1039,7 +1101,7 @@ struct StoreEpilogue {
 // at one time are neighbours in the grouped order (share operand panels in
 // L2) however many tiles each workgroup runs; for launches of many tiles per
 // workgroup.
-template <int LAYOUT, int EPI, bool SEG2, int MI = 4, int NI = 4, bool STRIDED = false,
+template <int LAYOUT, int EPI, bool SEG2, int MI = 4, int NI = 4, bool STRIDED = false, int TM = TM_NONE,
           class Epi = StoreEpilogue<EPI, MI, NI>>
 __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count, int g, int G, int xcd,
                                           const Epi& epilogue = Epi{}) {
@@ -1070,7 +1132,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
       pipe.no_next();
     }
     f32x4 acc[2 * MI][2 * NI];
-    pipe.run_tile(acc, zero_acc<MI, NI>);
+    pipe.template run_tile<TM>(acc, zero_acc<MI, NI>);
     {
       Problem P;
       int64_t m0, n0;
@@ -1157,7 +1219,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_edge_kernel(const GemmL
   pipe.cur = pipe.make_streams(P, m0, n0);
   pipe.prologue();
   pipe.no_next();
-  pipe.run_tile(acc, zero_acc<4>);
+  pipe.template run_tile<TM_ANY>(acc, zero_acc<4>);
   waitcnt<0, 0>();   // trailing (empty) copies land before the LDS is reused
   __syncthreads();
   generic_epilogue(P, m0, n0, acc);
@@ -1284,23 +1346,27 @@ struct CeEpilogue {
 // Persistent logit-tile kernel: workgroup g of G runs the tiles g, g + G,
 // ... of the launch (about 9 per workgroup for an 8192 x 18992 shard), the
 // next tile's first stages loading during this tile's epilogue (MI = 2: the
-// 128-row halves of a half-tile tail launch).
-template <int MI>
+// 128-row halves of a half-tile tail launch).  KTAIL: the hidden size ends
+// inside a 32-deep stage (the loop that zeroes its tail).
+template <int MI, bool KTAIL>
 __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_kernel(const GemmLaunch L, const CEArgs a, int tiles_n) {
   int xcd;
   const int g = wg_index(xcd);
-  tile_loop<L_NT, E_STORE, false, MI, 4, true>(L, 0, L.tiles, g, gridDim.x, xcd, CeEpilogue<MI>{a, tiles_n});
+  tile_loop<L_NT, E_STORE, false, MI, 4, true, KTAIL ? TM_TAIL : TM_NONE>(L, 0, L.tiles, g, gridDim.x, xcd,
+                                                                        CeEpilogue<MI>{a, tiles_n});
 }
 
 // The whole tiles (F) and then the 128-row halves of the last round (H) in
 // one launch, as gemm_bf16_tail_kernel does for the GEMMs.
+template <bool KTAIL>
 __global__ __launch_bounds__(NTHREADS, 1) void ce_tile_tail_kernel(const GemmLaunch F, const GemmLaunch H,
                                                                    const CEArgs a, int tiles_n) {
+  constexpr int TM = KTAIL ? TM_TAIL : TM_NONE;
   int xcd;
   const int g = wg_index(xcd);
-  tile_loop<L_NT, E_STORE, false, 4, 4, true>(F, 0, F.tiles, g, gridDim.x, xcd, CeEpilogue<4>{a, tiles_n});
+  tile_loop<L_NT, E_STORE, false, 4, 4, true, TM>(F, 0, F.tiles, g, gridDim.x, xcd, CeEpilogue<4>{a, tiles_n});
   ring_handover();
-  tile_loop<L_NT, E_STORE, false, 2, 4, false>(H, 0, H.tiles, g, gridDim.x, xcd, CeEpilogue<2>{a, tiles_n});
+  tile_loop<L_NT, E_STORE, false, 2, 4, false, TM>(H, 0, H.tiles, g, gridDim.x, xcd, CeEpilogue<2>{a, tiles_n});
 }
 
 // Combine the per-tile partials of each token: 8 lanes per token, lane j
@@ -1344,9 +1410,12 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // The tiles of this problem may take the fast kernel (no bias, 16-byte
-// aligned outputs).
+// aligned outputs, K-contiguous operands ending on a 32-deep stage: the fast
+// kernels carry no K-tail code).
 bool fast_ok(const Problem& P) {
   if (P.bias || P.bias2) return false;
+  for (int i = 0; i < P.nseg; ++i)
+    if (P.layout != L_TN && P.seg[i].K % BK != 0) return false;
   if (!aligned16(P.c) || (P.ldc & 7)) return false;
   if (P.epi != E_STORE && (!aligned16(P.pre) || (P.ldpre & 7))) return false;
   if (P.epi == E_SWIGLU && (P.N & 7)) return false;
@@ -1679,15 +1748,21 @@ hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s) {
   // last row).
   const int rem = nt % cus;
   const int tail = (a.M % BM == 0 && nt > cus && rem > 0 && 2 * rem <= cus) ? rem : 0;
+  const bool ktail = a.K % BK != 0;
   L.tiles = nt - tail;
   if (tail > 0) {   // L.tiles >= cus: one workgroup per CU runs its whole tiles, then at most one half
     GemmLaunch H = L;
     H.tiles = 2 * tail;
     H.half_base = nt - tail;
     H.half_tail = 1;
-    hipLaunchKernelGGL(ce_tile_tail_kernel, dim3(cus), dim3(NTHREADS), 0, s, L, H, a, tiles_n);
+    if (ktail)
+      hipLaunchKernelGGL(ce_tile_tail_kernel<true>, dim3(cus), dim3(NTHREADS), 0, s, L, H, a, tiles_n);
+    else
+      hipLaunchKernelGGL(ce_tile_tail_kernel<false>, dim3(cus), dim3(NTHREADS), 0, s, L, H, a, tiles_n);
   } else {
-    hipLaunchKernelGGL(ce_tile_kernel<4>, dim3(std::min(L.tiles, cus)), dim3(NTHREADS), 0, s, L, a, tiles_n);
+    const dim3 grid(std::min(L.tiles, cus));
+    if (ktail) hipLaunchKernelGGL((ce_tile_kernel<4, true>), grid, dim3(NTHREADS), 0, s, L, a, tiles_n);
+    else hipLaunchKernelGGL((ce_tile_kernel<4, false>), grid, dim3(NTHREADS), 0, s, L, a, tiles_n);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

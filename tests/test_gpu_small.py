@@ -342,8 +342,10 @@ def test_sp_reduce_scatter_ln_in_place_and_constant_rows():
 # (2048, 18992, 40): 600 logit tiles on 256 CUs -- workgroups run two or three
 # tiles in a row, and the last 88 tiles run as 176 half tiles; (2000, ...):
 # the same without the half tiles (M not a multiple of 256), rows past M masked.
+# K % 32 != 0 takes the kernels' K-tail variant, K % 32 == 0 the other one
+# ((2048, 18992, 64): half tiles without a K tail).
 @pytest.mark.parametrize("M,Vr,K", [(1, 1, 8), (37, 300, 72), (300, 600, 136), (260, 18992, 64),
-                                    (2048, 18992, 40), (2000, 18992, 72)])
+                                    (2048, 18992, 40), (2048, 18992, 64), (2000, 18992, 72)])
 def test_vocab_ce_small(M, Vr, K):
     rng = np.random.default_rng(M + Vr)
     H = syn.normal(70 + M, (M, K), 1.0, syn.BF16)
