@@ -152,6 +152,18 @@ TP_API tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K,
 TP_API size_t tp_row_bwd_workspace_bytes(int dtype, int64_t M, int64_t N);
 
 /*
+ * Planning query for tp_row_bwd (bf16, dXi and dBi both requested): which
+ * tile pairing its one-launch schedule of the two GEMMs takes for these sizes
+ * (same M, N, K as tp_row_bwd, 16-byte aligned operands) on a GPU with `cus`
+ * compute units.  For schedulers and tests that want the launch shape; host
+ * only: no GPU call, no allocation.  Returns 0 (256x256 weight-gradient tiles
+ * beside 256x256 input-gradient tiles), 1 (192x256 beside 256x192), 2
+ * (192x192 beside 128x192), -1 (the two GEMMs run as separate launches), or
+ * -2 for sizes tp_row_bwd rejects or cus < 1.
+ */
+TP_API int tp_row_bwd_plan(int64_t M, int64_t N, int64_t K, int cus);
+
+/*
  * Column-parallel shard backward.  [TP/SP] "Where column and row
  * communicate" and "Full flow: column parallel, t = 3": the input gradient is
  * a partial (dX = sum_i dY_i A_i^T, summed by f's backward -- use

@@ -22,7 +22,7 @@ import sys
 __all__ = [
     "TP_FP32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU", "TP_ACT_SWIGLU", "TPError", "LIB_PATH",
     "tp_abi_version", "tp_status_str", "tp_column_fwd", "tp_row_fwd", "tp_sum_partials", "tp_row_bwd",
-    "tp_row_bwd_workspace_bytes", "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_vocab_ce_partials",
+    "tp_row_bwd_workspace_bytes", "tp_row_bwd_plan", "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_vocab_ce_partials",
     "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_partials_noalloc", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "tp_sp_reduce_scatter_ln",
     "tp_vocab_embed_fwd", "tp_vocab_embed_bwd", "tp_vocab_embed_bwd_workspace_bytes", "tp_attention_fwd",
     "tp_attention_fwd_workspace_bytes", "tp_attention_bwd", "tp_attention_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
@@ -46,6 +46,7 @@ _SIGS = {
     "tp_row_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                           _vp, _sz, _vp]),
     "tp_row_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64]),
+    "tp_row_bwd_plan": (_i32, [_i64, _i64, _i64, _i32]),
     "tp_column_bwd": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                              _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "tp_column_bwd_workspace_bytes": (_sz, [_i32, _i32, _i64, _i64, _i32]),
@@ -161,6 +162,12 @@ def tp_row_bwd(dtype, M, N, K, dZ, lddz, Xi, ldx, Bi, ldb, dXi, lddx, dBi, lddb,
 
 def tp_row_bwd_workspace_bytes(dtype, M, N) -> int:
     return _load().tp_row_bwd_workspace_bytes(dtype, M, N)
+
+
+def tp_row_bwd_plan(M, N, K, cus) -> int:
+    """Tile pairing of tp_row_bwd's one-launch schedule (host-only query): 0 = 256x256 + 256x256,
+    1 = 192x256 + 256x192, 2 = 192x192 + 128x192, -1 = separate launches, -2 = invalid sizes."""
+    return _load().tp_row_bwd_plan(M, N, K, cus)
 
 
 def tp_column_bwd(dtype, act, M, N, K, dY, lddy, X, ldx, A, lda, A2, lda2, Pre, ldpre, dXpart, lddx, dA, ldda,

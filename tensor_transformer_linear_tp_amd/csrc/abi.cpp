@@ -81,6 +81,24 @@ Problem make_problem(int64_t M, int64_t N, int layout, int epi) {
   return P;
 }
 
+// tp_row_bwd's two GEMMs as one launch: dB_i = X_i^T dZ (TN over M), then
+// dX_i = dZ B_i^T (NT over N).
+GemmLaunch row_bwd_pair(int64_t M, int64_t N, int64_t K, const void* dZ, int64_t lddz, const void* Xi,
+                        int64_t ldx, const void* Bi, int64_t ldb, void* dXi, int64_t lddx, void* dBi,
+                        int64_t lddb) {
+  GemmLaunch L = {};
+  L.nprob = 2;
+  L.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);
+  L.p[0].seg[0] = tps::Seg{Xi, dZ, ldx, lddz, M};
+  L.p[0].c = dBi;
+  L.p[0].ldc = lddb;
+  L.p[1] = make_problem(M, K, tps::L_NT, tps::E_STORE);
+  L.p[1].seg[0] = tps::Seg{dZ, Bi, lddz, ldb, N};
+  L.p[1].c = dXi;
+  L.p[1].ldc = lddx;
+  return L;
+}
+
 int64_t colpart_rows(int64_t M) { return (M + tps::kColpartRows - 1) / tps::kColpartRows; }
 
 size_t colpart_bytes(int64_t M, int64_t N) {
@@ -228,16 +246,7 @@ tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* dZ,
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (dXi && dBi && dtype == TP_BF16) {   // both GEMMs in one launch (the library may share the CUs)
-    GemmLaunch L = {};
-    L.nprob = 2;
-    L.p[0] = make_problem(K, N, tps::L_TN, tps::E_STORE);   // dB_i = X_i^T dZ
-    L.p[0].seg[0] = tps::Seg{Xi, dZ, ldx, lddz, M};
-    L.p[0].c = dBi;
-    L.p[0].ldc = lddb;
-    L.p[1] = make_problem(M, K, tps::L_NT, tps::E_STORE);   // dX_i = dZ B_i^T
-    L.p[1].seg[0] = tps::Seg{dZ, Bi, lddz, ldb, N};
-    L.p[1].c = dXi;
-    L.p[1].ldc = lddx;
+    GemmLaunch L = row_bwd_pair(M, N, K, dZ, lddz, Xi, ldx, Bi, ldb, dXi, lddx, dBi, lddb);
     if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
   } else if (dXi) {   // dX_i = dZ B_i^T: NT over K' = N
     GemmLaunch L = {};
@@ -273,6 +282,18 @@ tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* dZ,
       return TP_E_HIP;
   }
   return TP_OK;
+}
+
+int tp_row_bwd_plan(int64_t M, int64_t N, int64_t K, int cus) {
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K) || cus < 1) return -2;
+  if (check_grid(TP_BF16, M, K) != TP_OK || check_grid(TP_BF16, K, N) != TP_OK) return -2;
+  // Stand-in operands: aligned addresses, leading dimensions rounded up to 8 elements.
+  char* const p = reinterpret_cast<char*>(uintptr_t(256));
+  const GemmLaunch L = row_bwd_pair(M, N, K, p, round_up(N, 8), p, round_up(K, 8), p, round_up(N, 8), p,
+                                    round_up(K, 8), p, round_up(N, 8));
+  int g0 = 0;
+  int64_t t0 = 0, t1 = 0;
+  return tps::dual_plan(L, cus, g0, t0, t1);
 }
 
 size_t tp_column_bwd_workspace_bytes(int dtype, int act, int64_t M, int64_t N, int with_bias_grad) {

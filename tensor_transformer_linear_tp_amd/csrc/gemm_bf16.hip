@@ -756,16 +756,16 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[2 * MI][2 * NI]) {
 // consecutive columns 4 (lane / 16) .. +3.  SwiGLU waves hold gate blocks
 // 0-3 and the matching up blocks 4-7 (same columns).
 //
-// Fast path (whole tile inside the output, 16-byte aligned rows, no bias;
-// the persistent kernel): blocks are finished in pairs (j, j + 1) of
+// Fast path (16-byte aligned rows; the persistent kernels; a column bias is
+// already in the accumulators, see TileInit): blocks are finished in pairs (j, j + 1) of
 // adjacent 16-column blocks -- values in fp32, packed to bf16 pairs, then
 // one v_permlane16_swap per packed register trades half of them between the
 // lanes of adjacent 16-lane rows, so that every lane holds eight consecutive
 // columns, written with one 16-byte store.  No LDS: the ring is already
 // filling with the next tile's stages.
 //
-// Generic path (edge tiles, bias, unaligned outputs; one tile per
-// workgroup): see generic_epilogue.
+// Generic path (edge tiles, unaligned outputs, bias outside NN products;
+// one tile per workgroup): see generic_epilogue.
 
 // p: the lane's packed block-j values (two registers), q: block j + 1's.
 // v_permlane16_swap swaps the odd 16-lane rows of its first operand with the
@@ -789,36 +789,45 @@ __device__ __forceinline__ void store_pq(uint16_t* p, const uint32_t (&a)[2], co
 // tile: block row I, column pair JP of its 8-column chunk lies at
 // c + I * rc + 32 JP elements (16 rows per block row; the pair step fits the
 // store's immediate offset), so the per-pair address work is one add per
-// block row.
+// block row.  Kept small (two pointers, two counts): the epilogue runs
+// beside the accumulators and the fragment registers of the K loop.
+template <int EPI>
 struct EpiLane {
-  uint16_t* c;     // output at (m, n)
-  uint16_t* pre;   // pre-activation output at (m, n) (GeLU, SwiGLU)
-  int64_t rc, rp;  // 16 rows of c / pre, in elements
-  int64_t m, n;    // the lane's row in block row 0, first column of its chunk in pair 0
-  int64_t cg;      // first column of the lane's 4-column group in block 0 (CE target offsets)
-  bool whole;      // the tile lies inside the output: no per-lane bounds
+  uint16_t* c;     // output at the lane's row of block row 0, first column of its chunk in pair 0
+  uint16_t* pre;   // pre-activation output at the same position (GeLU, SwiGLU)
+  int64_t rc, rp;  // 16 rows of c / pre, in elements (wave-uniform)
+  int rl, cl;      // rows below / columns right of that position inside the output (clamped to 2^30)
+  bool whole;      // the tile lies inside the output: no per-lane bounds (wave-uniform)
+  int64_t m, cg;   // E_CE_GRAD: the lane's row, first column of its 4-column group in block 0
 };
 
 template <int EPI, int MI, int NI>
-__device__ __forceinline__ EpiLane epi_lane(const Problem& P, int64_t m0, int64_t n0) {
+__device__ __forceinline__ EpiLane<EPI> epi_lane(const Problem& P, int64_t m0, int64_t n0) {
   constexpr bool dual = EPI == E_SWIGLU;
   const int tid = tid_opaque(), lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 4;
-  EpiLane e;
-  e.m = m0 + 32 * MI * wm + (lane & 15);
+  EpiLane<EPI> e;
+  const int64_t m = m0 + 32 * MI * wm + (lane & 15);
   const int64_t cj = n0 + (dual ? 64 * wn : 32 * NI * wn);   // first column of the wave's block 0
-  e.n = cj + 16 * (g & 1) + 4 * (g & 2);                    // this lane's 8 columns
-  e.cg = cj + 4 * g;
+  const int64_t n = cj + 16 * (g & 1) + 4 * (g & 2);        // this lane's 8 columns
   const int64_t bw = dual ? BN / 2 : 64 * NI;
-  e.whole = m0 + 64 * MI <= P.M && n0 + bw <= P.N;   // wave-uniform
-  e.c = static_cast<uint16_t*>(P.c) + e.m * P.ldc + e.n;
+  e.whole = m0 + 64 * MI <= P.M && n0 + bw <= P.N;
+  e.rl = (int)min<int64_t>(P.M - m, int64_t(1) << 30);
+  e.cl = (int)min<int64_t>(P.N - n, int64_t(1) << 30);
+  e.c = static_cast<uint16_t*>(P.c) + m * P.ldc + n;
   e.rc = 16 * P.ldc;
   if (EPI == E_GELU || EPI == E_SWIGLU) {
-    e.pre = static_cast<uint16_t*>(P.pre) + e.m * P.ldpre + e.n;
+    e.pre = static_cast<uint16_t*>(P.pre) + m * P.ldpre + n;
     e.rp = 16 * P.ldpre;
   } else {
     e.pre = nullptr;
     e.rp = 0;
+  }
+  if (EPI == E_CE_GRAD) {
+    e.m = m;
+    e.cg = cj + 4 * g;
+  } else {
+    e.m = e.cg = 0;
   }
   return e;
 }
@@ -826,15 +835,15 @@ __device__ __forceinline__ EpiLane epi_lane(const Problem& P, int64_t m0, int64_
 // Blocks (I, 2 JP) and (I, 2 JP + 1) of the wave (a, b); for SwiGLU also the
 // up blocks (I, 2 JP + 4), (I, 2 JP + 5) (ua, ub).  A tile may overhang the
 // matrix (rows past M; columns past N when N is a multiple of 8): unless
-// WHOLE, each lane's 8-column chunk is stored only inside the matrix.
-template <int EPI, int MI, int NI, int I, int JP, bool WHOLE>
-__device__ __forceinline__ void fast_pair(const Problem& P, const EpiLane& e, const f32x4& a, const f32x4& b,
+// the tile is whole, each lane's 8-column chunk is stored only inside it.
+template <int EPI, int MI, int NI, int I, int JP>
+__device__ __forceinline__ void fast_pair(const Problem& P, const EpiLane<EPI>& e, const f32x4& a, const f32x4& b,
                                           const f32x4& ua, const f32x4& ub) {
   constexpr bool dual = EPI == E_SWIGLU;
-  const int64_t m = e.m + 16 * I, n = e.n + 32 * JP;
   float ce_l = 0.f, ce_g = 0.f;
   int64_t ce_t = 0;
   if (EPI == E_CE_GRAD) {   // per-row loss terms; the target column relative to this lane's block-2JP columns
+    const int64_t m = e.m + 16 * I;
     const int64_t mr = m < P.M ? m : P.M - 1;
     ce_l = P.lse[mr];
     ce_g = P.gscale ? P.gscale[mr] : 1.0f;
@@ -870,32 +879,23 @@ __device__ __forceinline__ void fast_pair(const Problem& P, const EpiLane& e, co
   swap_pair(py, qy);
   if (EPI == E_GELU || EPI == E_SWIGLU) swap_pair(pg, qg);
   if (dual) swap_pair(pu, qu);
-  if (WHOLE || (m < P.M && n < P.N)) {
+  if (e.whole || (16 * I < e.rl && 32 * JP < e.cl)) {
     store_pq(e.c + I * e.rc + 32 * JP, py, qy);
     if (EPI == E_GELU || EPI == E_SWIGLU) store_pq(e.pre + I * e.rp + 32 * JP, pg, qg);
     if (dual) store_pq(e.pre + I * e.rp + P.N + 32 * JP, pu, qu);
   }
 }
 
-template <int EPI, int MI, int NI, bool WHOLE, int... Is>
-__device__ __forceinline__ void fast_pairs(const Problem& P, const EpiLane& e, f32x4 (&acc)[2 * MI][2 * NI],
-                                           std::integer_sequence<int, Is...>) {
+template <int EPI, int MI, int NI, int... Is>
+__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0,
+                                              f32x4 (&acc)[2 * MI][2 * NI], std::integer_sequence<int, Is...>) {
   constexpr int NP = EPI == E_SWIGLU ? 2 : NI;   // block pairs per block row
   constexpr int UP = EPI == E_SWIGLU ? 4 : 0;    // SwiGLU: block j's up values are block j + 4
-  ((fast_pair<EPI, MI, NI, Is / NP, Is % NP, WHOLE>(P, e, acc[Is / NP][2 * (Is % NP)],
-                                                    acc[Is / NP][2 * (Is % NP) + 1],
-                                                    acc[Is / NP][2 * (Is % NP) + UP],
-                                                    acc[Is / NP][2 * (Is % NP) + 1 + UP]),
+  const EpiLane<EPI> e = epi_lane<EPI, MI, NI>(P, m0, n0);
+  ((fast_pair<EPI, MI, NI, Is / NP, Is % NP>(P, e, acc[Is / NP][2 * (Is % NP)], acc[Is / NP][2 * (Is % NP) + 1],
+                                             acc[Is / NP][2 * (Is % NP) + UP], acc[Is / NP][2 * (Is % NP) + 1 + UP]),
     __builtin_amdgcn_sched_barrier(0)),
    ...);
-}
-
-template <int EPI, int MI, int NI, class Seq>
-__device__ __forceinline__ void fast_epilogue(const Problem& P, int64_t m0, int64_t n0,
-                                              f32x4 (&acc)[2 * MI][2 * NI], Seq seq) {
-  const EpiLane e = epi_lane<EPI, MI, NI>(P, m0, n0);
-  if (e.whole) fast_pairs<EPI, MI, NI, true>(P, e, acc, seq);
-  else fast_pairs<EPI, MI, NI, false>(P, e, acc, seq);
 }
 
 // Generic path: the ring is drained, and each wave stages 32-row slices of
@@ -1086,6 +1086,50 @@ __device__ __forceinline__ void locate_mi(const GemmLaunch& L, int tile, int epi
   }
 }
 
+// Starting accumulator values of a fast-kernel tile: zeros, or with a column
+// bias the bias of each lane's four columns in every block (alike for all
+// rows; SwiGLU: the gate bias in gate blocks 0-3, the up bias in up blocks
+// 4-7).  The fp32 accumulators then hold x W + b, the bias summed first.
+// Columns past N (tiles overhanging the output, N a multiple of 8, so a
+// lane's four columns are all inside or all outside) start at zero.
+template <int EPI, int MI, int NI>
+struct TileInit {
+  f32x4 bj[2 * NI];
+  __device__ __forceinline__ void operator()(f32x4 (&acc)[2 * MI][2 * NI]) const {
+#pragma unroll
+    for (int i = 0; i < 2 * MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2 * NI; ++j) acc[i][j] = bj[j];
+  }
+};
+
+template <int EPI, int MI, int NI>
+__device__ __forceinline__ TileInit<EPI, MI, NI> tile_init() {
+  TileInit<EPI, MI, NI> t;
+#pragma unroll
+  for (int j = 0; j < 2 * NI; ++j) t.bj[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  return t;
+}
+
+template <int EPI, int MI, int NI>
+__device__ __forceinline__ TileInit<EPI, MI, NI> tile_init(const Problem& P, int64_t n0) {
+  constexpr bool dual = EPI == E_SWIGLU;
+  TileInit<EPI, MI, NI> t;
+  const int tid = tid_opaque(), lane = tid & 63, wn = (tid >> 6) & 1, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 2 * NI; ++j) {
+    t.bj[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* b = static_cast<const uint16_t*>(dual && j >= 4 ? P.bias2 : P.bias);
+    const int64_t col = n0 + (dual ? 64 * wn + 16 * (j & 3) : 32 * NI * wn + 16 * j) + 4 * g;
+    if (b && col < P.N) {
+      const uint2 w = *reinterpret_cast<const uint2*>(b + col);
+      t.bj[j] = f32x4{bf2f((uint16_t)(w.x & 0xffffu)), bf2f((uint16_t)(w.x >> 16)), bf2f((uint16_t)(w.y & 0xffffu)),
+                      bf2f((uint16_t)(w.y >> 16))};
+    }
+  }
+  return t;
+}
+
 // The fused store epilogues of the GEMM kernels (the default of tile_loop).
 template <int EPI, int MI, int NI>
 struct StoreEpilogue {
@@ -1111,6 +1155,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
   const int stride = strided ? G : 1;
   if (ta >= tb) return;
   constexpr bool DUAL = LAYOUT == L_NN && EPI == E_SWIGLU;
+  const bool any_bias = L.p[0].bias || L.p[0].bias2 || (L.nprob > 1 && (L.p[1].bias || L.p[1].bias2));
   Pipe<LAYOUT, DUAL, SEG2, MI, NI> pipe;
   pipe.init_wave();
   int tile = ta;
@@ -1132,7 +1177,19 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
       pipe.no_next();
     }
     f32x4 acc[2 * MI][2 * NI];
-    pipe.template run_tile<TM>(acc, zero_acc<MI, NI>);
+    if constexpr (LAYOUT == L_NN && EPI != E_CE_GRAD) {   // only column-parallel forwards take a bias
+      // (One run_tile call: each call site inlines its own copy of the K loop.)
+      TileInit<EPI, MI, NI> init = tile_init<EPI, MI, NI>();
+      if (any_bias) {
+        Problem P;
+        int64_t m0, n0;
+        locate_mi<MI, NI>(L, tile, EPI, P, m0, n0);
+        init = tile_init<EPI, MI, NI>(P, n0);
+      }
+      pipe.template run_tile<TM>(acc, init);
+    } else {
+      pipe.template run_tile<TM>(acc, zero_acc<MI, NI>);
+    }
     {
       Problem P;
       int64_t m0, n0;
@@ -1156,8 +1213,8 @@ __device__ __forceinline__ int wg_index(int& xcd) {
 
 // Fast kernels: one per (operand layout, epilogue, K segments), so each role
 // of the shard path is a distinct kernel in traces.  Tiles overhanging the
-// matrix are masked at the stores (rows; columns in 8-wide chunks); no
-// bias, aligned outputs; one workgroup per CU.  Starting the K loops of the
+// matrix are masked at the stores (rows; columns in 8-wide chunks);
+// aligned outputs; one workgroup per CU.  Starting the K loops of the
 // XCDs at different points keeps the workgroups of one XCD in step (their
 // shared operand panels stay in its L2).
 template <int LAYOUT, int EPI, bool SEG2, int MI, int NI = 4>
@@ -1409,11 +1466,13 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// The tiles of this problem may take the fast kernel (no bias, 16-byte
-// aligned outputs, K-contiguous operands ending on a 32-deep stage: the fast
-// kernels carry no K-tail code).
+// The tiles of this problem may take the fast kernel (16-byte aligned
+// outputs and, with a bias, an NN product with 8-byte aligned bias vectors;
+// K-contiguous operands ending on a 32-deep stage: the fast kernels carry no
+// K-tail code).
 bool fast_ok(const Problem& P) {
-  if (P.bias || P.bias2) return false;
+  if ((P.bias || P.bias2) && (P.layout != L_NN || P.epi == E_CE_GRAD)) return false;
+  if ((reinterpret_cast<uintptr_t>(P.bias) & 7) || (reinterpret_cast<uintptr_t>(P.bias2) & 7)) return false;
   for (int i = 0; i < P.nseg; ++i)
     if (P.layout != L_TN && P.seg[i].K % BK != 0) return false;
   if (!aligned16(P.c) || (P.ldc & 7)) return false;
@@ -1478,6 +1537,37 @@ int64_t dual_split(int64_t t0, int64_t s0, int64_t t1, int64_t s1, int cus, int&
   return best;
 }
 
+// Tile pairings of the one-launch row backward: (MI, NI) of problem 0, then of problem 1.
+constexpr int kGeo[3][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}};
+
+int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1) {
+  if (!(L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
+        L.p[1].epi == E_STORE && L.p[0].nseg == 1 && L.p[1].nseg == 1 && fast_ok(L.p[0]) && fast_ok(L.p[1]) &&
+        (L.p[0].N & 7) == 0 && (L.p[1].N & 7) == 0 && cus % 8 == 0))
+    return -1;
+  const int64_t s0 = tile_stages(L.p[0]), s1 = tile_stages(L.p[1]);
+  const int64_t n0 = tiles_of(L.p[0], 4, 4), n1 = tiles_of(L.p[1], 4, 4);
+  const int64_t apart = ((n0 + cus - 1) / cus * s0 + (n1 + cus - 1) / cus * s1) * 18;   // one after the other
+  int best = -1;
+  int64_t best_cost = apart;
+  for (int c = 0; c < 3; ++c) {
+    const int64_t a = tiles_of(L.p[0], kGeo[c][0], kGeo[c][1]);
+    const int64_t b = tiles_of(L.p[1], kGeo[c][2], kGeo[c][3]);
+    if (a + b >= INT_MAX) continue;
+    int g = 1;
+    const int64_t w0 = s0 * (kGeo[c][0] * kGeo[c][1] + 2), w1 = s1 * (kGeo[c][2] * kGeo[c][3] + 2);
+    const int64_t m = dual_split(a, w0, b, w1, cus, g);
+    if (m < best_cost) {
+      best_cost = m;
+      best = c;
+      g0 = g;
+      t0 = a;
+      t1 = b;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   int dev = 0, cus = 256;
   {
@@ -1499,30 +1589,10 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   // launches.  (128 x 256 input-gradient tiles beside 192 x 256 balance the
   // first case too but ran slower: a stage's barrier and copies then serve
   // half the MFMAs.)
-  if (L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
-      L.p[1].epi == E_STORE && L.p[0].nseg == 1 && L.p[1].nseg == 1 && fast_ok(L.p[0]) && fast_ok(L.p[1]) &&
-      (L.p[0].N & 7) == 0 && (L.p[1].N & 7) == 0 && cus % 8 == 0) {
-    static constexpr int kGeo[3][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}};   // (MI, NI) of problem 0, 1
-    const int64_t s0 = tile_stages(L.p[0]), s1 = tile_stages(L.p[1]);
-    const int64_t n0 = tiles_of(L.p[0], 4, 4), n1 = tiles_of(L.p[1], 4, 4);
-    const int64_t apart = ((n0 + cus - 1) / cus * s0 + (n1 + cus - 1) / cus * s1) * 18;   // one after the other
-    int best = -1, g0 = 1;
-    int64_t best_cost = apart, t0 = 0, t1 = 0;
-    for (int c = 0; c < 3; ++c) {
-      const int64_t a = tiles_of(L.p[0], kGeo[c][0], kGeo[c][1]);
-      const int64_t b = tiles_of(L.p[1], kGeo[c][2], kGeo[c][3]);
-      if (a + b >= INT_MAX) continue;
-      int g = 1;
-      const int64_t w0 = s0 * (kGeo[c][0] * kGeo[c][1] + 2), w1 = s1 * (kGeo[c][2] * kGeo[c][3] + 2);
-      const int64_t m = dual_split(a, w0, b, w1, cus, g);
-      if (m < best_cost) {
-        best_cost = m;
-        best = c;
-        g0 = g;
-        t0 = a;
-        t1 = b;
-      }
-    }
+  {
+    int g0 = 1;
+    int64_t t0 = 0, t1 = 0;
+    const int best = dual_plan(L, cus, g0, t0, t1);
     if (best >= 0) {
       GemmLaunch D = L;
       for (int i = 0; i < 2; ++i) {

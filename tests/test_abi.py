@@ -159,6 +159,17 @@ def test_ce_noalloc_validation(lib):
     assert _rc("tp_vocab_ce_partials_noalloc", *a) == 6
 
 
+def test_row_bwd_plan(lib):
+    # The one-launch row backward's tile pairing, host-only (library order: dZ [M, N], X_i [M, K]).
+    assert tp.tp_row_bwd_plan(8192, 4096, 1536, 256) == 1    # the MLP shard step: 192x256 + 256x192
+    assert tp.tp_row_bwd_plan(768, 768, 8192, 256) == 0      # 256x256 + 256x256
+    assert tp.tp_row_bwd_plan(512, 512, 8192, 256) == 1
+    assert tp.tp_row_bwd_plan(2048, 768, 1024, 256) == 2     # 192x192 + 128x192
+    assert tp.tp_row_bwd_plan(4096, 8192, 8192, 256) == -1   # separate launches
+    assert tp.tp_row_bwd_plan(8192, 4096, 1536, 100) == -1   # CUs not a multiple of 8: no shared launch
+    assert tp.tp_row_bwd_plan(0, 1, 1, 256) == -2 and tp.tp_row_bwd_plan(1, 1, 1, 0) == -2
+
+
 def test_ce_combine_validation(lib):
     def call(R=8, M=64, ms=P, ss=P, ts=P, stride=64, lse=P, tgt=P, loss=P):
         return _rc("tp_vocab_ce_combine", R, M, ms, ss, ts, stride, lse, tgt, loss, None)

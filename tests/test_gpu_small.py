@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 ops = pytest.importorskip("tensor_transformer_linear_tp_amd.torch_ops")
+tp = pytest.importorskip("tensor_transformer_linear_tp_amd")
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 DTYPES = [syn.FP32, syn.BF16]
@@ -145,24 +146,56 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
 
 
 # Whole tiles only (the persistent whole-tile kernels; for the row backward,
-# its two GEMMs share one launch).  (768, 512, 256): 256 x 256 tiles for both
-# GEMMs; (512, 256, 768) and (2048, 1024, 768): 192 x 256 weight-gradient
-# tiles beside 256 x 192 input-gradient tiles.
+# its two GEMMs share one launch).  On 256 CUs all three take the 192 x 192
+# weight-gradient tiles beside 128 x 192 input-gradient tiles
+# (tp_row_bwd_plan); test_row_bwd_whole_matrix_pairings covers the other two
+# pairings.
 TILE_SHAPES = [(512, 256, 768), (768, 512, 256), (2048, 1024, 768)]
 
 
 @pytest.mark.parametrize("act", ["none", "gelu", "swiglu"])
-def test_column_fwd_half_tile_tail_round(act):
-    # 17 x 17 = 289 whole tiles on 256 CUs: the last 33 run as 128-row halves.
+@pytest.mark.parametrize("bias", [False, True])
+def test_column_fwd_half_tile_tail_round(act, bias):
+    # 17 x 17 = 289 whole tiles on 256 CUs: the last 33 run as 128-row halves
+    # (with a bias: the fast kernels start those tiles' accumulators at it).
     M, K = 17 * 256, 64
     N = 17 * (128 if act == "swiglu" else 256)
     dtype = syn.BF16
-    d = _inputs(dtype, M, N, K, 5, act)
-    Y, Pre = ops.column_fwd(dev(d["X"]), dev(d["A"]), act, A2=dev(d["A2"]) if act == "swiglu" else None)
+    d = _inputs(dtype, M, N, K, 5 + int(bias), act)
+    b2 = d["b2"] if (bias and act == "swiglu") else None
+    Y, Pre = ops.column_fwd(dev(d["X"]), dev(d["A"]), act, A2=dev(d["A2"]) if act == "swiglu" else None,
+                            bias=dev(d["b"]) if bias else None, bias2=dev(b2) if b2 is not None else None)
     torch.cuda.synchronize()
-    Yr, Prer = oracle.column_fwd(d["X"].f64, d["A"].f64, act, A2=d["A2"].f64 if act == "swiglu" else None)
+    Yr, Prer = oracle.column_fwd(d["X"].f64, d["A"].f64, act, bias=d["b"].f64 if bias else None,
+                                 A2=d["A2"].f64 if act == "swiglu" else None,
+                                 bias2=b2.f64 if b2 is not None else None)
     assert_close("Y", host64(Y), Yr, TOL[dtype])
     if act != "none":
+        assert_close("Pre", host64(Pre), Prer, TOL[dtype])
+
+
+# Biases on the fast kernels (K a multiple of 32, 16-byte aligned outputs):
+# (512, 512, 256) whole tiles; (300, 200, 64) tiles overhanging rows and
+# columns (N a multiple of 8: a lane's bias columns past N start at zero);
+# (2048, 768, 256) with no activation takes 128 x 192 tiles.  "up": SwiGLU
+# with only the up-projection bias.
+@pytest.mark.parametrize("act", ["none", "gelu", "swiglu", "up"])
+@pytest.mark.parametrize("shape", [(512, 512, 256), (300, 200, 64), (2048, 768, 256)])
+def test_column_fwd_bias_fast_kernels(act, shape):
+    M, N, K = shape
+    dtype = syn.BF16
+    kind = "swiglu" if act == "up" else act
+    d = _inputs(dtype, M, N, K, 3 * M + N + ["none", "gelu", "swiglu", "up"].index(act), kind)
+    b = None if act == "up" else d["b"]
+    b2 = d["b2"] if kind == "swiglu" else None
+    Y, Pre = ops.column_fwd(dev(d["X"]), dev(d["A"]), kind, A2=dev(d["A2"]) if kind == "swiglu" else None,
+                            bias=dev(b) if b is not None else None, bias2=dev(b2) if b2 is not None else None)
+    torch.cuda.synchronize()
+    Yr, Prer = oracle.column_fwd(d["X"].f64, d["A"].f64, kind, bias=b.f64 if b is not None else None,
+                                 A2=d["A2"].f64 if kind == "swiglu" else None,
+                                 bias2=b2.f64 if b2 is not None else None)
+    assert_close("Y", host64(Y), Yr, TOL[dtype])
+    if kind != "none":
         assert_close("Pre", host64(Pre), Prer, TOL[dtype])
 
 
@@ -184,6 +217,28 @@ def test_row_bwd_whole_tiles(shape):
     M, N, K = shape
     dtype = syn.BF16
     d = _inputs(dtype, M, N, K, 11 + M, "none")
+    Xi, Bi = dev(d["dY"]), dev(d["B"])
+    dX, dB, _ = ops.row_bwd(dev(d["dZ"]), Xi, Bi)
+    torch.cuda.synchronize()
+    rdX, rdB, _ = oracle.row_bwd(d["dZ"].f64, d["dY"].f64, d["B"].f64)
+    assert_close("dX", host64(dX), rdX, TOL[dtype])
+    assert_close("dB", host64(dB), rdB, TOL[dtype])
+
+
+# Whole-matrix checks of the one-launch row backward in its two large-tile
+# pairings (shapes in this file's order: X_i [M, N], B_i [N, K], dZ [M, K]):
+# (768, 8192, 768) takes 256 x 256 tiles for both GEMMs and (512, 8192, 512)
+# 192 x 256 weight-gradient tiles beside 256 x 192 input-gradient tiles (the
+# pairing of the MLP shard step's row backward), on 256 CUs.
+@pytest.mark.parametrize("shape,pairing", [((768, 8192, 768), 0), ((512, 8192, 512), 1)])
+def test_row_bwd_whole_matrix_pairings(shape, pairing):
+    M, N, K = shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = tp.tp_row_bwd_plan(M, K, N, cus)   # the library's (M, N, K): dZ [M, K], X_i [M, N]
+    if cus == 256:
+        assert plan == pairing, (plan, pairing)
+    dtype = syn.BF16
+    d = _inputs(dtype, M, N, K, 41 + pairing, "none")
     Xi, Bi = dev(d["dY"]), dev(d["B"])
     dX, dB, _ = ops.row_bwd(dev(d["dZ"]), Xi, Bi)
     torch.cuda.synchronize()
