@@ -40,6 +40,17 @@ extern "C" {
  */
 TPC_API int tpc_mfma_loop(const void* src, float* out, int cus, int iters, int shape, void* stream);
 
+/*
+ * Shader clock probe: `blocks` workgroups of one wave64 each read the shader
+ * cycle counter and the 100 MHz real-time counter, run `spin` dependent
+ * integer steps, and read both again.  out: device uint64 [2 * blocks]:
+ * (cycles, real-time ticks) elapsed per workgroup; cycles / ticks * 100 is
+ * the clock in MHz.  Returns 0, -1 for a NULL pointer, blocks < 1 or
+ * spin < 1 (nothing launched), else the hipError_t of the launch.
+ * Asynchronous on `stream` (NULL = default).
+ */
+TPC_API int tpc_clock_probe(unsigned long long* out, int blocks, int spin, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -94,6 +94,33 @@ __global__ __launch_bounds__(256, 1) void mfma16_loop_kernel(const bf16x8* __res
 
 }  // namespace
 
+// Shader clock probe: one wave per workgroup reads the shader cycle counter
+// (s_memtime) and the 100 MHz real-time counter (s_memrealtime), runs `spin`
+// dependent integer steps, and reads both again; lane 0 writes the two
+// differences.  The ratio times 100 MHz is the clock the wave ran at.
+__global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long* out, int spin) {
+  const unsigned long long c0 = __builtin_readcyclecounter();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  unsigned x = threadIdx.x;
+  for (int i = 0; i < spin; ++i) {
+    x = x * 3u + 1u;
+    asm volatile("" : "+v"(x));
+  }
+  const unsigned long long c1 = __builtin_readcyclecounter();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  asm volatile("" ::"v"(x));
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+extern "C" int tpc_clock_probe(unsigned long long* out, int blocks, int spin, void* stream) {
+  if (!out || blocks < 1 || spin < 1) return -1;
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(blocks), dim3(64), 0, static_cast<hipStream_t>(stream), out, spin);
+  return (int)hipGetLastError();
+}
+
 extern "C" int tpc_mfma_loop(const void* src, float* out, int cus, int iters, int shape, void* stream) {
   if (!src || !out || iters < 1 || cus < 1 || (shape != 32 && shape != 16)) return -1;
   if (shape == 32)

@@ -43,9 +43,13 @@ constexpr int GROUP_M = 8;                    // tile rows per L2 group
 
 // ---- LDS address maps ------------------------------------------------------
 // K-contiguous [256][32]: 64-byte rows of 4 chunks of 16 bytes; chunk c of row
-// r sits at c ^ kc_swz(r), which spreads any 16 consecutive rows reading the
-// same logical chunk over all 16 chunk slots of a 256-byte bank cycle.
-__device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// r sits at c ^ kc_swz(r), kc_swz(r) = (r / 2) mod 4.  A fragment read of
+// v_mfma_f32_16x16x32_bf16 (ds_read_b128, lane l: row l % 16 of a 16-row
+// block, chunk l / 16) with this map measured free of LDS bank conflicts on
+// gfx950, like a contiguous read; the map tuned for 32 x 32 fragments (an
+// extra flip of chunk bit 0 on rows 8-15) and three other candidates paid
+// 0.8 conflict cycles per read.
+__device__ __forceinline__ int kc_swz(int r) { return (r >> 1) & 3; }
 __device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ kc_swz(r)) << 4); }
 // MN-contiguous [32][W]: rows of W bf16 (512 or 256 bytes); row k XORs the
 // chunk index with 2 * ((k & 3) | (k & 8) >> 1): a transposing fragment read
