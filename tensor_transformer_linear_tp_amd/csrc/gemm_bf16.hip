@@ -250,17 +250,18 @@ struct TileStreams {
   int tail;                // a K-contiguous operand's segment ends inside a stage (K % 32 != 0)
 };
 
-// MI, NI: 32 x 32 MFMA blocks per wave along M and N; the tile is
-// (64 MI) x (64 NI).  MI = 4, 3 or 2 (2: K-contiguous A only), NI = 4 or 3
-// (SwiGLU: 4).  A K-contiguous operand of 64 MI rows is copied as MI blocks
-// of 16 rows per wave; an MN-contiguous one always fills the 256-wide LDS
-// layout (192-wide tiles leave its last 64 columns zero).
+// MI, NI: 32-row / 32-column units per wave along M and N (2 x 2 blocks of
+// 16 x 16 each); the tile is (64 MI) x (64 NI), MI, NI in {2, 3, 4} (SwiGLU:
+// NI = 4).  A K-contiguous operand of 64 MI rows is copied as MI blocks of 16
+// rows per wave; an MN-contiguous one always fills the 256-wide LDS layout
+// (narrower tiles leave its last columns zero: the lanes of those chunks are
+// sent past the range).
 template <int LAYOUT, bool DUAL, bool SEG2, int MI = 4, int NI = 4>
 struct Pipe {
   static constexpr bool A_KC = LAYOUT != L_TN;
   static constexpr bool B_KC = LAYOUT == L_NT;
-  static_assert(MI == 4 || MI == 3 || (MI == 2 && A_KC), "128-row tiles need a K-contiguous A");
-  static_assert(NI == 4 || (NI == 3 && !DUAL), "tile widths: 256, or 192 without the SwiGLU pairing");
+  static_assert(MI >= 2 && MI <= 4, "tile heights: 128, 192 or 256");
+  static_assert(NI >= 2 && NI <= 4 && (NI == 4 || !DUAL), "tile widths: 128, 192 or 256 (SwiGLU: 256)");
   static constexpr int NBA = A_KC ? MI : DMA_PER_OPERAND;   // A copies per wave per stage
   static constexpr int NBB = B_KC ? NI : DMA_PER_OPERAND;   // B copies per wave per stage
   static constexpr int NCOPY = NBA + NBB;                   // copies per wave per stage
@@ -1542,7 +1543,8 @@ int64_t dual_split(int64_t t0, int64_t s0, int64_t t1, int64_t s1, int cus, int&
 }
 
 // Tile pairings of the one-launch row backward: (MI, NI) of problem 0, then of problem 1.
-constexpr int kGeo[3][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}};
+constexpr int kGeoN = 5;
+constexpr int kGeo[kGeoN][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}, {2, 2, 2, 3}, {2, 2, 4, 4}};
 
 int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1) {
   if (!(L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
@@ -1554,7 +1556,7 @@ int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1) {
   const int64_t apart = ((n0 + cus - 1) / cus * s0 + (n1 + cus - 1) / cus * s1) * 18;   // one after the other
   int best = -1;
   int64_t best_cost = apart;
-  for (int c = 0; c < 3; ++c) {
+  for (int c = 0; c < kGeoN; ++c) {
     const int64_t a = tiles_of(L.p[0], kGeo[c][0], kGeo[c][1]);
     const int64_t b = tiles_of(L.p[1], kGeo[c][2], kGeo[c][3]);
     if (a + b >= INT_MAX) continue;
@@ -1615,8 +1617,12 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT>), dim3(cus), dim3(NTHREADS), 0, s, D);
       else if (best == 1)
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 3, 4, 4, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
-      else
+      else if (best == 2)
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 3, 3, 2, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      else if (best == 3)
+        hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 2, 2, 2, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      else
+        hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 2, 2, 4, 4>), dim3(cus), dim3(NTHREADS), 0, s, D);
       return hipGetLastError();
     }
   }

@@ -146,10 +146,10 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
 
 
 # Whole tiles only (the persistent whole-tile kernels; for the row backward,
-# its two GEMMs share one launch).  On 256 CUs all three take the 192 x 192
-# weight-gradient tiles beside 128 x 192 input-gradient tiles
-# (tp_row_bwd_plan); test_row_bwd_whole_matrix_pairings covers the other two
-# pairings.
+# its two GEMMs share one launch).  On 256 CUs the row backward takes 192 x
+# 192 weight-gradient tiles beside 128 x 192 input-gradient tiles for the
+# first shape and 128 x 128 beside 128 x 192 for the other two
+# (tp_row_bwd_plan); test_row_bwd_whole_matrix_pairings asserts each pairing.
 TILE_SHAPES = [(512, 256, 768), (768, 512, 256), (2048, 1024, 768)]
 
 
@@ -225,12 +225,16 @@ def test_row_bwd_whole_tiles(shape):
     assert_close("dB", host64(dB), rdB, TOL[dtype])
 
 
-# Whole-matrix checks of the one-launch row backward in its two large-tile
-# pairings (shapes in this file's order: X_i [M, N], B_i [N, K], dZ [M, K]):
-# (768, 8192, 768) takes 256 x 256 tiles for both GEMMs and (512, 8192, 512)
-# 192 x 256 weight-gradient tiles beside 256 x 192 input-gradient tiles (the
-# pairing of the MLP shard step's row backward), on 256 CUs.
-@pytest.mark.parametrize("shape,pairing", [((768, 8192, 768), 0), ((512, 8192, 512), 1)])
+# Whole-matrix checks of the one-launch row backward in each of its tile
+# pairings (shapes in this file's order: X_i [M, N], B_i [N, K], dZ [M, K]),
+# on 256 CUs: (768, 8192, 768) takes 256 x 256 tiles for both GEMMs,
+# (512, 8192, 512) 192 x 256 weight-gradient tiles beside 256 x 192
+# input-gradient tiles (the pairing of the MLP shard step's row backward),
+# (512, 256, 768) 192 x 192 beside 128 x 192, (2048, 1024, 768) 128 x 128
+# beside 128 x 192 (the pairing of the attention output projection's
+# backward), (1536, 4096, 512) 128 x 128 beside 256 x 256.
+@pytest.mark.parametrize("shape,pairing", [((768, 8192, 768), 0), ((512, 8192, 512), 1), ((512, 256, 768), 2),
+                                           ((2048, 1024, 768), 3), ((1536, 4096, 512), 4)])
 def test_row_bwd_whole_matrix_pairings(shape, pairing):
     M, N, K = shape
     cus = torch.cuda.get_device_properties(0).multi_processor_count
