@@ -581,9 +581,9 @@ def test_attention_fwd_small(B, S, n_q, n_kv, causal):
 
 ATTN_BWD_CASES = [(1, 1, 1, 1, True), (1, 37, 4, 1, True), (1, 200, 4, 1, True), (1, 300, 2, 1, True),
                   (1, 130, 2, 2, False), (1, 256, 8, 1, True), (2, 100, 4, 1, True), (1, 1100, 4, 1, True),
-                  (1, 2200, 4, 1, True), (2, 700, 8, 2, False)]
+                  (1, 2200, 4, 1, True), (2, 700, 8, 2, False), (1, 2300, 4, 1, False)]
 # (beyond 1024 keys the dQ pass is cut into key chunks; beyond 2048 queries the dK/dV pass into
-# query chunks)
+# query chunks, whole chunks launched before the shorter last ones)
 
 
 @pytest.mark.parametrize("B,S,n_q,n_kv,causal", ATTN_BWD_CASES)
