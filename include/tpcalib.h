@@ -51,6 +51,24 @@ TPC_API int tpc_mfma_loop(const void* src, float* out, int cus, int iters, int s
  */
 TPC_API int tpc_clock_probe(unsigned long long* out, int blocks, int spin, void* stream);
 
+/*
+ * LDS read-rate probe: `cus` workgroups of `waves` (1..16) wave64s, each
+ * reading its workgroup's 64 KiB LDS array `iters` times 8 reads (8 in
+ * flight, the address moving every iteration), in one pattern:
+ *   kind 0: ds_read_b128, 16 bytes per lane, 1 KiB of consecutive bytes;
+ *   kind 1: ds_read_b64_tr_b16, 8 bytes per lane, 512 consecutive bytes;
+ *   kind 2: ds_read_b64_tr_b16 as the attention kernels read the columns of
+ *           a 256-byte-row tile (chunk c of row r at c ^ (4 (r % 4) +
+ *           (r / 4) % 4)).
+ * Bytes read per workgroup: waves * 64 * (16 or 8) * 8 * iters.  cycles:
+ * device uint64 [cus], shader cycles of each workgroup's read loop; out:
+ * device uint32 [cus * 64 * waves] checksums.  Returns 0, -1 for a NULL
+ * pointer or an argument out of range (nothing launched), else the
+ * hipError_t of the launch.  Asynchronous on `stream` (NULL = default).
+ */
+TPC_API int tpc_lds_read_rate(unsigned* out, unsigned long long* cycles, int cus, int waves, int iters, int kind,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

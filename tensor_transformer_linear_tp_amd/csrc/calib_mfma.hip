@@ -115,6 +115,70 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long* out
   }
 }
 
+// LDS read-rate probe: one workgroup of `waves` wave64s per CU reads its 64 KiB LDS array in
+// one access pattern, 8 reads in flight per wave, the address moving every iteration (so that
+// no read can be reused); lane 0 of the workgroup records the shader cycles of the read loop
+// and every thread writes a checksum.
+//   kind 0: ds_read_b128, lanes on 1 KiB of consecutive bytes (one pass of all banks per
+//           16 lanes);
+//   kind 1: ds_read_b64_tr_b16, lanes on 512 consecutive bytes;
+//   kind 2: ds_read_b64_tr_b16 in the column-fragment pattern of a 256-byte-row tile whose
+//           16-byte chunk c of row r sits at c ^ (4 (r % 4) + (r / 4) % 4) (the attention
+//           kernels' tiles read both ways), 32 columns x 16 rows per read pair.
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+__global__ __launch_bounds__(1024) void lds_rate_kernel(unsigned* out, unsigned long long* cycles, int iters,
+                                                        int kind) {
+  __shared__ __attribute__((aligned(16))) char lds[65536];
+  for (int i = threadIdx.x; i < 65536 / 4; i += blockDim.x) reinterpret_cast<unsigned*>(lds)[i] = i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int base = (wave * 8192) & 65535;
+  unsigned acc = 0;
+  const unsigned long long t0 = __builtin_readcyclecounter();
+  for (int it = 0; it < iters; ++it) {
+    const int mv = (it * 64) & 4095;
+    if (kind == 0) {
+      u32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = *reinterpret_cast<const u32x4*>(lds + ((base + j * 1024 + lane * 16 + mv) & 65535));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    } else {
+      i16x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int off;
+        if (kind == 1) {
+          off = j * 512 + lane * 8;
+        } else {
+          const int h = lane >> 4, q = lane & 15;
+          const int col = 32 * (j & 3) + 16 * (h & 1) + 4 * (q & 3);
+          const int r = 16 * (j >> 2) + 8 * (h >> 1) + (q >> 2) + 4 * (it & 1);
+          off = r * 256 + (((col >> 3) ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 4) + (col & 7) * 2;
+        }
+        v[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(lds + ((base + off + mv) & 65535)));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += (unsigned)(v[j].x ^ v[j].y ^ v[j].z ^ v[j].w);
+    }
+  }
+  __syncthreads();
+  const unsigned long long t1 = __builtin_readcyclecounter();
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+  if (threadIdx.x == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
+extern "C" int tpc_lds_read_rate(unsigned* out, unsigned long long* cycles, int cus, int waves, int iters, int kind,
+                                 void* stream) {
+  if (!out || !cycles || cus < 1 || waves < 1 || waves > 16 || iters < 1 || kind < 0 || kind > 2) return -1;
+  hipLaunchKernelGGL(lds_rate_kernel, dim3(cus), dim3(64 * waves), 0, static_cast<hipStream_t>(stream), out, cycles,
+                     iters, kind);
+  return (int)hipGetLastError();
+}
+
 extern "C" int tpc_clock_probe(unsigned long long* out, int blocks, int spin, void* stream) {
   if (!out || blocks < 1 || spin < 1) return -1;
   hipLaunchKernelGGL(clock_probe_kernel, dim3(blocks), dim3(64), 0, static_cast<hipStream_t>(stream), out, spin);

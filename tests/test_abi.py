@@ -47,7 +47,7 @@ def test_calibration_library_exports_its_header():
     declared = sorted(set(re.findall(r"^TPC_API\s+[\w\s\*]+?\b(tpc_\w+)\s*\(", src, flags=re.M)))
     out = subprocess.run(["nm", "-D", "--defined-only", build.CALIB_PATH], capture_output=True, text=True, check=True)
     exported = sorted(l.split()[-1] for l in out.stdout.splitlines() if " T " in l)
-    assert declared == exported == ["tpc_clock_probe", "tpc_mfma_loop"]
+    assert declared == exported == ["tpc_clock_probe", "tpc_lds_read_rate", "tpc_mfma_loop"]
     lib = ctypes.CDLL(build.CALIB_PATH)
     lib.tpc_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_void_p]
@@ -57,6 +57,12 @@ def test_calibration_library_exports_its_header():
     lib.tpc_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     assert lib.tpc_clock_probe(None, 256, 1000, None) == -1
     assert lib.tpc_clock_probe(P, 0, 1000, None) == -1 and lib.tpc_clock_probe(P, 256, 0, None) == -1
+    lib.tpc_lds_read_rate.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    assert lib.tpc_lds_read_rate(None, P, 256, 8, 10, 0, None) == -1
+    assert lib.tpc_lds_read_rate(P, None, 256, 8, 10, 0, None) == -1
+    assert lib.tpc_lds_read_rate(P, P, 256, 17, 10, 0, None) == -1     # at most 16 waves
+    assert lib.tpc_lds_read_rate(P, P, 256, 8, 10, 3, None) == -1      # kinds 0..2
+    assert lib.tpc_lds_read_rate(P, P, 0, 8, 10, 0, None) == -1 and lib.tpc_lds_read_rate(P, P, 256, 8, 0, 0, None) == -1
 
 
 def test_version_and_status_strings(lib):
