@@ -159,8 +159,9 @@ TP_API size_t tp_row_bwd_workspace_bytes(int dtype, int64_t M, int64_t N);
  * only: no GPU call, no allocation.  Returns 0 (256x256 weight-gradient tiles
  * beside 256x256 input-gradient tiles), 1 (192x256 beside 256x192), 2
  * (192x192 beside 128x192), 3 (128x128 beside 128x192), 4 (128x128 beside
- * 256x256), -1 (the two GEMMs run as separate launches), or -2 for sizes
- * tp_row_bwd rejects or cus < 1.
+ * 256x256), 5 (128x192 beside 256x192), 6 (128x192 beside 128x192), -1 (the
+ * two GEMMs run as separate launches), or -2 for sizes tp_row_bwd rejects or
+ * cus < 1.
  */
 TP_API int tp_row_bwd_plan(int64_t M, int64_t N, int64_t K, int cus);
 

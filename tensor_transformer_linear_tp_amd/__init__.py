@@ -167,7 +167,7 @@ def tp_row_bwd_workspace_bytes(dtype, M, N) -> int:
 def tp_row_bwd_plan(M, N, K, cus) -> int:
     """Tile pairing of tp_row_bwd's one-launch schedule (host-only query): 0 = 256x256 + 256x256,
     1 = 192x256 + 256x192, 2 = 192x192 + 128x192, 3 = 128x128 + 128x192, 4 = 128x128 + 256x256,
-    -1 = separate launches, -2 = invalid sizes."""
+    5 = 128x192 + 256x192, 6 = 128x192 + 128x192, -1 = separate launches, -2 = invalid sizes."""
     return _load().tp_row_bwd_plan(M, N, K, cus)
 
 

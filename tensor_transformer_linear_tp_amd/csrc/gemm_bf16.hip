@@ -1543,8 +1543,9 @@ int64_t dual_split(int64_t t0, int64_t s0, int64_t t1, int64_t s1, int cus, int&
 }
 
 // Tile pairings of the one-launch row backward: (MI, NI) of problem 0, then of problem 1.
-constexpr int kGeoN = 5;
-constexpr int kGeo[kGeoN][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}, {2, 2, 2, 3}, {2, 2, 4, 4}};
+constexpr int kGeoN = 7;
+constexpr int kGeo[kGeoN][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}, {2, 2, 2, 3},
+                                {2, 2, 4, 4}, {2, 3, 4, 3}, {2, 3, 2, 3}};
 
 int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1) {
   if (!(L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
@@ -1563,7 +1564,11 @@ int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1) {
     int g = 1;
     const int64_t w0 = s0 * (kGeo[c][0] * kGeo[c][1] + 2), w1 = s1 * (kGeo[c][2] * kGeo[c][3] + 2);
     const int64_t m = dual_split(a, w0, b, w1, cus, g);
-    if (m < best_cost) {
+    // equal cost: the pairing with the larger tiles (the model's per-stage cost favours small
+    // tiles, which copy the full 256-wide MN-contiguous panels and measure slower)
+    const bool larger = best >= 0 && kGeo[c][0] * kGeo[c][1] + kGeo[c][2] * kGeo[c][3] >
+                                         kGeo[best][0] * kGeo[best][1] + kGeo[best][2] * kGeo[best][3];
+    if (m < best_cost || (m == best_cost && larger)) {
       best_cost = m;
       best = c;
       g0 = g;
@@ -1621,8 +1626,12 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 3, 3, 2, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
       else if (best == 3)
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 2, 2, 2, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
-      else
+      else if (best == 4)
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 2, 2, 4, 4>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      else if (best == 5)
+        hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 2, 3, 4, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      else
+        hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 2, 3, 2, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
       return hipGetLastError();
     }
   }

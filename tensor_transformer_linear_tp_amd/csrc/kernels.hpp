@@ -203,8 +203,9 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s);
 // The one-launch schedule of a (TN weight gradient, NT input gradient) pair
 // on `cus` CUs: its tile pairing (0: 256x256 + 256x256, 1: 192x256 +
 // 256x192, 2: 192x192 + 128x192, 3: 128x128 + 128x192, 4: 128x128 +
-// 256x256) with the workgroups of problem 0 and each problem's tile count,
-// or -1 when the two run as separate launches.
+// 256x256, 5: 128x192 + 256x192, 6: 128x192 + 128x192) with the workgroups
+// of problem 0 and each problem's tile count, or -1 when the two run as
+// separate launches.
 // Host-only.
 int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1);
 hipError_t launch_gemm_f32(GemmLaunch& L, hipStream_t s);

@@ -174,8 +174,11 @@ def test_row_bwd_plan(lib):
     assert tp.tp_row_bwd_plan(768, 768, 8192, 256) == 0      # 256x256 + 256x256
     assert tp.tp_row_bwd_plan(512, 512, 8192, 256) == 1
     assert tp.tp_row_bwd_plan(512, 768, 256, 256) == 2       # 192x192 + 128x192
-    assert tp.tp_row_bwd_plan(8192, 4096, 512, 256) == 3     # the attention output projection: 128x128 + 128x192
+    assert tp.tp_row_bwd_plan(2048, 768, 1024, 256) == 3     # 128x128 + 128x192
     assert tp.tp_row_bwd_plan(1536, 512, 4096, 256) == 4     # 128x128 + 256x256
+    assert tp.tp_row_bwd_plan(8192, 4096, 512, 256) == 5     # the attention output projection: 128x192 + 256x192
+    assert tp.tp_row_bwd_plan(8192, 768, 4096, 256) == 5     # the QKV projection's backward (same structure)
+    assert tp.tp_row_bwd_plan(256, 256, 128, 256) == 6       # 128x192 + 128x192
     assert tp.tp_row_bwd_plan(4096, 8192, 8192, 256) == -1   # separate launches
     assert tp.tp_row_bwd_plan(8192, 4096, 1536, 100) == -1   # CUs not a multiple of 8: no shared launch
     assert tp.tp_row_bwd_plan(0, 1, 1, 256) == -2 and tp.tp_row_bwd_plan(1, 1, 1, 0) == -2

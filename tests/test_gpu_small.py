@@ -148,8 +148,9 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
 # Whole tiles only (the persistent whole-tile kernels; for the row backward,
 # its two GEMMs share one launch).  On 256 CUs the row backward takes 192 x
 # 192 weight-gradient tiles beside 128 x 192 input-gradient tiles for the
-# first shape and 128 x 128 beside 128 x 192 for the other two
-# (tp_row_bwd_plan); test_row_bwd_whole_matrix_pairings asserts each pairing.
+# first shape, 128 x 128 beside 256 x 256 for the second and 128 x 128 beside
+# 128 x 192 for the third (tp_row_bwd_plan); test_row_bwd_whole_matrix_pairings
+# asserts each pairing.
 TILE_SHAPES = [(512, 256, 768), (768, 512, 256), (2048, 1024, 768)]
 
 
@@ -231,10 +232,12 @@ def test_row_bwd_whole_tiles(shape):
 # (512, 8192, 512) 192 x 256 weight-gradient tiles beside 256 x 192
 # input-gradient tiles (the pairing of the MLP shard step's row backward),
 # (512, 256, 768) 192 x 192 beside 128 x 192, (2048, 1024, 768) 128 x 128
-# beside 128 x 192 (the pairing of the attention output projection's
-# backward), (1536, 4096, 512) 128 x 128 beside 256 x 256.
+# beside 128 x 192, (1536, 4096, 512) 128 x 128 beside 256 x 256,
+# (1024, 4096, 512) 128 x 192 beside 256 x 192 (the pairing of the attention
+# projections' backwards), (256, 128, 256) 128 x 192 beside 128 x 192.
 @pytest.mark.parametrize("shape,pairing", [((768, 8192, 768), 0), ((512, 8192, 512), 1), ((512, 256, 768), 2),
-                                           ((2048, 1024, 768), 3), ((1536, 4096, 512), 4)])
+                                           ((2048, 1024, 768), 3), ((1536, 4096, 512), 4), ((1024, 4096, 512), 5),
+                                           ((256, 128, 256), 6)])
 def test_row_bwd_whole_matrix_pairings(shape, pairing):
     M, N, K = shape
     cus = torch.cuda.get_device_properties(0).multi_processor_count
