@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "attention_common.hpp"
+#include "attention_order.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -255,49 +256,8 @@ __device__ __forceinline__ int query_tiles(const AttnArgs& a, int64_t kbk) {
   return (int)((a.S - kv_q_begin(a, kbk) + QT - 1) / QT);
 }
 
-// Work items of the dK/dV pass (key block, query chunk, query head) in launch
-// order, longest first: the hardware hands workgroups out in index order, so
-// the short items fill in at the end.  Key block k has T(k) = ceil((S - 128 k)
-// / 32) query tiles when causal (T0 - 4 k, T0 = ceil(S / 32)), else T0; its
-// chunks of ct tiles come first, chunk-major (chunk c holds the key blocks
-// with T(k) >= (c + 1) ct, a prefix of them), then the last, shorter chunks,
-// longest first: the blocks with T(k) mod ct = v are, when causal, those with
-// k = (T0 - v) / 4 mod ct / 4, for v = T0 mod 4 (mod 4) only.  The query head
-// varies fastest.  Returns false past the last item.
-struct KvItem {
-  int64_t kbk;
-  int chunk, h;
-};
-__host__ __device__ inline bool kv_item(int64_t S, bool causal, int n_q, int ct, int64_t id, KvItem& it) {
-  const int64_t T0 = (S + QT - 1) / QT, nkb = (S + 127) / 128;
-  for (int c = 0;; ++c) {   // whole chunks
-    const int64_t need = (int64_t)(c + 1) * ct;
-    const int64_t cnt = T0 < need ? 0 : causal && (T0 - need) / 4 + 1 < nkb ? (T0 - need) / 4 + 1 : nkb;
-    if (cnt == 0) break;
-    if (id < cnt * n_q) {
-      it.kbk = id / n_q;
-      it.chunk = c;
-      it.h = (int)(id % n_q);
-      return true;
-    }
-    id -= cnt * n_q;
-  }
-  const int per = ct / 4;   // causal: key blocks per period of T(k) mod ct
-  for (int v = causal ? ct - 4 + (int)(T0 % 4) : (int)(T0 % ct); v > 0; v -= causal ? 4 : ct) {
-    if (v >= ct || v > T0) continue;
-    const int64_t k0 = causal ? ((T0 - v) / 4) % per : 0;
-    const int64_t step = causal ? per : 1;
-    const int64_t cnt = k0 < nkb ? (nkb - 1 - k0) / step + 1 : 0;
-    if (id < cnt * n_q) {
-      it.kbk = k0 + step * (id / n_q);
-      it.chunk = (int)((causal ? T0 - 4 * it.kbk : T0) / ct);
-      it.h = (int)(id % n_q);
-      return true;
-    }
-    id -= cnt * n_q;
-  }
-  return false;
-}
+using attn_order::KvItem;
+using attn_order::kv_item;
 
 __device__ __forceinline__ float* kv_slot(const AttnBwdArgs& p, int64_t b, int g, int64_t kbk, int hg, int chunk) {
   const AttnArgs& a = p.f;
@@ -588,14 +548,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_combine_kernel(const AttnBwd
 // 2048 queries (64 tiles) per workgroup.
 constexpr int KV_CHUNK_TILES = 64;
 static_assert(KV_CHUNK_TILES % 4 == 0, "the causal item order steps query tiles by 4 per key block");
+static_assert(attn_order::kQT == QT, "the item order counts the pass's query tiles");
 
-// Number of dK/dV work items of one sequence (all query heads).
-int64_t kv_items(int64_t S, int causal, int n_q) {
-  const int64_t T0 = (S + QT - 1) / QT, nkb = (S + 127) / 128;
-  int64_t n = 0;
-  for (int64_t k = 0; k < nkb; ++k) n += ((causal ? T0 - 4 * k : T0) + KV_CHUNK_TILES - 1) / KV_CHUNK_TILES;
-  return n * n_q;
-}
 
 void attn_bwd_layout(int64_t B, int64_t S, int n_q, int n_kv, int causal, AttnBwdLayout& L) {
   attn_chunking(B, S, n_q, n_kv, causal, L.chunk_tiles, L.max_chunks);
@@ -626,8 +580,8 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)(nqb * a.max_chunks), gy, (unsigned)a.B), dim3(256), 0, s, p);
   if (a.max_chunks > 1)
     hipLaunchKernelGGL(attn_bwd_dq_combine_kernel, dim3((unsigned)(nqb * 16), gy, (unsigned)a.B), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)kv_items(a.S, a.causal, a.n_q), 1, (unsigned)a.B),
-                     dim3(256), 0, s, p);
+  const int64_t items = attn_order::kv_items(a.S, a.causal != 0, a.n_q, KV_CHUNK_TILES);
+  hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)items, 1, (unsigned)a.B), dim3(256), 0, s, p);
   hipLaunchKernelGGL(attn_bwd_dkv_combine_kernel, dim3((unsigned)(nkb * 32), (unsigned)a.n_kv, (unsigned)a.B),
                      dim3(256), 0, s, p);
   return hipGetLastError();
