@@ -143,6 +143,16 @@ TP_API tp_status tp_sum_partials(int dtype, int t, int64_t M, int64_t N,
  *   dbias = sum_m dZ      fp32-accumulated, dtype out, [N]     (nullable: skipped)
  * dbias is the gradient of the replicated row bias; it needs a workspace of
  * tp_row_bwd_workspace_bytes() bytes (workspace may be NULL when dbias is NULL).
+ *
+ * Split contractions (bf16, dXi and dBi both requested): workspace bytes past
+ * tp_row_bwd_workspace_bytes(dtype, M, N) -- whether or not dbias is asked
+ * for -- are scratch that lets the one-launch schedule cut a long contraction
+ * into 2 or 4 parts (fp32 partial products [parts][rows][cols], then a second
+ * kernel sums them in ascending part order and rounds once to bf16).  It is
+ * taken only when it fits; tp_row_bwd_workspace_bytes_split() is the size
+ * that the fastest schedule for these sizes uses.  The workspace must be
+ * 16-byte aligned for the split to be taken.  Results may differ from the
+ * unsplit schedule's in the fp32 summation order only.
  */
 TP_API tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K,
                      const void* dZ, int64_t lddz, const void* Xi, int64_t ldx,
@@ -150,6 +160,9 @@ TP_API tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K,
                      void* dXi, int64_t lddx, void* dBi, int64_t lddb, void* dbias,
                      void* workspace, size_t ws_bytes, void* stream);
 TP_API size_t tp_row_bwd_workspace_bytes(int dtype, int64_t M, int64_t N);
+/* Workspace for tp_row_bwd with room for its split-contraction schedule on a
+ * GPU with `cus` compute units (host only; 0 for invalid sizes). */
+TP_API size_t tp_row_bwd_workspace_bytes_split(int dtype, int64_t M, int64_t N, int64_t K, int cus);
 
 /*
  * Planning query for tp_row_bwd (bf16, dXi and dBi both requested): which
@@ -164,6 +177,13 @@ TP_API size_t tp_row_bwd_workspace_bytes(int dtype, int64_t M, int64_t N);
  * cus < 1.
  */
 TP_API int tp_row_bwd_plan(int64_t M, int64_t N, int64_t K, int cus);
+/* As tp_row_bwd_plan with `split_bytes` of split scratch available (the
+ * workspace past tp_row_bwd_workspace_bytes): also returns how many parts
+ * each contraction is cut into (*ks_dB for dBi over M, *ks_dX for dXi over
+ * N; 1 = not cut, also for a return of -1 or -2; either pointer may be
+ * NULL). */
+TP_API int tp_row_bwd_plan_split(int64_t M, int64_t N, int64_t K, int cus, size_t split_bytes, int* ks_dB,
+                                 int* ks_dX);
 
 /*
  * Column-parallel shard backward.  [TP/SP] "Where column and row
@@ -180,7 +200,10 @@ TP_API int tp_row_bwd_plan(int64_t M, int64_t N, int64_t K, int cus);
  * dY [M,N], X [M,K], A/A2 [K,N].  dP is materialized in the workspace, in the
  * dtype, for GELU/SWIGLU; bias gradients use fp32 partial sums there too.
  * ws_bytes must be >= tp_column_bwd_workspace_bytes(dtype, act, M, N, bias
- * gradients requested).
+ * gradients requested).  Without an activation (bf16, dXpart and dA both
+ * requested) the two GEMMs run as tp_row_bwd's do, and workspace bytes past
+ * that size are split-contraction scratch as described there
+ * (tp_column_bwd_workspace_bytes_split: the size the fastest schedule uses).
  */
 TP_API tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t K,
                         const void* dY, int64_t lddy, const void* X, int64_t ldx,
@@ -190,6 +213,8 @@ TP_API tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t
                         void* dA2, int64_t ldda2, void* dbias, void* dbias2,
                         void* workspace, size_t ws_bytes, void* stream);
 TP_API size_t tp_column_bwd_workspace_bytes(int dtype, int act, int64_t M, int64_t N, int with_bias_grad);
+TP_API size_t tp_column_bwd_workspace_bytes_split(int dtype, int act, int64_t M, int64_t N, int64_t K,
+                                                  int with_bias_grad, int cus);
 
 /*
  * Vocab-parallel LM-head shard with cross-entropy partials.  [TP/SP]

@@ -22,7 +22,8 @@ import sys
 __all__ = [
     "TP_FP32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU", "TP_ACT_SWIGLU", "TPError", "LIB_PATH",
     "tp_abi_version", "tp_status_str", "tp_column_fwd", "tp_row_fwd", "tp_sum_partials", "tp_row_bwd",
-    "tp_row_bwd_workspace_bytes", "tp_row_bwd_plan", "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_vocab_ce_partials",
+    "tp_row_bwd_workspace_bytes", "tp_row_bwd_workspace_bytes_split", "tp_row_bwd_plan", "tp_row_bwd_plan_split",
+    "tp_column_bwd", "tp_column_bwd_workspace_bytes", "tp_column_bwd_workspace_bytes_split", "tp_vocab_ce_partials",
     "tp_vocab_ce_workspace_bytes", "tp_vocab_ce_partials_noalloc", "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "tp_vocab_ce_bwd_workspace_bytes", "tp_sp_reduce_scatter_ln",
     "tp_vocab_embed_fwd", "tp_vocab_embed_bwd", "tp_vocab_embed_bwd_workspace_bytes", "tp_attention_fwd",
     "tp_attention_fwd_workspace_bytes", "tp_attention_bwd", "tp_attention_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
@@ -46,10 +47,13 @@ _SIGS = {
     "tp_row_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                           _vp, _sz, _vp]),
     "tp_row_bwd_workspace_bytes": (_sz, [_i32, _i64, _i64]),
+    "tp_row_bwd_workspace_bytes_split": (_sz, [_i32, _i64, _i64, _i64, _i32]),
     "tp_row_bwd_plan": (_i32, [_i64, _i64, _i64, _i32]),
+    "tp_row_bwd_plan_split": (_i32, [_i64, _i64, _i64, _i32, _sz, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "tp_column_bwd": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                              _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "tp_column_bwd_workspace_bytes": (_sz, [_i32, _i32, _i64, _i64, _i32]),
+    "tp_column_bwd_workspace_bytes_split": (_sz, [_i32, _i32, _i64, _i64, _i64, _i32, _i32]),
     "tp_vocab_ce_partials": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
                                     _sz, _vp]),
     "tp_vocab_ce_workspace_bytes": (_sz, [_i64, _i64]),
@@ -164,11 +168,23 @@ def tp_row_bwd_workspace_bytes(dtype, M, N) -> int:
     return _load().tp_row_bwd_workspace_bytes(dtype, M, N)
 
 
+def tp_row_bwd_workspace_bytes_split(dtype, M, N, K, cus) -> int:
+    """Workspace with room for tp_row_bwd's split-contraction schedule on `cus` CUs (host only)."""
+    return _load().tp_row_bwd_workspace_bytes_split(dtype, M, N, K, cus)
+
+
 def tp_row_bwd_plan(M, N, K, cus) -> int:
     """Tile pairing of tp_row_bwd's one-launch schedule (host-only query): 0 = 256x256 + 256x256,
     1 = 192x256 + 256x192, 2 = 192x192 + 128x192, 3 = 128x128 + 128x192, 4 = 128x128 + 256x256,
     5 = 128x192 + 256x192, 6 = 128x192 + 128x192, -1 = separate launches, -2 = invalid sizes."""
     return _load().tp_row_bwd_plan(M, N, K, cus)
+
+
+def tp_row_bwd_plan_split(M, N, K, cus, split_bytes):
+    """(pairing, parts of dB's contraction, parts of dX's) with `split_bytes` of split scratch (host only)."""
+    k0, k1 = ctypes.c_int(0), ctypes.c_int(0)
+    plan = _load().tp_row_bwd_plan_split(M, N, K, cus, split_bytes, ctypes.byref(k0), ctypes.byref(k1))
+    return plan, k0.value, k1.value
 
 
 def tp_column_bwd(dtype, act, M, N, K, dY, lddy, X, ldx, A, lda, A2, lda2, Pre, ldpre, dXpart, lddx, dA, ldda,
@@ -181,6 +197,11 @@ def tp_column_bwd(dtype, act, M, N, K, dY, lddy, X, ldx, A, lda, A2, lda2, Pre, 
 
 def tp_column_bwd_workspace_bytes(dtype, act, M, N, with_bias_grad) -> int:
     return _load().tp_column_bwd_workspace_bytes(dtype, act, M, N, int(bool(with_bias_grad)))
+
+
+def tp_column_bwd_workspace_bytes_split(dtype, act, M, N, K, with_bias_grad, cus) -> int:
+    """Workspace with room for tp_column_bwd's split-contraction schedule on `cus` CUs (host only)."""
+    return _load().tp_column_bwd_workspace_bytes_split(dtype, act, M, N, K, int(bool(with_bias_grad)), cus)
 
 
 def tp_vocab_ce_partials(dtype, M, Vr, K, H, ldh, W, ldw, target, v0, out_max, out_sumexp, out_tgt, workspace,

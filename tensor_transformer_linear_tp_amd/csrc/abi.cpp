@@ -109,6 +109,33 @@ size_t dp_bytes(int dtype, int64_t M, int64_t N) {
   return align_ws((size_t)M * (size_t)round_up(N, 8) * esize(dtype));
 }
 
+// The workspace past `used` bytes, as scratch for split-contraction partials.
+void give_split_ws(GemmLaunch& L, void* workspace, size_t ws_bytes, size_t used) {
+  if (workspace && ws_bytes > used) {
+    L.split_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + used);
+    L.split_bytes = ws_bytes - used;
+  }
+}
+
+// Bytes of split-contraction scratch the one-launch schedule of L takes on
+// `cus` CUs when scratch is unlimited (0: it does not split).
+size_t split_scratch(GemmLaunch L, int cus) {
+  L.split_ws = reinterpret_cast<float*>(uintptr_t(256));
+  L.split_bytes = SIZE_MAX;
+  int g0 = 0, ks0 = 1, ks1 = 1;
+  int64_t t0 = 0, t1 = 0;
+  size_t need = 0;
+  return tps::dual_plan(L, cus, g0, t0, t1, ks0, ks1, need) >= 0 ? need : 0;
+}
+
+// Stand-in operands for host-only planning queries: aligned addresses,
+// leading dimensions rounded up to 8 elements.
+GemmLaunch row_bwd_standin(int64_t M, int64_t N, int64_t K) {
+  char* const p = reinterpret_cast<char*>(uintptr_t(256));
+  return row_bwd_pair(M, N, K, p, round_up(N, 8), p, round_up(K, 8), p, round_up(N, 8), p, round_up(K, 8), p,
+                      round_up(N, 8));
+}
+
 }  // namespace
 
 extern "C" {
@@ -247,6 +274,7 @@ tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* dZ,
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (dXi && dBi && dtype == TP_BF16) {   // both GEMMs in one launch (the library may share the CUs)
     GemmLaunch L = row_bwd_pair(M, N, K, dZ, lddz, Xi, ldx, Bi, ldb, dXi, lddx, dBi, lddb);
+    give_split_ws(L, workspace, ws_bytes, colpart_bytes(M, N));   // past the bias-gradient partials
     if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
   } else if (dXi) {   // dX_i = dZ B_i^T: NT over K' = N
     GemmLaunch L = {};
@@ -287,13 +315,34 @@ tp_status tp_row_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* dZ,
 int tp_row_bwd_plan(int64_t M, int64_t N, int64_t K, int cus) {
   if (bad_dim(M) || bad_dim(N) || bad_dim(K) || cus < 1) return -2;
   if (check_grid(TP_BF16, M, K) != TP_OK || check_grid(TP_BF16, K, N) != TP_OK) return -2;
-  // Stand-in operands: aligned addresses, leading dimensions rounded up to 8 elements.
-  char* const p = reinterpret_cast<char*>(uintptr_t(256));
-  const GemmLaunch L = row_bwd_pair(M, N, K, p, round_up(N, 8), p, round_up(K, 8), p, round_up(N, 8), p,
-                                    round_up(K, 8), p, round_up(N, 8));
+  const GemmLaunch L = row_bwd_standin(M, N, K);
   int g0 = 0;
   int64_t t0 = 0, t1 = 0;
   return tps::dual_plan(L, cus, g0, t0, t1);
+}
+
+int tp_row_bwd_plan_split(int64_t M, int64_t N, int64_t K, int cus, size_t split_bytes, int* ks_dB, int* ks_dX) {
+  if (ks_dB) *ks_dB = 1;
+  if (ks_dX) *ks_dX = 1;
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K) || cus < 1) return -2;
+  if (check_grid(TP_BF16, M, K) != TP_OK || check_grid(TP_BF16, K, N) != TP_OK) return -2;
+  GemmLaunch L = row_bwd_standin(M, N, K);
+  L.split_ws = split_bytes ? reinterpret_cast<float*>(uintptr_t(256)) : nullptr;
+  L.split_bytes = split_bytes;
+  int g0 = 0, k0 = 1, k1 = 1;
+  int64_t t0 = 0, t1 = 0;
+  size_t need = 0;
+  const int plan = tps::dual_plan(L, cus, g0, t0, t1, k0, k1, need);
+  if (ks_dB) *ks_dB = k0;
+  if (ks_dX) *ks_dX = k1;
+  return plan;
+}
+
+size_t tp_row_bwd_workspace_bytes_split(int dtype, int64_t M, int64_t N, int64_t K, int cus) {
+  if (!valid_dtype(dtype) || bad_dim(M) || bad_dim(N) || bad_dim(K) || cus < 1) return 0;
+  const size_t base = colpart_bytes(M, N);
+  if (dtype != TP_BF16 || check_grid(TP_BF16, M, K) != TP_OK || check_grid(TP_BF16, K, N) != TP_OK) return base;
+  return base + split_scratch(row_bwd_standin(M, N, K), cus);
 }
 
 size_t tp_column_bwd_workspace_bytes(int dtype, int act, int64_t M, int64_t N, int with_bias_grad) {
@@ -302,6 +351,19 @@ size_t tp_column_bwd_workspace_bytes(int dtype, int act, int64_t M, int64_t N, i
   if (act != TP_ACT_NONE) bytes += dp_bytes(dtype, M, N) * (act == TP_ACT_SWIGLU ? 2 : 1);
   if (with_bias_grad) bytes += colpart_bytes(M, N);
   return bytes;
+}
+
+size_t tp_column_bwd_workspace_bytes_split(int dtype, int act, int64_t M, int64_t N, int64_t K, int with_bias_grad,
+                                           int cus) {
+  const size_t base = tp_column_bwd_workspace_bytes(dtype, act, M, N, with_bias_grad);
+  if (base == 0 && (!valid_dtype(dtype) || !valid_act(act) || bad_dim(M) || bad_dim(N))) return 0;
+  if (bad_dim(K) || cus < 1) return 0;
+  // only the activation-free bf16 backward runs its two GEMMs as one launch
+  if (dtype != TP_BF16 || act != TP_ACT_NONE || check_grid(TP_BF16, M, K) != TP_OK ||
+      check_grid(TP_BF16, K, N) != TP_OK)
+    return base;
+  // the same pair of products as the row backward's (dA = X^T dP beside dX = dP A^T)
+  return base + split_scratch(row_bwd_standin(M, N, K), cus);
 }
 
 tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t K, const void* dY, int64_t lddy,
@@ -397,6 +459,7 @@ tp_status tp_column_bwd(int dtype, int act, int64_t M, int64_t N, int64_t K, con
     L.p[1].seg[0] = tps::Seg{dPg, A, ldp, lda, N};
     L.p[1].c = dXpart;
     L.p[1].ldc = lddx;
+    give_split_ws(L, workspace, ws_bytes, need);   // past the bias-gradient partials
     if (run_gemm(dtype, L, s) != hipSuccess) return TP_E_HIP;
     return TP_OK;
   }

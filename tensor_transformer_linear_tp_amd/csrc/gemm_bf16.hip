@@ -1036,6 +1036,7 @@ __device__ __forceinline__ Problem pick_problem(const GemmLaunch& L, bool s) {
   TPS_PICK(lse); TPS_PICK(gscale); TPS_PICK(target); TPS_PICK(v0);
   TPS_PICK(tiles_m); TPS_PICK(tiles_n); TPS_PICK(tile_begin);
   TPS_PICK(edge_only); TPS_PICK(full_m); TPS_PICK(full_n);
+  TPS_PICK(ksplit); TPS_PICK(c32);
 #undef TPS_PICK
   return P;
 }
@@ -1046,7 +1047,19 @@ template <bool EDGE, int MI = 4, int NI = 4>
 __device__ __forceinline__ void locate(const GemmLaunch& L, int id, int epi, Problem& P, int64_t& m0, int64_t& n0) {
   P = pick_problem(L, L.nprob > 1 && id >= L.p[1].tile_begin);
   P.epi = epi;
-  const int local = id - P.tile_begin;
+  int local = id - P.tile_begin;
+  if (P.ksplit > 1) {   // part-major: part j's tiles cover K range [j K/ks, (j+1) K/ks)
+    const int nt = P.tiles_m * P.tiles_n;
+    const int j = local / nt;
+    local -= j * nt;
+    const int64_t kl = P.seg[0].K / P.ksplit, k0 = (int64_t)j * kl;
+    const int64_t da = P.layout == L_TN ? k0 * P.seg[0].lda : k0;   // elements along A's K
+    const int64_t db = P.layout == L_NT ? k0 : k0 * P.seg[0].ldb;   // and along B's
+    P.seg[0].a = static_cast<const uint16_t*>(P.seg[0].a) + da;
+    P.seg[0].b = static_cast<const uint16_t*>(P.seg[0].b) + db;
+    P.seg[0].K = kl;
+    P.c32 += (int64_t)j * P.M * P.N;
+  }
   int tm, tn;
   if (EDGE && P.edge_only) {   // right strip (whole-tile rows, ragged columns), then the bottom strip
     const int rn = P.tiles_n - P.full_n;
@@ -1135,6 +1148,26 @@ __device__ __forceinline__ TileInit<EPI, MI, NI> tile_init(const Problem& P, int
   return t;
 }
 
+// A split-contraction part's tile: the fp32 accumulators straight to its
+// partial plane (a lane's four consecutive columns of each block are one
+// 16-byte store; N is a multiple of 8, so a group is all inside or all
+// past the right edge).
+template <int MI, int NI>
+__device__ __forceinline__ void f32_epilogue(const Problem& P, int64_t m0, int64_t n0,
+                                             const f32x4 (&acc)[2 * MI][2 * NI]) {
+  const int tid = tid_opaque(), lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int64_t m = m0 + 32 * MI * wm + (lane & 15);
+  const int64_t n = n0 + 32 * NI * wn + 4 * (lane >> 4);
+  float* c = P.c32 + m * P.N + n;
+  const bool whole = m0 + 64 * MI <= P.M && n0 + 64 * NI <= P.N;
+#pragma unroll
+  for (int i = 0; i < 2 * MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2 * NI; ++j)
+      if (whole || (m + 16 * i < P.M && n + 16 * j < P.N))
+        *reinterpret_cast<f32x4*>(c + 16 * i * P.N + 16 * j) = acc[i][j];
+}
+
 // The fused store epilogues of the GEMM kernels (the default of tile_loop).
 template <int EPI, int MI, int NI>
 struct StoreEpilogue {
@@ -1142,6 +1175,16 @@ struct StoreEpilogue {
                                             f32x4 (&acc)[2 * MI][2 * NI]) const {
     fast_epilogue<EPI, MI, NI>(P, m0, n0, acc,
                                std::make_integer_sequence<int, 2 * MI * (EPI == E_SWIGLU ? 2 : NI)>{});
+  }
+};
+
+// The two-layout launch's epilogue: bf16 stores, or a split part's fp32 plane.
+template <int MI, int NI>
+struct DualEpilogue {
+  __device__ __forceinline__ void operator()(const Problem& P, int64_t m0, int64_t n0,
+                                            f32x4 (&acc)[2 * MI][2 * NI]) const {
+    if (P.ksplit > 1) f32_epilogue<MI, NI>(P, m0, n0, acc);
+    else fast_epilogue<E_STORE, MI, NI>(P, m0, n0, acc, std::make_integer_sequence<int, 2 * MI * NI>{});
   }
 };
 
@@ -1263,8 +1306,57 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_dual_kernel(const GemmL
   int xcd;
   const int g = wg_index(xcd);
   const int t1 = L.p[1].tile_begin;
-  if (g < L.g0) tile_loop<LA, E_STORE, false, MIA, NIA>(L, 0, t1, g, L.g0, xcd);
-  else tile_loop<LB, E_STORE, false, MIB, NIB>(L, t1, L.tiles - t1, g - L.g0, (int)gridDim.x - L.g0, xcd);
+  if (g < L.g0)
+    tile_loop<LA, E_STORE, false, MIA, NIA, false, TM_NONE, DualEpilogue<MIA, NIA>>(L, 0, t1, g, L.g0, xcd);
+  else
+    tile_loop<LB, E_STORE, false, MIB, NIB, false, TM_NONE, DualEpilogue<MIB, NIB>>(L, t1, L.tiles - t1, g - L.g0,
+                                                                                  (int)gridDim.x - L.g0, xcd);
+}
+
+// Sum of a split problem's fp32 partial planes, in ascending part order, to
+// bf16 (round to nearest even): thread i takes 8 consecutive columns of one
+// row.  Both problems of a two-layout launch in one grid: rows of problem 0,
+// then of problem 1 (n8[q] = N / 8 groups per row, g[q] groups in all).
+struct SplitReduce {
+  const float* c32[2];
+  uint16_t* out[2];
+  int64_t N[2], ldo[2], n8[2], groups[2];
+  int ks[2];
+};
+
+template <int KS>
+__device__ __forceinline__ void splitk_sum(const float* p, int64_t plane, f32x4& lo, f32x4& hi) {
+  f32x4 l[KS], h[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {   // all loads first: KS x 32 bytes in flight per lane
+    l[j] = *reinterpret_cast<const f32x4*>(p + j * plane);
+    h[j] = *reinterpret_cast<const f32x4*>(p + j * plane + 4);
+  }
+  lo = l[0];
+  hi = h[0];
+#pragma unroll
+  for (int j = 1; j < KS; ++j) {
+    lo += l[j];
+    hi += h[j];
+  }
+}
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const SplitReduce r) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = i >= r.groups[0] ? 1 : 0;
+  if (q) i -= r.groups[0];
+  if (i >= r.groups[q]) return;
+  const int64_t n8 = q ? r.n8[1] : r.n8[0], N = q ? r.N[1] : r.N[0];
+  const int64_t m = i / n8, n = (i - m * n8) * 8;
+  const int64_t plane = (q ? r.groups[1] : r.groups[0]) * 8;
+  const float* p = (q ? r.c32[1] : r.c32[0]) + m * N + n;
+  f32x4 lo, hi;
+  const int ks = q ? r.ks[1] : r.ks[0];
+  if (ks == 4) splitk_sum<4>(p, plane, lo, hi);
+  else splitk_sum<2>(p, plane, lo, hi);
+  uint16_t* o = (q ? r.out[1] : r.out[0]) + m * (q ? r.ldo[1] : r.ldo[0]) + n;
+  *reinterpret_cast<u32x4*>(o) = u32x4{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]),
+                                       pack_bf2(hi[2], hi[3])};
 }
 
 // Generic kernels: one tile per workgroup, any shape, bias, alignment.
@@ -1528,16 +1620,33 @@ int64_t tiles_of(const Problem& P, int mi, int ni) {
 }
 
 // Problem 0 on g0 workgroups and problem 1 on the rest of `cus`, one launch:
-// the best g0 and its makespan (in units of a tile's cost).
+// the best g0 (the smallest of the best) and its makespan (in units of a
+// tile's cost).  Problem 0's rounds times its tile cost, f0(g), never grows
+// with g and problem 1's, f1(g), never shrinks, so the best g is the first
+// one with f0 <= f1 or the one before it; on a run of equal makespans below
+// that point the makespan is f0, and a second search finds the run's start.
 int64_t dual_split(int64_t t0, int64_t s0, int64_t t1, int64_t s1, int cus, int& g0) {
-  int64_t best = INT64_MAX;
   g0 = 1;
-  for (int g = 1; g < cus; ++g) {
-    const int64_t m = std::max((t0 + g - 1) / g * s0, (t1 + cus - g - 1) / (cus - g) * s1);
-    if (m < best) {
-      best = m;
-      g0 = g;
+  if (cus < 2) return INT64_MAX;
+  auto f0 = [&](int64_t g) { return (t0 + g - 1) / g * s0; };
+  auto f1 = [&](int64_t g) { return (t1 + cus - g - 1) / (cus - g) * s1; };
+  int lo = 1, hi = cus - 1;
+  while (lo < hi) {   // first g in [1, cus - 1] with f0(g) <= f1(g) (cus - 1 if none)
+    const int mid = (lo + hi) / 2;
+    if (f0(mid) <= f1(mid)) hi = mid;
+    else lo = mid + 1;
+  }
+  int64_t best = std::max(f0(lo), f1(lo));
+  g0 = lo;
+  if (lo > 1 && f0(lo - 1) <= best) {   // below lo the makespan is f0, never growing with g
+    best = f0(lo - 1);
+    int a = 1, b = lo - 1;   // first g with f0(g) == best
+    while (a < b) {
+      const int mid = (a + b) / 2;
+      if (f0(mid) <= best) b = mid;
+      else a = mid + 1;
     }
+    g0 = a;
   }
   return best;
 }
@@ -1547,7 +1656,24 @@ constexpr int kGeoN = 7;
 constexpr int kGeo[kGeoN][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}, {2, 2, 2, 3},
                                 {2, 2, 4, 4}, {2, 3, 4, 3}, {2, 3, 2, 3}};
 
-int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1) {
+// Split contractions.  A part's fp32 plane costs the model SPLIT_EPI units
+// per 256 x 256 tile more than a bf16 tile's stores would (twice the bytes),
+// scaled by tile area; the reduction launch reads the planes and writes the
+// output at an assumed 5 TB/s (a 256 x 256 stage, 18 units, takes ~0.73 us:
+// 1 unit ~ 0.041 us ~ 0.2 MB), plus REDUCE_LAUNCH units.  Parts must hold
+// whole 32-deep stages.
+constexpr int64_t SPLIT_EPI = 45;
+constexpr int64_t REDUCE_LAUNCH = 50;
+constexpr int64_t BYTES_PER_UNIT = 203000;
+
+size_t split_bytes(const Problem& P, int ks) {
+  return ks > 1 ? ((size_t)ks * (size_t)P.M * (size_t)P.N * 4 + 255) / 256 * 256 : 0;
+}
+
+int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1, int& ks0, int& ks1,
+              size_t& split_need) {
+  ks0 = ks1 = 1;
+  split_need = 0;
   if (!(L.nprob == 2 && L.p[0].layout == L_TN && L.p[1].layout == L_NT && L.p[0].epi == E_STORE &&
         L.p[1].epi == E_STORE && L.p[0].nseg == 1 && L.p[1].nseg == 1 && fast_ok(L.p[0]) && fast_ok(L.p[1]) &&
         (L.p[0].N & 7) == 0 && (L.p[1].N & 7) == 0 && cus % 8 == 0))
@@ -1555,28 +1681,63 @@ int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1) {
   const int64_t s0 = tile_stages(L.p[0]), s1 = tile_stages(L.p[1]);
   const int64_t n0 = tiles_of(L.p[0], 4, 4), n1 = tiles_of(L.p[1], 4, 4);
   const int64_t apart = ((n0 + cus - 1) / cus * s0 + (n1 + cus - 1) / cus * s1) * 18;   // one after the other
+  const bool can_split = L.split_ws != nullptr && (reinterpret_cast<uintptr_t>(L.split_ws) & 15) == 0;
   int best = -1;
   int64_t best_cost = apart;
-  for (int c = 0; c < kGeoN; ++c) {
-    const int64_t a = tiles_of(L.p[0], kGeo[c][0], kGeo[c][1]);
-    const int64_t b = tiles_of(L.p[1], kGeo[c][2], kGeo[c][3]);
-    if (a + b >= INT_MAX) continue;
-    int g = 1;
-    const int64_t w0 = s0 * (kGeo[c][0] * kGeo[c][1] + 2), w1 = s1 * (kGeo[c][2] * kGeo[c][3] + 2);
-    const int64_t m = dual_split(a, w0, b, w1, cus, g);
-    // equal cost: the pairing with the larger tiles (the model's per-stage cost favours small
-    // tiles, which copy the full 256-wide MN-contiguous panels and measure slower)
-    const bool larger = best >= 0 && kGeo[c][0] * kGeo[c][1] + kGeo[c][2] * kGeo[c][3] >
-                                         kGeo[best][0] * kGeo[best][1] + kGeo[best][2] * kGeo[best][3];
-    if (m < best_cost || (m == best_cost && larger)) {
-      best_cost = m;
-      best = c;
-      g0 = g;
-      t0 = a;
-      t1 = b;
+  for (int k0 = 1; k0 <= 4; k0 *= 2) {
+    for (int k1 = 1; k1 <= 4; k1 *= 2) {
+      const bool split = k0 > 1 || k1 > 1;
+      if (split && !can_split) continue;
+      if ((k0 > 1 && L.p[0].seg[0].K % (BK * k0) != 0) || (k1 > 1 && L.p[1].seg[0].K % (BK * k1) != 0)) continue;
+      const size_t need = split_bytes(L.p[0], k0) + split_bytes(L.p[1], k1);
+      if (split && need > L.split_bytes) continue;
+      const int64_t ss0 = (s0 / k0 + NSTAGE - 1) / NSTAGE * NSTAGE, ss1 = (s1 / k1 + NSTAGE - 1) / NSTAGE * NSTAGE;
+      int64_t red = 0;
+      if (split) {
+        for (int q = 0; q < 2; ++q) {
+          const int k = q ? k1 : k0;
+          if (k > 1) red += (int64_t)((4 * k + 2) * L.p[q].M * L.p[q].N / BYTES_PER_UNIT);
+        }
+        red += REDUCE_LAUNCH;
+      }
+      for (int c = 0; c < kGeoN; ++c) {
+        const int64_t a = tiles_of(L.p[0], kGeo[c][0], kGeo[c][1]) * k0;
+        const int64_t b = tiles_of(L.p[1], kGeo[c][2], kGeo[c][3]) * k1;
+        if (a + b >= INT_MAX) continue;
+        int g = 1;
+        const int64_t e0 = k0 > 1 ? SPLIT_EPI * kGeo[c][0] * kGeo[c][1] / 16 : 0;
+        const int64_t e1 = k1 > 1 ? SPLIT_EPI * kGeo[c][2] * kGeo[c][3] / 16 : 0;
+        const int64_t w0 = ss0 * (kGeo[c][0] * kGeo[c][1] + 2) + e0, w1 = ss1 * (kGeo[c][2] * kGeo[c][3] + 2) + e1;
+        const int64_t m = dual_split(a, w0, b, w1, cus, g) + red;
+        // equal cost: no split before a split, then the pairing with the larger tiles (the model's
+        // per-stage cost favours small tiles, which copy the full 256-wide MN-contiguous panels and
+        // measure slower)
+        const bool larger = best >= 0 && kGeo[c][0] * kGeo[c][1] + kGeo[c][2] * kGeo[c][3] >
+                                             kGeo[best][0] * kGeo[best][1] + kGeo[best][2] * kGeo[best][3];
+        const bool same_split = best < 0 || (ks0 == k0 && ks1 == k1);
+        if (m < best_cost || (m == best_cost && same_split && larger)) {
+          best_cost = m;
+          best = c;
+          g0 = g;
+          t0 = a;
+          t1 = b;
+          ks0 = k0;
+          ks1 = k1;
+          split_need = need;
+        }
+      }
     }
   }
   return best;
+}
+
+int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1) {
+  GemmLaunch U = L;
+  U.split_ws = nullptr;
+  U.split_bytes = 0;
+  int ks0 = 1, ks1 = 1;
+  size_t need = 0;
+  return dual_plan(U, cus, g0, t0, t1, ks0, ks1, need);
 }
 
 hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
@@ -1601,16 +1762,21 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   // first case too but ran slower: a stage's barrier and copies then serve
   // half the MFMAs.)
   {
-    int g0 = 1;
+    int g0 = 1, ks[2] = {1, 1};
     int64_t t0 = 0, t1 = 0;
-    const int best = dual_plan(L, cus, g0, t0, t1);
+    size_t need = 0;
+    const int best = dual_plan(L, cus, g0, t0, t1, ks[0], ks[1], need);
     if (best >= 0) {
       GemmLaunch D = L;
+      float* part = L.split_ws;
       for (int i = 0; i < 2; ++i) {
         const int64_t bm = 64 * kGeo[best][2 * i], bn = 64 * kGeo[best][2 * i + 1];
         D.p[i].tiles_m = (int)((L.p[i].M + bm - 1) / bm);
         D.p[i].tiles_n = (int)((L.p[i].N + bn - 1) / bn);
         D.p[i].edge_only = 0;
+        D.p[i].ksplit = ks[i];
+        D.p[i].c32 = ks[i] > 1 ? part : nullptr;
+        if (ks[i] > 1) part += split_bytes(L.p[i], ks[i]) / sizeof(float);
       }
       D.p[0].tile_begin = 0;
       D.p[1].tile_begin = (int)t0;
@@ -1632,6 +1798,29 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 2, 3, 4, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
       else
         hipLaunchKernelGGL((gemm_bf16_dual_kernel<L_TN, L_NT, 2, 3, 2, 3>), dim3(cus), dim3(NTHREADS), 0, s, D);
+      if (ks[0] > 1 || ks[1] > 1) {
+        SplitReduce r = {};
+        for (int i = 0; i < 2; ++i) {
+          r.ks[i] = ks[i];
+          r.c32[i] = D.p[i].c32;
+          r.out[i] = static_cast<uint16_t*>(D.p[i].c);
+          r.N[i] = D.p[i].N;
+          r.ldo[i] = D.p[i].ldc;
+          r.n8[i] = D.p[i].N / 8;
+          r.groups[i] = ks[i] > 1 ? D.p[i].M * r.n8[i] : 0;
+        }
+        if (r.groups[0] == 0) {   // problem 1 only: its rows first
+          std::swap(r.ks[0], r.ks[1]);
+          std::swap(r.c32[0], r.c32[1]);
+          std::swap(r.out[0], r.out[1]);
+          std::swap(r.N[0], r.N[1]);
+          std::swap(r.ldo[0], r.ldo[1]);
+          std::swap(r.n8[0], r.n8[1]);
+          std::swap(r.groups[0], r.groups[1]);
+        }
+        const int64_t total = r.groups[0] + r.groups[1];
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, r);
+      }
       return hipGetLastError();
     }
   }

@@ -51,12 +51,20 @@ struct Problem {
   int tiles_m, tiles_n, tile_begin;
   int edge_only;         // tiles enumerate only the ragged edge (right strip, then bottom strip)
   int full_m, full_n;    // whole tiles along M and N (edge_only)
+  // Split contraction (one-segment plain-store problems of the two-layout
+  // launch): ksplit > 1 cuts K into ksplit equal parts, each a tile set of
+  // its own whose fp32 result goes to c32 + part * M * N ([M][N], rows of N
+  // floats); splitk_reduce then sums the parts in ascending order into c.
+  int ksplit;
+  float* c32;
 };
 
 // Up to two independent GEMM problems share one launch (their tiles are
 // concatenated), so a short GEMM can fill the CUs another one leaves idle.
 struct GemmLaunch {
   Problem p[2];
+  float* split_ws;       // caller scratch for split-contraction partials (two-layout launch), or nullptr
+  size_t split_bytes;    // its size
   int nprob;
   int tiles;             // bf16 whole-tile kernels: tiles of the launch
   int g0;                // two-layout launch: workgroups of problem 0
@@ -207,7 +215,12 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s);
 // of problem 0 and each problem's tile count, or -1 when the two run as
 // separate launches.
 // Host-only.
+// With L.split_bytes > 0 the plan may also cut either problem's contraction
+// into ks0 / ks1 parts (1, 2 or 4; fp32 partials in L.split_ws, summed by a
+// second launch); `split_need` returns the bytes that plan uses.
 int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1);
+int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1, int& ks0, int& ks1,
+              size_t& split_need);
 hipError_t launch_gemm_f32(GemmLaunch& L, hipStream_t s);
 hipError_t launch_ce_partials(const CEArgs& a, hipStream_t s);
 // Size of the library's own CE scratch array (one per device), and its

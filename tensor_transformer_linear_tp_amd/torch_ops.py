@@ -11,7 +11,8 @@ from __future__ import annotations
 import torch
 
 from . import (TP_ACT_GELU, TP_ACT_NONE, TP_ACT_SWIGLU, TP_BF16, TP_FP32, tp_column_bwd,
-               tp_column_bwd_workspace_bytes, tp_column_fwd, tp_row_bwd, tp_row_bwd_workspace_bytes, tp_row_fwd,
+               tp_column_bwd_workspace_bytes, tp_column_bwd_workspace_bytes_split, tp_column_fwd, tp_row_bwd,
+               tp_row_bwd_workspace_bytes, tp_row_bwd_workspace_bytes_split, tp_row_fwd,
                tp_sp_reduce_scatter_ln, tp_sum_partials, tp_vocab_ce_bwd, tp_vocab_embed_bwd,
                tp_vocab_embed_bwd_workspace_bytes, tp_vocab_embed_fwd, tp_attention_fwd,
                tp_attention_fwd_workspace_bytes, tp_attention_bwd, tp_attention_bwd_workspace_bytes, tp_vocab_ce_bwd_workspace_bytes, tp_vocab_ce_combine, tp_vocab_ce_partials,
@@ -127,8 +128,13 @@ def sp_reduce_scatter_ln(buf, N, r0, Mr, bias=None, resid=None, gamma=None, beta
     return y, h
 
 
-def row_bwd(dZ, Xi, Bi, want_dx=True, want_dw=True, want_db=False):
-    """(dX_i, dB_i, dbias) of the row shard; unrequested outputs are None."""
+def _cus(device):
+    return torch.cuda.get_device_properties(device).multi_processor_count
+
+
+def row_bwd(dZ, Xi, Bi, want_dx=True, want_dw=True, want_db=False, split=False):
+    """(dX_i, dB_i, dbias) of the row shard; unrequested outputs are None.  split: give the call
+    the workspace its split-contraction schedule takes (tp_row_bwd_workspace_bytes_split)."""
     dZ, Xi, Bi = aligned(dZ), aligned(Xi), aligned(Bi)
     M, N = dZ.shape
     K = Xi.shape[1]
@@ -136,15 +142,19 @@ def row_bwd(dZ, Xi, Bi, want_dx=True, want_dw=True, want_db=False):
     dX = empty_padded(M, K, dZ.dtype, dZ.device) if want_dx else None
     dB = empty_padded(K, N, dZ.dtype, dZ.device) if want_dw else None
     db = torch.empty(N, dtype=dZ.dtype, device=dZ.device) if want_db else None
-    ws_n = tp_row_bwd_workspace_bytes(dt, M, N) if want_db else 0
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dZ.device) if want_db else None
+    if split:
+        ws_n = tp_row_bwd_workspace_bytes_split(dt, M, N, K, _cus(dZ.device))
+    else:
+        ws_n = tp_row_bwd_workspace_bytes(dt, M, N) if want_db else 0
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dZ.device) if (want_db or split) else None
     tp_row_bwd(dt, M, N, K, dZ, ld(dZ), Xi, ld(Xi), Bi, ld(Bi), dX, ld(dX) if dX is not None else 0,
                dB, ld(dB) if dB is not None else 0, db, ws, ws_n)
     return dX, dB, db
 
 
-def column_bwd(dY, X, A, Pre=None, act="none", A2=None, want_dx=True, want_dw=True, want_db=False):
-    """(dX_part, dA, dA2, dbias, dbias2) of the column shard; unrequested outputs are None."""
+def column_bwd(dY, X, A, Pre=None, act="none", A2=None, want_dx=True, want_dw=True, want_db=False, split=False):
+    """(dX_part, dA, dA2, dbias, dbias2) of the column shard; unrequested outputs are None.  split: the
+    workspace of the split-contraction schedule (tp_column_bwd_workspace_bytes_split)."""
     dY, X, A, A2, Pre = (aligned(t) for t in (dY, X, A, A2, Pre))
     M, N = dY.shape
     K = X.shape[1]
@@ -155,7 +165,10 @@ def column_bwd(dY, X, A, Pre=None, act="none", A2=None, want_dx=True, want_dw=Tr
     dA2 = empty_padded(K, N, dY.dtype, dY.device) if (want_dw and sw) else None
     db = torch.empty(N, dtype=dY.dtype, device=dY.device) if want_db else None
     db2 = torch.empty(N, dtype=dY.dtype, device=dY.device) if (want_db and sw) else None
-    ws_n = tp_column_bwd_workspace_bytes(dt, ACTS[act], M, N, want_db)
+    if split:
+        ws_n = tp_column_bwd_workspace_bytes_split(dt, ACTS[act], M, N, K, want_db, _cus(dY.device))
+    else:
+        ws_n = tp_column_bwd_workspace_bytes(dt, ACTS[act], M, N, want_db)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dY.device)
     tp_column_bwd(dt, ACTS[act], M, N, K, dY, ld(dY), X, ld(X), A, ld(A), A2, ld(A2) if A2 is not None else 0,
                   Pre, ld(Pre) if Pre is not None else 0, dX, ld(dX) if dX is not None else 0,

@@ -184,6 +184,33 @@ def test_row_bwd_plan(lib):
     assert tp.tp_row_bwd_plan(0, 1, 1, 256) == -2 and tp.tp_row_bwd_plan(1, 1, 1, 0) == -2
 
 
+def test_row_bwd_split_plan(lib):
+    # Split contractions need scratch past the bias-gradient partials; without it the plan is tp_row_bwd_plan's.
+    BF = tp.TP_BF16
+    for shape in [(8192, 4096, 1536), (8192, 4096, 512), (8192, 768, 4096), (512, 512, 128)]:
+        assert tp.tp_row_bwd_plan_split(*shape, 256, 0) == (tp.tp_row_bwd_plan(*shape, 256), 1, 1)
+    # the attention output projection's backward: dW [512, 4096] over 8192 tokens in 4 parts, dX [8192, 512]
+    # over 4096 in 2, both in 256x256 tiles: 4 * 512 * 4096 + 2 * 8192 * 512 floats of scratch
+    need = (4 * 512 * 4096 + 2 * 8192 * 512) * 4
+    base = tp.tp_row_bwd_workspace_bytes(BF, 8192, 4096)
+    assert tp.tp_row_bwd_workspace_bytes_split(BF, 8192, 4096, 512, 256) == base + need
+    assert tp.tp_row_bwd_plan_split(8192, 4096, 512, 256, need) == (0, 4, 2)
+    assert tp.tp_row_bwd_plan_split(8192, 4096, 512, 256, need - 1)[1:] != (4, 2)   # does not fit: another plan
+    # the MLP shard step and the QKV projection's backward do not split
+    assert tp.tp_row_bwd_workspace_bytes_split(BF, 8192, 4096, 1536, 256) == base
+    assert tp.tp_row_bwd_plan_split(8192, 4096, 1536, 256, 1 << 40) == (1, 1, 1)
+    assert tp.tp_row_bwd_plan_split(8192, 768, 4096, 256, 1 << 40) == (5, 1, 1)
+    col = tp.tp_column_bwd_workspace_bytes(BF, tp.TP_ACT_NONE, 8192, 4096, 1)
+    assert tp.tp_column_bwd_workspace_bytes_split(BF, tp.TP_ACT_NONE, 8192, 4096, 512, 1, 256) == col + need
+    # only the activation-free bf16 backward runs the pair as one launch
+    assert (tp.tp_column_bwd_workspace_bytes_split(BF, tp.TP_ACT_GELU, 8192, 4096, 512, 0, 256) ==
+            tp.tp_column_bwd_workspace_bytes(BF, tp.TP_ACT_GELU, 8192, 4096, 0))
+    assert (tp.tp_row_bwd_workspace_bytes_split(tp.TP_FP32, 8192, 4096, 512, 256) ==
+            tp.tp_row_bwd_workspace_bytes(tp.TP_FP32, 8192, 4096))
+    assert tp.tp_row_bwd_workspace_bytes_split(BF, 0, 4096, 512, 256) == 0
+    assert tp.tp_row_bwd_plan_split(8192, 4096, 512, 0, need) == (-2, 1, 1)
+
+
 def test_ce_combine_validation(lib):
     def call(R=8, M=64, ms=P, ss=P, ts=P, stride=64, lse=P, tgt=P, loss=P):
         return _rc("tp_vocab_ce_combine", R, M, ms, ss, ts, stride, lse, tgt, loss, None)

@@ -254,6 +254,52 @@ def test_row_bwd_whole_matrix_pairings(shape, pairing):
     assert_close("dB", host64(dB), rdB, TOL[dtype])
 
 
+# Split contractions: with the workspace of tp_row_bwd_workspace_bytes_split the one-launch
+# schedule may cut either product's contraction into parts (fp32 partial planes, then a
+# reduction launch).  Shapes in this file's order (X_i [M, N], B_i [N, K], dZ [M, K]); on 256
+# CUs the planner cuts (ks_dB, ks_dX) as listed: the weight gradient only, the input gradient
+# only, both; (1000, 520, 136) has tiles overhanging both outputs.
+SPLIT_CASES = [((512, 128, 128), (4, 1)), ((512, 128, 1536), (1, 4)), ((512, 128, 512), (4, 4)),
+               ((8192, 512, 4096), None), ((1000, 520, 136), None)]
+
+
+@pytest.mark.parametrize("shape,parts", SPLIT_CASES)
+def test_row_bwd_split_contraction(shape, parts):
+    M, N, K = shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ws = tp.tp_row_bwd_workspace_bytes_split(tp.TP_BF16, M, K, N, cus) - tp.tp_row_bwd_workspace_bytes(tp.TP_BF16, M, K)
+    plan, k0, k1 = tp.tp_row_bwd_plan_split(M, K, N, cus, ws)
+    if cus == 256 and parts is not None:
+        assert (k0, k1) == parts, (plan, k0, k1)
+    dtype = syn.BF16
+    d = _inputs(dtype, M, N, K, 61 + M + K, "none")
+    Xi, Bi = dev(d["dY"]), dev(d["B"])
+    dX, dB, _ = ops.row_bwd(dev(d["dZ"]), Xi, Bi, split=True)
+    torch.cuda.synchronize()
+    rdX, rdB, _ = oracle.row_bwd(d["dZ"].f64, d["dY"].f64, d["B"].f64)
+    assert_close("dX", host64(dX), rdX, TOL[dtype])
+    assert_close("dB", host64(dB), rdB, TOL[dtype])
+    # the same call twice gives the same bits (fixed summation order)
+    dX2, dB2, _ = ops.row_bwd(dev(d["dZ"]), Xi, Bi, split=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX2) and torch.equal(dB, dB2)
+
+
+@pytest.mark.parametrize("shape", [(512, 128, 512), (1024, 256, 1024)])
+def test_column_bwd_split_contraction(shape):
+    # the activation-free column backward's pair of GEMMs with its split workspace (and a bias gradient,
+    # whose column partials come first in the workspace)
+    M, N, K = shape
+    dtype = syn.BF16
+    d = _inputs(dtype, M, N, K, 71 + N, "none")
+    dX, dA, _, db, _ = ops.column_bwd(dev(d["dY"]), dev(d["X"]), dev(d["A"]), act="none", want_db=True, split=True)
+    torch.cuda.synchronize()
+    r = oracle.column_bwd(d["dY"].f64, d["X"].f64, d["A"].f64, None, "none", None)
+    assert_close("dXpart", host64(dX), r[0], TOL[dtype])
+    assert_close("dA", host64(dA), r[1], TOL[dtype])
+    assert_close("db", host64(db), r[3], TOL[dtype])
+
+
 @pytest.mark.parametrize("act", ["none", "swiglu"])
 def test_column_bwd_wgrad_narrow_tiles_two_rounds(act):
     # Weight gradient [2560, 7680] (per problem): 300 tiles of 256 x 256 or
