@@ -1043,16 +1043,17 @@ __device__ __forceinline__ Problem pick_problem(const GemmLaunch& L, bool s) {
 
 // Tile of a launch: its problem (selected field-wise) and its origin; tiles
 // are (64 MI) x (64 NI) (SwiGLU: 128 columns of Y).
-template <bool EDGE, int MI = 4, int NI = 4>
+// SPLIT: the launch may hold split-contraction problems (the two-layout kernel).
+template <bool EDGE, int MI = 4, int NI = 4, bool SPLIT = false>
 __device__ __forceinline__ void locate(const GemmLaunch& L, int id, int epi, Problem& P, int64_t& m0, int64_t& n0) {
   P = pick_problem(L, L.nprob > 1 && id >= L.p[1].tile_begin);
   P.epi = epi;
   int local = id - P.tile_begin;
-  if (P.ksplit > 1) {   // part-major: part j's tiles cover K range [j K/ks, (j+1) K/ks)
+  if (SPLIT && P.ksplit > 1) {   // part-major: part j's tiles cover K range [j K/ks, (j+1) K/ks); ks is 2 or 4
     const int nt = P.tiles_m * P.tiles_n;
-    const int j = local / nt;
+    const int j = (local >= nt) + (local >= 2 * nt) + (local >= 3 * nt);
     local -= j * nt;
-    const int64_t kl = P.seg[0].K / P.ksplit, k0 = (int64_t)j * kl;
+    const int64_t kl = P.ksplit == 4 ? P.seg[0].K >> 2 : P.seg[0].K >> 1, k0 = (int64_t)j * kl;
     const int64_t da = P.layout == L_TN ? k0 * P.seg[0].lda : k0;   // elements along A's K
     const int64_t db = P.layout == L_NT ? k0 : k0 * P.seg[0].ldb;   // and along B's
     P.seg[0].a = static_cast<const uint16_t*>(P.seg[0].a) + da;
@@ -1093,14 +1094,14 @@ __device__ __forceinline__ int range_begin(int g, int T, int G) { return (int)((
 // (L.half_tail, MI == 2) the launch's tiles are the two 128-row halves of
 // the 256-row tiles from L.half_base on; otherwise the problems' tile grids
 // are in (64 MI) x (64 NI) tiles.
-template <int MI, int NI>
+template <int MI, int NI, bool SPLIT = false>
 __device__ __forceinline__ void locate_mi(const GemmLaunch& L, int tile, int epi, Problem& P, int64_t& m0,
                                           int64_t& n0) {
   if (MI == 2 && NI == 4 && L.half_tail) {
     locate<false>(L, L.half_base + (tile >> 1), epi, P, m0, n0);
     m0 += (tile & 1) * (BM / 2);
   } else {
-    locate<false, MI, NI>(L, tile, epi, P, m0, n0);
+    locate<false, MI, NI, SPLIT>(L, tile, epi, P, m0, n0);
   }
 }
 
@@ -1194,7 +1195,7 @@ struct DualEpilogue {
 // L2) however many tiles each workgroup runs; for launches of many tiles per
 // workgroup.
 template <int LAYOUT, int EPI, bool SEG2, int MI = 4, int NI = 4, bool STRIDED = false, int TM = TM_NONE,
-          class Epi = StoreEpilogue<EPI, MI, NI>>
+          class Epi = StoreEpilogue<EPI, MI, NI>, bool SPLIT = false>
 __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count, int g, int G, int xcd,
                                           const Epi& epilogue = Epi{}) {
   const bool strided = STRIDED || L.strided;
@@ -1210,7 +1211,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
   {
     Problem P;
     int64_t m0, n0;
-    locate_mi<MI, NI>(L, tile, EPI, P, m0, n0);
+    locate_mi<MI, NI, SPLIT>(L, tile, EPI, P, m0, n0);
     pipe.cur = pipe.make_streams(P, m0, n0, xcd);
   }
   pipe.prologue();
@@ -1219,7 +1220,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
     if (more) {
       Problem Pn;
       int64_t m0n, n0n;
-      locate_mi<MI, NI>(L, tile + stride, EPI, Pn, m0n, n0n);
+      locate_mi<MI, NI, SPLIT>(L, tile + stride, EPI, Pn, m0n, n0n);
       pipe.nxt = pipe.make_streams(Pn, m0n, n0n, xcd);
     } else {
       pipe.no_next();
@@ -1231,7 +1232,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
       if (any_bias) {
         Problem P;
         int64_t m0, n0;
-        locate_mi<MI, NI>(L, tile, EPI, P, m0, n0);
+        locate_mi<MI, NI, SPLIT>(L, tile, EPI, P, m0, n0);
         init = tile_init<EPI, MI, NI>(P, n0);
       }
       pipe.template run_tile<TM>(acc, init);
@@ -1241,7 +1242,7 @@ __device__ __forceinline__ void tile_loop(const GemmLaunch& L, int t0, int count
     {
       Problem P;
       int64_t m0, n0;
-      locate_mi<MI, NI>(L, tile, EPI, P, m0, n0);
+      locate_mi<MI, NI, SPLIT>(L, tile, EPI, P, m0, n0);
       epilogue(P, m0, n0, acc);
     }
     if (!more) break;
@@ -1307,10 +1308,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_dual_kernel(const GemmL
   const int g = wg_index(xcd);
   const int t1 = L.p[1].tile_begin;
   if (g < L.g0)
-    tile_loop<LA, E_STORE, false, MIA, NIA, false, TM_NONE, DualEpilogue<MIA, NIA>>(L, 0, t1, g, L.g0, xcd);
+    tile_loop<LA, E_STORE, false, MIA, NIA, false, TM_NONE, DualEpilogue<MIA, NIA>, true>(L, 0, t1, g, L.g0, xcd);
   else
-    tile_loop<LB, E_STORE, false, MIB, NIB, false, TM_NONE, DualEpilogue<MIB, NIB>>(L, t1, L.tiles - t1, g - L.g0,
-                                                                                  (int)gridDim.x - L.g0, xcd);
+    tile_loop<LB, E_STORE, false, MIB, NIB, false, TM_NONE, DualEpilogue<MIB, NIB>, true>(
+        L, t1, L.tiles - t1, g - L.g0, (int)gridDim.x - L.g0, xcd);
 }
 
 // Sum of a split problem's fp32 partial planes, in ascending part order, to
