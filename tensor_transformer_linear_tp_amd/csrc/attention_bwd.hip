@@ -57,27 +57,33 @@ __device__ __forceinline__ Geo geo_of(const AttnArgs& a) {
 }
 
 // ---- prep ---------------------------------------------------------------------
+// 16 lanes per row, 8 of its 128 elements each (one 16-byte load of O and of
+// dO: a wave reads four whole rows per load), then a fixed butterfly over the
+// 16 lanes.
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const AttnBwdArgs p) {
   const AttnArgs& a = p.f;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (b, h, token) flattened
-  if (i >= a.B * a.n_q * a.S) return;
-  const int64_t tok = i % a.S, bh = i / a.S;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = a.B * a.n_q * a.S;
+  const int64_t i = t >> 4;                    // (b, h, token) flattened
+  const int c = (int)(t & 15);                 // this lane's 8 elements: 8 c .. 8 c + 7
+  const bool live = i < rows;
+  const int64_t ir = live ? i : rows - 1;      // past the end: a repeat, kept in the shuffles, not written
+  const int64_t tok = ir % a.S, bh = ir / a.S;
   const int h = (int)(bh % a.n_q);
   const int64_t b = bh / a.n_q;
-  const uint16_t* o = static_cast<const uint16_t*>(a.o) + (b * a.S + tok) * a.ldo + (int64_t)h * HD;
-  const uint16_t* g = static_cast<const uint16_t*>(p.dout) + (b * a.S + tok) * p.ldg + (int64_t)h * HD;
+  const uint16_t* o = static_cast<const uint16_t*>(a.o) + (b * a.S + tok) * a.ldo + (int64_t)h * HD + 8 * c;
+  const uint16_t* g = static_cast<const uint16_t*>(p.dout) + (b * a.S + tok) * p.ldg + (int64_t)h * HD + 8 * c;
+  const u32x4 x = *reinterpret_cast<const u32x4*>(o);
+  const u32x4 y = *reinterpret_cast<const u32x4*>(g);
   float d = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < HD / 8; ++c) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(o + 8 * c);
-    const u32x4 y = *reinterpret_cast<const u32x4*>(g + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      d += __uint_as_float(x[e] << 16) * __uint_as_float(y[e] << 16);
-      d += __uint_as_float(x[e] & 0xffff0000u) * __uint_as_float(y[e] & 0xffff0000u);
-    }
+  for (int e = 0; e < 4; ++e) {
+    d += __uint_as_float(x[e] << 16) * __uint_as_float(y[e] << 16);
+    d += __uint_as_float(x[e] & 0xffff0000u) * __uint_as_float(y[e] & 0xffff0000u);
   }
-  reinterpret_cast<f32x2_t*>(p.ld)[i] = f32x2_t{a.lse[i] * LOG2E, d};
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+  if (live && c == 0) reinterpret_cast<f32x2_t*>(p.ld)[i] = f32x2_t{a.lse[i] * LOG2E, d};
 }
 
 // ---- dQ ---------------------------------------------------------------------------
@@ -576,7 +582,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& p, hipStream_t s) {
   const int64_t nkb = (a.S + 127) / 128;
   const unsigned gy = (unsigned)(a.n_kv * (group / hpw));
   const int64_t rows = a.B * a.n_q * a.S;
-  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)(nqb * a.max_chunks), gy, (unsigned)a.B), dim3(256), 0, s, p);
   if (a.max_chunks > 1)
     hipLaunchKernelGGL(attn_bwd_dq_combine_kernel, dim3((unsigned)(nqb * 16), gy, (unsigned)a.B), dim3(256), 0, s, p);
