@@ -238,7 +238,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnArgs a) {
 // ascending chunk order; lse = (M + log2 L) ln 2.  A workgroup takes 8 rows of
 // one block (32 threads per row, 4 columns each); the chunks' values are loaded
 // 8 at a time before they are combined (past the last chunk the load repeats
-// it and is not used).
+// it and is not used).  Up to 8 chunks (one group) everything is loaded in one
+// round, M taken from those registers; past that a first pass finds M.
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   const AttnGeo geo = attn_geo(a);
   const int64_t qb = blockIdx.x >> 4;
@@ -254,14 +255,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
   if (tok >= a.S) return;
   const float* s0 = attn_slot(a, geo, qb, 0);
   float M = -INFINITY;
-  for (int c0 = 0; c0 < nchunks; c0 += 8) {
-    float mc[8];
+  if (nchunks > 8) {
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      float mc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mc[j] = s0[min(c0 + j, nchunks - 1) * AT_SLOT + 128 * 128 + row];
+      for (int j = 0; j < 8; ++j) mc[j] = s0[min(c0 + j, nchunks - 1) * AT_SLOT + 128 * 128 + row];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) M = fmaxf(M, mc[j]);   // repeats of the last chunk change nothing
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, mc[j]);   // repeats of the last chunk change nothing
+    }
   }
-  const float Mu = M == -INFINITY ? 0.f : M;
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < nchunks; c0 += 8) {
@@ -274,6 +276,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a) {
       lc[j] = sl[128 * 128 + 128 + row];
       oc[j] = *reinterpret_cast<const f32x4*>(sl + row * 128 + d4);
     }
+    if (nchunks <= 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, mc[j]);
+    }
+    const float Mu = M == -INFINITY ? 0.f : M;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (c0 + j < nchunks) {
