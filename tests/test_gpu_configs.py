@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 ops = pytest.importorskip("tensor_transformer_linear_tp_amd.torch_ops")
+tp = pytest.importorskip("tensor_transformer_linear_tp_amd")
 
 BF = TOL[syn.BF16]
 
@@ -163,6 +164,30 @@ def test_c3_attention_projections_sampled():
     assert_close("Z", rows(Z, ms), oracle.row_fwd(attn[ms], Wo), BF)
     assert_close("dAttn", rows(dAttn, ms), oracle.dgrad(dZ[ms], Wo), BF)
     ns = tile_sample_idx(cfg.H, 192, 7, per_tile=2)
+    assert_close("dWo", cols(dWo, ns), oracle.wgrad(attn, dZ[:, ns]), BF)
+    assert_close("dX", rows(dX, ms), oracle.dgrad(dQKV[ms], Wqkv), BF)
+    assert_close("dWqkv", host64(dWqkv), oracle.wgrad(X, dQKV), BF)
+
+
+def test_c3_attention_projection_backwards_split_sampled():
+    # The backward calls as the bench makes them: with the workspace of their split-contraction
+    # schedules (on 256 CUs the W_O backward cuts dW's 8192-token contraction into 4 parts and dX's
+    # 4096 into 2, 256 x 256 tiles; the QKV backward keeps its unsplit pairing).
+    cfg = syn.C3
+    d = syn.attn_proj_inputs(cfg)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus == 256:
+        M, H, Na = cfg.M, d["Wo"].shape[1], d["Wo"].shape[0]
+        need = tp.tp_row_bwd_workspace_bytes_split(tp.TP_BF16, M, H, Na, cus) - tp.tp_row_bwd_workspace_bytes(
+            tp.TP_BF16, M, H)
+        assert tp.tp_row_bwd_plan_split(M, H, Na, cus, need) == (0, 4, 2)
+    dAttn, dWo, _ = ops.row_bwd(dev(d["dZ"]), dev(d["attn"]), dev(d["Wo"]), split=True)
+    dX, dWqkv, _, _, _ = ops.column_bwd(dev(d["dQKV"]), dev(d["X"]), dev(d["Wqkv"]), act="none", split=True)
+    torch.cuda.synchronize()
+    ms = tile_sample_idx(cfg.M, 256, 6, per_tile=2)
+    X, Wqkv, attn, Wo, dZ, dQKV = (d[k].f64 for k in ("X", "Wqkv", "attn", "Wo", "dZ", "dQKV"))
+    assert_close("dAttn", rows(dAttn, ms), oracle.dgrad(dZ[ms], Wo), BF)
+    ns = tile_sample_idx(d["Wo"].shape[1], 256, 7, per_tile=2)
     assert_close("dWo", cols(dWo, ns), oracle.wgrad(attn, dZ[:, ns]), BF)
     assert_close("dX", rows(dX, ms), oracle.dgrad(dQKV[ms], Wqkv), BF)
     assert_close("dWqkv", host64(dWqkv), oracle.wgrad(X, dQKV), BF)
