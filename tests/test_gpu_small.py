@@ -285,6 +285,34 @@ def test_row_bwd_split_contraction(shape, parts):
     assert torch.equal(dX, dX2) and torch.equal(dB, dB2)
 
 
+def test_row_bwd_split_with_bias_gradient_and_misaligned_scratch():
+    # The bias-gradient column partials sit at the start of the workspace and the split planes after
+    # them: both in one call.  Then the same call through a workspace 8 bytes off 16-byte alignment
+    # (no bias gradient, which needs an aligned workspace): the schedule must not split, and the
+    # results are those of the unsplit launch.
+    M, N, K = 512, 128, 512   # this file's order: X_i [M, N], B_i [N, K], dZ [M, K]
+    dtype = syn.BF16
+    d = _inputs(dtype, M, N, K, 91, "none")
+    dZ, Xi, Bi = dev(d["dZ"]), dev(d["dY"]), dev(d["B"])
+    dX, dB, db = ops.row_bwd(dZ, Xi, Bi, want_db=True, split=True)
+    torch.cuda.synchronize()
+    rdX, rdB, rdb = oracle.row_bwd(d["dZ"].f64, d["dY"].f64, d["B"].f64)
+    assert_close("dX", host64(dX), rdX, TOL[dtype])
+    assert_close("dB", host64(dB), rdB, TOL[dtype])
+    assert_close("db", host64(db), rdb, TOL[dtype])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = tp.tp_row_bwd_workspace_bytes_split(tp.TP_BF16, M, K, N, cus)
+    raw = torch.empty(n + 64, dtype=torch.uint8, device="cuda")
+    off = (16 - raw.data_ptr() % 16) % 16 + 8   # 8 bytes past a 16-byte boundary
+    dX2 = torch.empty_like(dX)
+    dB2 = torch.empty_like(dB)
+    dXu, dBu, _ = ops.row_bwd(dZ, Xi, Bi)     # unsplit reference launch
+    tp.tp_row_bwd(tp.TP_BF16, M, K, N, dZ, dZ.stride(0), Xi, Xi.stride(0), Bi, Bi.stride(0), dX2, dX2.stride(0),
+                  dB2, dB2.stride(0), None, raw.data_ptr() + off, n)
+    torch.cuda.synchronize()
+    assert torch.equal(dX2, dXu) and torch.equal(dB2, dBu)
+
+
 @pytest.mark.parametrize("shape", [(512, 128, 512), (1024, 256, 1024)])
 def test_column_bwd_split_contraction(shape):
     # the activation-free column backward's pair of GEMMs with its split workspace (and a bias gradient,
