@@ -551,8 +551,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_combine_kernel(const AttnBwd
 }  // namespace
 
 // Key chunks of the dQ pass follow the forward's chunking; the dK/dV pass takes
-// 2048 queries (64 tiles) per workgroup.
-constexpr int KV_CHUNK_TILES = 64;
+// 4096 queries (128 tiles) per workgroup: with the longest-first launch order,
+// fewer and longer items beat 2048 queries (8192 tokens, 4 heads: 327 against
+// 335 µs for the whole backward; 6144 and 8192 queries ran slower), and the
+// partials the merge reads shrink with the item count.
+constexpr int KV_CHUNK_TILES = 128;
 static_assert(KV_CHUNK_TILES % 4 == 0, "the causal item order steps query tiles by 4 per key block");
 static_assert(attn_order::kQT == QT, "the item order counts the pass's query tiles");
 

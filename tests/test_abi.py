@@ -350,7 +350,7 @@ def test_attention_bwd_validation(lib):
     ws = tp.tp_attention_bwd_workspace_bytes(1, 8192, 4, 1, 1)
     ld = 4 * 8192 * 8                                          # (lse2, D) pairs
     dq = 256 * 4 * 128 * 128 * 4                               # dQ partials: 256 blocks x 4 key chunks
-    kv = 64 * 4 * 4 * 128 * 256 * 4                            # dK/dV partials: 64 key blocks x 4 heads x 4 chunks
+    kv = 64 * 4 * 2 * 128 * 256 * 4                            # dK/dV partials: 64 key blocks x 4 heads x 2 chunks
     assert ws == ld + dq + kv
     assert tp.tp_attention_bwd_workspace_bytes(1, 8192, 4, 3, 1) == 0
     base = [tp.TP_BF16, 1, 8192, 4, 1, 128, 1, sc, P, 768, P + 1024, 768, P + 1280, 768, P, 512, P, P, 512,

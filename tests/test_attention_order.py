@@ -24,7 +24,7 @@ int main() {
     for (long S : {1L, 2L, 31L, 32L, 33L, 127L, 128L, 129L, 500L, 1000L, 2047L, 2048L, 2049L, 4096L, 5000L,
                    8191L, 8192L, 8193L, 12345L, 16384L})
       for (int nq : {1, 2, 4, 8})
-        for (int ct : {4, 16, 64}) {
+        for (int ct : {4, 16, 32, 64, 96, 128, 160, 192, 256}) {
           ++cases;
           const long nkb = (S + kKeyBlock - 1) / kKeyBlock;
           std::set<std::tuple<long, int, int>> want, got;
