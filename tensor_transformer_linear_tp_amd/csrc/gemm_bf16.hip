@@ -1657,15 +1657,32 @@ constexpr int kGeoN = 7;
 constexpr int kGeo[kGeoN][4] = {{4, 4, 4, 4}, {3, 4, 4, 3}, {3, 3, 2, 3}, {2, 2, 2, 3},
                                 {2, 2, 4, 4}, {2, 3, 4, 3}, {2, 3, 2, 3}};
 
-// Split contractions.  A part's fp32 plane costs the model SPLIT_EPI units
-// per 256 x 256 tile more than a bf16 tile's stores would (twice the bytes),
-// scaled by tile area; the reduction launch reads the planes and writes the
-// output at an assumed 5 TB/s (a 256 x 256 stage, 18 units, takes ~0.73 us:
-// 1 unit ~ 0.041 us ~ 0.2 MB), plus REDUCE_LAUNCH units.  Parts must hold
+// Cost model of the two-layout launch, in shader cycles.  A 32-deep stage of a
+// (64 MI) x (64 NI) tile: 64 cycles per 16 x 16 MFMA block and wave, 47/4 per
+// KiB it copies (a TN tile copies both 256-wide MN-contiguous panels, 32 KiB,
+// whatever its width; an NT tile 4 KiB per 16-row block of either operand),
+// and 100 of fixed work (waits, barrier); no stage takes under 900 cycles,
+// the time the four-stage ring needs to cover a load's latency (small tiles
+// hit that floor: a 128 x 128 tile's stages take ~30% longer than their MFMA
+// and copy counts say).  A tile's epilogue: 8800 cycles for
+// a 256 x 256 tile's bf16 stores, 13200 for a split part's fp32 plane, scaled
+// by area.  Fit to per-step and per-tile timestamps (s_memtime) of the 256 x
+// 256 kernels (~1.5 k cycles per stage, ~8.8 k per epilogue); the copy term
+// is what makes narrow TN tiles dearer than their MFMA count says (they run
+// the full panels' copies for fewer MFMAs).  Split contractions add the
+// reduction launch: its planes read and its output written at ~5 TB/s (2439
+// bytes per cycle at ~2.05 GHz), plus ~2 us for the launch.  Parts must hold
 // whole 32-deep stages.
-constexpr int64_t SPLIT_EPI = 45;
-constexpr int64_t REDUCE_LAUNCH = 50;
-constexpr int64_t BYTES_PER_UNIT = 203000;
+constexpr int64_t EPI_BF16 = 8800, EPI_F32 = 13200;
+constexpr int64_t REDUCE_LAUNCH = 4200;
+constexpr int64_t REDUCE_BYTES_PER_CYCLE = 2439;
+constexpr int64_t STAGE_FLOOR = 900;
+
+int64_t stage_cycles(bool tn, int mi, int ni) {
+  const int64_t kib = tn ? 32 : 4 * (mi + ni);
+  return std::max<int64_t>(64 * mi * ni + kib * 47 / 4 + 100, STAGE_FLOOR);
+}
+int64_t epi_cycles(bool f32, int mi, int ni) { return (f32 ? EPI_F32 : EPI_BF16) * mi * ni / 16; }
 
 size_t split_bytes(const Problem& P, int ks) {
   return ks > 1 ? ((size_t)ks * (size_t)P.M * (size_t)P.N * 4 + 255) / 256 * 256 : 0;
@@ -1681,10 +1698,11 @@ int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1, i
     return -1;
   const int64_t s0 = tile_stages(L.p[0]), s1 = tile_stages(L.p[1]);
   const int64_t n0 = tiles_of(L.p[0], 4, 4), n1 = tiles_of(L.p[1], 4, 4);
-  const int64_t apart = ((n0 + cus - 1) / cus * s0 + (n1 + cus - 1) / cus * s1) * 18;   // one after the other
+  const int64_t apart = (n0 + cus - 1) / cus * (s0 * stage_cycles(true, 4, 4) + epi_cycles(false, 4, 4)) +
+                        (n1 + cus - 1) / cus * (s1 * stage_cycles(false, 4, 4) + epi_cycles(false, 4, 4));
   const bool can_split = L.split_ws != nullptr && (reinterpret_cast<uintptr_t>(L.split_ws) & 15) == 0;
   int best = -1;
-  int64_t best_cost = apart;
+  int64_t best_cost = apart, best_tiles = 0;
   for (int k0 = 1; k0 <= 4; k0 *= 2) {
     for (int k1 = 1; k1 <= 4; k1 *= 2) {
       const bool split = k0 > 1 || k1 > 1;
@@ -1697,7 +1715,7 @@ int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1, i
       if (split) {
         for (int q = 0; q < 2; ++q) {
           const int k = q ? k1 : k0;
-          if (k > 1) red += (int64_t)((4 * k + 2) * L.p[q].M * L.p[q].N / BYTES_PER_UNIT);
+          if (k > 1) red += (int64_t)((4 * k + 2) * L.p[q].M * L.p[q].N / REDUCE_BYTES_PER_CYCLE);
         }
         red += REDUCE_LAUNCH;
       }
@@ -1706,18 +1724,19 @@ int dual_plan(const GemmLaunch& L, int cus, int& g0, int64_t& t0, int64_t& t1, i
         const int64_t b = tiles_of(L.p[1], kGeo[c][2], kGeo[c][3]) * k1;
         if (a + b >= INT_MAX) continue;
         int g = 1;
-        const int64_t e0 = k0 > 1 ? SPLIT_EPI * kGeo[c][0] * kGeo[c][1] / 16 : 0;
-        const int64_t e1 = k1 > 1 ? SPLIT_EPI * kGeo[c][2] * kGeo[c][3] / 16 : 0;
-        const int64_t w0 = ss0 * (kGeo[c][0] * kGeo[c][1] + 2) + e0, w1 = ss1 * (kGeo[c][2] * kGeo[c][3] + 2) + e1;
+        const int64_t w0 = ss0 * stage_cycles(true, kGeo[c][0], kGeo[c][1]) + epi_cycles(k0 > 1, kGeo[c][0], kGeo[c][1]);
+        const int64_t w1 = ss1 * stage_cycles(false, kGeo[c][2], kGeo[c][3]) + epi_cycles(k1 > 1, kGeo[c][2], kGeo[c][3]);
         const int64_t m = dual_split(a, w0, b, w1, cus, g) + red;
-        // equal cost: no split before a split, then the pairing with the larger tiles (the model's
-        // per-stage cost favours small tiles, which copy the full 256-wide MN-contiguous panels and
-        // measure slower)
-        const bool larger = best >= 0 && kGeo[c][0] * kGeo[c][1] + kGeo[c][2] * kGeo[c][3] >
-                                             kGeo[best][0] * kGeo[best][1] + kGeo[best][2] * kGeo[best][3];
-        const bool same_split = best < 0 || (ks0 == k0 && ks1 == k1);
-        if (m < best_cost || (m == best_cost && same_split && larger)) {
+        // Costs within 2% of each other are a tie (the model's resolution: it puts 128 x 128
+        // weight-gradient tiles beside 256 x 256 level with 128 x 192 beside 256 x 192 for the
+        // attention output projection's backward, which measure 106 and 97 us); a tie goes to
+        // the plan with fewer tiles.
+        bool take = m < best_cost;
+        if (best >= 0 && (m > best_cost ? m - best_cost : best_cost - m) * 50 <= best_cost)
+          take = a + b < best_tiles || (a + b == best_tiles && m < best_cost);
+        if (take) {
           best_cost = m;
+          best_tiles = a + b;
           best = c;
           g0 = g;
           t0 = a;
@@ -1758,8 +1777,8 @@ hipError_t launch_gemm_bf16(GemmLaunch& L, hipStream_t s) {
   // quarter of the CU-time idle); 192 x 192 beside 128 x 192 (for a narrow
   // 512 x 4096 weight gradient over 8192 tokens: 66 tiles instead of 32).
   // Tiles may overhang the outputs (masked stores; N a multiple of 8).  A
-  // tile's cost is its stages times (MFMA blocks + 2), as for one-problem
-  // launches.  (128 x 256 input-gradient tiles beside 192 x 256 balance the
+  // tile's cost is its stages' cycles plus its epilogue's (the cycle model
+  // above).  (128 x 256 input-gradient tiles beside 192 x 256 balance the
   // first case too but ran slower: a stage's barrier and copies then serve
   // half the MFMAs.)
   {

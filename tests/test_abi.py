@@ -174,11 +174,11 @@ def test_row_bwd_plan(lib):
     assert tp.tp_row_bwd_plan(768, 768, 8192, 256) == 0      # 256x256 + 256x256
     assert tp.tp_row_bwd_plan(512, 512, 8192, 256) == 1
     assert tp.tp_row_bwd_plan(512, 768, 256, 256) == 2       # 192x192 + 128x192
-    assert tp.tp_row_bwd_plan(2048, 768, 1024, 256) == 3     # 128x128 + 128x192
+    assert tp.tp_row_bwd_plan(768, 512, 512, 256) == 3       # 128x128 + 128x192
     assert tp.tp_row_bwd_plan(1536, 512, 4096, 256) == 4     # 128x128 + 256x256
-    assert tp.tp_row_bwd_plan(8192, 4096, 512, 256) == 5     # the attention output projection: 128x192 + 256x192
-    assert tp.tp_row_bwd_plan(8192, 768, 4096, 256) == 5     # the QKV projection's backward (same structure)
-    assert tp.tp_row_bwd_plan(256, 256, 128, 256) == 6       # 128x192 + 128x192
+    assert tp.tp_row_bwd_plan(8192, 4096, 512, 256) == 5     # the attention output projection, without scratch: 128x192 + 256x192
+    assert tp.tp_row_bwd_plan(8192, 768, 4096, 256) == 5     # the QKV projection's backward, without scratch
+    assert tp.tp_row_bwd_plan(512, 512, 256, 256) == 6       # 128x192 + 128x192
     assert tp.tp_row_bwd_plan(4096, 8192, 8192, 256) == -1   # separate launches
     assert tp.tp_row_bwd_plan(8192, 4096, 1536, 100) == -1   # CUs not a multiple of 8: no shared launch
     assert tp.tp_row_bwd_plan(0, 1, 1, 256) == -2 and tp.tp_row_bwd_plan(1, 1, 1, 0) == -2
@@ -196,10 +196,13 @@ def test_row_bwd_split_plan(lib):
     assert tp.tp_row_bwd_workspace_bytes_split(BF, 8192, 4096, 512, 256) == base + need
     assert tp.tp_row_bwd_plan_split(8192, 4096, 512, 256, need) == (0, 4, 2)
     assert tp.tp_row_bwd_plan_split(8192, 4096, 512, 256, need - 1)[1:] != (4, 2)   # does not fit: another plan
-    # the MLP shard step and the QKV projection's backward do not split
+    # the MLP shard step does not split
     assert tp.tp_row_bwd_workspace_bytes_split(BF, 8192, 4096, 1536, 256) == base
     assert tp.tp_row_bwd_plan_split(8192, 4096, 1536, 256, 1 << 40) == (1, 1, 1)
-    assert tp.tp_row_bwd_plan_split(8192, 768, 4096, 256, 1 << 40) == (5, 1, 1)
+    # the QKV projection's backward: 256x256 tiles, dW [4096, 768] over 8192 tokens in 2 parts
+    assert tp.tp_row_bwd_plan_split(8192, 768, 4096, 256, 1 << 40) == (0, 2, 1)
+    qkv = tp.tp_column_bwd_workspace_bytes(BF, tp.TP_ACT_NONE, 8192, 768, 0)
+    assert tp.tp_column_bwd_workspace_bytes_split(BF, tp.TP_ACT_NONE, 8192, 768, 4096, 0, 256) == qkv + 2 * 4096 * 768 * 4
     col = tp.tp_column_bwd_workspace_bytes(BF, tp.TP_ACT_NONE, 8192, 4096, 1)
     assert tp.tp_column_bwd_workspace_bytes_split(BF, tp.TP_ACT_NONE, 8192, 4096, 512, 1, 256) == col + need
     # only the activation-free bf16 backward runs the pair as one launch

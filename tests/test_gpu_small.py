@@ -148,8 +148,8 @@ def test_row_fwd_and_bwd_ragged(dtype, shape):
 # Whole tiles only (the persistent whole-tile kernels; for the row backward,
 # its two GEMMs share one launch).  On 256 CUs the row backward takes 192 x
 # 192 weight-gradient tiles beside 128 x 192 input-gradient tiles for the
-# first shape, 128 x 128 beside 256 x 256 for the second and 128 x 128 beside
-# 128 x 192 for the third (tp_row_bwd_plan); test_row_bwd_whole_matrix_pairings
+# first shape and 128 x 128 beside 256 x 256 for the second and third
+# (tp_row_bwd_plan); test_row_bwd_whole_matrix_pairings
 # asserts each pairing.
 TILE_SHAPES = [(512, 256, 768), (768, 512, 256), (2048, 1024, 768)]
 
@@ -231,13 +231,13 @@ def test_row_bwd_whole_tiles(shape):
 # on 256 CUs: (768, 8192, 768) takes 256 x 256 tiles for both GEMMs,
 # (512, 8192, 512) 192 x 256 weight-gradient tiles beside 256 x 192
 # input-gradient tiles (the pairing of the MLP shard step's row backward),
-# (512, 256, 768) 192 x 192 beside 128 x 192, (2048, 1024, 768) 128 x 128
+# (512, 256, 768) 192 x 192 beside 128 x 192, (768, 512, 512) 128 x 128
 # beside 128 x 192, (1536, 4096, 512) 128 x 128 beside 256 x 256,
 # (1024, 4096, 512) 128 x 192 beside 256 x 192 (the pairing of the attention
-# projections' backwards), (256, 128, 256) 128 x 192 beside 128 x 192.
+# projections' backwards), (512, 256, 512) 128 x 192 beside 128 x 192.
 @pytest.mark.parametrize("shape,pairing", [((768, 8192, 768), 0), ((512, 8192, 512), 1), ((512, 256, 768), 2),
-                                           ((2048, 1024, 768), 3), ((1536, 4096, 512), 4), ((1024, 4096, 512), 5),
-                                           ((256, 128, 256), 6)])
+                                           ((768, 512, 512), 3), ((1536, 4096, 512), 4), ((1024, 4096, 512), 5),
+                                           ((512, 256, 512), 6)])
 def test_row_bwd_whole_matrix_pairings(shape, pairing):
     M, N, K = shape
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -258,9 +258,11 @@ def test_row_bwd_whole_matrix_pairings(shape, pairing):
 # schedule may cut either product's contraction into parts (fp32 partial planes, then a
 # reduction launch).  Shapes in this file's order (X_i [M, N], B_i [N, K], dZ [M, K]); on 256
 # CUs the planner cuts (ks_dB, ks_dX) as listed: the weight gradient only, the input gradient
-# only, both; (1000, 520, 136) has tiles overhanging both outputs.
-SPLIT_CASES = [((512, 128, 128), (4, 1)), ((512, 128, 1536), (1, 4)), ((512, 128, 512), (4, 4)),
-               ((8192, 512, 4096), None), ((1000, 520, 136), None)]
+# only, both, in 2 or 4 parts; (8192, 512, 4096) is the attention output projection's backward;
+# (1000, 520, 136) has tiles overhanging both outputs.
+SPLIT_CASES = [((512, 128, 128), (4, 1)), ((128, 128, 1024), (1, 4)), ((512, 128, 512), (4, 4)),
+               ((512, 768, 256), (2, 1)), ((512, 1024, 768), (1, 2)), ((1024, 768, 1024), (2, 2)),
+               ((8192, 512, 4096), (4, 2)), ((1000, 520, 136), None)]
 
 
 @pytest.mark.parametrize("shape,parts", SPLIT_CASES)
