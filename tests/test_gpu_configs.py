@@ -171,8 +171,8 @@ def test_c3_attention_projections_sampled():
 
 def test_c3_attention_projection_backwards_split_sampled():
     # The backward calls as the bench makes them: with the workspace of their split-contraction
-    # schedules (on 256 CUs the W_O backward cuts dW's 8192-token contraction into 4 parts and dX's
-    # 4096 into 2, 256 x 256 tiles; the QKV backward keeps its unsplit pairing).
+    # schedules (on 256 CUs, 256 x 256 tiles: the W_O backward cuts dW's 8192-token contraction into
+    # 4 parts and dX's 4096 into 2; the QKV backward cuts dW's 8192-token contraction into 2).
     cfg = syn.C3
     d = syn.attn_proj_inputs(cfg)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -181,6 +181,8 @@ def test_c3_attention_projection_backwards_split_sampled():
         need = tp.tp_row_bwd_workspace_bytes_split(tp.TP_BF16, M, H, Na, cus) - tp.tp_row_bwd_workspace_bytes(
             tp.TP_BF16, M, H)
         assert tp.tp_row_bwd_plan_split(M, H, Na, cus, need) == (0, 4, 2)
+        Nq = d["Wqkv"].shape[1]   # the column backward's pair has the row backward's structure
+        assert tp.tp_row_bwd_plan_split(M, Nq, H, cus, 1 << 40) == (0, 2, 1)
     dAttn, dWo, _ = ops.row_bwd(dev(d["dZ"]), dev(d["attn"]), dev(d["Wo"]), split=True)
     dX, dWqkv, _, _, _ = ops.column_bwd(dev(d["dQKV"]), dev(d["X"]), dev(d["Wqkv"]), act="none", split=True)
     torch.cuda.synchronize()
