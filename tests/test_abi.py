@@ -214,6 +214,30 @@ def test_row_bwd_split_plan(lib):
     assert tp.tp_row_bwd_plan_split(8192, 4096, 512, 0, need) == (-2, 1, 1)
 
 
+def test_row_bwd_split_workspace_matches_plan(lib):
+    # Over a grid of shapes: the workspace that tp_row_bwd_workspace_bytes_split reports holds exactly
+    # the planes of the plan taken with unlimited scratch (ks * rows * cols fp32 per split product,
+    # 256-byte rounded), that plan is the one taken with just that much, and a plan never splits a
+    # contraction into parts that are not whole 32-deep stages.
+    BF = tp.TP_BF16
+    dims = [128, 384, 768, 1536, 4096, 8192]
+    seen = set()
+    for M in dims:
+        for N in dims:
+            for K in dims:
+                base = tp.tp_row_bwd_workspace_bytes(BF, M, N)
+                extra = tp.tp_row_bwd_workspace_bytes_split(BF, M, N, K, 256) - base
+                plan, k0, k1 = tp.tp_row_bwd_plan_split(M, N, K, 256, 1 << 50)
+                planes = lambda ks, r, c: 0 if ks == 1 else (ks * r * c * 4 + 255) // 256 * 256
+                assert extra == planes(k0, K, N) + planes(k1, M, K), (M, N, K, plan, k0, k1)
+                assert tp.tp_row_bwd_plan_split(M, N, K, 256, extra) == (plan, k0, k1)
+                assert M % (32 * k0) == 0 and N % (32 * k1) == 0
+                if plan == -1:
+                    assert (k0, k1) == (1, 1)
+                seen.add((k0 > 1, k1 > 1))
+    assert seen == {(False, False), (True, False), (False, True), (True, True)}
+
+
 def test_ce_combine_validation(lib):
     def call(R=8, M=64, ms=P, ss=P, ts=P, stride=64, lse=P, tgt=P, loss=P):
         return _rc("tp_vocab_ce_combine", R, M, ms, ss, ts, stride, lse, tgt, loss, None)
