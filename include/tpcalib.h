@@ -2,7 +2,7 @@
  * tpcalib.h -- C ABI of libtpcalib: a measurement helper, not part of the
  * method.  It measures the bf16 MFMA rate a gfx950 GPU sustains when nothing
  * but matrix instructions run, which is the practical ceiling the GEMM
- * kernels of libtpshard are judged against (the nominal peak assumes the
+ * kernels of libtpshard are measured against (the nominal peak assumes the
  * 2.4 GHz clock at every MFMA density; under a board power limit the clock
  * drops with the power the matrix cores draw, which depends on the data).
  */
